@@ -1,0 +1,195 @@
+"""Python binding of libdomino.so, the Domino draft-head hot path for gfx950.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Tensors are torch tensors on the GPU (torch supplies device memory
+and streams); the functions below pass their raw pointers through the C ABI
+declared in include/domino.h, under the same names.
+
+Importing this package does not touch the GPU.  Loading the library fails
+loudly when it has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdomino.so")
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+STATUS_FINE, STATUS_BAD_FIRST_TOKEN, STATUS_TIMEOUT = 0, 1, 2
+
+EXPORTS = ("domino_version", "domino_last_error", "domino_base_logits", "domino_chain_workspace_size",
+           "domino_draft_chain", "domino_set_chain_mode")
+
+
+class DominoError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"domino status {status}: {message}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("hidden", "vocab", "gru_hidden", "rank", "block", "dtype")]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("lm_head", "embed", "w_ih", "w_hh", "b_ih", "b_hh", "w1", "b1", "w2", "b2")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build(); "
+                               "the draft head has no non-HIP path")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.domino_version.restype = ctypes.c_char_p
+        L.domino_version.argtypes = []
+        L.domino_last_error.restype = ctypes.c_char_p
+        L.domino_last_error.argtypes = []
+        L.domino_base_logits.restype = ctypes.c_int
+        L.domino_base_logits.argtypes = [P, P, P, i32, P, P]
+        L.domino_chain_workspace_size.restype = sz
+        L.domino_chain_workspace_size.argtypes = [P, i32]
+        L.domino_draft_chain.restype = ctypes.c_int
+        L.domino_draft_chain.argtypes = [P, P, P, P, P, i32, P, P, P, sz, P]
+        L.domino_set_chain_mode.restype = i32
+        L.domino_set_chain_mode.argtypes = [i32]
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != OK:
+        raise DominoError(status, lib().domino_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr()) if hasattr(t, "data_ptr") else ctypes.c_void_p(t)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def version() -> str:
+    return lib().domino_version().decode()
+
+
+def last_error() -> str:
+    return lib().domino_last_error().decode()
+
+
+def set_chain_mode(mode: int) -> int:
+    prev = lib().domino_set_chain_mode(int(mode))
+    if prev < 0:
+        raise ValueError(f"chain mode {mode}")
+    return prev
+
+
+def make_dims(hidden, vocab, gru_hidden, rank, block, dtype) -> Dims:
+    return Dims(hidden, vocab, gru_hidden, rank, block, {"f32": F32, "bf16": BF16}.get(dtype, dtype))
+
+
+def make_weights(t: dict) -> Weights:
+    """Weights struct from a dict of device tensors (missing biases -> NULL)."""
+    names = [f for f, _ in Weights._fields_]
+    return Weights(**{k: (t[k].data_ptr() if t.get(k) is not None else None) for k in names})
+
+
+def domino_base_logits(dims: Dims, weights: Weights, H, batch: int, base_logits, stream=None):
+    _check(lib().domino_base_logits(ctypes.byref(dims), ctypes.byref(weights), _ptr(H), int(batch),
+                                    _ptr(base_logits), _stream(stream)))
+
+
+def domino_chain_workspace_size(dims: Dims, batch: int) -> int:
+    return int(lib().domino_chain_workspace_size(ctypes.byref(dims), int(batch)))
+
+
+def domino_draft_chain(dims: Dims, weights: Weights, H, base_logits, first_tokens, batch: int, out_tokens,
+                       out_logits, workspace, workspace_bytes: int, stream=None):
+    _check(lib().domino_draft_chain(ctypes.byref(dims), ctypes.byref(weights), _ptr(H), _ptr(base_logits),
+                                    _ptr(first_tokens), int(batch), _ptr(out_tokens), _ptr(out_logits),
+                                    _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+class DraftHead:
+    """Device-resident weights plus the three calls, for tests and the bench.
+
+    `weights` holds host arrays as produced by synth.make_weights (bf16 as
+    uint16 bit patterns).  Uploading them is the only work done here.
+    """
+
+    def __init__(self, hidden, vocab, gru_hidden, rank, block, dtype, weights: dict, device="cuda:0"):
+        import numpy as np
+        import torch
+        self.device = torch.device(device)
+        self.dtype = dtype
+        self.dims = make_dims(hidden, vocab, gru_hidden, rank, block, dtype)
+        self.tensors = {}
+        for k, a in weights.items():
+            if a is None:
+                continue
+            if a.dtype == np.uint16:
+                t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+            else:
+                t = torch.from_numpy(np.ascontiguousarray(a))
+            self.tensors[k] = t.to(self.device)
+        self.weights = make_weights(self.tensors)
+
+    @classmethod
+    def from_config(cls, cfg, weights, device="cuda:0", block=None):
+        return cls(cfg.hidden, cfg.vocab, cfg.gru_hidden, cfg.rank, cfg.block if block is None else block,
+                   cfg.dtype, weights, device)
+
+    def upload(self, a):
+        import numpy as np
+        import torch
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(self.device)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(self.device)
+
+    def base_logits(self, H, out=None, stream=None):
+        import torch
+        B = H.shape[0]
+        if out is None:
+            out = torch.empty((B, self.dims.block, self.dims.vocab), dtype=torch.float32, device=self.device)
+        domino_base_logits(self.dims, self.weights, H, B, out, stream)
+        return out
+
+    def workspace(self, batch):
+        import torch
+        n = domino_chain_workspace_size(self.dims, batch)
+        return torch.zeros(max(n, 16), dtype=torch.uint8, device=self.device)
+
+    def draft_chain(self, H, base_logits, first_tokens, want_logits=True, out_tokens=None, out_logits=None,
+                    workspace=None, stream=None):
+        import torch
+        B = H.shape[0]
+        if out_tokens is None:
+            out_tokens = torch.empty((B, self.dims.block), dtype=torch.int32, device=self.device)
+        if want_logits and out_logits is None:
+            out_logits = torch.empty((B, self.dims.block, self.dims.vocab), dtype=torch.float32, device=self.device)
+        if workspace is None:
+            workspace = self.workspace(B)
+        domino_draft_chain(self.dims, self.weights, H, base_logits, first_tokens, B, out_tokens,
+                           out_logits if want_logits else None, workspace, workspace.numel(), stream)
+        return out_tokens, (out_logits if want_logits else None), workspace
+
+    @staticmethod
+    def device_status(workspace) -> int:
+        """The device-side status word at offset 0 of a chain workspace (synchronises)."""
+        return int(workspace[:4].view(__import__("torch").int32).item())

@@ -1,0 +1,185 @@
+// C ABI of the draft-head library: argument checks, workspace carving and
+// kernel dispatch.  Nothing here computes model values; every arithmetic
+// step runs in the gfx950 kernels of gemm.hip and chain.hip.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/domino.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+int g_chain_mode = 0;
+
+domino_status fail(domino_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+domino_status fail(domino_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return s;
+}
+
+domino_status ok() {
+  g_error.clear();
+  return DOMINO_OK;
+}
+
+domino_status device_fail(hipError_t e, const char* what) {
+  return fail(DOMINO_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE_PTR(p, name)                                                                   \
+  do {                                                                                         \
+    if (!(p)) return fail(DOMINO_ERR_INVALID_ARGUMENT, "%s is NULL", name);                    \
+    if (!aligned16(p)) return fail(DOMINO_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define OPTIONAL_PTR(p, name)                                                                  \
+  do {                                                                                         \
+    if ((p) && !aligned16(p)) return fail(DOMINO_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+domino_status check_dims(const domino_dims* d) {
+  if (!d) return fail(DOMINO_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (d->dtype != DOMINO_F32 && d->dtype != DOMINO_BF16)
+    return fail(DOMINO_ERR_INVALID_ARGUMENT, "dims.dtype %d is neither DOMINO_F32 nor DOMINO_BF16", d->dtype);
+  if (d->hidden <= 0 || d->hidden % 8)
+    return fail(DOMINO_ERR_INVALID_ARGUMENT, "dims.hidden %d must be a positive multiple of 8", d->hidden);
+  if (d->gru_hidden <= 0 || d->gru_hidden % 8)
+    return fail(DOMINO_ERR_INVALID_ARGUMENT, "dims.gru_hidden %d must be a positive multiple of 8", d->gru_hidden);
+  if (d->rank <= 0 || d->rank % 8)
+    return fail(DOMINO_ERR_INVALID_ARGUMENT, "dims.rank %d must be a positive multiple of 8", d->rank);
+  if (d->vocab <= 0) return fail(DOMINO_ERR_INVALID_ARGUMENT, "dims.vocab %d must be positive", d->vocab);
+  if (d->block <= 0 || d->block > 64)
+    return fail(DOMINO_ERR_INVALID_ARGUMENT, "dims.block %d must be in [1, 64]", d->block);
+  if (d->rank > 256) return fail(DOMINO_ERR_UNSUPPORTED, "dims.rank %d exceeds 256", d->rank);
+  if ((int64_t)d->hidden + d->gru_hidden > (1 << 30) || (int64_t)d->vocab * 16 > INT32_MAX)
+    return fail(DOMINO_ERR_UNSUPPORTED, "dimensions too large");
+  return DOMINO_OK;
+}
+
+size_t elem_size(const domino_dims* d) { return d->dtype == DOMINO_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char* domino_version(void) { return "domino-gfx950 0.1"; }
+
+const char* domino_last_error(void) { return g_error.c_str(); }
+
+int32_t domino_set_chain_mode(int32_t mode) {
+  if (mode != 0 && mode != 1) return -1;
+  const int32_t prev = g_chain_mode;
+  g_chain_mode = mode;
+  return prev;
+}
+
+domino_status domino_base_logits(const domino_dims* dims, const domino_weights* w, const void* H, int32_t batch,
+                                 float* base_logits, void* stream) {
+  domino_status st = check_dims(dims);
+  if (st != DOMINO_OK) return st;
+  if (!w) return fail(DOMINO_ERR_INVALID_ARGUMENT, "weights is NULL");
+  if (batch < 0) return fail(DOMINO_ERR_INVALID_ARGUMENT, "batch %d is negative", batch);
+  if (batch == 0) return ok();
+  REQUIRE_PTR(w->lm_head, "weights.lm_head");
+  REQUIRE_PTR(H, "H");
+  REQUIRE_PTR(base_logits, "base_logits");
+  if ((int64_t)batch * dims->block > INT32_MAX / 2) return fail(DOMINO_ERR_UNSUPPORTED, "batch too large");
+  const int M = batch * dims->block;
+  hipError_t e = dh::launch_gemm_nt(dims->dtype, H, dims->hidden, w->lm_head, dims->hidden, base_logits, dims->vocab,
+                                    M, dims->vocab, dims->hidden, true, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "base-logit GEMM launch");
+  return ok();
+}
+
+size_t domino_chain_workspace_size(const domino_dims* dims, int32_t batch) {
+  if (check_dims(dims) != DOMINO_OK || batch < 0) return 0;
+  const int group = batch < dh::kMaxChainGroup ? (batch > 0 ? batch : 1) : dh::kMaxChainGroup;
+  return dh::chain_layout(dims->hidden, dims->gru_hidden, dims->rank, dims->block, group).total;
+}
+
+domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* w, const void* H,
+                                 const float* base_logits, const int32_t* first_tokens, int32_t batch,
+                                 int32_t* out_tokens, float* out_logits, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  domino_status st = check_dims(dims);
+  if (st != DOMINO_OK) return st;
+  if (!w) return fail(DOMINO_ERR_INVALID_ARGUMENT, "weights is NULL");
+  if (batch < 0) return fail(DOMINO_ERR_INVALID_ARGUMENT, "batch %d is negative", batch);
+  if (batch == 0) return ok();
+  REQUIRE_PTR(w->embed, "weights.embed");
+  REQUIRE_PTR(w->w_ih, "weights.w_ih");
+  REQUIRE_PTR(w->w_hh, "weights.w_hh");
+  REQUIRE_PTR(w->w1, "weights.w1");
+  REQUIRE_PTR(w->w2, "weights.w2");
+  OPTIONAL_PTR(w->b_ih, "weights.b_ih");
+  OPTIONAL_PTR(w->b_hh, "weights.b_hh");
+  OPTIONAL_PTR(w->b1, "weights.b1");
+  OPTIONAL_PTR(w->b2, "weights.b2");
+  REQUIRE_PTR(H, "H");
+  REQUIRE_PTR(base_logits, "base_logits");
+  REQUIRE_PTR(first_tokens, "first_tokens");
+  REQUIRE_PTR(out_tokens, "out_tokens");
+  OPTIONAL_PTR(out_logits, "out_logits");
+  REQUIRE_PTR(workspace, "workspace");
+  const size_t need = domino_chain_workspace_size(dims, batch);
+  if (workspace_bytes < need)
+    return fail(DOMINO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes,
+                need);
+
+  const int d = dims->hidden, V = dims->vocab, Hs = dims->gru_hidden, r = dims->rank, P = dims->block;
+  const int group_max = batch < dh::kMaxChainGroup ? batch : dh::kMaxChainGroup;
+  const dh::ChainLayout L = dh::chain_layout(d, Hs, r, P, group_max);
+  char* ws = (char*)workspace;
+  const size_t es = elem_size(dims);
+  hipStream_t s = (hipStream_t)stream;
+
+  for (int g0 = 0; g0 < batch; g0 += dh::kMaxChainGroup) {
+    const int Bg = batch - g0 < dh::kMaxChainGroup ? batch - g0 : dh::kMaxChainGroup;
+    const char* Hg = (const char*)H + (size_t)g0 * P * d * es;
+    dh::ChainArgs a;
+    a.d = d;
+    a.V = V;
+    a.Hs = Hs;
+    a.r = r;
+    a.P = P;
+    a.B = Bg;
+    a.embed = w->embed;
+    a.w_ih = w->w_ih;
+    a.w_hh = w->w_hh;
+    a.w1 = w->w1;
+    a.w2 = w->w2;
+    a.b_ih = w->b_ih;
+    a.b_hh = w->b_hh;
+    a.b1 = w->b1;
+    a.b2 = w->b2;
+    a.Lb = base_logits + (size_t)g0 * P * V;
+    a.out_logits = out_logits ? out_logits + (size_t)g0 * P * V : nullptr;
+    a.out_tokens = out_tokens + (size_t)g0 * P;
+    a.t0 = first_tokens + g0;
+    a.zh = (const float*)(ws + L.zh);
+    a.h = (float*)(ws + L.h);
+    a.act = ws + L.act;
+    a.keys = (uint64_t*)(ws + L.keys);
+    a.counters = (uint32_t*)(ws + L.counters);
+    a.status = (int32_t*)(ws + L.status);
+    // H half of the bottleneck for every position: zh[b][p][k] = sum_i H[b][p][i] W1[k][i]
+    hipError_t e = dh::launch_gemm_nt(dims->dtype, Hg, d, w->w1, d + Hs, (float*)(ws + L.zh), r, Bg * P, r, d, false, s);
+    if (e != hipSuccess) return device_fail(e, "bottleneck pre-GEMM launch");
+    e = dh::launch_chain(dims->dtype, a, g_chain_mode, g0 == 0, s);
+    if (e != hipSuccess) return device_fail(e, "chain launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

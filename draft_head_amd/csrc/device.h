@@ -1,0 +1,211 @@
+// Device-side building blocks shared by the gfx950 kernels of this library.
+//
+// Fragment convention (one 64-lane wavefront, MFMA 16x16 with a 32-deep k chunk):
+//   lane l supplies row (l % 16) of the left operand and column (l % 16) of
+//   the right operand, each as 8 consecutive k values starting at
+//   k0 + 8 * (l / 16).  Both operands use the same lane -> k map, so the
+//   instruction's internal k order does not matter.  The 16x16 fp32 result
+//   lands as: lane l holds column (l % 16), rows 4 * (l / 16) + 0..3.
+//
+// Storage types: bf16 (uint16_t bit patterns) or fp32.  bf16 x bf16
+// products are exact in fp32; fp32 activations (GRU state, bottleneck)
+// meet bf16 weights as a hi + lo pair of bf16 values (two MFMAs), which
+// keeps about 16 significant bits of the activation instead of 8.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dh {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct f32x8 {
+  float4 lo, hi;
+};
+
+struct bf16pair {
+  bf16x8 hi, lo;
+};
+
+// ---- scalar conversions ---------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even; inputs are finite
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---- fragment loads -----------------------------------------------------------
+__device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ f32x8 load8(const float* p) {
+  f32x8 r;
+  r.lo = reinterpret_cast<const float4*>(p)[0];
+  r.hi = reinterpret_cast<const float4*>(p)[1];
+  return r;
+}
+template <class W>
+struct frag;
+template <>
+struct frag<uint16_t> {
+  using type = bf16x8;
+};
+template <>
+struct frag<float> {
+  using type = f32x8;
+};
+template <class W>
+using frag_t = typename frag<W>::type;
+
+template <class W>
+__device__ __forceinline__ frag_t<W> zero8();
+template <>
+__device__ __forceinline__ bf16x8 zero8<uint16_t>() {
+  return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+}
+template <>
+__device__ __forceinline__ f32x8 zero8<float>() {
+  f32x8 r;
+  r.lo = make_float4(0.f, 0.f, 0.f, 0.f);
+  r.hi = r.lo;
+  return r;
+}
+
+// 8 consecutive elements, or zeros when `ok` is false (no memory access then)
+template <class W>
+__device__ __forceinline__ frag_t<W> load8_or_zero(const W* p, bool ok) {
+  return ok ? load8(p) : zero8<W>();
+}
+
+// ---- fp32 activations as right-hand operands ---------------------------------
+__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
+
+__device__ __forceinline__ bf16pair split_hi_lo(const float4& x0, const float4& x1) {
+  const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  uint16_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = f2bf(v[i]);
+    l[i] = f2bf(v[i] - bf2f(h[i]));  // exact difference, then rounded
+  }
+  bf16pair r;
+  r.hi = __builtin_bit_cast(bf16x8, make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])));
+  r.lo = __builtin_bit_cast(bf16x8, make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])));
+  return r;
+}
+
+// activation fragment type matching weight storage W
+template <class W>
+struct act;
+template <>
+struct act<uint16_t> {
+  using type = bf16pair;
+  __device__ static __forceinline__ type zero() {
+    bf16pair r;
+    r.hi = zero8<uint16_t>();
+    r.lo = r.hi;
+    return r;
+  }
+  __device__ static __forceinline__ type from_f32(const float* p) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+    return split_hi_lo(q[0], q[1]);
+  }
+};
+template <>
+struct act<float> {
+  using type = f32x8;
+  __device__ static __forceinline__ type zero() { return zero8<float>(); }
+  __device__ static __forceinline__ type from_f32(const float* p) { return load8(p); }
+};
+
+template <class W>
+__device__ __forceinline__ typename act<W>::type act_or_zero(const float* p, bool ok) {
+  return ok ? act<W>::from_f32(p) : act<W>::zero();
+}
+
+// ---- MFMA on one 32-deep k chunk ------------------------------------------------
+__device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16pair& b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b.lo, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b.hi, c, 0, 0, 0);
+}
+// fp32: eight 16x16x4 instructions; instruction i takes element i of every lane's 8
+__device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, c, 0, 0, 0);
+}
+
+// ---- greedy argmax as one 64-bit max ------------------------------------------
+// key = (order-preserving bits of the value) << 32 | (0xFFFFFFFF - index):
+// the largest key has the largest value and, among equal values, the lowest
+// index.  -0.0 is folded to +0.0 first.  Key 0 is below every real key.
+__device__ __forceinline__ uint64_t amax_key(float v, uint32_t idx) {
+  if (v == 0.0f) v = 0.0f;
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+__device__ __forceinline__ int32_t amax_index(uint64_t key) { return (int32_t)(0xFFFFFFFFu - (uint32_t)key); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// ---- bounded waits between workgroups of one persistent launch ------------------
+// Every wait ends: on success, on an error already flagged by another
+// workgroup, or after kWaitTicks of the 100 MHz constant clock (then the
+// status word is set to 2 and the caller leaves the kernel).
+constexpr uint64_t kWaitTicks = 200000000ull;  // 2 s
+constexpr int kStatusTimeout = 2;
+
+__device__ __forceinline__ uint32_t ld_acquire_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// whole workgroup calls; returns false when the kernel must stop
+__device__ __forceinline__ bool wg_wait_geq(const uint32_t* counter, uint32_t target, int32_t* status) {
+  __shared__ int ok_flag;
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    const uint64_t t0 = wall_clock64();
+    while (ld_acquire_relaxed(counter) < target) {
+      if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kStatusTimeout) {
+        ok = 0;
+        break;
+      }
+      if (wall_clock64() - t0 > kWaitTicks) {
+        __hip_atomic_store(status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    ok_flag = ok;
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return ok_flag != 0;
+}
+
+// whole workgroup calls after its last global store of a phase
+__device__ __forceinline__ void wg_arrive(uint32_t* counter) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace dh

@@ -1,0 +1,199 @@
+// "NT" matrix products on the MFMA matrix cores:
+//   C[m][n] = sum_k A[m][k] * B[n][k]      (fp32 accumulate, fp32 out)
+// A is the activation side (rows = draft-block positions), B the weight side
+// (rows = vocabulary entries or bottleneck units); both are k-contiguous.
+// Used for the block-parallel base logits Lb = H W_lm^T through the frozen LM
+// head (Dutch Domino summary, "Methodologie", part 1; 163.com explainer,
+// section 3) and for the H-half of the bottleneck projection, W1[:, :d] H_i.
+//
+// Two kernels:
+//  * gemm_stream: every wave owns 16 columns (16 weight rows) and streams
+//    their full k range from HBM straight into MFMA fragments; each
+//    workgroup row covers MT 16-row tiles of A.  For few activation rows
+//    the product is bound by reading B once, so nothing is staged in LDS.
+//  * gemm_tiled: 128x128 output tiles, k staged through LDS in 64-deep
+//    slabs (double buffered), 2x2 waves of 64x64, bf16 only.  Tiles that
+//    share B columns are issued to the same XCD so they meet in its L2.
+#include "device.h"
+#include "internal.h"
+
+namespace dh {
+
+template <class W, int MT>
+__global__ __launch_bounds__(256) void gemm_stream(const W* __restrict__ A, int lda, const W* __restrict__ B, int ldb,
+                                                   float* __restrict__ C, int ldc, int M, int N, int K) {
+  constexpr int U = sizeof(W) == 2 ? 8 : 4;  // k chunks in flight per wave
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * 4 + wv) * 16;
+  if (n0 >= N) return;
+  const int row = lane & 15, kg = lane >> 4;
+  const int m_base = blockIdx.y * MT * 16;
+  // rows past the end read a valid row; their results are never stored
+  const W* brow = B + (size_t)min(n0 + row, N - 1) * ldb + kg * 8;
+  const W* arow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) arow[t] = A + (size_t)min(m_base + t * 16 + row, M - 1) * lda + kg * 8;
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nck = (K + 31) / 32;
+  for (int c0 = 0; c0 < nck; c0 += U) {
+    frag_t<W> bf[U];
+    frag_t<W> af[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (c0 + u) * 32;
+      const bool ok = k + kg * 8 < K;
+      bf[u] = load8_or_zero(brow + k, ok);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) af[u][t] = load8_or_zero(arow[t] + k, ok);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[t] = mma(af[u][t], bf[u], acc[t]);
+  }
+
+  const int n = n0 + row;
+  if (n < N) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m_base + t * 16 + kg * 4 + i;
+        if (m < M) C[(size_t)m * ldc + n] = acc[t][i];
+      }
+  }
+}
+
+constexpr int TBM = 128, TBN = 128, TBK = 64, TPAD = 8;
+
+__global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A, int lda,
+                                                  const uint16_t* __restrict__ B, int ldb, float* __restrict__ C,
+                                                  int ldc, int M, int N, int K, int m_tiles, int n_tiles,
+                                                  int per_xcd) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][TBM][TBK + TPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][TBN][TBK + TPAD];
+
+  // blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
+  // run of tiles, m fastest, so the m tiles of one n tile share an L2
+  const int bid = blockIdx.x;
+  const int t = (bid & 7) * per_xcd + (bid >> 3);
+  if (t >= m_tiles * n_tiles) return;
+  const int mt = t % m_tiles, nt = t / m_tiles;
+  const int m0 = mt * TBM, n0 = nt * TBN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int row = lane & 15, kg = lane >> 4;
+
+  // global -> LDS assignment: 1024 16-byte pieces per operand tile, 4 per thread
+  int g_row[4], g_col[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + 256 * i;
+    g_row[i] = q >> 3;
+    g_col[i] = (q & 7) * 8;
+  }
+  const uint16_t* a_src[4];
+  const uint16_t* b_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a_src[i] = A + (size_t)min(m0 + g_row[i], M - 1) * lda + g_col[i];
+    b_src[i] = B + (size_t)min(n0 + g_row[i], N - 1) * ldb + g_col[i];
+  }
+
+  uint4 ra[4], rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = k0 + g_col[i] < K;
+      ra[i] = ok ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
+      rb[i] = ok ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4*>(&sA[buf][g_row[i]][g_col[i]]) = ra[i];
+      *reinterpret_cast<uint4*>(&sB[buf][g_row[i]][g_col[i]]) = rb[i];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (K + TBK - 1) / TBK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nk) gload((ks + 1) * TBK);
+#pragma unroll
+    for (int kc = 0; kc < TBK / 32; ++kc) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = load8(&sA[buf][wm * 64 + i * 16 + row][kc * 32 + kg * 8]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = load8(&sB[buf][wn * 64 + j * 16 + row][kc * 32 + kg * 8]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma(af[i], bfr[j], acc[i][j]);
+    }
+    if (ks + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * 64 + j * 16 + row;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm * 64 + i * 16 + kg * 4 + e;
+        if (m < M) C[(size_t)m * ldc + n] = acc[i][j][e];
+      }
+  }
+}
+
+template <class W>
+static hipError_t launch_stream(const W* A, int lda, const W* B, int ldb, float* C, int ldc, int M, int N, int K,
+                                hipStream_t s) {
+  const int n_waves = (N + 15) / 16;
+  const int m_tiles = (M + 15) / 16;
+  const int mt = m_tiles >= 4 ? 4 : (m_tiles >= 2 ? 2 : 1);
+  dim3 grid((n_waves + 3) / 4, (m_tiles + mt - 1) / mt);
+  if (mt == 4)
+    hipLaunchKernelGGL((gemm_stream<W, 4>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K);
+  else if (mt == 2)
+    hipLaunchKernelGGL((gemm_stream<W, 2>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K);
+  else
+    hipLaunchKernelGGL((gemm_stream<W, 1>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int ldb, float* C, int ldc, int M, int N,
+                          int K, bool prefer_tiles, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (dtype == kF32)
+    return launch_stream((const float*)A, lda, (const float*)B, ldb, C, ldc, M, N, K, s);
+  if (!prefer_tiles || M <= 64)
+    return launch_stream((const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, M, N, K, s);
+  const int m_tiles = (M + TBM - 1) / TBM, n_tiles = (N + TBN - 1) / TBN;
+  const int total = m_tiles * n_tiles;
+  const int per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL(gemm_tiled, dim3(per_xcd * 8), dim3(256), 0, s, (const uint16_t*)A, lda, (const uint16_t*)B,
+                     ldb, C, ldc, M, N, K, m_tiles, n_tiles, per_xcd);
+  return hipGetLastError();
+}
+
+}  // namespace dh

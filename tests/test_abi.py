@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_head_amd as dh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "domino.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(domino_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("domino_base_logits", "domino_draft_chain", "domino_chain_workspace_size", "domino_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dh.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(dh.EXPORTS) >= set(declared_functions())
+
+
+def test_version_and_empty_error():
+    assert dh.version().startswith("domino-gfx950")
+
+
+def _dims(**kw):
+    base = dict(hidden=2560, vocab=151936, gru_hidden=1024, rank=256, block=16, dtype="bf16")
+    base.update(kw)
+    return dh.make_dims(**base)
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation or is a no-op
+
+
+def _weights(**kw):
+    w = {k: FAKE for k in ("lm_head", "embed", "w_ih", "w_hh", "w1", "w2")}
+    w.update(kw)
+    return dh.Weights(**w)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(hidden=0), "hidden"), (dict(hidden=12), "hidden"), (dict(gru_hidden=-8), "gru_hidden"),
+    (dict(rank=7), "rank"), (dict(vocab=0), "vocab"), (dict(block=0), "block"), (dict(block=65), "block"),
+    (dict(dtype=5), "dtype"),
+])
+def test_bad_dims_rejected(kw, msg):
+    L = dh.lib()
+    st = L.domino_base_logits(ctypes.byref(_dims(**kw)), ctypes.byref(_weights()), FAKE, 1, FAKE, None)
+    assert st == dh.ERR_INVALID_ARGUMENT
+    assert msg in dh.last_error()
+
+
+def test_rank_above_256_unsupported():
+    L = dh.lib()
+    st = L.domino_base_logits(ctypes.byref(_dims(rank=264)), ctypes.byref(_weights()), FAKE, 1, FAKE, None)
+    assert st == dh.ERR_UNSUPPORTED
+
+
+def test_null_and_misaligned_pointers_rejected():
+    L = dh.lib()
+    d = _dims()
+    assert L.domino_base_logits(ctypes.byref(d), ctypes.byref(_weights()), None, 1, FAKE, None) == \
+        dh.ERR_INVALID_ARGUMENT
+    assert "H is NULL" in dh.last_error()
+    assert L.domino_base_logits(ctypes.byref(d), ctypes.byref(_weights(lm_head=FAKE + 8)), FAKE, 1, FAKE,
+                                None) == dh.ERR_INVALID_ARGUMENT
+    assert "aligned" in dh.last_error()
+    assert L.domino_base_logits(None, ctypes.byref(_weights()), FAKE, 1, FAKE, None) == dh.ERR_INVALID_ARGUMENT
+    assert L.domino_base_logits(ctypes.byref(d), None, FAKE, 1, FAKE, None) == dh.ERR_INVALID_ARGUMENT
+    ws = dh.domino_chain_workspace_size(d, 4)
+    # every call below is short of workspace or has one bad argument, so none reaches a launch
+    args = (ctypes.byref(d), ctypes.byref(_weights()), FAKE, FAKE, FAKE, 4, FAKE, None, FAKE, ws - 1, None)
+    assert L.domino_draft_chain(*args) == dh.ERR_WORKSPACE
+    for i, name in ((2, "H"), (3, "base_logits"), (4, "first_tokens"), (6, "out_tokens"), (8, "workspace")):
+        bad = list(args)
+        bad[i] = None
+        bad[9] = 1 << 40
+        assert L.domino_draft_chain(*bad) == dh.ERR_INVALID_ARGUMENT, name
+        assert name in dh.last_error()
+    bad = list(args)
+    bad[7], bad[9] = FAKE + 4, 1 << 40
+    assert L.domino_draft_chain(*bad) == dh.ERR_INVALID_ARGUMENT
+    assert "out_logits" in dh.last_error()
+    for wname in ("embed", "w_ih", "w_hh", "w1", "w2"):
+        bad = list(args)
+        bad[1] = ctypes.byref(_weights(**{wname: None}))
+        bad[9] = 1 << 40
+        assert L.domino_draft_chain(*bad) == dh.ERR_INVALID_ARGUMENT
+        assert wname in dh.last_error()
+
+
+def test_workspace_too_small():
+    L = dh.lib()
+    d = _dims()
+    need = dh.domino_chain_workspace_size(d, 8)
+    st = L.domino_draft_chain(ctypes.byref(d), ctypes.byref(_weights()), FAKE, FAKE, FAKE, 8, FAKE, None, FAKE,
+                              need - 1, None)
+    assert st == dh.ERR_WORKSPACE
+    assert str(need) in dh.last_error()
+
+
+def test_negative_and_zero_batch():
+    L = dh.lib()
+    d = _dims()
+    assert L.domino_base_logits(ctypes.byref(d), ctypes.byref(_weights()), FAKE, -1, FAKE, None) == \
+        dh.ERR_INVALID_ARGUMENT
+    # batch 0 is a no-op: returns OK without touching memory or the device
+    assert L.domino_base_logits(ctypes.byref(d), ctypes.byref(_weights()), None, 0, None, None) == dh.OK
+    assert L.domino_draft_chain(ctypes.byref(d), ctypes.byref(_weights()), None, None, None, 0, None, None, None, 0,
+                                None) == dh.OK
+
+
+def test_workspace_size_grows_then_saturates():
+    d = _dims()
+    s = [dh.domino_chain_workspace_size(d, b) for b in (1, 2, 16, 32, 33, 1000)]
+    assert s[0] < s[1] < s[2] < s[3]
+    assert s[3] == s[4] == s[5]  # sequences run in groups of at most 32
+    assert dh.domino_chain_workspace_size(_dims(hidden=3), 1) == 0
+
+
+def test_chain_mode_switch():
+    prev = dh.set_chain_mode(1)
+    assert dh.set_chain_mode(prev) == 1
+    with pytest.raises(ValueError):
+        dh.set_chain_mode(7)

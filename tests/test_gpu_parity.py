@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path through the C ABI against the oracle.
+
+Element-wise at sizes the oracle finishes in seconds (several tiles and a
+ragged tail in every dimension), and on sampled sequences / rows at the full
+Qwen3-4B / Qwen3-8B shapes, in the launch configuration the bench times.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import draft_head_amd as dh
+import oracle
+import synth
+from gpu_common import compare_chain, gemm_bound, say, weights_for
+from helpers import small_config, widen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    dh.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(params=[0, 1], ids=["persistent", "stepwise"])
+def chain_mode(request):
+    prev = dh.set_chain_mode(request.param)
+    yield request.param
+    dh.set_chain_mode(prev)
+
+
+@functools.lru_cache(maxsize=2)
+def device_head(cfg_key):
+    cfg = synth.CONFIGS[cfg_key]
+    return dh.DraftHead.from_config(cfg, weights_for(cfg_key))
+
+
+def _run(cfg, w, inp, want_logits=True, head=None):
+    head = head or dh.DraftHead.from_config(cfg, w)
+    H = head.upload(inp["H"])
+    t0 = head.upload(inp["t0"])
+    Lb = head.base_logits(H)
+    toks, L, ws = head.draft_chain(H, Lb, t0, want_logits=want_logits)
+    torch.cuda.synchronize()
+    status = dh.DraftHead.device_status(ws)
+    return head, Lb.cpu().numpy(), toks.cpu().numpy(), None if L is None else L.cpu().numpy(), status
+
+
+# ---- base logits ------------------------------------------------------------------
+def _check_gemm(g, H, Wlm, dtype, label):
+    Hd = widen(H, dtype).reshape(-1, H.shape[-1])
+    Wd = widen(Wlm, dtype)
+    exact = Hd @ Wd.T
+    bound = gemm_bound(Hd, Wd) + np.abs(exact) * 2.0 ** -24
+    err = np.abs(g.reshape(exact.shape).astype(np.float64) - exact)
+    assert np.all(err <= bound), f"{label}: worst excess {(err - bound).max():.3e}"
+
+
+def test_base_logits_tiny_f32():
+    cfg = synth.CONFIGS["tiny_f32"]
+    say("case tiny_f32 base logits")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    g = head.base_logits(head.upload(inp["H"])).cpu().numpy()
+    _check_gemm(g, inp["H"], w["lm_head"], "f32", "tiny_f32")
+    ref = oracle.Model.from_config(cfg, w).base_logits(inp["H"])
+    assert np.max(np.abs(g - ref) / np.maximum(np.abs(ref), 1)) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d,V,B,P", [(72, 1003, 3, 5), (136, 2051, 13, 16), (264, 1000, 5, 16), (40, 17, 1, 1)])
+def test_base_logits_ragged(dtype, d, V, B, P):
+    cfg = small_config(d=d, V=V, B=B, P=P, dtype=dtype)
+    say(f"case base logits ragged dtype={dtype} d={d} V={V} B={B} P={P}")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    g = head.base_logits(head.upload(inp["H"])).cpu().numpy()
+    _check_gemm(g, inp["H"], w["lm_head"], dtype, "ragged")
+
+
+@pytest.mark.parametrize("key,rows", [("qwen3_4b_b1", [(0, 0), (0, 15)]), ("qwen3_4b_b32", [(0, 0), (31, 9)]),
+                                      ("qwen3_8b_b16", [(0, 3), (15, 15)])])
+def test_base_logits_full_size_sampled(key, rows):
+    cfg = synth.CONFIGS[key]
+    say(f"case base logits full {key}")
+    head = device_head(key)
+    inp = synth.make_inputs(cfg)
+    g = head.base_logits(head.upload(inp["H"]))
+    torch.cuda.synchronize()
+    assert torch.isfinite(g).all().item()
+    w = weights_for(key)
+    for b, p in rows:
+        row = g[b, p].cpu().numpy()
+        _check_gemm(row[None], inp["H"][b, p][None], w["lm_head"], cfg.dtype, f"{key} row {(b, p)}")
+
+
+# ---- chain ---------------------------------------------------------------------------
+def test_chain_tiny_f32(chain_mode):
+    cfg = synth.CONFIGS["tiny_f32"]
+    say(f"case chain tiny_f32 mode={chain_mode}")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    _, Lb, toks, L, status = _run(cfg, w, inp)
+    assert status == 0
+    m = oracle.Model.from_config(cfg, w)
+    info = compare_chain(m, inp["H"], m.base_logits(inp["H"]), inp["t0"], toks, L, "tiny_f32")
+    say("  ", info)
+
+
+CHAIN_SHAPES = [
+    # d, V, Hs, r, P, B, dtype
+    (16, 37, 8, 8, 5, 2, "f32"),
+    (64, 1003, 40, 24, 7, 5, "bf16"),
+    (200, 2051, 64, 64, 16, 17, "bf16"),
+    (96, 4099, 128, 256, 16, 32, "bf16"),
+    (48, 515, 16, 16, 3, 40, "bf16"),   # two launches of <= 32 sequences
+    (64, 999, 32, 40, 16, 9, "f32"),
+    (32, 64, 8, 8, 1, 1, "bf16"),
+]
+
+
+@pytest.mark.parametrize("d,V,Hs,r,P,B,dtype", CHAIN_SHAPES)
+def test_chain_small_shapes(chain_mode, d, V, Hs, r, P, B, dtype):
+    cfg = small_config(d=d, V=V, Hs=Hs, r=r, P=P, B=B, dtype=dtype, biases=True)
+    say(f"case chain small mode={chain_mode} d={d} V={V} Hs={Hs} r={r} P={P} B={B} {dtype}")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    _, Lb, toks, L, status = _run(cfg, w, inp)
+    assert status == 0
+    m = oracle.Model.from_config(cfg, w)
+    info = compare_chain(m, inp["H"], m.base_logits(inp["H"]), inp["t0"], toks, L, "small")
+    say("  ", info)
+
+
+def test_chain_zero_correction_is_base_argmax(chain_mode):
+    cfg = small_config(d=64, V=2003, Hs=32, r=32, P=16, B=6, dtype="bf16", biases=False)
+    say(f"case chain zero correction mode={chain_mode}")
+    w = synth.make_weights(cfg)
+    w["w2"] = np.zeros_like(w["w2"])
+    inp = synth.make_inputs(cfg)
+    _, Lb, toks, L, status = _run(cfg, w, inp)
+    assert status == 0
+    assert np.array_equal(L, Lb)
+    assert np.array_equal(toks, np.argmax(Lb, axis=-1))
+
+
+def test_chain_deterministic_and_prefix_stable():
+    cfg = small_config(d=128, V=3001, Hs=64, r=64, P=16, B=7, dtype="bf16")
+    say("case chain determinism / prefix")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    head, Lb, t1, L1, s1 = _run(cfg, w, inp)
+    _, _, t2, L2, s2 = _run(cfg, w, inp, head=head)
+    assert s1 == s2 == 0
+    assert np.array_equal(t1, t2) and np.array_equal(L1, L2)
+    cfg8 = cfg.with_(block=8)
+    inp8 = {"H": np.ascontiguousarray(inp["H"][:, :8]), "t0": inp["t0"]}
+    _, _, t8, L8, s8 = _run(cfg8, w, inp8)
+    assert s8 == 0
+    assert np.array_equal(t8, t1[:, :8]) and np.array_equal(L8, L1[:, :8])
+
+
+def test_chain_modes_agree_bitwise():
+    cfg = small_config(d=96, V=1501, Hs=48, r=32, P=12, B=20, dtype="bf16")
+    say("case chain modes agree")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    prev = dh.set_chain_mode(0)
+    try:
+        head, _, t0_, L0, s0 = _run(cfg, w, inp)
+        dh.set_chain_mode(1)
+        _, _, t1_, L1, s1 = _run(cfg, w, inp, head=head)
+    finally:
+        dh.set_chain_mode(prev)
+    assert s0 == s1 == 0
+    assert np.array_equal(t0_, t1_) and np.array_equal(L0, L1)
+
+
+def test_chain_bad_first_token_flagged():
+    cfg = small_config(d=32, V=101, Hs=16, r=16, P=4, B=3, dtype="bf16")
+    say("case chain bad first token")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    inp["t0"] = np.array([5, cfg.vocab + 7, -3], np.int32)
+    _, _, toks, _, status = _run(cfg, w, inp, want_logits=False)
+    assert status == dh.STATUS_BAD_FIRST_TOKEN
+    assert toks.min() >= 0 and toks.max() < cfg.vocab
+
+
+def test_chain_in_place_logits_and_guard_bytes():
+    cfg = small_config(d=64, V=777, Hs=32, r=32, P=6, B=4, dtype="bf16")
+    say("case chain in place + guards")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    H = head.upload(inp["H"])
+    t0 = head.upload(inp["t0"])
+    B, P, V = cfg.batch, cfg.block, cfg.vocab
+    guard = 4096
+    lb_buf = torch.full((guard + B * P * V + guard,), 7.5, dtype=torch.float32, device=head.device)
+    tok_buf = torch.full((guard + B * P + guard,), -77, dtype=torch.int32, device=head.device)
+    Lb = lb_buf[guard:guard + B * P * V].view(B, P, V)
+    toks = tok_buf[guard:guard + B * P].view(B, P)
+    head.base_logits(H, out=Lb)
+    Lb_copy = Lb.clone()
+    ws = head.workspace(B)
+    toks_ref, L_ref, _ = head.draft_chain(H, Lb_copy, t0)
+    head.draft_chain(H, Lb, t0, out_tokens=toks, out_logits=Lb, workspace=ws)  # in place
+    torch.cuda.synchronize()
+    assert torch.equal(Lb, L_ref) and torch.equal(toks, toks_ref)
+    assert torch.all(lb_buf[:guard] == 7.5) and torch.all(lb_buf[-guard:] == 7.5)
+    assert torch.all(tok_buf[:guard] == -77) and torch.all(tok_buf[-guard:] == -77)
+
+
+def test_chain_on_side_stream():
+    cfg = small_config(d=64, V=1001, Hs=32, r=32, P=8, B=3, dtype="bf16")
+    say("case chain side stream")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    H = head.upload(inp["H"])
+    t0 = head.upload(inp["t0"])
+    ref_L = head.base_logits(H)
+    ref_t, ref_logits, _ = head.draft_chain(H, ref_L, t0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Lb = head.base_logits(H, stream=s)
+        toks, L, _ = head.draft_chain(H, Lb, t0, stream=s)
+    s.synchronize()
+    assert torch.equal(toks, ref_t) and torch.equal(L, ref_logits)
+
+
+@pytest.mark.parametrize("key,sample,mode", [("qwen3_4b_b1", [0], 0), ("qwen3_4b_b1", [0], 1),
+                                             ("qwen3_4b_b32", [0, 13, 31], 0), ("qwen3_8b_b16", [0, 15], 0)])
+def test_chain_full_size_sampled(key, sample, mode):
+    cfg = synth.CONFIGS[key]
+    say(f"case chain full {key} mode={mode} sample={sample}")
+    prev = dh.set_chain_mode(mode)
+    try:
+        head = device_head(key)
+        inp = synth.make_inputs(cfg)
+        H = head.upload(inp["H"])
+        t0 = head.upload(inp["t0"])
+        Lb = head.base_logits(H)
+        toks, L, ws = head.draft_chain(H, Lb, t0)
+        torch.cuda.synchronize()
+        assert dh.DraftHead.device_status(ws) == 0
+    finally:
+        dh.set_chain_mode(prev)
+    w = weights_for(key)
+    m = oracle.Model.from_config(cfg, w)
+    Hs_ = np.ascontiguousarray(inp["H"][sample])
+    Lb_ref = m.base_logits(Hs_)
+    info = compare_chain(m, Hs_, Lb_ref, inp["t0"][sample], toks.cpu().numpy()[sample], L.cpu().numpy()[sample], key)
+    say("  ", info)
+    t = toks.cpu().numpy()
+    assert t.min() >= 0 and t.max() < cfg.vocab
