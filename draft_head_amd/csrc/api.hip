@@ -173,6 +173,13 @@ domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* 
     a.keys = (uint64_t*)(ws + L.keys);
     a.counters = (uint32_t*)(ws + L.counters);
     a.status = (int32_t*)(ws + L.status);
+    a.h_step = L.h_step;
+    a.act_step = L.act_step;
+#ifdef DH_TRACE_PHASES
+    a.trace = (uint64_t*)(ws + L.trace);
+#else
+    a.trace = nullptr;
+#endif
     // H half of the bottleneck for every position: zh[b][p][k] = sum_i H[b][p][i] W1[k][i]
     hipError_t e = dh::launch_gemm_nt(dims->dtype, Hg, d, w->w1, d + Hs, (float*)(ws + L.zh), r, Bg * P, r, d, false, s);
     if (e != hipSuccess) return device_fail(e, "bottleneck pre-GEMM launch");

@@ -172,17 +172,31 @@ __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > 
 constexpr uint64_t kWaitTicks = 200000000ull;  // 2 s
 constexpr int kStatusTimeout = 2;
 
-__device__ __forceinline__ uint32_t ld_acquire_relaxed(const uint32_t* p) {
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// whole workgroup calls; returns false when the kernel must stop
+// Arrival counters are split into kSubCounters lines (workgroup w counts into
+// line w % kSubCounters) so that hundreds of workgroups finishing together do
+// not serialize on one atomic; a waiter sums the lines.
+constexpr int kSubCounters = 8;
+constexpr int kCounterStride = 64;  // uint32 per line: 256 bytes
+
+// whole workgroup calls; returns false when the kernel must stop.
+// Data handed between workgroups is written with agent-coherent stores (see
+// store_agent) into buffers that no workgroup reads before they are
+// written within the launch, so a reader can hold no stale copy and no
+// cache writeback or invalidate is needed around the counters.
 __device__ __forceinline__ bool wg_wait_geq(const uint32_t* counter, uint32_t target, int32_t* status) {
   __shared__ int ok_flag;
   if (threadIdx.x == 0) {
     int ok = 1;
     const uint64_t t0 = wall_clock64();
-    while (ld_acquire_relaxed(counter) < target) {
+    while (true) {
+      uint32_t sum = 0;
+#pragma unroll
+      for (int i = 0; i < kSubCounters; ++i) sum += ld_agent(counter + i * kCounterStride);
+      if (sum >= target) break;
       if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kStatusTimeout) {
         ok = 0;
         break;
@@ -192,20 +206,31 @@ __device__ __forceinline__ bool wg_wait_geq(const uint32_t* counter, uint32_t ta
         ok = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
     }
     ok_flag = ok;
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return ok_flag != 0;
 }
 
-// whole workgroup calls after its last global store of a phase
+// whole workgroup calls after its last hand-off store of a phase: every wave
+// waits for its own stores to complete before the barrier, then one thread
+// counts the workgroup in
 __device__ __forceinline__ void wg_arrive(uint32_t* counter) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(counter + (blockIdx.x % kSubCounters) * kCounterStride, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// stores that are visible device-wide once complete (they bypass the
+// per-XCD L2 write-back)
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace dh

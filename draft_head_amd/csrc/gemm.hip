@@ -19,52 +19,120 @@
 
 namespace dh {
 
-template <class W, int MT>
+#ifndef DH_STREAM_NT
+#define DH_STREAM_NT 2  // 16-column tiles per wave
+#endif
+#ifndef DH_STREAM_U
+#define DH_STREAM_U 4   // k chunks per batch of loads
+#endif
+
+// Each wave owns NT adjacent 16-column tiles and MT 16-row tiles of A, so one
+// A fragment feeds NT MFMAs and one B fragment MT MFMAs.
+template <class W, int MT, int NT>
 __global__ __launch_bounds__(256) void gemm_stream(const W* __restrict__ A, int lda, const W* __restrict__ B, int ldb,
                                                    float* __restrict__ C, int ldc, int M, int N, int K) {
-  constexpr int U = sizeof(W) == 2 ? 8 : 4;  // k chunks in flight per wave
+  constexpr int U = sizeof(W) == 2 ? DH_STREAM_U : (DH_STREAM_U > 2 ? DH_STREAM_U / 2 : 1);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x * 4 + wv) * 16;
+  const int n0 = (blockIdx.x * 4 + wv) * 16 * NT;
   if (n0 >= N) return;
   const int row = lane & 15, kg = lane >> 4;
   const int m_base = blockIdx.y * MT * 16;
   // rows past the end read a valid row; their results are never stored
-  const W* brow = B + (size_t)min(n0 + row, N - 1) * ldb + kg * 8;
+  const W* brow[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) brow[j] = B + (size_t)min(n0 + j * 16 + row, N - 1) * ldb + kg * 8;
   const W* arow[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) arow[t] = A + (size_t)min(m_base + t * 16 + row, M - 1) * lda + kg * 8;
 
-  f32x4 acc[MT];
+  f32x4 acc[MT][NT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nck = (K + 31) / 32;
   for (int c0 = 0; c0 < nck; c0 += U) {
-    frag_t<W> bf[U];
+    frag_t<W> bf[U][NT];
     frag_t<W> af[U][MT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = (c0 + u) * 32;
       const bool ok = k + kg * 8 < K;
-      bf[u] = load8_or_zero(brow + k, ok);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) bf[u][j] = load8_or_zero(brow[j] + k, ok);
 #pragma unroll
       for (int t = 0; t < MT; ++t) af[u][t] = load8_or_zero(arow[t] + k, ok);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = mma(af[u][t], bf[u], acc[t]);
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[t][j] = mma(af[u][t], bf[u][j], acc[t][j]);
   }
 
-  const int n = n0 + row;
-  if (n < N) {
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int n = n0 + j * 16 + row;
+    if (n >= N) continue;
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = m_base + t * 16 + kg * 4 + i;
-        if (m < M) C[(size_t)m * ldc + n] = acc[t][i];
+        if (m < M) C[(size_t)m * ldc + n] = acc[t][j][i];
       }
+  }
+}
+
+// Small products (few columns, e.g. the 256 bottleneck units): one 16x16
+// output tile per workgroup with k split over its 4 waves and summed in LDS,
+// so even a few hundred output tiles keep many CUs busy.
+template <class W>
+__global__ __launch_bounds__(256) void gemm_splitk(const W* __restrict__ A, int lda, const W* __restrict__ B, int ldb,
+                                                   float* __restrict__ C, int ldc, int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 4];
+  constexpr int U = sizeof(W) == 2 ? 8 : 4;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+  const W* brow = B + (size_t)min(n0 + row, N - 1) * ldb + kg * 8;
+  const W* arow = A + (size_t)min(m0 + row, M - 1) * lda + kg * 8;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int nck = (K + 31) / 32;
+  for (int c0 = wv * U; c0 < nck; c0 += 4 * U) {
+    frag_t<W> af[U], bf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (c0 + u) * 32;
+      const bool ok = c0 + u < nck && k + kg * 8 < K;
+      af[u] = load8_or_zero(arow + k, ok);
+      bf[u] = load8_or_zero(brow + k, ok);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = mma(af[u], bf[u], acc);
+  }
+  *reinterpret_cast<float4*>(&red[(wv * 64 + lane) * 4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  __syncthreads();
+  if (wv == 0) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 q = *reinterpret_cast<const float4*>(&red[(w * 64 + lane) * 4]);
+      v[0] += q.x;
+      v[1] += q.y;
+      v[2] += q.z;
+      v[3] += q.w;
+    }
+    const int n = n0 + row;
+    if (n < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + kg * 4 + i;
+        if (m < M) C[(size_t)m * ldc + n] = v[i];
+      }
+    }
   }
 }
 
@@ -168,22 +236,33 @@ __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A
 template <class W>
 static hipError_t launch_stream(const W* A, int lda, const W* B, int ldb, float* C, int ldc, int M, int N, int K,
                                 hipStream_t s) {
-  const int n_waves = (N + 15) / 16;
+  constexpr int NT = DH_STREAM_NT;
+  const int n_waves = (N + 16 * NT - 1) / (16 * NT);
   const int m_tiles = (M + 15) / 16;
   const int mt = m_tiles >= 4 ? 4 : (m_tiles >= 2 ? 2 : 1);
   dim3 grid((n_waves + 3) / 4, (m_tiles + mt - 1) / mt);
   if (mt == 4)
-    hipLaunchKernelGGL((gemm_stream<W, 4>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K);
+    hipLaunchKernelGGL((gemm_stream<W, 4, NT>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K);
   else if (mt == 2)
-    hipLaunchKernelGGL((gemm_stream<W, 2>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K);
+    hipLaunchKernelGGL((gemm_stream<W, 2, NT>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K);
   else
-    hipLaunchKernelGGL((gemm_stream<W, 1>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K);
+    hipLaunchKernelGGL((gemm_stream<W, 1, NT>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int ldb, float* C, int ldc, int M, int N,
                           int K, bool prefer_tiles, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (N <= 4096) {  // few columns: split k inside each workgroup
+    dim3 grid((N + 15) / 16, (M + 15) / 16);
+    if (dtype == kF32)
+      hipLaunchKernelGGL(gemm_splitk<float>, grid, dim3(256), 0, s, (const float*)A, lda, (const float*)B, ldb, C, ldc,
+                         M, N, K);
+    else
+      hipLaunchKernelGGL(gemm_splitk<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)A, lda, (const uint16_t*)B,
+                         ldb, C, ldc, M, N, K);
+    return hipGetLastError();
+  }
   if (dtype == kF32)
     return launch_stream((const float*)A, lda, (const float*)B, ldb, C, ldc, M, N, K, s);
   if (!prefer_tiles || M <= 64)

@@ -33,16 +33,21 @@ struct ChainArgs {
   int32_t* out_tokens;     // [B][P]
   const int32_t* t0;       // [B]
   const float* zh;         // [B][P][r]  W1[:, :d] H
-  float* h;                // [2][B][Hs] GRU state, double buffered by step parity
-  void* act;               // bottleneck activations: bf16 hi [B][r] then lo [B][r], or fp32 [B][r]
+  float* h;                // [P+1][h_step] GRU state after each step (slot 0 = zeros)
+  void* act;               // [P][act_step bytes] bottleneck activations of each step:
+                           //   bf16 hi [B][r] then lo [B][r], or fp32 [B][r]
   uint64_t* keys;          // [P][B] packed argmax keys
-  uint32_t* counters;      // [4] phase arrival counters
+  uint32_t* counters;      // [4][sub-counters][line] phase arrival counters
   int32_t* status;         // device status word
+  int h_step;              // floats between consecutive state slots (256-byte multiple)
+  int act_step;            // bytes between consecutive activation slots (256-byte multiple)
+  uint64_t* trace;         // phase timestamps [P][grid][6] when built with DH_TRACE_PHASES, else null
 };
 
 // workspace carving for a chain launch of up to `group` sequences
 struct ChainLayout {
-  size_t status, counters, keys, zh, h, act, total;
+  size_t status, counters, keys, zh, h, act, trace, total;
+  int h_step, act_step;
 };
 ChainLayout chain_layout(int d, int Hs, int r, int P, int group);
 

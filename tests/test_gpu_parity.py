@@ -74,7 +74,8 @@ def test_base_logits_tiny_f32():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("d,V,B,P", [(72, 1003, 3, 5), (136, 2051, 13, 16), (264, 1000, 5, 16), (40, 17, 1, 1)])
+@pytest.mark.parametrize("d,V,B,P", [(72, 1003, 3, 5), (136, 2051, 13, 16), (264, 1000, 5, 16), (40, 17, 1, 1),
+                                     (72, 5003, 3, 5), (136, 6007, 13, 16), (264, 4099, 5, 16)])
 def test_base_logits_ragged(dtype, d, V, B, P):
     cfg = small_config(d=d, V=V, B=B, P=P, dtype=dtype)
     say(f"case base logits ragged dtype={dtype} d={d} V={V} B={B} P={P}")
