@@ -6,15 +6,19 @@ block-parallel base logits (domino_base_logits, LM-head GEMM on the MFMA
 cores) followed by the 16-step causal-correction chain (domino_draft_chain),
 inputs resident in HBM.  Metric: draft blocks per second.
 
-Prints one JSON line.  `roofline` covers the call that takes the most time
-per step, with its algorithmic bytes (or flops) per launch divided by its
-average duration from HIP events recorded on the launch stream inside the
-timed region.  `cpu_baseline` times the oracle on a bounded sample of the same
+Prints one JSON line.  `roofline` covers the launch that takes the most time
+per step (the chain's persistent kernel or the LM-head GEMM), with its
+algorithmic bytes (or flops) per launch divided by its average duration from
+HIP events that the library records on the launch stream right around it
+inside the timed region (domino_set_timing_events); `traffic` comes from the
+committed rocprofv3 counter summary when it was taken on the current sources.  `cpu_baseline` times the oracle on a bounded sample of the same
 workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 """
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -38,15 +42,33 @@ def parse():
     ap.add_argument("--logits", action="store_true", help="also write the final logits")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 256 MiB once on the device (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
 
 
+def copy_probe():
+    """One 256 MiB device-to-device copy: a kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": src.numel() * 4, "copy_probe_bytes_written": dst.numel() * 4}))
+
+
 def algorithmic_traffic(cfg, B, write_logits):
-    """Bytes each call must move and flops it must do, from the method's definition."""
+    """Bytes each launch must move and flops it must do, from the method's definition.
+
+    base:  the LM-head GEMM, L^base = H W_lm^T (W_lm once, H, L^base out).
+    chain: the P sequential steps; every step reads W2, the GRU weights, the
+           state half of W1, one base-logit row and the fed-back embedding
+           rows, whatever the kernel keeps on chip between steps.
+    """
     es = 2 if cfg.dtype == "bf16" else 4
     d, V, Hs, r, P = cfg.hidden, cfg.vocab, cfg.gru_hidden, cfg.rank, cfg.block
     M = B * P
-    base_bytes = V * d * es + M * d * es + M * V * 4           # W_lm once, H, L^base out
+    base_bytes = V * d * es + M * d * es + M * V * 4
     base_flops = 2.0 * M * V * d
     step = (V * r * es                      # W2
             + 3 * Hs * (d + Hs) * es        # W_ih, W_hh
@@ -54,9 +76,32 @@ def algorithmic_traffic(cfg, B, write_logits):
             + B * V * 4                     # base-logit row of this position
             + B * d * es                    # embedding rows of the fed-back tokens
             + (B * V * 4 if write_logits else 0))
-    chain_bytes = P * step + M * d * es + r * d * es + M * 4  # + H half of W1 once, tokens out
-    chain_flops = 2.0 * P * B * (3 * Hs * (d + Hs) + r * (d + Hs) + V * r)
+    chain_bytes = P * step + M * r * 4 + M * 4  # + H half of the bottleneck in, tokens out
+    chain_flops = 2.0 * P * B * (3 * Hs * (d + Hs) + r * Hs + V * r)
     return {"base": (base_bytes, base_flops), "chain": (chain_bytes, chain_flops), "chain_step_bytes": step}
+
+
+def source_digest():
+    """sha256 of the HIP sources; counter summaries are valid only for the sources they were taken on."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "draft_head_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_sha256") != source_digest() or kernel_key not in t.get("kernels", {}):
+        return None
+    k = t["kernels"][kernel_key]
+    return (k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024.0
 
 
 def cpu_baseline(cfg, w, inp, target_s):
@@ -83,6 +128,8 @@ def cpu_baseline(cfg, w, inp, target_s):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        return copy_probe()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (see the sharding notes); "
               "run with --gpus 1", file=sys.stderr)
@@ -117,15 +164,9 @@ def main():
     dh.set_chain_mode(args.chain_mode)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         dh.domino_base_logits(head.dims, head.weights, H, B, Lb, stream)
-        if ev is not None:
-            ev[1].record(stream)
         dh.domino_draft_chain(head.dims, head.weights, H, Lb, t0, B, toks, logits, ws, ws.numel(), stream)
-        if ev is not None:
-            ev[2].record(stream)
 
     print("bench: warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -146,18 +187,25 @@ def main():
     wall = time.perf_counter() - t_wall
     ms_per_step = e0.elapsed_time(e1) / K
 
-    # per-call durations, events on the launch stream around each call
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # durations of the main launch of each call: the library records these
+    # events on the launch stream right around it
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for e in evs:  # torch creates the HIP event on its first record
+        for x in e:
+            x.record(stream)
     torch.cuda.synchronize()
     for i in range(K):
-        step(evs[i])
+        dh.domino_set_timing_events(*evs[i])
+        step()
     torch.cuda.synchronize()
-    t_base = np.mean([a.elapsed_time(b) for a, b, _ in evs]) * 1e-3
-    t_chain = np.mean([b.elapsed_time(c) for _, b, c in evs]) * 1e-3
+    dh.domino_set_timing_events()
+    t_base = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_chain = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
     assert dh.DraftHead.device_status(ws) == 0
 
     tr = algorithmic_traffic(cfg, B, args.logits)
     peak_mfma = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    kernel_key = {"base": "base_gemm", "chain": "chain_steps"}
     kernels = {}
     for name, t in (("base", t_base), ("chain", t_chain)):
         byts, flops = tr[name]
@@ -169,13 +217,13 @@ def main():
             kernels[name] = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": peak_mfma, "unit": "TFLOP/s"}
         k = kernels[name]
         k["frac"] = k["achieved"] / k["peak"]
+        k["traffic"] = measured_traffic(cfg.name, kernel_key[name])
         k["us"] = t * 1e6
         k["algorithmic_bytes"] = byts
         k["flops"] = flops
     dom = "chain" if t_chain >= t_base else "base"
-    roof = {kk: kernels[dom][kk] for kk in ("bound", "achieved", "peak", "unit", "frac")}
-    roof["traffic"] = None
-    roof["kernel"] = "domino_draft_chain" if dom == "chain" else "domino_base_logits"
+    roof = {kk: kernels[dom][kk] for kk in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roof["kernel"] = "chain_persistent (domino_draft_chain steps)" if dom == "chain" else "LM-head GEMM (domino_base_logits)"
 
     value = B / (ms_per_step * 1e-3)
     out = {

@@ -21,7 +21,7 @@ F32, BF16 = 0, 1
 STATUS_FINE, STATUS_BAD_FIRST_TOKEN, STATUS_TIMEOUT = 0, 1, 2
 
 EXPORTS = ("domino_version", "domino_last_error", "domino_base_logits", "domino_chain_workspace_size",
-           "domino_draft_chain", "domino_set_chain_mode")
+           "domino_draft_chain", "domino_set_chain_mode", "domino_set_timing_events")
 
 
 class DominoError(RuntimeError):
@@ -63,6 +63,8 @@ def lib():
         L.domino_draft_chain.argtypes = [P, P, P, P, P, i32, P, P, P, sz, P]
         L.domino_set_chain_mode.restype = i32
         L.domino_set_chain_mode.argtypes = [i32]
+        L.domino_set_timing_events.restype = None
+        L.domino_set_timing_events.argtypes = [P, P, P, P]
         _lib = L
     return _lib
 
@@ -98,6 +100,12 @@ def set_chain_mode(mode: int) -> int:
     if prev < 0:
         raise ValueError(f"chain mode {mode}")
     return prev
+
+
+def domino_set_timing_events(base_start=None, base_stop=None, chain_start=None, chain_stop=None):
+    """torch.cuda.Event objects (or None) recorded around the main launches of the calls."""
+    h = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)
+    lib().domino_set_timing_events(h(base_start), h(base_stop), h(chain_start), h(chain_stop))
 
 
 def make_dims(hidden, vocab, gru_hidden, rank, block, dtype) -> Dims:

@@ -14,6 +14,7 @@ namespace {
 
 thread_local std::string g_error;
 int g_chain_mode = 0;
+hipEvent_t g_base_start = nullptr, g_base_stop = nullptr, g_chain_start = nullptr, g_chain_stop = nullptr;
 
 domino_status fail(domino_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 domino_status fail(domino_status s, const char* fmt, ...) {
@@ -77,6 +78,14 @@ const char* domino_version(void) { return "domino-gfx950 0.1"; }
 
 const char* domino_last_error(void) { return g_error.c_str(); }
 
+void domino_set_timing_events(void* base_start, void* base_stop, void* chain_start, void* chain_stop) {
+  const bool base = base_start && base_stop, chain = chain_start && chain_stop;
+  g_base_start = base ? (hipEvent_t)base_start : nullptr;
+  g_base_stop = base ? (hipEvent_t)base_stop : nullptr;
+  g_chain_start = chain ? (hipEvent_t)chain_start : nullptr;
+  g_chain_stop = chain ? (hipEvent_t)chain_stop : nullptr;
+}
+
 int32_t domino_set_chain_mode(int32_t mode) {
   if (mode != 0 && mode != 1) return -1;
   const int32_t prev = g_chain_mode;
@@ -96,9 +105,14 @@ domino_status domino_base_logits(const domino_dims* dims, const domino_weights* 
   REQUIRE_PTR(base_logits, "base_logits");
   if ((int64_t)batch * dims->block > INT32_MAX / 2) return fail(DOMINO_ERR_UNSUPPORTED, "batch too large");
   const int M = batch * dims->block;
-  hipError_t e = dh::launch_gemm_nt(dims->dtype, H, dims->hidden, w->lm_head, dims->hidden, base_logits, dims->vocab,
-                                    M, dims->vocab, dims->hidden, true, (hipStream_t)stream);
+  hipError_t e = hipSuccess;
+  if (g_base_start && (e = hipEventRecord(g_base_start, (hipStream_t)stream)) != hipSuccess)
+    return device_fail(e, "timing event");
+  e = dh::launch_gemm_nt(dims->dtype, H, dims->hidden, w->lm_head, dims->hidden, base_logits, dims->vocab, M,
+                         dims->vocab, dims->hidden, true, (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "base-logit GEMM launch");
+  if (g_base_stop && (e = hipEventRecord(g_base_stop, (hipStream_t)stream)) != hipSuccess)
+    return device_fail(e, "timing event");
   return ok();
 }
 
@@ -180,10 +194,7 @@ domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* 
 #else
     a.trace = nullptr;
 #endif
-    // H half of the bottleneck for every position: zh[b][p][k] = sum_i H[b][p][i] W1[k][i]
-    hipError_t e = dh::launch_gemm_nt(dims->dtype, Hg, d, w->w1, d + Hs, (float*)(ws + L.zh), r, Bg * P, r, d, false, s);
-    if (e != hipSuccess) return device_fail(e, "bottleneck pre-GEMM launch");
-    e = dh::launch_chain(dims->dtype, a, g_chain_mode, g0 == 0, s);
+    hipError_t e = dh::launch_chain(dims->dtype, a, Hg, g_chain_mode, g0 == 0, s, g_chain_start, g_chain_stop);
     if (e != hipSuccess) return device_fail(e, "chain launch");
   }
   return ok();

@@ -49,7 +49,7 @@ __device__ __forceinline__ int32_t prev_token(const ChainArgs& a, int p, int b) 
   int32_t t = p == 0 ? a.t0[b]
                      : amax_index(__hip_atomic_load(&a.keys[(size_t)(p - 1) * a.B + b], __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT));
-  return (t < 0 || t >= a.V) ? 0 : t;  // out-of-range first tokens are flagged by chain_init
+  return (t < 0 || t >= a.V) ? 0 : t;  // out-of-range first tokens are flagged by chain_prologue
 }
 
 // ---- GRU weight slice resident in LDS ----------------------------------------------
@@ -496,8 +496,17 @@ __device__ bool logits_range(const ChainArgs& a, int p, int t_begin, int t_end, 
 }
 
 // ---- kernels ------------------------------------------------------------------------
-__global__ void chain_init(ChainArgs a, int reset_status) {
-  const int tid = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
+// Before the steps: the H half of the bottleneck for every position,
+// zh[b][p][k] = sum_i H[b][p][i] W1[k][i] (one 16x16 tile per workgroup, k
+// split over the waves), and the zeroed keys, counters and initial state.
+template <class W>
+__global__ __launch_bounds__(256) void chain_prologue(ChainArgs a, const void* H, int reset_status) {
+  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 4];
+  const int M = a.B * a.P;
+  splitk_tile<W>((const W*)H, a.d, (const W*)a.w1, a.d + a.Hs, (float*)a.zh, a.r, M, a.r, a.d, blockIdx.x, blockIdx.y,
+                 red);
+  const int nblk = gridDim.x * gridDim.y, blk = blockIdx.y * gridDim.x + blockIdx.x;
+  const int tid = blk * blockDim.x + threadIdx.x, stride = nblk * blockDim.x;
   for (int i = tid; i < a.P * a.B; i += stride) a.keys[i] = 0;
   for (int i = tid; i < a.B * a.Hs; i += stride) a.h[i] = 0.f;  // state slot 0
   for (int i = tid; i < 4 * kSubCounters * kCounterStride; i += stride) a.counters[i] = 0;
@@ -507,6 +516,13 @@ __global__ void chain_init(ChainArgs a, int reset_status) {
       if ((a.t0[b] < 0 || a.t0[b] >= a.V) && s == 0) s = 1;
     *a.status = s;
   }
+}
+
+// drafted tokens of step p from the packed argmax keys
+__device__ __forceinline__ void write_tokens(const ChainArgs& a, int p) {
+  for (int b = threadIdx.x; b < a.B; b += blockDim.x)
+    a.out_tokens[(size_t)b * a.P + p] =
+        amax_index(__hip_atomic_load(&a.keys[(size_t)p * a.B + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 __global__ void chain_finalize(ChainArgs a) {
@@ -578,6 +594,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
     if (wg < nG) {
       if (p > 0 && !wg_wait_geq(cO, (uint32_t)(p * G), a.status)) return;
       DH_STAMP(p, 0);
+      if (wg == 0 && p > 0) write_tokens(a, p - 1);
       gru_finish<W, NCB, (kLds >= 1)>(a, p, wg, red, gl, acc_h);
     }
     wg_arrive(cG);
@@ -603,6 +620,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
     wg_arrive(cO);
     DH_STAMP(p, 5);
   }
+  if (wg == 0 && wg_wait_geq(cO, (uint32_t)(a.P * G), a.status)) write_tokens(a, a.P - 1);
 }
 
 // ---- host side ------------------------------------------------------------------------
@@ -683,10 +701,11 @@ static int device_cus() {
 constexpr size_t kLdsBudget = 144 * 1024;  // dynamic LDS the persistent kernel may use (160 KB per CU)
 
 template <class W, int NCB, int KC>
-static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s) {
+static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& persistent) {
   const int cus = device_cus();
   // the persistent schedule needs one GRU work item per workgroup
-  if (mode == 0 && cus > 0 && a.Hs / 4 <= cus) {
+  persistent = mode == 0 && cus > 0 && a.Hs / 4 <= cus;
+  if (persistent) {
     const size_t g = gru_slice_elems(a.d, a.Hs) * sizeof(W);
     const size_t w = (size_t)16 * (a.Hs + 8) * sizeof(W);
     if (g + w <= kLdsBudget) return launch_persistent<W, NCB, KC, 2>(a, g + w, s);
@@ -705,28 +724,41 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s) {
 
 // k chunks of 32 in the bottleneck, rounded up to 1, 2, 4 or 8 (zero padded)
 template <class W, int NCB>
-static hipError_t run_chain_kc(const ChainArgs& a, int mode, hipStream_t s) {
+static hipError_t run_chain_kc(const ChainArgs& a, int mode, hipStream_t s, bool& persistent) {
   const int kc = (a.r + 31) / 32;
-  if (kc <= 1) return run_chain<W, NCB, 1>(a, mode, s);
-  if (kc <= 2) return run_chain<W, NCB, 2>(a, mode, s);
-  if (kc <= 4) return run_chain<W, NCB, 4>(a, mode, s);
-  if (kc <= 8) return run_chain<W, NCB, 8>(a, mode, s);
+  if (kc <= 1) return run_chain<W, NCB, 1>(a, mode, s, persistent);
+  if (kc <= 2) return run_chain<W, NCB, 2>(a, mode, s, persistent);
+  if (kc <= 4) return run_chain<W, NCB, 4>(a, mode, s, persistent);
+  if (kc <= 8) return run_chain<W, NCB, 8>(a, mode, s, persistent);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_chain(int dtype, const ChainArgs& a, int mode, bool reset_status, hipStream_t s) {
+hipError_t launch_chain(int dtype, const ChainArgs& a, const void* H, int mode, bool reset_status, hipStream_t s,
+                        hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (a.B <= 0) return hipSuccess;
-  const int n_init = a.B * a.Hs > a.P * a.B ? a.B * a.Hs : a.P * a.B;
-  hipLaunchKernelGGL(chain_init, dim3((n_init + 255) / 256), dim3(256), 0, s, a, reset_status ? 1 : 0);
+  const dim3 pro((a.r + 15) / 16, (a.B * a.P + 15) / 16);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(chain_prologue<uint16_t>, pro, dim3(256), 0, s, a, H, reset_status ? 1 : 0);
+  else
+    hipLaunchKernelGGL(chain_prologue<float>, pro, dim3(256), 0, s, a, H, reset_status ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool two = a.B > 16;
+  bool persistent = false;
+  if (ev_start && ev_stop) {
+    e = hipEventRecord(ev_start, s);
+    if (e != hipSuccess) return e;
+  }
   if (dtype == kBF16)
-    e = two ? run_chain_kc<uint16_t, 2>(a, mode, s) : run_chain_kc<uint16_t, 1>(a, mode, s);
+    e = two ? run_chain_kc<uint16_t, 2>(a, mode, s, persistent) : run_chain_kc<uint16_t, 1>(a, mode, s, persistent);
   else
-    e = two ? run_chain_kc<float, 2>(a, mode, s) : run_chain_kc<float, 1>(a, mode, s);
+    e = two ? run_chain_kc<float, 2>(a, mode, s, persistent) : run_chain_kc<float, 1>(a, mode, s, persistent);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chain_finalize, dim3((a.B * a.P + 255) / 256), dim3(256), 0, s, a);
+  if (ev_start && ev_stop) {
+    e = hipEventRecord(ev_stop, s);
+    if (e != hipSuccess) return e;
+  }
+  if (!persistent) hipLaunchKernelGGL(chain_finalize, dim3((a.B * a.P + 255) / 256), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

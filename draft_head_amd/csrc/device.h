@@ -147,6 +147,56 @@ __device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, c, 0, 0, 0);
 }
 
+// ---- one 16x16 tile of C = A B^T with k split over the 4 waves -------------------
+// For narrow products: each wave sums its share of the k chunks, the partials
+// meet in LDS (red: 4 * 64 * 4 floats) and wave 0 writes the tile.
+template <class W>
+__device__ void splitk_tile(const W* __restrict__ A, int lda, const W* __restrict__ B, int ldb, float* __restrict__ C,
+                            int ldc, int M, int N, int K, int n_tile, int m_tile, float* red) {
+  constexpr int U = sizeof(W) == 2 ? 8 : 4;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int n0 = n_tile * 16, m0 = m_tile * 16;
+  const W* brow = B + (size_t)min(n0 + row, N - 1) * ldb + kg * 8;
+  const W* arow = A + (size_t)min(m0 + row, M - 1) * lda + kg * 8;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int nck = (K + 31) / 32;
+  for (int c0 = wv * U; c0 < nck; c0 += 4 * U) {
+    frag_t<W> af[U], bf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (c0 + u) * 32;
+      const bool ok = c0 + u < nck && k + kg * 8 < K;
+      af[u] = load8_or_zero(arow + k, ok);
+      bf[u] = load8_or_zero(brow + k, ok);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = mma(af[u], bf[u], acc);
+  }
+  *reinterpret_cast<float4*>(&red[(wv * 64 + lane) * 4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  __syncthreads();
+  if (wv == 0) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 q = *reinterpret_cast<const float4*>(&red[(w * 64 + lane) * 4]);
+      v[0] += q.x;
+      v[1] += q.y;
+      v[2] += q.z;
+      v[3] += q.w;
+    }
+    const int n = n0 + row;
+    if (n < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + kg * 4 + i;
+        if (m < M) C[(size_t)m * ldc + n] = v[i];
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // ---- greedy argmax as one 64-bit max ------------------------------------------
 // key = (order-preserving bits of the value) << 32 | (0xFFFFFFFF - index):
 // the largest key has the largest value and, among equal values, the lowest

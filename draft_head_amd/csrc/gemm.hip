@@ -87,53 +87,12 @@ __global__ __launch_bounds__(256) void gemm_stream(const W* __restrict__ A, int 
 }
 
 // Small products (few columns, e.g. the 256 bottleneck units): one 16x16
-// output tile per workgroup with k split over its 4 waves and summed in LDS,
-// so even a few hundred output tiles keep many CUs busy.
+// output tile per workgroup, k split over its 4 waves (splitk_tile).
 template <class W>
 __global__ __launch_bounds__(256) void gemm_splitk(const W* __restrict__ A, int lda, const W* __restrict__ B, int ldb,
                                                    float* __restrict__ C, int ldc, int M, int N, int K) {
   __shared__ __attribute__((aligned(16))) float red[4 * 64 * 4];
-  constexpr int U = sizeof(W) == 2 ? 8 : 4;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int row = lane & 15, kg = lane >> 4;
-  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
-  const W* brow = B + (size_t)min(n0 + row, N - 1) * ldb + kg * 8;
-  const W* arow = A + (size_t)min(m0 + row, M - 1) * lda + kg * 8;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int nck = (K + 31) / 32;
-  for (int c0 = wv * U; c0 < nck; c0 += 4 * U) {
-    frag_t<W> af[U], bf[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = (c0 + u) * 32;
-      const bool ok = c0 + u < nck && k + kg * 8 < K;
-      af[u] = load8_or_zero(arow + k, ok);
-      bf[u] = load8_or_zero(brow + k, ok);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc = mma(af[u], bf[u], acc);
-  }
-  *reinterpret_cast<float4*>(&red[(wv * 64 + lane) * 4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  __syncthreads();
-  if (wv == 0) {
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float4 q = *reinterpret_cast<const float4*>(&red[(w * 64 + lane) * 4]);
-      v[0] += q.x;
-      v[1] += q.y;
-      v[2] += q.z;
-      v[3] += q.w;
-    }
-    const int n = n0 + row;
-    if (n < N) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + kg * 4 + i;
-        if (m < M) C[(size_t)m * ldc + n] = v[i];
-      }
-    }
-  }
+  splitk_tile<W>(A, lda, B, ldb, C, ldc, M, N, K, blockIdx.x, blockIdx.y, red);
 }
 
 constexpr int TBM = 128, TBN = 128, TBK = 64, TPAD = 8;

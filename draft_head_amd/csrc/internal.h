@@ -51,6 +51,8 @@ struct ChainLayout {
 };
 ChainLayout chain_layout(int d, int Hs, int r, int P, int group);
 
-hipError_t launch_chain(int dtype, const ChainArgs& a, int mode, bool reset_status, hipStream_t s);
+// prologue (H half of the bottleneck, zeroed state) then the P steps
+hipError_t launch_chain(int dtype, const ChainArgs& a, const void* H, int mode, bool reset_status, hipStream_t s,
+                        hipEvent_t ev_start, hipEvent_t ev_stop);
 
 }  // namespace dh

@@ -127,6 +127,17 @@ domino_status domino_draft_chain(const domino_dims *dims, const domino_weights *
                                  void *stream);
 
 /*
+ * Timing hooks for benchmarks and profilers (hipEvent_t handles passed as
+ * void*).  While set, each later domino_base_logits call records base_start
+ * on its stream right before its GEMM launch and base_stop right after it,
+ * and each domino_draft_chain call records chain_start right before the
+ * launch(es) that run the P steps (after the short prologue) and chain_stop
+ * right after them.  A NULL pair disables that pair.  The events stay owned
+ * by the caller.  Process-wide setting; not for concurrent callers.
+ */
+void domino_set_timing_events(void *base_start, void *base_stop, void *chain_start, void *chain_stop);
+
+/*
  * Chain scheduling.  0 (default): one persistent cooperative launch runs
  * all P steps; 1: three kernel launches per step.  Both compute the same
  * values.  Returns the previous mode; any other value is rejected with -1.

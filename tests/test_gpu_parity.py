@@ -264,3 +264,30 @@ def test_chain_full_size_sampled(key, sample, mode):
     say("  ", info)
     t = toks.cpu().numpy()
     assert t.min() >= 0 and t.max() < cfg.vocab
+
+
+def test_timing_events_bracket_main_launches():
+    cfg = small_config(d=64, V=1001, Hs=32, r=32, P=8, B=3, dtype="bf16")
+    say("case timing events")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    H = head.upload(inp["H"])
+    t0 = head.upload(inp["t0"])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    dh.domino_set_timing_events(*ev)
+    try:
+        Lb = head.base_logits(H)
+        toks, L, ws = head.draft_chain(H, Lb, t0)
+        torch.cuda.synchronize()
+    finally:
+        dh.domino_set_timing_events()
+    assert ev[0].elapsed_time(ev[1]) > 0 and ev[2].elapsed_time(ev[3]) > 0
+    assert ev[1].elapsed_time(ev[2]) >= 0  # the chain's main launch follows the GEMM
+    Lb2 = head.base_logits(H)
+    toks2, L2, _ = head.draft_chain(H, Lb2, t0)
+    torch.cuda.synchronize()
+    assert torch.equal(toks, toks2) and torch.equal(L, L2)
