@@ -21,7 +21,8 @@ F32, BF16 = 0, 1
 STATUS_FINE, STATUS_BAD_FIRST_TOKEN, STATUS_TIMEOUT = 0, 1, 2
 
 EXPORTS = ("domino_version", "domino_last_error", "domino_base_logits", "domino_chain_workspace_size",
-           "domino_draft_chain", "domino_set_chain_mode", "domino_set_timing_events")
+           "domino_draft_chain", "domino_set_chain_mode", "domino_set_timing_events", "domino_tree_workspace_size",
+           "domino_tree_draft", "domino_tree_candidates")
 
 
 class DominoError(RuntimeError):
@@ -65,6 +66,12 @@ def lib():
         L.domino_set_chain_mode.argtypes = [i32]
         L.domino_set_timing_events.restype = None
         L.domino_set_timing_events.argtypes = [P, P, P, P]
+        L.domino_tree_workspace_size.restype = sz
+        L.domino_tree_workspace_size.argtypes = [P, i32, i32, i32]
+        L.domino_tree_candidates.restype = ctypes.c_int
+        L.domino_tree_candidates.argtypes = [P, P, i32, i32, P, P, P]
+        L.domino_tree_draft.restype = ctypes.c_int
+        L.domino_tree_draft.argtypes = [P, P, P, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
         _lib = L
     return _lib
 
@@ -134,6 +141,23 @@ def domino_draft_chain(dims: Dims, weights: Weights, H, base_logits, first_token
                                     _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
+def domino_tree_candidates(dims: Dims, base_logits, batch: int, topm: int, out_index, out_value, stream=None):
+    _check(lib().domino_tree_candidates(ctypes.byref(dims), _ptr(base_logits), int(batch), int(topm), _ptr(out_index),
+                                        _ptr(out_value), _stream(stream)))
+
+
+def domino_tree_workspace_size(dims: Dims, batch: int, nodes: int, topm: int) -> int:
+    return int(lib().domino_tree_workspace_size(ctypes.byref(dims), int(batch), int(nodes), int(topm)))
+
+
+def domino_tree_draft(dims: Dims, weights: Weights, H, base_logits, first_tokens, batch: int, nodes: int, topm: int,
+                      out_parents, out_tokens, out_depth, out_scores, workspace, workspace_bytes: int, stream=None):
+    _check(lib().domino_tree_draft(ctypes.byref(dims), ctypes.byref(weights), _ptr(H), _ptr(base_logits),
+                                   _ptr(first_tokens), int(batch), int(nodes), int(topm), _ptr(out_parents),
+                                   _ptr(out_tokens), _ptr(out_depth), _ptr(out_scores), _ptr(workspace),
+                                   int(workspace_bytes), _stream(stream)))
+
+
 class DraftHead:
     """Device-resident weights plus the three calls, for tests and the bench.
 
@@ -196,6 +220,19 @@ class DraftHead:
         domino_draft_chain(self.dims, self.weights, H, base_logits, first_tokens, B, out_tokens,
                            out_logits if want_logits else None, workspace, workspace.numel(), stream)
         return out_tokens, (out_logits if want_logits else None), workspace
+
+    def tree_draft(self, H, base_logits, first_tokens, nodes, topm, workspace=None, stream=None):
+        """-> dict of device tensors parents, tokens, depth [B][N] int32 and scores [B][N] fp64, and the workspace."""
+        import torch
+        B = H.shape[0]
+        out = {k: torch.empty((B, nodes), dtype=torch.int32, device=self.device) for k in ("parents", "tokens", "depth")}
+        out["scores"] = torch.empty((B, nodes), dtype=torch.float64, device=self.device)
+        if workspace is None:
+            n = domino_tree_workspace_size(self.dims, B, nodes, topm)
+            workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=self.device)
+        domino_tree_draft(self.dims, self.weights, H, base_logits, first_tokens, B, nodes, topm, out["parents"],
+                          out["tokens"], out["depth"], out["scores"], workspace, workspace.numel(), stream)
+        return out, workspace
 
     @staticmethod
     def device_status(workspace) -> int:

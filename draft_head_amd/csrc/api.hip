@@ -200,4 +200,105 @@ domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* 
   return ok();
 }
 
+domino_status domino_tree_candidates(const domino_dims* dims, const float* base_logits, int32_t batch, int32_t topm,
+                                     int32_t* out_index, float* out_value, void* stream) {
+  domino_status st = check_dims(dims);
+  if (st != DOMINO_OK) return st;
+  if (batch < 0) return fail(DOMINO_ERR_INVALID_ARGUMENT, "batch %d is negative", batch);
+  if (topm < 1 || topm > 256) return fail(DOMINO_ERR_INVALID_ARGUMENT, "topm %d must be in [1, 256]", topm);
+  if (topm > dims->vocab) return fail(DOMINO_ERR_INVALID_ARGUMENT, "topm %d exceeds the vocabulary", topm);
+  if (batch == 0) return ok();
+  REQUIRE_PTR(base_logits, "base_logits");
+  REQUIRE_PTR(out_index, "out_index");
+  REQUIRE_PTR(out_value, "out_value");
+  hipError_t e = dh::launch_topm(base_logits, batch * dims->block, dims->vocab, topm, out_index, out_value,
+                                 (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "top-M launch");
+  return ok();
+}
+
+size_t domino_tree_workspace_size(const domino_dims* dims, int32_t batch, int32_t nodes, int32_t topm) {
+  if (check_dims(dims) != DOMINO_OK || batch < 0 || nodes < 1 || nodes > 64 || topm < 1 || topm > 256) return 0;
+  return dh::tree_layout(dims->hidden, dims->gru_hidden, dims->rank, dims->block, batch > 0 ? batch : 1, nodes, topm)
+      .total;
+}
+
+domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w, const void* H,
+                                const float* base_logits, const int32_t* first_tokens, int32_t batch, int32_t nodes,
+                                int32_t topm, int32_t* out_parents, int32_t* out_tokens, int32_t* out_depth,
+                                double* out_scores, void* workspace, size_t workspace_bytes, void* stream) {
+  domino_status st = check_dims(dims);
+  if (st != DOMINO_OK) return st;
+  if (!w) return fail(DOMINO_ERR_INVALID_ARGUMENT, "weights is NULL");
+  if (batch < 0) return fail(DOMINO_ERR_INVALID_ARGUMENT, "batch %d is negative", batch);
+  if (nodes < 1 || nodes > 64) return fail(DOMINO_ERR_INVALID_ARGUMENT, "nodes %d must be in [1, 64]", nodes);
+  if (topm < 1 || topm > 256) return fail(DOMINO_ERR_INVALID_ARGUMENT, "topm %d must be in [1, 256]", topm);
+  if (topm > dims->vocab) return fail(DOMINO_ERR_INVALID_ARGUMENT, "topm %d exceeds the vocabulary", topm);
+  if (dims->gru_hidden > 4096) return fail(DOMINO_ERR_UNSUPPORTED, "gru_hidden %d exceeds 4096 for the tree", dims->gru_hidden);
+  if (batch == 0) return ok();
+  REQUIRE_PTR(w->embed, "weights.embed");
+  REQUIRE_PTR(w->w_ih, "weights.w_ih");
+  REQUIRE_PTR(w->w_hh, "weights.w_hh");
+  REQUIRE_PTR(w->w1, "weights.w1");
+  REQUIRE_PTR(w->w2, "weights.w2");
+  OPTIONAL_PTR(w->b_ih, "weights.b_ih");
+  OPTIONAL_PTR(w->b_hh, "weights.b_hh");
+  OPTIONAL_PTR(w->b1, "weights.b1");
+  OPTIONAL_PTR(w->b2, "weights.b2");
+  REQUIRE_PTR(H, "H");
+  REQUIRE_PTR(base_logits, "base_logits");
+  REQUIRE_PTR(first_tokens, "first_tokens");
+  REQUIRE_PTR(out_parents, "out_parents");
+  REQUIRE_PTR(out_tokens, "out_tokens");
+  OPTIONAL_PTR(out_depth, "out_depth");
+  OPTIONAL_PTR(out_scores, "out_scores");
+  REQUIRE_PTR(workspace, "workspace");
+  const size_t need = domino_tree_workspace_size(dims, batch, nodes, topm);
+  if (workspace_bytes < need)
+    return fail(DOMINO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes,
+                need);
+  const dh::TreeLayout L =
+      dh::tree_layout(dims->hidden, dims->gru_hidden, dims->rank, dims->block, batch, nodes, topm);
+  char* ws = (char*)workspace;
+  dh::TreeArgs t;
+  t.d = dims->hidden;
+  t.V = dims->vocab;
+  t.Hs = dims->gru_hidden;
+  t.r = dims->rank;
+  t.P = dims->block;
+  t.B = batch;
+  t.N = nodes;
+  t.M = topm;
+  t.dtype = dims->dtype;
+  t.H = H;
+  t.embed = w->embed;
+  t.w_ih = w->w_ih;
+  t.w_hh = w->w_hh;
+  t.w1 = w->w1;
+  t.w2 = w->w2;
+  t.b_ih = w->b_ih;
+  t.b_hh = w->b_hh;
+  t.b1 = w->b1;
+  t.b2 = w->b2;
+  t.Lb = base_logits;
+  t.t0 = first_tokens;
+  t.out_parents = out_parents;
+  t.out_tokens = out_tokens;
+  t.out_depth = out_depth;
+  t.out_scores = out_scores;
+  t.cand_idx = (int32_t*)(ws + L.cand_idx);
+  t.cand_val = (float*)(ws + L.cand_val);
+  t.zh = (double*)(ws + L.zh);
+  t.states = (double*)(ws + L.states);
+  t.heap_score = (double*)(ws + L.heap_score);
+  t.heap_meta = (int4*)(ws + L.heap_meta);
+  t.heap_count = (int32_t*)(ws + L.heap_count);
+  t.cur = ws + L.cur;
+  t.status = (int32_t*)(ws + L.status);
+  t.heap_cap = L.heap_cap;
+  hipError_t e = dh::launch_tree(t, true, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "tree launch");
+  return ok();
+}
+
 }  // extern "C"

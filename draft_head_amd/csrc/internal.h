@@ -55,4 +55,45 @@ ChainLayout chain_layout(int d, int Hs, int r, int P, int group);
 hipError_t launch_chain(int dtype, const ChainArgs& a, const void* H, int mode, bool reset_status, hipStream_t s,
                         hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// Everything one tree call needs; device pointers.
+struct TreeArgs {
+  int d, V, Hs, r, P, B, N, M, dtype;
+  const void* H;
+  const void* embed;
+  const void* w_ih;
+  const void* w_hh;
+  const void* w1;
+  const void* w2;
+  const float* b_ih;
+  const float* b_hh;
+  const float* b1;
+  const float* b2;
+  const float* Lb;          // [B][P][V]
+  const int32_t* t0;        // [B]
+  int32_t* out_parents;     // [B][N]
+  int32_t* out_tokens;      // [B][N]
+  int32_t* out_depth;       // [B][N] or null
+  double* out_scores;       // [B][N] or null
+  int32_t* cand_idx;        // [B][P][M] top-M candidates per row
+  float* cand_val;          // [B][P][M]
+  double* zh;               // [B][P][r] W1[:, :d] H in fp64
+  double* states;           // [B][N+1][Hs] fp64 GRU state per node (slot 0 = anchor)
+  double* heap_score;       // [B][heap_cap]
+  int4* heap_meta;          // [B][heap_cap] (parent, rank, token, depth)
+  int32_t* heap_count;      // [B]
+  void* cur;                // [B] node being expanded this round
+  int32_t* status;
+  int heap_cap;
+};
+
+struct TreeLayout {
+  size_t status, cand_idx, cand_val, zh, states, heap_score, heap_meta, heap_count, cur, total;
+  int heap_cap;
+};
+TreeLayout tree_layout(int d, int Hs, int r, int P, int group, int N, int M);
+
+hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s);
+// top-M of each of `rows` rows of length V, ordered (value desc, index asc)
+hipError_t launch_topm(const float* Lb, int rows, int V, int M, int32_t* idx, float* val, hipStream_t s);
+
 }  // namespace dh

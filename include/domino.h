@@ -127,6 +127,51 @@ domino_status domino_draft_chain(const domino_dims *dims, const domino_weights *
                                  void *stream);
 
 /*
+ * Top-M candidates of every base-logit row (the tree's candidate lists,
+ * DominoTree summary, "Top-M" restriction): for each of batch*block rows of
+ * base_logits [batch][block][vocab] (device, fp32), out_index/out_value
+ * [batch][block][topm] (device) hold the topm largest entries ordered by
+ * (value desc, index asc); -0.0 counts as +0.0.  1 <= topm <= min(256, vocab).
+ */
+domino_status domino_tree_candidates(const domino_dims *dims, const float *base_logits, int32_t batch, int32_t topm,
+                                     int32_t *out_index, float *out_value, void *stream);
+
+/* Bytes of workspace domino_tree_draft needs (0 for invalid arguments). */
+size_t domino_tree_workspace_size(const domino_dims *dims, int32_t batch, int32_t nodes, int32_t topm);
+
+/*
+ * Best-first draft tree with path-conditioned scoring (DominoTree summary,
+ * gist.science Chinese page, technical abstract, "方法论 / 核心组件": the
+ * conditional best-first heap and the top-M candidate restriction), for
+ * `batch` independent sequences.
+ *   - Candidates of depth delta (1-based) are the top `topm` entries of
+ *     base_logits[b][delta-1], ordered by (value desc, index asc).
+ *   - The anchor first_tokens[b] is the root (not counted); its GRU state is
+ *     GRU(embed[t0], 0).  Expanding a node at depth delta with state S scores
+ *     its topm children on row delta:
+ *       l_j = base_logits[b][delta][C_j] + (W2 a)[C_j] + b2[C_j],
+ *       a = SiLU(W1 [H[b][delta] ; S] + b1),
+ *       child score = node score + l_j - logsumexp_j(l)
+ *   - The entry with the highest score is popped next (ties: lower parent
+ *     index, then lower candidate rank) and becomes node k = 0, 1, ...; it
+ *     gets state GRU(embed[token], S_parent) and is expanded unless it sits at
+ *     depth P or is the last node of the budget.
+ *   - GRU, bottleneck and scores are fp64.
+ * Outputs (device) [batch][nodes]: out_parents (node index, -1 = anchor),
+ *   out_tokens, out_depth (1-based; may be NULL), out_scores (fp64; may be
+ *   NULL).  Nodes are numbered in pop order, so parents[k] < k.  Slots left
+ *   when the tree runs out of nodes hold parent -1, token -1, depth 0,
+ *   score -inf.
+ * Limits: 1 <= nodes <= 64, 1 <= topm <= min(256, vocab), gru_hidden <= 4096.
+ * The int32 at workspace offset 0 holds the device status after the call
+ * (1 = a first token was outside [0, V) and token 0 was used).
+ */
+domino_status domino_tree_draft(const domino_dims *dims, const domino_weights *weights, const void *H,
+                                const float *base_logits, const int32_t *first_tokens, int32_t batch, int32_t nodes,
+                                int32_t topm, int32_t *out_parents, int32_t *out_tokens, int32_t *out_depth,
+                                double *out_scores, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Timing hooks for benchmarks and profilers (hipEvent_t handles passed as
  * void*).  While set, each later domino_base_logits call records base_start
  * on its stream right before its GEMM launch and base_stop right after it,

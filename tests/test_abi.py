@@ -135,3 +135,33 @@ def test_chain_mode_switch():
     assert dh.set_chain_mode(prev) == 1
     with pytest.raises(ValueError):
         dh.set_chain_mode(7)
+
+
+def test_tree_arguments_rejected_before_launch():
+    L = dh.lib()
+    d = _dims()
+    ws = dh.domino_tree_workspace_size(d, 8, 16, 64)
+    assert ws > 0
+    assert dh.domino_tree_workspace_size(d, 8, 0, 64) == 0
+    assert dh.domino_tree_workspace_size(d, 8, 65, 64) == 0
+    assert dh.domino_tree_workspace_size(d, 8, 16, 257) == 0
+    good = dict(dims=ctypes.byref(d), w=ctypes.byref(_weights()), H=FAKE, Lb=FAKE, t0=FAKE, B=8, N=16, M=64,
+                par=FAKE, tok=FAKE, dep=None, sc=None, ws=FAKE, wsb=ws - 1, s=None)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return L.domino_tree_draft(*a.values())
+
+    assert call() == dh.ERR_WORKSPACE  # one byte short: still no launch
+    for kw, msg in ((dict(N=0), "nodes"), (dict(N=65), "nodes"), (dict(M=0), "topm"), (dict(M=300), "topm"),
+                    (dict(par=None, wsb=1 << 40), "out_parents"), (dict(tok=None, wsb=1 << 40), "out_tokens"),
+                    (dict(sc=FAKE + 8, wsb=1 << 40), "out_scores"), (dict(H=None, wsb=1 << 40), "H")):
+        assert call(**kw) == dh.ERR_INVALID_ARGUMENT, kw
+        assert msg in dh.last_error()
+    small_v = _dims(vocab=50)
+    assert call(dims=ctypes.byref(small_v), M=64, wsb=1 << 40) == dh.ERR_INVALID_ARGUMENT
+    assert "vocabulary" in dh.last_error()
+    assert L.domino_tree_candidates(ctypes.byref(d), FAKE, 2, 0, FAKE, FAKE, None) == dh.ERR_INVALID_ARGUMENT
+    assert L.domino_tree_candidates(ctypes.byref(d), None, 2, 8, FAKE, FAKE, None) == dh.ERR_INVALID_ARGUMENT
+    assert L.domino_tree_candidates(ctypes.byref(d), FAKE, 0, 8, None, None, None) == dh.OK

@@ -1,0 +1,144 @@
+"""GPU parity of the best-first tree and its top-M candidate lists against the oracle.
+
+Both sides receive the same fp32 base logits (the oracle's own, or a seeded
+draw at the full shape), so every decision is taken on identical inputs; the
+tree is scored in fp64 on both sides.  Parents, tokens and depths must be
+identical, scores equal within 1e-9.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_head_amd as dh
+import oracle
+import synth
+from gpu_common import say, weights_for
+from helpers import small_config
+
+pytestmark = pytest.mark.gpu
+
+SCORE_TOL = 1e-9
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    dh.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _gpu_tree(cfg, w, H, Lb, t0, N, M):
+    head = dh.DraftHead.from_config(cfg, w)
+    out, ws = head.tree_draft(head.upload(H), head.upload(Lb), head.upload(t0), N, M)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}, dh.DraftHead.device_status(ws)
+
+
+def _compare(g, o, label):
+    for k in ("parents", "tokens", "depth"):
+        assert np.array_equal(g[k], o[k]), f"{label}: {k} differ\n{g[k]}\n{o[k]}"
+    fin = np.isfinite(o["scores"])
+    assert np.array_equal(fin, np.isfinite(g["scores"]))
+    assert np.all(np.abs(g["scores"][fin] - o["scores"][fin]) <= SCORE_TOL), label
+
+
+@pytest.mark.parametrize("d,V,Hs,r,P,B,N,M,dtype", [
+    (16, 37, 8, 8, 4, 2, 16, 3, "f32"),
+    (64, 1003, 40, 24, 6, 3, 16, 8, "bf16"),
+    (96, 2051, 64, 64, 16, 5, 16, 64, "bf16"),
+    (48, 515, 16, 16, 5, 9, 40, 5, "bf16"),      # more sequences than one GRU pass
+    (32, 300, 8, 32, 3, 2, 64, 256, "f32"),      # largest budget and candidate count
+    (32, 64, 8, 8, 1, 2, 10, 4, "bf16"),         # one position: the tree runs out of nodes
+])
+def test_tree_matches_oracle(d, V, Hs, r, P, B, N, M, dtype):
+    cfg = small_config(d=d, V=V, Hs=Hs, r=r, P=P, B=B, dtype=dtype, biases=True)
+    say(f"case tree d={d} V={V} Hs={Hs} r={r} P={P} B={B} N={N} M={M} {dtype}")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    m = oracle.Model.from_config(cfg, w)
+    Lb = m.base_logits(inp["H"])
+    g, st = _gpu_tree(cfg, w, inp["H"], Lb, inp["t0"], N, M)
+    assert st == 0
+    o = m.tree(inp["H"], Lb, inp["t0"], N, M)
+    _compare(g, o, "small")
+
+
+def test_tree_single_candidate_and_zero_correction():
+    cfg = small_config(d=32, V=211, Hs=16, r=16, P=6, B=3, dtype="bf16", biases=False)
+    say("case tree M=1 / W2=0")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    m = oracle.Model.from_config(cfg, w)
+    Lb = m.base_logits(inp["H"])
+    g, _ = _gpu_tree(cfg, w, inp["H"], Lb, inp["t0"], 9, 1)
+    assert g["tokens"][:, :6].tolist() == np.argmax(Lb, axis=-1).tolist()
+    assert np.all(g["parents"][:, 6:] == -1) and np.all(g["tokens"][:, 6:] == -1)
+    w0 = dict(w)
+    w0["w2"] = np.zeros_like(w["w2"])
+    m0 = oracle.Model.from_config(cfg, w0)
+    g0, _ = _gpu_tree(cfg, w0, inp["H"], Lb, inp["t0"], 16, 4)
+    _compare(g0, m0.tree(inp["H"], Lb, inp["t0"], 16, 4), "zero correction")
+
+
+def test_tree_bad_first_token_flagged():
+    cfg = small_config(d=32, V=101, Hs=16, r=16, P=3, B=2, dtype="bf16")
+    say("case tree bad first token")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    m = oracle.Model.from_config(cfg, w)
+    Lb = m.base_logits(inp["H"])
+    g, st = _gpu_tree(cfg, w, inp["H"], Lb, np.array([cfg.vocab, 3], np.int32), 8, 4)
+    assert st == dh.STATUS_BAD_FIRST_TOKEN
+    o = m.tree(inp["H"], Lb, np.array([0, 3], np.int32), 8, 4)  # drafted from token 0 instead
+    _compare(g, o, "bad first token")
+
+
+def test_tree_full_size():
+    key = "qwen3_4b_tree"
+    cfg = synth.CONFIGS[key]
+    say(f"case tree full {key}")
+    w = weights_for("qwen3_4b_b1")  # same weights (seed 4)
+    inp = synth.make_inputs(cfg)
+    # base logits with the distribution of H W_lm^T at these shapes (std ~ 1.01), drawn directly
+    Lb = synth.normal((cfg.batch, cfg.block, cfg.vocab), 1.0, cfg.input_seed, 20, "f32")
+    head = dh.DraftHead.from_config(cfg, w)
+    out, ws = head.tree_draft(head.upload(inp["H"]), head.upload(Lb), head.upload(inp["t0"]), cfg.nodes, cfg.topm)
+    torch.cuda.synchronize()
+    assert dh.DraftHead.device_status(ws) == 0
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    o = oracle.Model.from_config(cfg, w).tree(inp["H"], Lb, inp["t0"], cfg.nodes, cfg.topm)
+    _compare(g, o, key)
+
+
+@pytest.mark.parametrize("kind", ["random", "ties", "constant", "ascending", "small_v"])
+def test_candidates_match_oracle_topm(kind):
+    say(f"case top-M {kind}")
+    B, P, V, M = 2, 3, 5003, 64
+    rng = np.random.default_rng(5)
+    if kind == "random":
+        Lb = rng.standard_normal((B, P, V)).astype(np.float32)
+    elif kind == "ties":
+        Lb = (np.round(rng.standard_normal((B, P, V)) * 2) / 2).astype(np.float32)
+        Lb[0, 0, :10] = -0.0
+        Lb[0, 0, 10:20] = 0.0
+    elif kind == "constant":
+        Lb = np.full((B, P, V), 0.25, np.float32)
+    elif kind == "ascending":
+        Lb = np.tile(np.linspace(-3, 3, V, dtype=np.float32), (B, P, 1))
+    else:
+        V, M = 70, 70
+        Lb = rng.standard_normal((B, P, V)).astype(np.float32)
+    dims = dh.make_dims(16, V, 8, 8, P, "bf16")
+    x = torch.from_numpy(np.ascontiguousarray(Lb)).cuda()
+    idx = torch.empty((B, P, M), dtype=torch.int32, device="cuda")
+    val = torch.empty((B, P, M), dtype=torch.float32, device="cuda")
+    dh.domino_tree_candidates(dims, x, B, M, idx, val)
+    torch.cuda.synchronize()
+    gi, gv = idx.cpu().numpy(), val.cpu().numpy()
+    for b in range(B):
+        for p in range(P):
+            row = Lb[b, p] + np.float32(0.0)  # -0 counts as +0 on both sides
+            oi, ov = oracle.topm(row, M)
+            assert np.array_equal(gi[b, p], oi), (kind, b, p)
+            assert np.array_equal(gv[b, p], ov)
