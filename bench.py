@@ -81,6 +81,19 @@ def algorithmic_traffic(cfg, B, write_logits):
     return {"base": (base_bytes, base_flops), "chain": (chain_bytes, chain_flops), "chain_step_bytes": step}
 
 
+def tree_traffic(cfg, B):
+    """Bytes and flops of one tree call: the top-M pass over every base-logit row, then
+    N rounds that each read the GRU weights, the state half of W1 and, per sequence,
+    M rows of W2, M base-logit entries, one embedding row and two fp64 states."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    d, V, Hs, r, P, N, M = cfg.hidden, cfg.vocab, cfg.gru_hidden, cfg.rank, cfg.block, cfg.nodes, cfg.topm
+    topm_bytes = B * P * V * 4
+    rnd = 3 * Hs * (d + Hs) * es + r * Hs * es + B * (M * r * es + M * 4 + d * es + 2 * Hs * 8)
+    byts = topm_bytes + B * P * d * es + r * d * es + N * rnd
+    flops = 2.0 * B * N * (3 * Hs * (d + Hs) + r * Hs + M * r) + 2.0 * B * P * r * d
+    return byts, flops
+
+
 def source_digest():
     """sha256 of the HIP sources; counter summaries are valid only for the sources they were taken on."""
     h = hashlib.sha256()
@@ -116,14 +129,17 @@ def cpu_baseline(cfg, w, inp, target_s):
         b = done % B
         H = np.ascontiguousarray(inp["H"][b:b + 1])
         Lb = m.base_logits(H)
-        m.chain(H, Lb, inp["t0"][b:b + 1], want_logits=False)
+        if cfg.tree:
+            m.tree(H, Lb, inp["t0"][b:b + 1], cfg.nodes, cfg.topm)
+        else:
+            m.chain(H, Lb, inp["t0"][b:b + 1], want_logits=False)
         done += 1
         el = time.perf_counter() - t_start
         if el >= target_s or done >= 64:
             break
     return {"value": done / el, "unit": "draft blocks/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{done} whole blocks (one sequence each: base logits + {cfg.block}-step chain) of "
-                      f"{cfg.name}, {el:.1f} s"}
+            "sample": f"{done} whole blocks (one sequence each: base logits + "
+                      f"{f'{cfg.nodes}-node tree' if cfg.tree else f'{cfg.block}-step chain'}) of {cfg.name}, {el:.1f} s"}
 
 
 def main():
@@ -160,13 +176,23 @@ def main():
     Lb = torch.empty((B, P, V), dtype=torch.float32, device=dev)
     toks = torch.empty((B, P), dtype=torch.int32, device=dev)
     logits = torch.empty((B, P, V), dtype=torch.float32, device=dev) if args.logits else None
-    ws = head.workspace(B)
+    if cfg.tree:
+        N, Mc = cfg.nodes, cfg.topm
+        tree_out = {k: torch.empty((B, N), dtype=torch.int32, device=dev) for k in ("parents", "tokens", "depth")}
+        tree_scores = torch.empty((B, N), dtype=torch.float64, device=dev)
+        ws = torch.zeros(dh.domino_tree_workspace_size(head.dims, B, N, Mc), dtype=torch.uint8, device=dev)
+    else:
+        ws = head.workspace(B)
     dh.set_chain_mode(args.chain_mode)
     stream = torch.cuda.current_stream()
 
     def step():
         dh.domino_base_logits(head.dims, head.weights, H, B, Lb, stream)
-        dh.domino_draft_chain(head.dims, head.weights, H, Lb, t0, B, toks, logits, ws, ws.numel(), stream)
+        if cfg.tree:
+            dh.domino_tree_draft(head.dims, head.weights, H, Lb, t0, B, N, Mc, tree_out["parents"],
+                                 tree_out["tokens"], tree_out["depth"], tree_scores, ws, ws.numel(), stream)
+        else:
+            dh.domino_draft_chain(head.dims, head.weights, H, Lb, t0, B, toks, logits, ws, ws.numel(), stream)
 
     print("bench: warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -204,6 +230,8 @@ def main():
     assert dh.DraftHead.device_status(ws) == 0
 
     tr = algorithmic_traffic(cfg, B, args.logits)
+    if cfg.tree:
+        tr["chain"] = tree_traffic(cfg, B)
     peak_mfma = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     kernel_key = {"base": "base_gemm", "chain": "chain_steps"}
     kernels = {}
@@ -223,7 +251,11 @@ def main():
         k["flops"] = flops
     dom = "chain" if t_chain >= t_base else "base"
     roof = {kk: kernels[dom][kk] for kk in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
-    roof["kernel"] = "chain_persistent (domino_draft_chain steps)" if dom == "chain" else "LM-head GEMM (domino_base_logits)"
+    if cfg.tree:
+        roof["kernel"] = "tree launches (domino_tree_draft)" if dom == "chain" else "LM-head GEMM (domino_base_logits)"
+    else:
+        roof["kernel"] = ("chain_persistent (domino_draft_chain steps)" if dom == "chain"
+                          else "LM-head GEMM (domino_base_logits)")
 
     value = B / (ms_per_step * 1e-3)
     out = {
@@ -241,7 +273,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": B, "block": P, "hidden": cfg.hidden, "vocab": V,
                    "gru_hidden": cfg.gru_hidden, "rank": cfg.rank, "chain_mode": args.chain_mode,
-                   "write_logits": bool(args.logits), "parallelism": "none (one GPU)"},
+                   "write_logits": bool(args.logits), "parallelism": "none (one GPU)",
+                   **({"tree_nodes": cfg.nodes, "tree_topm": cfg.topm} if cfg.tree else {})},
         "roofline": roof,
         "kernels": kernels,
         "wall_s_timed": wall,

@@ -22,7 +22,7 @@ STATUS_FINE, STATUS_BAD_FIRST_TOKEN, STATUS_TIMEOUT = 0, 1, 2
 
 EXPORTS = ("domino_version", "domino_last_error", "domino_base_logits", "domino_chain_workspace_size",
            "domino_draft_chain", "domino_set_chain_mode", "domino_set_timing_events", "domino_tree_workspace_size",
-           "domino_tree_draft", "domino_tree_candidates")
+           "domino_tree_draft", "domino_tree_candidates", "domino_tree_candidates_workspace_size")
 
 
 class DominoError(RuntimeError):
@@ -69,7 +69,9 @@ def lib():
         L.domino_tree_workspace_size.restype = sz
         L.domino_tree_workspace_size.argtypes = [P, i32, i32, i32]
         L.domino_tree_candidates.restype = ctypes.c_int
-        L.domino_tree_candidates.argtypes = [P, P, i32, i32, P, P, P]
+        L.domino_tree_candidates.argtypes = [P, P, i32, i32, P, P, P, sz, P]
+        L.domino_tree_candidates_workspace_size.restype = sz
+        L.domino_tree_candidates_workspace_size.argtypes = [P, i32, i32]
         L.domino_tree_draft.restype = ctypes.c_int
         L.domino_tree_draft.argtypes = [P, P, P, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
         _lib = L
@@ -141,9 +143,14 @@ def domino_draft_chain(dims: Dims, weights: Weights, H, base_logits, first_token
                                     _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
-def domino_tree_candidates(dims: Dims, base_logits, batch: int, topm: int, out_index, out_value, stream=None):
+def domino_tree_candidates_workspace_size(dims: Dims, batch: int, topm: int) -> int:
+    return int(lib().domino_tree_candidates_workspace_size(ctypes.byref(dims), int(batch), int(topm)))
+
+
+def domino_tree_candidates(dims: Dims, base_logits, batch: int, topm: int, out_index, out_value, workspace,
+                           workspace_bytes: int, stream=None):
     _check(lib().domino_tree_candidates(ctypes.byref(dims), _ptr(base_logits), int(batch), int(topm), _ptr(out_index),
-                                        _ptr(out_value), _stream(stream)))
+                                        _ptr(out_value), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def domino_tree_workspace_size(dims: Dims, batch: int, nodes: int, topm: int) -> int:

@@ -200,8 +200,14 @@ domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* 
   return ok();
 }
 
+size_t domino_tree_candidates_workspace_size(const domino_dims* dims, int32_t batch, int32_t topm) {
+  if (check_dims(dims) != DOMINO_OK || batch < 0 || topm < 1 || topm > 256) return 0;
+  return dh::topm_scratch_bytes((batch > 0 ? batch : 1) * dims->block, topm);
+}
+
 domino_status domino_tree_candidates(const domino_dims* dims, const float* base_logits, int32_t batch, int32_t topm,
-                                     int32_t* out_index, float* out_value, void* stream) {
+                                     int32_t* out_index, float* out_value, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
   domino_status st = check_dims(dims);
   if (st != DOMINO_OK) return st;
   if (batch < 0) return fail(DOMINO_ERR_INVALID_ARGUMENT, "batch %d is negative", batch);
@@ -211,7 +217,12 @@ domino_status domino_tree_candidates(const domino_dims* dims, const float* base_
   REQUIRE_PTR(base_logits, "base_logits");
   REQUIRE_PTR(out_index, "out_index");
   REQUIRE_PTR(out_value, "out_value");
-  hipError_t e = dh::launch_topm(base_logits, batch * dims->block, dims->vocab, topm, out_index, out_value,
+  REQUIRE_PTR(workspace, "workspace");
+  const size_t need = domino_tree_candidates_workspace_size(dims, batch, topm);
+  if (workspace_bytes < need)
+    return fail(DOMINO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes,
+                need);
+  hipError_t e = dh::launch_topm(base_logits, batch * dims->block, dims->vocab, topm, workspace, out_index, out_value,
                                  (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "top-M launch");
   return ok();
@@ -235,6 +246,9 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   if (topm < 1 || topm > 256) return fail(DOMINO_ERR_INVALID_ARGUMENT, "topm %d must be in [1, 256]", topm);
   if (topm > dims->vocab) return fail(DOMINO_ERR_INVALID_ARGUMENT, "topm %d exceeds the vocabulary", topm);
   if (dims->gru_hidden > 4096) return fail(DOMINO_ERR_UNSUPPORTED, "gru_hidden %d exceeds 4096 for the tree", dims->gru_hidden);
+  if (dh::tree_gru_lds(dims->hidden, dims->gru_hidden, dims->dtype) > 156 * 1024)
+    return fail(DOMINO_ERR_UNSUPPORTED, "hidden %d with gru_hidden %d exceeds the tree's LDS budget", dims->hidden,
+                dims->gru_hidden);
   if (batch == 0) return ok();
   REQUIRE_PTR(w->embed, "weights.embed");
   REQUIRE_PTR(w->w_ih, "weights.w_ih");
@@ -286,6 +300,8 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   t.out_tokens = out_tokens;
   t.out_depth = out_depth;
   t.out_scores = out_scores;
+  t.seg_keys = (uint64_t*)(ws + L.seg_keys);
+  t.act = (double*)(ws + L.act);
   t.cand_idx = (int32_t*)(ws + L.cand_idx);
   t.cand_val = (float*)(ws + L.cand_val);
   t.zh = (double*)(ws + L.zh);
@@ -296,7 +312,7 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   t.cur = ws + L.cur;
   t.status = (int32_t*)(ws + L.status);
   t.heap_cap = L.heap_cap;
-  hipError_t e = dh::launch_tree(t, true, (hipStream_t)stream);
+  hipError_t e = dh::launch_tree(t, true, (hipStream_t)stream, g_chain_start, g_chain_stop);
   if (e != hipSuccess) return device_fail(e, "tree launch");
   return ok();
 }

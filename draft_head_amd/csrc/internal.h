@@ -74,9 +74,11 @@ struct TreeArgs {
   int32_t* out_tokens;      // [B][N]
   int32_t* out_depth;       // [B][N] or null
   double* out_scores;       // [B][N] or null
+  uint64_t* seg_keys;       // [B*P][segments][M] per-segment top-M keys
   int32_t* cand_idx;        // [B][P][M] top-M candidates per row
   float* cand_val;          // [B][P][M]
   double* zh;               // [B][P][r] W1[:, :d] H in fp64
+  double* act;              // [B][r] bottleneck of the node being expanded, fp64
   double* states;           // [B][N+1][Hs] fp64 GRU state per node (slot 0 = anchor)
   double* heap_score;       // [B][heap_cap]
   int4* heap_meta;          // [B][heap_cap] (parent, rank, token, depth)
@@ -87,13 +89,17 @@ struct TreeArgs {
 };
 
 struct TreeLayout {
-  size_t status, cand_idx, cand_val, zh, states, heap_score, heap_meta, heap_count, cur, total;
+  size_t status, seg_keys, cand_idx, cand_val, zh, act, states, heap_score, heap_meta, heap_count, cur, total;
   int heap_cap;
 };
 TreeLayout tree_layout(int d, int Hs, int r, int P, int group, int N, int M);
 
-hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s);
-// top-M of each of `rows` rows of length V, ordered (value desc, index asc)
-hipError_t launch_topm(const float* Lb, int rows, int V, int M, int32_t* idx, float* val, hipStream_t s);
+hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
+// dynamic LDS of the tree's GRU kernel (must stay within the CU's 160 KB)
+size_t tree_gru_lds(int d, int Hs, int dtype);
+// top-M of each of `rows` rows of length V, ordered (value desc, index asc);
+// scratch holds topm_scratch_bytes(rows, M)
+size_t topm_scratch_bytes(int rows, int M);
+hipError_t launch_topm(const float* Lb, int rows, int V, int M, void* scratch, int32_t* idx, float* val, hipStream_t s);
 
 }  // namespace dh

@@ -10,14 +10,16 @@
 // structure does not depend on summation order.
 //
 // Kernels, in launch order for one call:
-//  tree_topm        T1: top-M of each base-logit row, ordered (value desc,
-//                   index asc); one workgroup per row, a single pass with a
-//                   running threshold and an LDS buffer trimmed by a bitonic sort
-//  tree_prologue    W1[:, :d] H for every position in fp64; empty heaps; the
-//                   anchor as each sequence's first node to expand
+//  topm_segment     T1: top-M of each segment of each base-logit row, ordered
+//                   (value desc, index asc): a single pass with a running
+//                   threshold and an LDS buffer trimmed by a bitonic sort
+//  topm_merge       the row's top-M from its segment lists
+//  tree_zh          W1[:, :d] H for every position, fp64
+//  tree_init        empty heaps; the anchor as each sequence's first node
 //  per round (N rounds):
 //   tree_gru        fp64 GRU step of each sequence's current node
-//   tree_expand_pop push the node's M children, then pop the best entry
+//   tree_bottleneck fp64 a = SiLU(W1 [H ; S] + b1) of those nodes
+//   tree_score_pop  score and push the node's M children, then pop the best entry
 #include <math.h>
 
 #include "device.h"
@@ -26,9 +28,11 @@
 namespace dh {
 
 // ---- T1: top-M candidates per row ---------------------------------------------------
-constexpr int kTopCap = 2048;  // LDS key buffer; M <= kTopCap / 2
+// Each row is split into kTopSegs segments; one workgroup per segment keeps the
+// segment's top M, then one workgroup per row merges the segment lists.
+constexpr int kTopCap = 2048;  // LDS key buffer; M <= kTopCap / kTopSegs
+constexpr int kTopSegs = 8;
 
-__device__ __forceinline__ uint64_t cand_key(float v, uint32_t idx) { return amax_key(v, idx); }
 __device__ __forceinline__ float key_value(uint64_t k) {
   uint32_t u = (uint32_t)(k >> 32);
   u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
@@ -54,13 +58,20 @@ __device__ void bitonic_desc(uint64_t* buf) {
   }
 }
 
-__global__ __launch_bounds__(256) void tree_topm(const float* __restrict__ Lb, int V, int M, int32_t* cand_idx,
-                                                 float* cand_val, int32_t* status, int reset_status) {
+// Top M keys (value bits, inverted index; key 0 = none) of one row segment.
+// A single pass: keys above the running threshold (the M-th best so far) are
+// appended to an LDS buffer, which is sorted and cut back to M whenever fewer
+// than 1024 slots remain.  The next 1024 elements are loaded while the
+// current ones are filtered.
+__global__ __launch_bounds__(256) void topm_segment(const float* __restrict__ Lb, int V, int M, uint64_t* seg_keys,
+                                                    int32_t* status, int reset_status) {
   __shared__ uint64_t buf[kTopCap];
   __shared__ int count;
   __shared__ uint64_t thresh;
-  const int row = blockIdx.x;
-  if (reset_status && row == 0 && threadIdx.x == 0) *status = 0;
+  const int seg = blockIdx.x, row = blockIdx.y;
+  if (reset_status && seg == 0 && row == 0 && threadIdx.x == 0) *status = 0;
+  const int per = (V + kTopSegs - 1) / kTopSegs;
+  const int v_begin = seg * per, v_end = min(V, v_begin + per);
   const float* x = Lb + (size_t)row * V;
   if (threadIdx.x == 0) {
     count = 0;
@@ -68,15 +79,24 @@ __global__ __launch_bounds__(256) void tree_topm(const float* __restrict__ Lb, i
   }
   for (int i = threadIdx.x; i < kTopCap; i += blockDim.x) buf[i] = 0;
   __syncthreads();
-  // chunks of 1024 elements: at most 1024 appends per chunk, and the buffer is
-  // trimmed to M whenever fewer than 1024 free slots remain
-  for (int c0 = 0; c0 < V; c0 += 1024) {
+  float cur[4], nxt[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int v = v_begin + q * 256 + threadIdx.x;
+    cur[q] = v < v_end ? x[v] : 0.f;
+  }
+  for (int c0 = v_begin; c0 < v_end; c0 += 1024) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v = c0 + 1024 + q * 256 + threadIdx.x;
+      nxt[q] = v < v_end ? x[v] : 0.f;
+    }
     const uint64_t th = thresh;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int v = c0 + q * 256 + threadIdx.x;
-      if (v < V) {
-        const uint64_t k = cand_key(x[v], (uint32_t)v);
+      if (v < v_end) {
+        const uint64_t k = amax_key(cur[q], (uint32_t)v);
         if (k > th) buf[atomicAdd(&count, 1)] = k;
       }
     }
@@ -91,7 +111,21 @@ __global__ __launch_bounds__(256) void tree_topm(const float* __restrict__ Lb, i
       for (int i = M + threadIdx.x; i < kTopCap; i += blockDim.x) buf[i] = 0;
       __syncthreads();
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
   }
+  bitonic_desc(buf);
+  uint64_t* out = seg_keys + ((size_t)row * kTopSegs + seg) * M;
+  for (int j = threadIdx.x; j < M; j += blockDim.x) out[j] = buf[j];
+}
+
+// merge the segment lists of one row into its top M
+__global__ __launch_bounds__(256) void topm_merge(const uint64_t* seg_keys, int M, int32_t* cand_idx, float* cand_val) {
+  __shared__ uint64_t buf[kTopCap];
+  const int row = blockIdx.x;
+  const uint64_t* src = seg_keys + (size_t)row * kTopSegs * M;
+  for (int i = threadIdx.x; i < kTopCap; i += blockDim.x) buf[i] = i < kTopSegs * M ? src[i] : 0;
+  __syncthreads();
   bitonic_desc(buf);
   for (int j = threadIdx.x; j < M; j += blockDim.x) {
     const uint64_t k = buf[j];
@@ -111,109 +145,169 @@ struct TreeCur {
   double score;         // its cumulative score
 };
 
-__device__ __forceinline__ double bf_or_f(const void* p, int dtype, size_t i) {
-  return dtype == kBF16 ? (double)bf2f(((const uint16_t*)p)[i]) : (double)((const float*)p)[i];
-}
-
-// W1[:, :d] H[b][p] in fp64, one output per thread; empty heaps; anchors
-__global__ __launch_bounds__(256) void tree_prologue(TreeArgs t) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const int n = t.B * t.P * t.r;
-  if (i < n) {
-    const int k = i % t.r, row = i / t.r;  // row = b * P + p
-    double s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-    const size_t w0 = (size_t)k * (t.d + t.Hs), h0 = (size_t)row * t.d;
-    int j = 0;
-    for (; j + 4 <= t.d; j += 4) {
-      s0 += bf_or_f(t.w1, t.dtype, w0 + j) * bf_or_f(t.H, t.dtype, h0 + j);
-      s1 += bf_or_f(t.w1, t.dtype, w0 + j + 1) * bf_or_f(t.H, t.dtype, h0 + j + 1);
-      s2 += bf_or_f(t.w1, t.dtype, w0 + j + 2) * bf_or_f(t.H, t.dtype, h0 + j + 2);
-      s3 += bf_or_f(t.w1, t.dtype, w0 + j + 3) * bf_or_f(t.H, t.dtype, h0 + j + 3);
-    }
-    for (; j < t.d; ++j) s0 += bf_or_f(t.w1, t.dtype, w0 + j) * bf_or_f(t.H, t.dtype, h0 + j);
-    t.zh[i] = (s0 + s1) + (s2 + s3);
-  }
-  if (i < t.B) {
-    t.heap_count[i] = 0;
-    TreeCur c;
-    int32_t t0 = t.t0[i];
-    if (t0 < 0 || t0 >= t.V) {
-      atomicMax(t.status, 1);
-      t0 = 0;
-    }
-    c.slot = 0;
-    c.parent_slot = -1;
-    c.token = t0;
-    c.depth = 0;
-    c.expand = t.P > 0 ? 1 : 0;
-    c.node = -1;
-    c.score = 0.0;
-    reinterpret_cast<TreeCur*>(t.cur)[i] = c;
-  }
-}
-
-// ---- fp64 GRU step of each sequence's current node -----------------------------------------
-// Workgroup = 4 GRU units, wave w = unit 4*blockIdx + w.  Lanes split k in
-// runs of 8; 6 partial sums (gi_r, gi_z, gi_n, gh_r, gh_z, gh_n) per sequence
-// are reduced across the wave, and lane b finishes sequence b.
-constexpr int kTreeSeqs = 8;  // sequences per GRU pass
-
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
   return v;
 }
 
-__global__ __launch_bounds__(256) void tree_gru(TreeArgs t, int b0) {
+// 8 consecutive stored elements widened to fp64
+__device__ __forceinline__ void load8_f64(const void* base, int dtype, size_t i, double (&o)[8]) {
+  if (dtype == kBF16) {
+    const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)base + i);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = (double)__uint_as_float(w[e] << 16);
+      o[2 * e + 1] = (double)__uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* q = reinterpret_cast<const float4*>((const float*)base + i);
+    const float4 a = q[0], b = q[1];
+    o[0] = a.x, o[1] = a.y, o[2] = a.z, o[3] = a.w, o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
+  }
+}
+
+// W1[:, :d] H[b][p] in fp64.  Workgroup = one row of H and 16 rows of W1;
+// wave w takes 4 W1 rows, lanes split d in runs of 8.
+__global__ __launch_bounds__(256) void tree_zh(TreeArgs t) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int j = blockIdx.x * 4 + wv;
-  if (j >= t.Hs) return;
+  const int m = blockIdx.y, k0 = blockIdx.x * 16 + wv * 4;
+  const int d = t.d;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int j = lane * 8; j < d; j += 512) {
+    double h[8];
+    load8_f64(t.H, t.dtype, (size_t)m * d + j, h);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (k0 + q >= t.r) break;
+      double w[8];
+      load8_f64(t.w1, t.dtype, (size_t)(k0 + q) * (d + t.Hs) + j, w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q] += w[e] * h[e];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const double v = wave_sum(acc[q]);
+    if (lane == 0 && k0 + q < t.r) t.zh[(size_t)m * t.r + k0 + q] = v;
+  }
+}
+
+// empty heaps; the anchor as each sequence's first node to expand
+__global__ void tree_init(TreeArgs t) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= t.B) return;
+  t.heap_count[b] = 0;
+  int32_t t0 = t.t0[b];
+  if (t0 < 0 || t0 >= t.V) {
+    atomicMax(t.status, 1);
+    t0 = 0;
+  }
+  TreeCur c;
+  c.slot = 0;
+  c.parent_slot = -1;
+  c.token = t0;
+  c.depth = 0;
+  c.expand = t.P > 0 ? 1 : 0;
+  c.node = -1;
+  c.score = 0.0;
+  reinterpret_cast<TreeCur*>(t.cur)[b] = c;
+}
+
+// ---- fp64 GRU step of each sequence's current node -----------------------------------------
+// Workgroup = 4 GRU units, wave w = unit 4*blockIdx + w.  The current nodes'
+// embedding rows (stored type) and parent states (fp64) of up to kTreeSeqs
+// sequences are staged in LDS; lanes split k in runs of 8 and the 6 partial
+// sums (gi_r, gi_z, gi_n, gh_r, gh_z, gh_n) per sequence are reduced across
+// the wave; lane s finishes sequence s.
+constexpr int kTreeSeqs = 8;
+
+__global__ __launch_bounds__(256) void tree_gru(TreeArgs t, int b0) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  __shared__ TreeCur sc[kTreeSeqs];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int d = t.d, Hs = t.Hs;
-  const TreeCur* cur = reinterpret_cast<const TreeCur*>(t.cur);
+  const int es = t.dtype == kBF16 ? 2 : 4;
   const int nb = min(kTreeSeqs, t.B - b0);
+  double* hl = reinterpret_cast<double*>(lds);                      // [kTreeSeqs][Hs]
+  unsigned char* xl = lds + (size_t)kTreeSeqs * Hs * sizeof(double);  // [kTreeSeqs][d] stored type
+  if (threadIdx.x < nb) sc[threadIdx.x] = reinterpret_cast<const TreeCur*>(t.cur)[b0 + threadIdx.x];
+  __syncthreads();
+  // stage every sequence's parent state and embedding row in one flat pass
+  {
+    const int hchunks = Hs / 2, xchunks = d * es / 16;  // 16-byte pieces
+    const int per = hchunks + xchunks;
+    for (int i = threadIdx.x; i < nb * per; i += blockDim.x) {
+      const int s = i / per, q = i - s * per;
+      const TreeCur& c = sc[s];
+      if (q < hchunks) {
+        double2 v = make_double2(0.0, 0.0);
+        if (c.expand && c.parent_slot >= 0)
+          v = reinterpret_cast<const double2*>(t.states + ((size_t)(b0 + s) * (t.N + 1) + c.parent_slot) * Hs)[q];
+        reinterpret_cast<double2*>(hl + (size_t)s * Hs)[q] = v;
+      } else {
+        const int x = q - hchunks;
+        const unsigned char* xe = (const unsigned char*)t.embed + (size_t)c.token * d * es;
+        *reinterpret_cast<uint4*>(xl + (size_t)s * d * es + (size_t)x * 16) =
+            *reinterpret_cast<const uint4*>(xe + (size_t)x * 16);
+      }
+    }
+  }
+  __syncthreads();
+  const int j = blockIdx.x * 4 + wv;
+  if (j >= Hs) return;
+  int expand[kTreeSeqs];
+#pragma unroll
+  for (int s = 0; s < kTreeSeqs; ++s) expand[s] = s < nb ? sc[s].expand : 0;
   double acc[kTreeSeqs][6];
 #pragma unroll
   for (int s = 0; s < kTreeSeqs; ++s)
 #pragma unroll
     for (int g = 0; g < 6; ++g) acc[s][g] = 0.0;
-  // input half: x = E[token]
-  for (int k0 = lane * 8; k0 < d; k0 += 512) {
-    double w[3][8];
+  // input half, four 8-wide runs of every gate row in flight at a time
+  constexpr int R = 4;
+  for (int k0 = lane * 8; k0 < d; k0 += 512 * R) {
+    double w[R][3][8];
 #pragma unroll
-    for (int g = 0; g < 3; ++g)
+    for (int u = 0; u < R; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[g][e] = bf_or_f(t.w_ih, t.dtype, ((size_t)g * Hs + j) * d + k0 + e);
+      for (int g = 0; g < 3; ++g)
+        if (k0 + u * 512 < d) load8_f64(t.w_ih, t.dtype, ((size_t)g * Hs + j) * d + k0 + u * 512, w[u][g]);
 #pragma unroll
-    for (int s = 0; s < kTreeSeqs; ++s) {
-      if (s >= nb) break;
-      const TreeCur c = cur[b0 + s];
-      if (!c.expand) continue;
+    for (int u = 0; u < R; ++u) {
+      if (k0 + u * 512 >= d) break;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double x = bf_or_f(t.embed, t.dtype, (size_t)c.token * d + k0 + e);
+      for (int s = 0; s < kTreeSeqs; ++s) {
+        if (!expand[s]) continue;
+        double x[8];
+        load8_f64(xl + (size_t)s * d * es, t.dtype, k0 + u * 512, x);
 #pragma unroll
-        for (int g = 0; g < 3; ++g) acc[s][g] += w[g][e] * x;
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int g = 0; g < 3; ++g) acc[s][g] += w[u][g][e] * x[e];
       }
     }
   }
-  // hidden half: the parent's state (zero for the anchor)
-  for (int k0 = lane * 8; k0 < Hs; k0 += 512) {
-    double w[3][8];
+  for (int k0 = lane * 8; k0 < Hs; k0 += 512 * R) {
+    double w[R][3][8];
 #pragma unroll
-    for (int g = 0; g < 3; ++g)
+    for (int u = 0; u < R; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[g][e] = bf_or_f(t.w_hh, t.dtype, ((size_t)g * Hs + j) * Hs + k0 + e);
+      for (int g = 0; g < 3; ++g)
+        if (k0 + u * 512 < Hs) load8_f64(t.w_hh, t.dtype, ((size_t)g * Hs + j) * Hs + k0 + u * 512, w[u][g]);
 #pragma unroll
-    for (int s = 0; s < kTreeSeqs; ++s) {
-      if (s >= nb) break;
-      const TreeCur c = cur[b0 + s];
-      if (!c.expand || c.parent_slot < 0) continue;
-      const double* hp = t.states + ((size_t)(b0 + s) * (t.N + 1) + c.parent_slot) * Hs;
+    for (int u = 0; u < R; ++u) {
+      if (k0 + u * 512 >= Hs) break;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double h = hp[k0 + e];
+      for (int s = 0; s < kTreeSeqs; ++s) {
+        if (!expand[s]) continue;
 #pragma unroll
-        for (int g = 0; g < 3; ++g) acc[s][3 + g] += w[g][e] * h;
+        for (int e = 0; e < 8; ++e) {
+          const double h = hl[(size_t)s * Hs + k0 + u * 512 + e];
+#pragma unroll
+          for (int g = 0; g < 3; ++g) acc[s][3 + g] += w[u][g][e] * h;
+        }
       }
     }
   }
@@ -221,23 +315,57 @@ __global__ __launch_bounds__(256) void tree_gru(TreeArgs t, int b0) {
   for (int s = 0; s < kTreeSeqs; ++s)
 #pragma unroll
     for (int g = 0; g < 6; ++g) acc[s][g] = wave_sum(acc[s][g]);
-  if (lane < nb) {
-    const TreeCur c = cur[b0 + lane];
-    if (c.expand) {
-      double a6[6];
+  double a6[6] = {0, 0, 0, 0, 0, 0};
+  int mine = 0;
 #pragma unroll
-      for (int s = 0; s < kTreeSeqs; ++s)
-        if (s == lane)
+  for (int s = 0; s < kTreeSeqs; ++s)
+    if (s == lane) {
+      mine = expand[s];
 #pragma unroll
-          for (int g = 0; g < 6; ++g) a6[g] = acc[s][g];
-      auto bi = [&](int row) { return t.b_ih ? (double)t.b_ih[row] : 0.0; };
-      auto bh = [&](int row) { return t.b_hh ? (double)t.b_hh[row] : 0.0; };
-      const double r = 1.0 / (1.0 + exp(-(a6[0] + bi(j) + a6[3] + bh(j))));
-      const double z = 1.0 / (1.0 + exp(-(a6[1] + bi(Hs + j) + a6[4] + bh(Hs + j))));
-      const double nn = tanh(a6[2] + bi(2 * Hs + j) + r * (a6[5] + bh(2 * Hs + j)));
-      const double hprev =
-          c.parent_slot < 0 ? 0.0 : t.states[((size_t)(b0 + lane) * (t.N + 1) + c.parent_slot) * Hs + j];
-      t.states[((size_t)(b0 + lane) * (t.N + 1) + c.slot) * Hs + j] = (1.0 - z) * nn + z * hprev;
+      for (int g = 0; g < 6; ++g) a6[g] = acc[s][g];
+    }
+  if (lane < nb && mine) {
+    const TreeCur c = sc[lane];
+    auto bi = [&](int row) { return t.b_ih ? (double)t.b_ih[row] : 0.0; };
+    auto bh = [&](int row) { return t.b_hh ? (double)t.b_hh[row] : 0.0; };
+    const double r = 1.0 / (1.0 + exp(-(a6[0] + bi(j) + a6[3] + bh(j))));
+    const double z = 1.0 / (1.0 + exp(-(a6[1] + bi(Hs + j) + a6[4] + bh(Hs + j))));
+    const double nn = tanh(a6[2] + bi(2 * Hs + j) + r * (a6[5] + bh(2 * Hs + j)));
+    const double hprev = hl[(size_t)lane * Hs + j];
+    t.states[((size_t)(b0 + lane) * (t.N + 1) + c.slot) * Hs + j] = (1.0 - z) * nn + z * hprev;
+  }
+}
+
+// ---- fp64 bottleneck of each sequence's current node: a = SiLU(W1 [H_delta ; S] + b1) -------
+// Workgroup = 16 bottleneck units of one sequence; wave w takes 4, lanes split Hs.
+__global__ __launch_bounds__(256) void tree_bottleneck(TreeArgs t) {
+  __shared__ double S[4096];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int b = blockIdx.y, k0 = blockIdx.x * 16 + wv * 4;
+  const TreeCur c = reinterpret_cast<const TreeCur*>(t.cur)[b];
+  if (!c.expand) return;
+  const int Hs = t.Hs;
+  const double* st = t.states + ((size_t)b * (t.N + 1) + c.slot) * Hs;
+  for (int i = threadIdx.x; i < Hs; i += blockDim.x) S[i] = st[i];
+  __syncthreads();
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int jj = lane * 8; jj < Hs; jj += 512) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (k0 + q >= t.r) break;
+      double w[8];
+      load8_f64(t.w1, t.dtype, (size_t)(k0 + q) * (t.d + Hs) + t.d + jj, w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q] += w[e] * S[jj + e];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const double v = wave_sum(acc[q]);
+    const int k = k0 + q;
+    if (lane == 0 && k < t.r) {
+      const double z = v + t.zh[((size_t)b * t.P + c.depth) * t.r + k] + (t.b1 ? (double)t.b1[k] : 0.0);
+      t.act[(size_t)b * t.r + k] = z / (1.0 + exp(-z));
     }
   }
 }
@@ -249,14 +377,16 @@ __device__ __forceinline__ bool entry_before(double sa, int4 ma, double sb, int4
   return ma.y < mb.y;                    // candidate rank
 }
 
-__global__ __launch_bounds__(256) void tree_expand_pop(TreeArgs t, int k) {
-  __shared__ double S[4096];   // the node's GRU state (Hs <= 4096)
+// One workgroup per sequence.  Wave w scores candidates w, w+4, ...: lanes
+// split the bottleneck in runs of 4 and the partial dot products are reduced
+// across the wave.
+__global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
   __shared__ double a[256];    // bottleneck (r <= 256)
   __shared__ double l[256];    // corrected candidate logits (M <= 256)
   __shared__ double red_s[256];
   __shared__ int red_i[256];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int Hs = t.Hs, r = t.r, M = t.M, P = t.P, V = t.V;
+  const int r = t.r, M = t.M, P = t.P;
   TreeCur* curp = reinterpret_cast<TreeCur*>(t.cur) + b;
   const TreeCur c = *curp;
   double* hs = t.heap_score + (size_t)b * t.heap_cap;
@@ -265,30 +395,49 @@ __global__ __launch_bounds__(256) void tree_expand_pop(TreeArgs t, int k) {
 
   if (c.expand) {
     const int delta = c.depth;
-    const double* st = t.states + ((size_t)b * (t.N + 1) + c.slot) * Hs;
-    for (int i = tid; i < Hs; i += blockDim.x) S[i] = st[i];
+    for (int i = tid; i < r; i += blockDim.x) a[i] = t.act[(size_t)b * r + i];
     __syncthreads();
-    // a = SiLU(W1 [H_delta ; S] + b1): wave per row, lanes split the state half
-    for (int row = wv; row < r; row += 4) {
-      double s = 0.0;
-      const size_t w0 = (size_t)row * (t.d + Hs) + t.d;
-      for (int jj = lane; jj < Hs; jj += 64) s += bf_or_f(t.w1, t.dtype, w0 + jj) * S[jj];
-      s = wave_sum(s);
-      if (lane == 0) {
-        const double z = s + t.zh[((size_t)b * P + delta) * r + row] + (t.b1 ? (double)t.b1[row] : 0.0);
-        a[row] = z / (1.0 + exp(-z));
-      }
-    }
-    __syncthreads();
-    // corrected candidate logits on row delta
     const int32_t* cidx = t.cand_idx + ((size_t)b * P + delta) * M;
-    const float* Lrow = t.Lb + ((size_t)b * P + delta) * V;
-    for (int j = wv; j < M; j += 4) {
-      const int v = cidx[j];
-      double s = 0.0;
-      for (int kk = lane; kk < r; kk += 64) s += bf_or_f(t.w2, t.dtype, (size_t)v * r + kk) * a[kk];
-      s = wave_sum(s);
-      if (lane == 0) l[j] = (double)Lrow[v] + (t.b2 ? (double)t.b2[v] : 0.0) + s;
+    const float* cval = t.cand_val + ((size_t)b * P + delta) * M;
+    const int kk = lane * 4;
+    // wave w scores candidates w, w+4, ...; 16 W2 rows per batch in flight
+    constexpr int CB = 16;
+    for (int j0 = wv; j0 < M; j0 += 4 * CB) {
+      double w[CB][4];
+      int vv[CB];
+#pragma unroll
+      for (int q = 0; q < CB; ++q) {
+        const int j = j0 + 4 * q;
+        vv[q] = j < M ? cidx[j] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < CB; ++q) {
+        const int j = j0 + 4 * q;
+        if (j < M && kk < r) {
+          if (t.dtype == kBF16) {
+            const uint2 u = *reinterpret_cast<const uint2*>((const uint16_t*)t.w2 + (size_t)vv[q] * r + kk);
+            w[q][0] = (double)__uint_as_float(u.x << 16);
+            w[q][1] = (double)__uint_as_float(u.x & 0xFFFF0000u);
+            w[q][2] = (double)__uint_as_float(u.y << 16);
+            w[q][3] = (double)__uint_as_float(u.y & 0xFFFF0000u);
+          } else {
+            const float4 u = *reinterpret_cast<const float4*>((const float*)t.w2 + (size_t)vv[q] * r + kk);
+            w[q][0] = u.x, w[q][1] = u.y, w[q][2] = u.z, w[q][3] = u.w;
+          }
+        } else {
+          w[q][0] = w[q][1] = w[q][2] = w[q][3] = 0.0;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < CB; ++q) {
+        const int j = j0 + 4 * q;
+        double sdot = 0.0;
+        if (kk < r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sdot += w[q][e] * a[kk + e];
+        sdot = wave_sum(sdot);
+        if (lane == 0 && j < M) l[j] = (double)cval[j] + (t.b2 ? (double)t.b2[vv[q]] : 0.0) + sdot;
+      }
     }
     __syncthreads();
     // log-sum-exp over the M candidates (one wave)
@@ -381,18 +530,24 @@ __global__ __launch_bounds__(256) void tree_expand_pop(TreeArgs t, int k) {
 // ---- host side ------------------------------------------------------------------------------
 static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
+size_t topm_scratch_bytes(int rows, int M) { return al256((size_t)rows * kTopSegs * M * 8); }
+
 TreeLayout tree_layout(int d, int Hs, int r, int P, int group, int N, int M) {
   (void)d;
   TreeLayout L;
   size_t off = 0;
   L.status = off;
   off += 256;
+  L.seg_keys = off;
+  off += topm_scratch_bytes(group * P, M);
   L.cand_idx = off;
   off += al256((size_t)group * P * M * 4);
   L.cand_val = off;
   off += al256((size_t)group * P * M * 4);
   L.zh = off;
   off += al256((size_t)group * P * r * 8);
+  L.act = off;
+  off += al256((size_t)group * r * 8);
   L.states = off;
   off += al256((size_t)group * (N + 1) * Hs * 8);
   L.heap_cap = N * M;
@@ -408,24 +563,46 @@ TreeLayout tree_layout(int d, int Hs, int r, int P, int group, int N, int M) {
   return L;
 }
 
-hipError_t launch_topm(const float* Lb, int rows, int V, int M, int32_t* idx, float* val, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(tree_topm, dim3(rows), dim3(256), 0, s, Lb, V, M, idx, val, nullptr, 0);
+static hipError_t launch_topm_impl(const float* Lb, int rows, int V, int M, uint64_t* seg, int32_t* idx, float* val,
+                                   int32_t* status, bool reset_status, hipStream_t s) {
+  hipLaunchKernelGGL(topm_segment, dim3(kTopSegs, rows), dim3(256), 0, s, Lb, V, M, seg, status, reset_status ? 1 : 0);
+  hipLaunchKernelGGL(topm_merge, dim3(rows), dim3(256), 0, s, seg, M, idx, val);
   return hipGetLastError();
 }
 
-hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s) {
+hipError_t launch_topm(const float* Lb, int rows, int V, int M, void* scratch, int32_t* idx, float* val, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  return launch_topm_impl(Lb, rows, V, M, (uint64_t*)scratch, idx, val, nullptr, false, s);
+}
+
+size_t tree_gru_lds(int d, int Hs, int dtype) {
+  return (size_t)kTreeSeqs * Hs * sizeof(double) + (size_t)kTreeSeqs * d * (dtype == kBF16 ? 2 : 4);
+}
+
+hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (t.B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(tree_topm, dim3(t.B * t.P), dim3(256), 0, s, t.Lb, t.V, t.M, t.cand_idx, t.cand_val, t.status,
-                     reset_status ? 1 : 0);
-  const int n = t.B * t.P * t.r;
-  hipLaunchKernelGGL(tree_prologue, dim3((n + 255) / 256), dim3(256), 0, s, t);
+  hipError_t e = hipSuccess;
+  if (ev_start && ev_stop && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;
+  e = launch_topm_impl(t.Lb, t.B * t.P, t.V, t.M, t.seg_keys, t.cand_idx, t.cand_val, t.status, reset_status, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tree_zh, dim3((t.r + 15) / 16, t.B * t.P), dim3(256), 0, s, t);
+  hipLaunchKernelGGL(tree_init, dim3((t.B + 255) / 256), dim3(256), 0, s, t);
+  const size_t lds = tree_gru_lds(t.d, t.Hs, t.dtype);
+  static thread_local size_t attr_lds = 0;
+  if (lds > attr_lds) {
+    e = hipFuncSetAttribute((const void*)tree_gru, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_lds = lds;
+  }
   for (int k = 0; k < t.N; ++k) {
     for (int b0 = 0; b0 < t.B; b0 += kTreeSeqs)
-      hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(256), 0, s, t, b0);
-    hipLaunchKernelGGL(tree_expand_pop, dim3(t.B), dim3(256), 0, s, t, k);
+      hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(256), lds, s, t, b0);
+    hipLaunchKernelGGL(tree_bottleneck, dim3((t.r + 15) / 16, t.B), dim3(256), 0, s, t);
+    hipLaunchKernelGGL(tree_score_pop, dim3(t.B), dim3(256), 0, s, t, k);
   }
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess && ev_start && ev_stop) e = hipEventRecord(ev_stop, s);
+  return e;
 }
 
 }  // namespace dh

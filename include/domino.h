@@ -126,15 +126,20 @@ domino_status domino_draft_chain(const domino_dims *dims, const domino_weights *
                                  int32_t *out_tokens, float *out_logits, void *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* Bytes of workspace domino_tree_candidates needs (0 for invalid arguments). */
+size_t domino_tree_candidates_workspace_size(const domino_dims *dims, int32_t batch, int32_t topm);
+
 /*
  * Top-M candidates of every base-logit row (the tree's candidate lists,
  * DominoTree summary, "Top-M" restriction): for each of batch*block rows of
  * base_logits [batch][block][vocab] (device, fp32), out_index/out_value
  * [batch][block][topm] (device) hold the topm largest entries ordered by
  * (value desc, index asc); -0.0 counts as +0.0.  1 <= topm <= min(256, vocab).
+ * workspace (device): domino_tree_candidates_workspace_size bytes of scratch.
  */
 domino_status domino_tree_candidates(const domino_dims *dims, const float *base_logits, int32_t batch, int32_t topm,
-                                     int32_t *out_index, float *out_value, void *stream);
+                                     int32_t *out_index, float *out_value, void *workspace, size_t workspace_bytes,
+                                     void *stream);
 
 /* Bytes of workspace domino_tree_draft needs (0 for invalid arguments). */
 size_t domino_tree_workspace_size(const domino_dims *dims, int32_t batch, int32_t nodes, int32_t topm);
@@ -162,7 +167,8 @@ size_t domino_tree_workspace_size(const domino_dims *dims, int32_t batch, int32_
  *   NULL).  Nodes are numbered in pop order, so parents[k] < k.  Slots left
  *   when the tree runs out of nodes hold parent -1, token -1, depth 0,
  *   score -inf.
- * Limits: 1 <= nodes <= 64, 1 <= topm <= min(256, vocab), gru_hidden <= 4096.
+ * Limits: 1 <= nodes <= 64, 1 <= topm <= min(256, vocab), gru_hidden <= 4096,
+ * and 64*gru_hidden + 8*hidden*sizeof(storage) <= 156 KB (LDS of the GRU step).
  * The int32 at workspace offset 0 holds the device status after the call
  * (1 = a first token was outside [0, V) and token 0 was used).
  */
@@ -177,7 +183,8 @@ domino_status domino_tree_draft(const domino_dims *dims, const domino_weights *w
  * on its stream right before its GEMM launch and base_stop right after it,
  * and each domino_draft_chain call records chain_start right before the
  * launch(es) that run the P steps (after the short prologue) and chain_stop
- * right after them.  A NULL pair disables that pair.  The events stay owned
+ * right after them; each domino_tree_draft call records the chain pair around
+ * all of its launches.  A NULL pair disables that pair.  The events stay owned
  * by the caller.  Process-wide setting; not for concurrent callers.
  */
 void domino_set_timing_events(void *base_start, void *base_stop, void *chain_start, void *chain_stop);

@@ -100,6 +100,7 @@ class Config:
     biases: bool = False
     nodes: int = 16      # tree budget
     topm: int = 64       # tree candidates per depth
+    tree: bool = False   # best-first tree instead of the chain
     extra: dict = field(default_factory=dict)
 
     def with_(self, **kw) -> "Config":
@@ -135,7 +136,7 @@ CONFIGS = {
     "qwen3_8b_b16": Config("qwen3_8b_b16", 4096, 151936, 1024, 256, 16, 16, "bf16", 8, 103),
     # best-first tree on Qwen3-4B shapes: 8 sequences, 16 nodes, top-64
     "qwen3_4b_tree": Config("qwen3_4b_tree", 2560, 151936, 1024, 256, 16, 8, "bf16", 4, 104,
-                            nodes=16, topm=64),
+                            nodes=16, topm=64, tree=True),
 }
 
 

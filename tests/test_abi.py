@@ -162,6 +162,11 @@ def test_tree_arguments_rejected_before_launch():
     small_v = _dims(vocab=50)
     assert call(dims=ctypes.byref(small_v), M=64, wsb=1 << 40) == dh.ERR_INVALID_ARGUMENT
     assert "vocabulary" in dh.last_error()
-    assert L.domino_tree_candidates(ctypes.byref(d), FAKE, 2, 0, FAKE, FAKE, None) == dh.ERR_INVALID_ARGUMENT
-    assert L.domino_tree_candidates(ctypes.byref(d), None, 2, 8, FAKE, FAKE, None) == dh.ERR_INVALID_ARGUMENT
-    assert L.domino_tree_candidates(ctypes.byref(d), FAKE, 0, 8, None, None, None) == dh.OK
+    cw = dh.domino_tree_candidates_workspace_size(d, 2, 8)
+    assert cw > 0
+    assert L.domino_tree_candidates(ctypes.byref(d), FAKE, 2, 0, FAKE, FAKE, FAKE, cw, None) == dh.ERR_INVALID_ARGUMENT
+    assert L.domino_tree_candidates(ctypes.byref(d), None, 2, 8, FAKE, FAKE, FAKE, cw, None) == dh.ERR_INVALID_ARGUMENT
+    assert L.domino_tree_candidates(ctypes.byref(d), FAKE, 2, 8, FAKE, FAKE, FAKE, cw - 1, None) == dh.ERR_WORKSPACE
+    assert L.domino_tree_candidates(ctypes.byref(d), FAKE, 0, 8, None, None, None, 0, None) == dh.OK
+    big = _dims(hidden=8192, gru_hidden=2048)
+    assert call(dims=ctypes.byref(big), wsb=1 << 40) == dh.ERR_UNSUPPORTED

@@ -133,7 +133,8 @@ def test_candidates_match_oracle_topm(kind):
     x = torch.from_numpy(np.ascontiguousarray(Lb)).cuda()
     idx = torch.empty((B, P, M), dtype=torch.int32, device="cuda")
     val = torch.empty((B, P, M), dtype=torch.float32, device="cuda")
-    dh.domino_tree_candidates(dims, x, B, M, idx, val)
+    ws = torch.zeros(dh.domino_tree_candidates_workspace_size(dims, B, M), dtype=torch.uint8, device="cuda")
+    dh.domino_tree_candidates(dims, x, B, M, idx, val, ws, ws.numel())
     torch.cuda.synchronize()
     gi, gv = idx.cpu().numpy(), val.cpu().numpy()
     for b in range(B):
