@@ -87,7 +87,7 @@ void domino_set_timing_events(void* base_start, void* base_stop, void* chain_sta
 }
 
 int32_t domino_set_chain_mode(int32_t mode) {
-  if (mode != 0 && mode != 1) return -1;
+  if (mode < 0 || mode > 2) return -1;
   const int32_t prev = g_chain_mode;
   g_chain_mode = mode;
   return prev;
@@ -183,6 +183,8 @@ domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* 
     a.t0 = first_tokens + g0;
     a.zh = (const float*)(ws + L.zh);
     a.h = (float*)(ws + L.h);
+    a.hb = (uint16_t*)(ws + L.hb);
+    a.hb_step = L.hb_step;
     a.act = ws + L.act;
     a.keys = (uint64_t*)(ws + L.keys);
     a.counters = (uint32_t*)(ws + L.counters);

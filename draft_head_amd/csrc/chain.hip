@@ -34,13 +34,24 @@
 namespace dh {
 
 // Opt-in phase timestamps (constant 100 MHz clock) for tuning builds only.
+[[maybe_unused]] constexpr int kTraceSlots = 12;
 #ifdef DH_TRACE_PHASES
 #define DH_STAMP(p, slot) \
-  do { if (a.trace && threadIdx.x == 0) a.trace[((size_t)(p) * gridDim.x + blockIdx.x) * 6 + (slot)] = wall_clock64(); } while (0)
+  do { if (a.trace && threadIdx.x == 0) a.trace[((size_t)(p) * gridDim.x + blockIdx.x) * kTraceSlots + (slot)] = wall_clock64(); } while (0)
 #else
 #define DH_STAMP(p, slot) \
   do { } while (0)
 #endif
+
+// Lane index through an opaque move.  Every per-lane address a phase derives
+// from it is then recomputed inside the step loop instead of being hoisted
+// out of it as a live 64-bit value, which would cost two registers for the
+// whole kernel each.
+__device__ __forceinline__ int opaque_lane() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
 
 __device__ __forceinline__ float bias_at(const float* b, int i) { return b ? b[i] : 0.f; }
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
@@ -108,39 +119,53 @@ __device__ __forceinline__ void gru_rows(const ChainArgs& a, int item, const W* 
   }
 }
 
+// MFMA right operand from GRU state slot `slot`, sequence b, elements k..k+7:
+// with bf16 weights the pre-split hi/lo copy, else the fp32 state
+template <class W>
+__device__ __forceinline__ typename act<W>::type state_frag(const ChainArgs& a, int slot, int b, int k, bool ok) {
+  if constexpr (sizeof(W) == 2) {
+    bf16pair f;
+    const uint16_t* hi = a.hb + (size_t)slot * a.hb_step + (size_t)b * a.Hs + k;
+    f.hi = load8_or_zero(hi, ok);
+    f.lo = load8_or_zero(hi + (size_t)a.B * a.Hs, ok);
+    return f;
+  } else {
+    return act_or_zero<W>(a.h + (size_t)slot * a.h_step + (size_t)b * a.Hs + k, ok);
+  }
+}
+
 // per-wave partial sums of W_hh h(p) over this wave's k chunks
 template <class W, int NCB, bool kLds>
 __device__ void gru_hidden_part(const ChainArgs& a, int p, int item, const W* lds, f32x4 (&acc)[NCB]) {
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (p == 0) return;  // h(0) = 0
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int Hs = a.Hs, B = a.B;
   const W *rx, *rh;
   bool has_x, has_h;
   gru_rows<W, kLds>(a, item, lds, rx, rh, has_x, has_h);
-  const float* h_in = a.h + (size_t)p * a.h_step;
-  const float* hv[NCB];
+  int bb[NCB];
   bool bok[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int b = cb * 16 + row;
     bok[cb] = b < B;
-    hv[cb] = h_in + (size_t)(bok[cb] ? b : 0) * Hs + kg * 8;
+    bb[cb] = bok[cb] ? b : 0;
   }
   constexpr int U = NCB == 1 ? 8 : 4;
   const int nch = (Hs + 31) / 32;
-  for (int c0 = wv * U; c0 < nch; c0 += 4 * U) {
+  for (int c0 = wv; c0 < nch; c0 += 4 * U) {  // this wave's chunks wv, wv + 4, ... in order
     frag_t<W> A[U];
     typename act<W>::type S[U][NCB];
 #pragma unroll
     for (int q = 0; q < U; ++q) {
-      const int k = (c0 + q) * 32;
-      const bool kok = c0 + q < nch && k + kg * 8 < Hs;
+      const int c = c0 + 4 * q, k = c * 32;
+      const bool kok = c < nch && k + kg * 8 < Hs;
       A[q] = load8_or_zero(rh + k, kok && has_h);
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) S[q][cb] = act_or_zero<W>(hv[cb] + k, kok && bok[cb]);
+      for (int cb = 0; cb < NCB; ++cb) S[q][cb] = state_frag<W>(a, p, bb[cb], k + kg * 8, kok && bok[cb]);
     }
 #pragma unroll
     for (int q = 0; q < U; ++q)
@@ -149,18 +174,18 @@ __device__ void gru_hidden_part(const ChainArgs& a, int p, int item, const W* ld
   }
 }
 
+template <class W, int NCB>
+__device__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[NCB]);
+
 // input half on top of the hidden-half partials, then the gates: h(p+1)
 template <class W, int NCB, bool kLds>
 __device__ void gru_finish(const ChainArgs& a, int p, int item, float* red, const W* lds, const f32x4 (&acc_h)[NCB]) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
-  const int d = a.d, Hs = a.Hs, B = a.B;
-  const int j0 = item * 4;
+  const int d = a.d, B = a.B;
   const W *rx, *rh;
   bool has_x, has_h;
   gru_rows<W, kLds>(a, item, lds, rx, rh, has_x, has_h);
-  const float* h_in = a.h + (size_t)p * a.h_step;
-  float* h_out = a.h + (size_t)(p + 1) * a.h_step;
 
   const W* xe[NCB];
   bool bok[NCB];
@@ -178,12 +203,12 @@ __device__ void gru_finish(const ChainArgs& a, int p, int item, float* red, cons
   // E[prev] is stored exactly in W: one MFMA per chunk
   constexpr int U = NCB == 1 ? 16 : 8;
   const int ncx = (d + 31) / 32;
-  for (int c0 = wv * U; c0 < ncx; c0 += 4 * U) {
+  for (int c0 = wv; c0 < ncx; c0 += 4 * U) {  // this wave's chunks wv, wv + 4, ... in order
     frag_t<W> A[U], X[U][NCB];
 #pragma unroll
     for (int q = 0; q < U; ++q) {
-      const int k = (c0 + q) * 32;
-      const bool kok = c0 + q < ncx && k + kg * 8 < d;
+      const int c = c0 + 4 * q, k = c * 32;
+      const bool kok = c < ncx && k + kg * 8 < d;
       A[q] = load8_or_zero(rx + k, kok && has_x);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) X[q][cb] = load8_or_zero(xe[cb] + k, kok && bok[cb]);
@@ -194,6 +219,19 @@ __device__ void gru_finish(const ChainArgs& a, int p, int item, float* red, cons
       for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(A[q], X[q][cb], acc[cb]);
   }
 
+  gru_gates<W, NCB>(a, p, item, red, acc);
+}
+
+// sum the four waves' pre-activation partials and apply the gates: h(p+1),
+// stored fp32 and, for bf16 weights, also split into bf16 hi + lo once here
+// rather than by every reader
+template <class W, int NCB>
+__device__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[NCB]) {
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int Hs = a.Hs, B = a.B, j0 = item * 4;
+  const float* h_in = a.h + (size_t)p * a.h_step;
+  float* h_out = a.h + (size_t)(p + 1) * a.h_step;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
     *reinterpret_cast<float4*>(&red[((wv * NCB + cb) * 64 + lane) * 4]) =
@@ -212,14 +250,109 @@ __device__ void gru_finish(const ChainArgs& a, int p, int item, float* red, cons
     }
     // result rows 4*kg + i are gate i of unit j0 + kg; column = sequence
     const int b = cb * 16 + row, j = j0 + kg;
+    float hn = 0.f;
     if (b < B) {
       const float rg = sigmoidf_(pre[0] + bias_at(a.b_ih, j) + bias_at(a.b_hh, j));
       const float zg = sigmoidf_(pre[1] + bias_at(a.b_ih, Hs + j) + bias_at(a.b_hh, Hs + j));
       const float ng = tanhf(pre[2] + bias_at(a.b_ih, 2 * Hs + j) + rg * (pre[3] + bias_at(a.b_hh, 2 * Hs + j)));
-      store_agent(&h_out[(size_t)b * Hs + j], (1.f - zg) * ng + zg * h_in[(size_t)b * Hs + j]);
+      hn = (1.f - zg) * ng + zg * h_in[(size_t)b * Hs + j];
+      store_agent(&h_out[(size_t)b * Hs + j], hn);
+    }
+    if constexpr (sizeof(W) == 2) {
+      // units j0..j0+3 of sequence b sit in lanes row, row+16, row+32, row+48
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = __shfl(hn, row + 16 * q);
+      if (kg == 0 && b < B) {
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hi[q] = f2bf(v[q]);
+          lo[q] = f2bf(v[q] - bf2f(hi[q]));
+        }
+        uint16_t* dst = a.hb + (size_t)(p + 1) * a.hb_step + (size_t)b * Hs + j0;
+        store_agent(reinterpret_cast<uint64_t*>(dst), (uint64_t)pack2(hi[0], hi[1]) | ((uint64_t)pack2(hi[2], hi[3]) << 32));
+        store_agent(reinterpret_cast<uint64_t*>(dst + (size_t)B * Hs),
+                    (uint64_t)pack2(lo[0], lo[1]) | ((uint64_t)pack2(lo[2], lo[3]) << 32));
+      }
     }
   }
   __syncthreads();
+}
+
+// Phase G with W_ih read from memory (kernels that give their LDS to W2).
+// This wave's W_ih fragments (k chunks wv + 4j) do not depend on the token,
+// so they are fetched while the workgroup still waits for it; each workgroup
+// reads the same rows every step, so they stay in its XCD's L2.
+constexpr int kXPre = 20;  // chunks per wave fetched ahead: all of them for d <= 2560
+template <class W>
+__device__ __forceinline__ void gru_x_prefetch(const ChainArgs& a, int item, frag_t<W> (&xw)[kXPre]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, kg = lane >> 4;
+  const W *rx, *rh;
+  bool has_x, has_h;
+  gru_rows<W, false>(a, item, nullptr, rx, rh, has_x, has_h);
+  const int ncx = (a.d + 31) / 32;
+#pragma unroll
+  for (int j = 0; j < kXPre; ++j) {
+    const int c = wv + 4 * j, k = c * 32;
+    xw[j] = load8_or_zero(rx + k, has_x && c < ncx && k + kg * 8 < a.d);
+  }
+}
+
+template <class W, int NCB>
+__device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int item, float* red, const frag_t<W> (&xw)[kXPre],
+                               const f32x4 (&acc_h)[NCB]) {
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int d = a.d, B = a.B;
+  const W *rx, *rh;
+  bool has_x, has_h;
+  gru_rows<W, false>(a, item, nullptr, rx, rh, has_x, has_h);
+  const W* xe[NCB];
+  bool bok[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int b = cb * 16 + row;
+    bok[cb] = b < B;
+    const int tok = bok[cb] ? prev_token(a, p, b) : 0;
+    xe[cb] = (const W*)a.embed + (size_t)tok * d + kg * 8;
+  }
+  f32x4 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = acc_h[cb];
+  const int ncx = (d + 31) / 32;
+  {
+    frag_t<W> X[kXPre][NCB];
+#pragma unroll
+    for (int j = 0; j < kXPre; ++j) {
+      const int c = wv + 4 * j, k = c * 32;
+      const bool kok = c < ncx && k + kg * 8 < d;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) X[j][cb] = load8_or_zero(xe[cb] + k, kok && bok[cb]);
+    }
+#pragma unroll
+    for (int j = 0; j < kXPre; ++j)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(xw[j], X[j][cb], acc[cb]);
+  }
+  // chunks beyond the prefetched ones (d > 4 * 32 * kXPre), same order, four per batch
+  for (int c0 = wv + 4 * kXPre; c0 < ncx; c0 += 16) {
+    frag_t<W> A[4], X[4][NCB];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = c0 + 4 * q, k = c * 32;
+      const bool kok = c < ncx && k + kg * 8 < d;
+      A[q] = load8_or_zero(rx + k, kok && has_x);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) X[q][cb] = load8_or_zero(xe[cb] + k, kok && bok[cb]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(A[q], X[q][cb], acc[cb]);
+  }
+  DH_STAMP(p, 8);
+  gru_gates<W, NCB>(a, p, item, red, acc);
 }
 
 // ---- phase W: 16 bottleneck units, all sequences ----------------------------------
@@ -243,7 +376,7 @@ struct BottleneckPre {
 };
 template <int NCB>
 __device__ __forceinline__ BottleneckPre bottleneck_pre(const ChainArgs& a, int p, int item) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   BottleneckPre q;
   q.zh = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -259,7 +392,7 @@ __device__ __forceinline__ BottleneckPre bottleneck_pre(const ChainArgs& a, int 
 template <class W, int NCB, bool kLdsW>
 __device__ void bottleneck_item(const ChainArgs& a, int p, int item, float* red, const W* w1_lds,
                                 const BottleneckPre& pre_terms) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int Hs = a.Hs, B = a.B, r = a.r;
   const int k0 = item * 16;
@@ -268,36 +401,36 @@ __device__ void bottleneck_item(const ChainArgs& a, int p, int item, float* red,
     rw = w1_lds + (size_t)row * (Hs + 8) + kg * 8;
   else
     rw = (const W*)a.w1 + (size_t)min(k0 + row, r - 1) * (a.d + Hs) + a.d + kg * 8;
-  const float* h_new = a.h + (size_t)(p + 1) * a.h_step;
-  const float* hv[NCB];
+  int bb[NCB];
   bool bok[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int b = cb * 16 + row;
     bok[cb] = b < B;
-    hv[cb] = h_new + (size_t)(bok[cb] ? b : 0) * Hs + kg * 8;
+    bb[cb] = bok[cb] ? b : 0;
   }
   f32x4 acc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int U = NCB == 1 ? 8 : 4;
   const int nch = (Hs + 31) / 32;
-  for (int c0 = wv * U; c0 < nch; c0 += 4 * U) {
+  for (int c0 = wv; c0 < nch; c0 += 4 * U) {  // this wave's chunks wv, wv + 4, ... in order
     frag_t<W> A[U];
     typename act<W>::type S[U][NCB];
 #pragma unroll
     for (int q = 0; q < U; ++q) {
-      const int k = (c0 + q) * 32;
-      const bool kok = c0 + q < nch && k + kg * 8 < Hs;
+      const int c = c0 + 4 * q, k = c * 32;
+      const bool kok = c < nch && k + kg * 8 < Hs;
       A[q] = load8_or_zero(rw + k, kok);
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) S[q][cb] = act_or_zero<W>(hv[cb] + k, kok && bok[cb]);
+      for (int cb = 0; cb < NCB; ++cb) S[q][cb] = state_frag<W>(a, p + 1, bb[cb], k + kg * 8, kok && bok[cb]);
     }
 #pragma unroll
     for (int q = 0; q < U; ++q)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(A[q], S[q][cb], acc[cb]);
   }
+  DH_STAMP(p, 9);
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
     *reinterpret_cast<float4*>(&red[((wv * NCB + cb) * 64 + lane) * 4]) =
@@ -352,6 +485,240 @@ __device__ void bottleneck_item(const ChainArgs& a, int p, int item, float* red,
 #define DH_W_SHARE 3     // W2 share of a bottleneck workgroup, in eighths of the others'
 #endif
 
+// Running argmax of one lane over the logits it has seen, in increasing
+// vocabulary order: the value and index of its first maximum (i < 0: none
+// yet).  -0 and +0 compare equal; the packed key is formed once at the end.
+struct LaneMax {
+  float v;
+  int32_t i;
+};
+__device__ __forceinline__ void lane_max(LaneMax& m, float L, int32_t idx) {
+  const bool take = L > m.v || m.i < 0;
+  m.v = take ? L : m.v;
+  m.i = take ? idx : m.i;
+}
+__device__ __forceinline__ uint64_t lane_key(const LaneMax& m) { return m.i < 0 ? 0 : amax_key(m.v, (uint32_t)m.i); }
+
+// One lane's four logits of a tile, L = (Lb + b2) + (even k chunks + odd k
+// chunks), folded into its running argmax and written out on request.  Both
+// phase-O variants use this, so they agree to the bit.
+__device__ __forceinline__ void tile_epilogue(const ChainArgs& a, int vv, const float (&base)[4], const f32x4 (&acc)[2],
+                                              bool bok, size_t lrow, LaneMax& m) {
+  const int V = a.V;
+  float L[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) L[e] = base[e] + (acc[0][e] + acc[1][e]);
+  if (vv + 3 < V) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lane_max(m, L[e], vv + e);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (vv + e < V) lane_max(m, L[e], vv + e);
+  }
+  if (a.out_logits && bok) {
+    float* dst = a.out_logits + lrow + vv;
+    if ((V & 3) == 0 && vv + 3 < V) {
+      *reinterpret_cast<float4*>(dst) = make_float4(L[0], L[1], L[2], L[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (vv + e < V) dst[e] = L[e];
+    }
+  }
+}
+
+// Lb + b2 for one lane's four vocabulary entries vv.. of row lrow (zeros
+// past V or when !ok)
+__device__ __forceinline__ void load_base4(const ChainArgs& a, size_t lrow, int vv, bool ok, float (&out)[4]) {
+  const float* src = a.Lb + lrow + vv;
+  if (ok && (a.V & 3) == 0 && vv + 3 < a.V) {
+    const float4 q = *reinterpret_cast<const float4*>(src);
+    out[0] = q.x;
+    out[1] = q.y;
+    out[2] = q.z;
+    out[3] = q.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = (ok && vv + e < a.V) ? src[e] : 0.f;
+  }
+  if (a.b2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] += (ok && vv + e < a.V) ? a.b2[vv + e] : 0.f;
+  }
+}
+
+// W2 tiles of workgroup `wg`: the bottleneck workgroups start phase O late,
+// so they take a smaller share (DH_W_SHARE / 8 of the others').
+__host__ __device__ inline void o_tile_range(int wg, int G, int nW, int T, int& t_begin, int& t_end) {
+  const int64_t wsh = DH_W_SHARE, units = (int64_t)nW * wsh + (int64_t)(G - nW) * 8;
+  auto start_of = [&](int w) -> int64_t {
+    const int64_t u = w <= nW ? (int64_t)w * wsh : (int64_t)nW * wsh + (int64_t)(w - nW) * 8;
+    return (int64_t)T * u / units;
+  };
+  t_begin = (int)start_of(wg);
+  t_end = (int)start_of(wg + 1);
+}
+
+// Resident W2.  Of a workgroup's tiles [t_begin, t_end) the first 4*NTW live
+// in registers for all P steps (wave wv owns t_begin + wv + 4i, i < NTW, as
+// MFMA left operands) and the rest, at most kLdsTiles, in LDS in fragment
+// order (tile j, k chunk c, lane l at 16-byte slot (j*KC + c)*64 + l, so a
+// wave's fragment read is 1 KB contiguous).  Slot i of wave wv is tile
+// t_begin + wv + 4i throughout.  Phase O then reads no weights from memory.
+constexpr int kLdsTilesPerWave = 5;
+constexpr int kLdsTiles = 4 * kLdsTilesPerWave;
+template <int KC>
+constexpr int resident_tiles() {  // 4 AGPRs per lane per k chunk: at most 192 of them
+  return KC >= 8 ? 6 : (KC >= 4 ? 12 : 8);
+}
+template <class W, int KC>
+constexpr bool resident_fits() {
+  return sizeof(W) == 2 && KC <= 8;
+}
+__host__ __device__ inline size_t w2_lds_tile_bytes(int KC) { return (size_t)KC * 64 * 16; }
+
+// Loads from clamped, in-bounds addresses (no select).  Rows past V are never
+// stored; k positions past r meet zero activations, so the finite weights
+// read there add exactly zero.
+// (t may be -1 for a workgroup that owns no tile; such rows are never used)
+template <class W>
+__device__ __forceinline__ const W* w2_frag_ptr(const ChainArgs& a, int t, int row, int kg, int c) {
+  const int v = min(max(t * 16 + row, 0), a.V - 1);
+  return (const W*)a.w2 + (size_t)v * a.r + min(c * 32 + kg * 8, a.r - 8);
+}
+
+// The register tier is loaded straight into AGPRs (the MFMA reads its left
+// operand from there), so it does not compete with the VGPRs the phases use.
+// The loads are not visible to the compiler's wait-count tracking, hence the
+// explicit wait for all of them; later compiler-issued waits are only ever
+// stricter while these are outstanding, since loads retire in order.
+template <class W, int KC, int NTW>
+__device__ __forceinline__ void load_resident_w2(const ChainArgs& a, int t_begin, int t_end, frag_t<W> (&w2r)[NTW][KC]) {
+  static_assert(sizeof(W) == 2, "resident W2 is bf16");
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int t = min(t_begin + wv + 4 * i, t_end - 1);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const W* ptr = w2_frag_ptr<W>(a, t, row, kg, c);
+      asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(w2r[i][c]) : "v"(ptr) : "memory");
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// the LDS tier: tiles t_begin + 4*NTW + j, j < n_lds
+template <class W, int KC>
+__device__ void stage_w2_lds(const ChainArgs& a, int t_first, int n_lds, unsigned char* lds) {
+  for (int q = threadIdx.x; q < n_lds * KC * 64; q += blockDim.x) {
+    const int l = q & 63, c = (q >> 6) % KC, j = q / (KC * 64);
+    *reinterpret_cast<uint4*>(lds + (size_t)q * 16) =
+        *reinterpret_cast<const uint4*>(w2_frag_ptr<W>(a, t_first + j, l & 15, l >> 4, c));
+  }
+  __syncthreads();
+}
+
+// fold this workgroup's per-lane best keys into the device-wide keys of step p
+template <int NCB>
+__device__ __forceinline__ void publish_best(const ChainArgs& a, int p, uint64_t (&best)[NCB], uint64_t* sbest) {
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 16));
+    best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 32));
+    if (kg == 0) sbest[(wv * NCB + cb) * 16 + row] = best[cb];
+  }
+  __syncthreads();
+  if (threadIdx.x < NCB * 16) {
+    const int cb = threadIdx.x >> 4, rr = threadIdx.x & 15, b = cb * 16 + rr;
+    uint64_t m = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) m = umax64(m, sbest[(w * NCB + cb) * 16 + rr]);
+    if (b < a.B && m != 0) atomicMax((unsigned long long*)&a.keys[(size_t)p * a.B + b], (unsigned long long)m);
+  }
+  __syncthreads();
+}
+
+// base logits, then the correction from resident W2 tiles, then the argmax;
+// same arithmetic and summation order as logits_range
+template <class W, int NCB, int KC, int NTW, class Ready>
+__device__ __forceinline__ bool logits_resident(const ChainArgs& a, int p, int t_begin, int t_end, const frag_t<W> (&w2r)[NTW][KC],
+                                const unsigned char* w2_lds, uint64_t* sbest, Ready ready) {
+  constexpr int NT = NTW + kLdsTilesPerWave;  // slots below NTW: registers; then LDS
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int B = a.B, r = a.r, V = a.V, P = a.P;
+  const char* act_p = (const char*)a.act + (size_t)p * a.act_step;
+  auto tile_of = [&](int i) { return t_begin + wv + 4 * i; };
+  size_t lrow[NCB];
+  bool bok[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int b = cb * 16 + row;
+    bok[cb] = b < B;
+    lrow[cb] = ((size_t)(bok[cb] ? b : 0) * P + p) * V;
+  }
+  // Lb + b2 of every owned tile: inputs, fetched before the activations exist
+  float lb[NCB][NT][4];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int t = tile_of(i);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) load_base4(a, lrow[cb], t * 16 + kg * 4, t < t_end, lb[cb][i]);
+  }
+  if (!ready()) return false;
+
+  uint64_t best[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    LaneMax lm{0.f, -1};
+    const int b = cb * 16 + row;
+    typename act<W>::type bf[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int k = c * 32 + kg * 8;
+      const bool ok = bok[cb] && k < r;
+      if constexpr (sizeof(W) == 2) {
+        const uint16_t* hi = (const uint16_t*)act_p + (size_t)b * r + k;
+        bf[c].hi = load8_or_zero(hi, ok);
+        bf[c].lo = load8_or_zero(hi + (size_t)B * r, ok);
+      } else {
+        bf[c] = load8_or_zero((const float*)act_p + (size_t)b * r + k, ok);
+      }
+    }
+#ifdef DH_TRACE_PHASES
+    __builtin_amdgcn_s_waitcnt(0);
+    if (cb == 0) DH_STAMP(p, 10);
+#endif
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      if (tile_of(i) >= t_end) break;
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      if (i < NTW) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c) acc[c & 1] = mma(w2r[i < NTW ? i : 0][c], bf[c], acc[c & 1]);
+      } else {
+        const unsigned char* src = w2_lds + ((size_t)(4 * (i - NTW) + wv) * KC * 64 + lane) * 16;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const frag_t<W> w = *reinterpret_cast<const frag_t<W>*>(src + (size_t)c * 64 * 16);
+          acc[c & 1] = mma(w, bf[c], acc[c & 1]);
+        }
+      }
+      tile_epilogue(a, tile_of(i) * 16 + kg * 4, lb[cb][i], acc, bok[cb], lrow[cb], lm);
+    }
+    best[cb] = lane_key(lm);
+  }
+  DH_STAMP(p, 6);
+  publish_best<NCB>(a, p, best, sbest);
+  DH_STAMP(p, 7);
+  return true;
+}
+
 template <class W, int NCB, int KC>
 struct TileBuf {
   frag_t<W> w[KC];    // 16 W2 rows x all of k, MFMA left operand
@@ -362,9 +729,9 @@ struct TileBuf {
 // `ready` is called by the whole workgroup after the first tiles are in flight
 // and before the activations are read; it returns false when the kernel must stop.
 template <class W, int NCB, int KC, class Ready>
-__device__ bool logits_range(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest, Ready ready) {
+__device__ __forceinline__ bool logits_range(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest, Ready ready) {
   constexpr int PF = DH_O_PREFETCH;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int B = a.B, r = a.r, V = a.V, P = a.P;
   const bool vec4 = (V & 3) == 0;
@@ -380,9 +747,9 @@ __device__ bool logits_range(const ChainArgs& a, int p, int t_begin, int t_end, 
     lrow[cb] = ((size_t)(bok[cb] ? b : 0) * P + p) * V;
   }
 
-  uint64_t best[NCB];
+  LaneMax lm[NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) best[cb] = 0;
+  for (int cb = 0; cb < NCB; ++cb) lm[cb] = LaneMax{0.f, -1};
 
   const W* w2 = (const W*)a.w2;
   auto issue = [&](int t, TileBuf<W, NCB, KC>& tb) {
@@ -447,23 +814,10 @@ __device__ bool logits_range(const ChainArgs& a, int p, int t_begin, int t_end, 
       for (int cb = 0; cb < NCB; ++cb) acc[cb][c & 1] = mma(tb.w[c], bf[cb][c], acc[cb][c & 1]);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      if (!bok[cb]) continue;
-      float L[4];
+      float base[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        L[i] = tb.lb[cb][i] + (acc[cb][0][i] + acc[cb][1][i]) + tb.b2[i];
-        if (vv + i < V) best[cb] = umax64(best[cb], amax_key(L[i], (uint32_t)(vv + i)));
-      }
-      if (a.out_logits) {
-        float* dst = a.out_logits + lrow[cb] + vv;
-        if (vec4 && vv + 3 < V) {
-          *reinterpret_cast<float4*>(dst) = make_float4(L[0], L[1], L[2], L[3]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (vv + i < V) dst[i] = L[i];
-        }
-      }
+      for (int e = 0; e < 4; ++e) base[e] = a.b2 ? tb.lb[cb][e] + tb.b2[e] : tb.lb[cb][e];
+      tile_epilogue(a, vv, base, acc[cb], bok[cb], lrow[cb], lm[cb]);
     }
   };
 
@@ -477,21 +831,10 @@ __device__ bool logits_range(const ChainArgs& a, int p, int t_begin, int t_end, 
     }
   }
 
+  uint64_t best[NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 16));
-    best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 32));
-    if (kg == 0) sbest[(wv * NCB + cb) * 16 + row] = best[cb];
-  }
-  __syncthreads();
-  if (threadIdx.x < NCB * 16) {
-    const int cb = threadIdx.x >> 4, rr = threadIdx.x & 15, b = cb * 16 + rr;
-    uint64_t m = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) m = umax64(m, sbest[(w * NCB + cb) * 16 + rr]);
-    if (b < B && m != 0) atomicMax((unsigned long long*)&a.keys[(size_t)p * B + b], (unsigned long long)m);
-  }
-  __syncthreads();
+  for (int cb = 0; cb < NCB; ++cb) best[cb] = lane_key(lm[cb]);
+  publish_best<NCB>(a, p, best, sbest);
   return true;
 }
 
@@ -559,43 +902,53 @@ __global__ __launch_bounds__(256) void chain_logits_k(ChainArgs a, int p) {
 }
 
 // All P steps in one cooperative launch; every workgroup owns one GRU work
-// item (Hs/4 <= grid).  kLds: 0 weights from global memory, 1 the GRU slice
-// in LDS, 2 also the bottleneck slice of W1 in LDS.
-template <class W, int NCB, int KC, int kLds>
+// item (Hs/4 <= grid).  NTW == 0 (W2 streamed every step), kLds: 0 weights
+// from global memory, 1 the GRU slice in LDS, 2 also the bottleneck slice of
+// W1 in LDS.  NTW > 0 (W2 resident on chip): the GRU weights come from
+// memory, W_ih fetched ahead of the token; kLds 2 puts the W1 slice in LDS;
+// the LDS tier of W2 follows it.
+template <class W, int NCB, int KC, int kLds, int NTW>
 __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
+  constexpr bool kGruLds = kLds >= 1 && NTW == 0;
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
   __shared__ __attribute__((aligned(16))) float red[4 * NCB * 64 * 4];
   __shared__ uint64_t sbest[4 * NCB * 16];
   W* gl = reinterpret_cast<W*>(dyn_lds);
-  W* wl = gl + (kLds >= 1 ? gru_slice_elems(a.d, a.Hs) : 0);
+  W* wl = gl + (kGruLds ? gru_slice_elems(a.d, a.Hs) : 0);
   const int G = gridDim.x, wg = blockIdx.x;
   const int nG = a.Hs / 4, nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
   uint32_t* cG = a.counters + 0 * kSubCounters * kCounterStride;
   uint32_t* cW = a.counters + 1 * kSubCounters * kCounterStride;
   uint32_t* cO = a.counters + 2 * kSubCounters * kCounterStride;
-  // W2 tiles: the bottleneck workgroups start the phase late, so they take a
-  // smaller share (DH_W_SHARE / 8 of the others')
   int t_begin, t_end;
-  {
-    const int64_t wsh = DH_W_SHARE, units = (int64_t)nW * wsh + (int64_t)(G - nW) * 8;
-    auto start_of = [&](int w) -> int64_t {
-      const int64_t u = w <= nW ? (int64_t)w * wsh : (int64_t)nW * wsh + (int64_t)(w - nW) * 8;
-      return (int64_t)T * u / units;
-    };
-    t_begin = (int)start_of(wg);
-    t_end = (int)start_of(wg + 1);
-  }
-  if (kLds >= 1 && wg < nG) stage_gru_slice<W>(a, wg, gl);
+  o_tile_range(wg, G, nW, T, t_begin, t_end);
+  frag_t<W> w2r[NTW > 0 ? NTW : 1][KC];
+  // LDS tier of resident W2: after the GRU slice, and after the W1 slice in
+  // bottleneck workgroups
+  unsigned char* w2l = reinterpret_cast<unsigned char*>(wl) +
+                       (kLds >= 2 && wg < nW ? (size_t)16 * (a.Hs + 8) * sizeof(W) : 0);
+  if constexpr (NTW > 0) load_resident_w2<W, KC>(a, t_begin, t_end, w2r);
+  if (kGruLds && wg < nG) stage_gru_slice<W>(a, wg, gl);
   if (kLds >= 2 && wg < nW) stage_w1_slice<W>(a, wg, wl);
+  if constexpr (NTW > 0) stage_w2_lds<W, KC>(a, t_begin + 4 * NTW, max(0, t_end - t_begin - 4 * NTW), w2l);
   f32x4 acc_h[NCB];  // hidden half of this workgroup's next GRU step
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc_h[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int p = 0; p < a.P; ++p) {
     if (wg < nG) {
-      if (p > 0 && !wg_wait_geq(cO, (uint32_t)(p * G), a.status)) return;
-      DH_STAMP(p, 0);
-      if (wg == 0 && p > 0) write_tokens(a, p - 1);
-      gru_finish<W, NCB, (kLds >= 1)>(a, p, wg, red, gl, acc_h);
+      if constexpr (NTW > 0) {
+        frag_t<W> xw[kXPre];
+        gru_x_prefetch<W>(a, wg, xw);
+        if (p > 0 && !wg_wait_geq(cO, (uint32_t)(p * G), a.status)) return;
+        DH_STAMP(p, 0);
+        if (wg == 0 && p > 0) write_tokens(a, p - 1);
+        gru_finish_pre<W, NCB>(a, p, wg, red, xw, acc_h);
+      } else {
+        if (p > 0 && !wg_wait_geq(cO, (uint32_t)(p * G), a.status)) return;
+        DH_STAMP(p, 0);
+        if (wg == 0 && p > 0) write_tokens(a, p - 1);
+        gru_finish<W, NCB, kGruLds>(a, p, wg, red, gl, acc_h);
+      }
     }
     wg_arrive(cG);
     DH_STAMP(p, 1);
@@ -609,14 +962,19 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
     DH_STAMP(p, 3);
     if (wg < nG && p + 1 < a.P) {  // W_hh h(p+1) while the bottleneck runs
       if (!wg_wait_geq(cG, (uint32_t)((p + 1) * G), a.status)) return;
-      gru_hidden_part<W, NCB, (kLds >= 1)>(a, p + 1, wg, gl, acc_h);
+      gru_hidden_part<W, NCB, kGruLds>(a, p + 1, wg, gl, acc_h);
     }
-    if (!logits_range<W, NCB, KC>(a, p, t_begin, t_end, sbest, [&] {
-          const bool ok = wg_wait_geq(cW, (uint32_t)((p + 1) * G), a.status);
-          DH_STAMP(p, 4);
-          return ok;
-        }))
-      return;
+    auto ready = [&] {
+      const bool ok = wg_wait_geq(cW, (uint32_t)((p + 1) * G), a.status);
+      DH_STAMP(p, 4);
+      return ok;
+    };
+    bool go;
+    if constexpr (NTW > 0)
+      go = logits_resident<W, NCB, KC, NTW>(a, p, t_begin, t_end, w2r, w2l, sbest, ready);
+    else
+      go = logits_range<W, NCB, KC>(a, p, t_begin, t_end, sbest, ready);
+    if (!go) return;
     wg_arrive(cO);
     DH_STAMP(p, 5);
   }
@@ -643,15 +1001,37 @@ ChainLayout chain_layout(int d, int Hs, int r, int P, int group) {
   L.h_step = (int)(align256((size_t)group * Hs * 4) / 4);
   L.h = off;
   off += (size_t)(P + 1) * L.h_step * 4;
+  L.hb_step = (int)(align256((size_t)group * Hs * 2 * 2) / 2);
+  L.hb = off;
+  off += (size_t)(P + 1) * L.hb_step * 2;
   L.act_step = (int)align256((size_t)group * r * 4);
   L.act = off;
   off += (size_t)P * L.act_step;
   L.trace = off;
 #ifdef DH_TRACE_PHASES
-  off += (size_t)P * 1024 * 6 * 8;
+  off += (size_t)P * 1024 * kTraceSlots * 8;
 #endif
   L.total = off;
   return L;
+}
+
+// Dynamic LDS a resident-W2 launch on G workgroups needs (the W1 slice
+// region, then the LDS tiles), or 0 if some workgroup owns more tiles than
+// its register and LDS slots hold.
+static size_t resident_lds(int G, const ChainArgs& a, int ntw, int kc, size_t w1_bytes) {
+  const int nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
+  size_t need = w1_bytes;
+  for (int w = 0; w < G; ++w) {
+    int b, e;
+    o_tile_range(w, G, nW, T, b, e);
+    const int n_lds = e - b - 4 * ntw;
+    if (n_lds > kLdsTiles) return 0;
+    if (n_lds > 0) {
+      const size_t at = (w < nW ? w1_bytes : 0) + (size_t)n_lds * w2_lds_tile_bytes(kc);
+      need = at > need ? at : need;
+    }
+  }
+  return need;
 }
 
 struct CoopGrid {
@@ -661,10 +1041,10 @@ struct CoopGrid {
   int blocks = 0;
 };
 
-template <class W, int NCB, int KC, int kLds>
+template <class W, int NCB, int KC, int kLds, int NTW>
 static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStream_t s) {
   static thread_local CoopGrid cache;
-  const void* fn = (const void*)chain_persistent<W, NCB, KC, kLds>;
+  const void* fn = (const void*)chain_persistent<W, NCB, KC, kLds, NTW>;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -682,7 +1062,8 @@ static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStr
     cache.fn = fn;
     cache.device = dev;
     cache.lds = lds_bytes;
-    cache.blocks = cus * (per_cu > 2 ? 2 : per_cu);
+    // resident W2 was sized for one workgroup per CU
+    cache.blocks = NTW > 0 ? cus : cus * (per_cu > 2 ? 2 : per_cu);
   }
   if (cache.blocks < a.Hs / 4) return hipErrorInvalidConfiguration;  // one GRU item per workgroup
   ChainArgs arg = a;
@@ -704,13 +1085,22 @@ template <class W, int NCB, int KC>
 static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& persistent) {
   const int cus = device_cus();
   // the persistent schedule needs one GRU work item per workgroup
-  persistent = mode == 0 && cus > 0 && a.Hs / 4 <= cus;
+  persistent = mode != 1 && cus > 0 && a.Hs / 4 <= cus;
   if (persistent) {
     const size_t g = gru_slice_elems(a.d, a.Hs) * sizeof(W);
     const size_t w = (size_t)16 * (a.Hs + 8) * sizeof(W);
-    if (g + w <= kLdsBudget) return launch_persistent<W, NCB, KC, 2>(a, g + w, s);
-    if (g <= kLdsBudget) return launch_persistent<W, NCB, KC, 1>(a, g, s);
-    return launch_persistent<W, NCB, KC, 0>(a, 0, s);
+    // W2 stays on chip (registers + LDS) when every workgroup's share fits;
+    // the grid is then one workgroup per CU
+    if constexpr (NCB == 1 && resident_fits<W, KC>()) {
+      constexpr int NTW = resident_tiles<KC>();
+      if (mode == 0) {
+        const size_t l2 = resident_lds(cus, a, NTW, KC, w);
+        if (l2 > 0 && l2 <= kLdsBudget) return launch_persistent<W, NCB, KC, 2, NTW>(a, l2, s);
+      }
+    }
+    if (g + w <= kLdsBudget) return launch_persistent<W, NCB, KC, 2, 0>(a, g + w, s);
+    if (g <= kLdsBudget) return launch_persistent<W, NCB, KC, 1, 0>(a, g, s);
+    return launch_persistent<W, NCB, KC, 0, 0>(a, 0, s);
   }
   const int nG = a.Hs / 4, nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
   const int nO = T < cus ? T : (cus > 0 ? cus : 256);

@@ -34,20 +34,22 @@ struct ChainArgs {
   const int32_t* t0;       // [B]
   const float* zh;         // [B][P][r]  W1[:, :d] H
   float* h;                // [P+1][h_step] GRU state after each step (slot 0 = zeros)
+  uint16_t* hb;            // [P+1][hb_step] the same states split for bf16 MFMA: hi [B][Hs], lo [B][Hs]
   void* act;               // [P][act_step bytes] bottleneck activations of each step:
                            //   bf16 hi [B][r] then lo [B][r], or fp32 [B][r]
   uint64_t* keys;          // [P][B] packed argmax keys
   uint32_t* counters;      // [4][sub-counters][line] phase arrival counters
   int32_t* status;         // device status word
   int h_step;              // floats between consecutive state slots (256-byte multiple)
+  int hb_step;             // bf16 elements between consecutive split-state slots (256-byte multiple)
   int act_step;            // bytes between consecutive activation slots (256-byte multiple)
-  uint64_t* trace;         // phase timestamps [P][grid][6] when built with DH_TRACE_PHASES, else null
+  uint64_t* trace;         // phase timestamps [P][grid][slots] when built with DH_TRACE_PHASES, else null
 };
 
 // workspace carving for a chain launch of up to `group` sequences
 struct ChainLayout {
-  size_t status, counters, keys, zh, h, act, trace, total;
-  int h_step, act_step;
+  size_t status, counters, keys, zh, h, hb, act, trace, total;
+  int h_step, hb_step, act_step;
 };
 ChainLayout chain_layout(int d, int Hs, int r, int P, int group);
 

@@ -191,9 +191,12 @@ void domino_set_timing_events(void *base_start, void *base_stop, void *chain_sta
 
 /*
  * Chain scheduling.  0 (default): one persistent cooperative launch runs
- * all P steps; 1: three kernel launches per step.  Both compute the same
- * values.  Returns the previous mode; any other value is rejected with -1.
- * Process-wide setting.
+ * all P steps and, for bf16 weights and batch <= 16 where it fits, keeps W2
+ * on chip (registers and LDS) for all of them; 2: the same launch with W2
+ * read from memory every step; 1: three kernel launches per step.  All
+ * compute the same function; they may differ in the last bits of fp32 sums
+ * (different k-split orders).  Returns the previous mode; any other value is
+ * rejected with -1.  Process-wide setting.
  */
 int32_t domino_set_chain_mode(int32_t mode);
 

@@ -132,9 +132,11 @@ def test_workspace_size_grows_then_saturates():
 
 def test_chain_mode_switch():
     prev = dh.set_chain_mode(1)
-    assert dh.set_chain_mode(prev) == 1
-    with pytest.raises(ValueError):
-        dh.set_chain_mode(7)
+    assert dh.set_chain_mode(2) == 1
+    assert dh.set_chain_mode(prev) == 2
+    for bad in (7, 3, -1):
+        with pytest.raises(ValueError):
+            dh.set_chain_mode(bad)
 
 
 def test_tree_arguments_rejected_before_launch():

@@ -27,7 +27,7 @@ def _device():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=[0, 1], ids=["persistent", "stepwise"])
+@pytest.fixture(params=[0, 1, 2], ids=["persistent", "stepwise", "persistent-streamed"])
 def chain_mode(request):
     prev = dh.set_chain_mode(request.param)
     yield request.param
@@ -168,9 +168,12 @@ def test_chain_deterministic_and_prefix_stable():
     assert np.array_equal(t8, t1[:, :8]) and np.array_equal(L8, L1[:, :8])
 
 
-def test_chain_modes_agree_bitwise():
-    cfg = small_config(d=96, V=1501, Hs=48, r=32, P=12, B=20, dtype="bf16")
-    say("case chain modes agree")
+# B <= 16 with bf16 weights keeps W2 on chip in mode 0; every mode splits k
+# over the waves in the same order, so all three agree to the bit
+@pytest.mark.parametrize("B,r", [(20, 32), (9, 32), (16, 256), (1, 256)])
+def test_chain_modes_agree_bitwise(B, r):
+    cfg = small_config(d=96, V=1501, Hs=48, r=r, P=12, B=B, dtype="bf16", biases=True)
+    say(f"case chain modes agree B={B} r={r}")
     w = synth.make_weights(cfg)
     inp = synth.make_inputs(cfg)
     prev = dh.set_chain_mode(0)
@@ -178,10 +181,13 @@ def test_chain_modes_agree_bitwise():
         head, _, t0_, L0, s0 = _run(cfg, w, inp)
         dh.set_chain_mode(1)
         _, _, t1_, L1, s1 = _run(cfg, w, inp, head=head)
+        dh.set_chain_mode(2)
+        _, _, t2_, L2, s2 = _run(cfg, w, inp, head=head)
     finally:
         dh.set_chain_mode(prev)
-    assert s0 == s1 == 0
+    assert s0 == s1 == s2 == 0
     assert np.array_equal(t0_, t1_) and np.array_equal(L0, L1)
+    assert np.array_equal(t0_, t2_) and np.array_equal(L0, L2)
 
 
 def test_chain_bad_first_token_flagged():
@@ -240,7 +246,8 @@ def test_chain_on_side_stream():
 
 
 @pytest.mark.parametrize("key,sample,mode", [("qwen3_4b_b1", [0], 0), ("qwen3_4b_b1", [0], 1),
-                                             ("qwen3_4b_b32", [0, 13, 31], 0), ("qwen3_8b_b16", [0, 15], 0)])
+                                             ("qwen3_4b_b1", [0], 2), ("qwen3_4b_b32", [0, 13, 31], 0),
+                                             ("qwen3_8b_b16", [0, 15], 0), ("qwen3_8b_b16", [3], 2)])
 def test_chain_full_size_sampled(key, sample, mode):
     cfg = synth.CONFIGS[key]
     say(f"case chain full {key} mode={mode} sample={sample}")
