@@ -500,15 +500,17 @@ __device__ __forceinline__ void lane_max(LaneMax& m, float L, int32_t idx) {
 __device__ __forceinline__ uint64_t lane_key(const LaneMax& m) { return m.i < 0 ? 0 : amax_key(m.v, (uint32_t)m.i); }
 
 // One lane's four logits of a tile, L = (Lb + b2) + (even k chunks + odd k
-// chunks), folded into its running argmax and written out on request.  Both
-// phase-O variants use this, so they agree to the bit.
-__device__ __forceinline__ void tile_epilogue(const ChainArgs& a, int vv, const float (&base)[4], const f32x4 (&acc)[2],
-                                              bool bok, size_t lrow, LaneMax& m) {
+// chunks), folded into its running argmax and, with kWrite, written out.
+// `full` (uniform): the whole tile lies inside the vocabulary.  Both phase-O
+// variants use this, so they agree to the bit.
+template <bool kWrite>
+__device__ __forceinline__ void tile_epilogue(const ChainArgs& a, int vv, bool full, const float (&base)[4],
+                                              const f32x4 (&acc)[2], bool bok, size_t lrow, LaneMax& m) {
   const int V = a.V;
   float L[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) L[e] = base[e] + (acc[0][e] + acc[1][e]);
-  if (vv + 3 < V) {
+  if (full) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) lane_max(m, L[e], vv + e);
   } else {
@@ -516,14 +518,16 @@ __device__ __forceinline__ void tile_epilogue(const ChainArgs& a, int vv, const 
     for (int e = 0; e < 4; ++e)
       if (vv + e < V) lane_max(m, L[e], vv + e);
   }
-  if (a.out_logits && bok) {
-    float* dst = a.out_logits + lrow + vv;
-    if ((V & 3) == 0 && vv + 3 < V) {
-      *reinterpret_cast<float4*>(dst) = make_float4(L[0], L[1], L[2], L[3]);
-    } else {
+  if constexpr (kWrite) {
+    if (bok) {
+      float* dst = a.out_logits + lrow + vv;
+      if ((V & 3) == 0 && full) {
+        *reinterpret_cast<float4*>(dst) = make_float4(L[0], L[1], L[2], L[3]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (vv + e < V) dst[e] = L[e];
+        for (int e = 0; e < 4; ++e)
+          if (vv + e < V) dst[e] = L[e];
+      }
     }
   }
 }
@@ -645,11 +649,12 @@ __device__ __forceinline__ void publish_best(const ChainArgs& a, int p, uint64_t
 
 // base logits, then the correction from resident W2 tiles, then the argmax;
 // same arithmetic and summation order as logits_range
-template <class W, int NCB, int KC, int NTW, class Ready>
-__device__ __forceinline__ bool logits_resident(const ChainArgs& a, int p, int t_begin, int t_end, const frag_t<W> (&w2r)[NTW][KC],
-                                const unsigned char* w2_lds, uint64_t* sbest, Ready ready) {
+template <class W, int NCB, int KC, int NTW, bool kWrite, class Ready>
+__device__ __forceinline__ bool logits_resident_(const ChainArgs& a, int p, int t_begin, int t_end,
+                                                 const frag_t<W> (&w2r)[NTW][KC], const unsigned char* w2_lds,
+                                                 uint64_t* sbest, Ready ready) {
   constexpr int NT = NTW + kLdsTilesPerWave;  // slots below NTW: registers; then LDS
-  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
+  const int lane = opaque_lane(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15, kg = lane >> 4;
   const int B = a.B, r = a.r, V = a.V, P = a.P;
   const char* act_p = (const char*)a.act + (size_t)p * a.act_step;
@@ -709,7 +714,8 @@ __device__ __forceinline__ bool logits_resident(const ChainArgs& a, int p, int t
           acc[c & 1] = mma(w, bf[c], acc[c & 1]);
         }
       }
-      tile_epilogue(a, tile_of(i) * 16 + kg * 4, lb[cb][i], acc, bok[cb], lrow[cb], lm);
+      tile_epilogue<kWrite>(a, tile_of(i) * 16 + kg * 4, (tile_of(i) + 1) * 16 <= V, lb[cb][i], acc, bok[cb], lrow[cb],
+                            lm);
     }
     best[cb] = lane_key(lm);
   }
@@ -717,6 +723,14 @@ __device__ __forceinline__ bool logits_resident(const ChainArgs& a, int p, int t
   publish_best<NCB>(a, p, best, sbest);
   DH_STAMP(p, 7);
   return true;
+}
+
+template <class W, int NCB, int KC, int NTW, class Ready>
+__device__ __forceinline__ bool logits_resident(const ChainArgs& a, int p, int t_begin, int t_end,
+                                                const frag_t<W> (&w2r)[NTW][KC], const unsigned char* w2_lds,
+                                                uint64_t* sbest, Ready ready) {
+  if (a.out_logits) return logits_resident_<W, NCB, KC, NTW, true>(a, p, t_begin, t_end, w2r, w2_lds, sbest, ready);
+  return logits_resident_<W, NCB, KC, NTW, false>(a, p, t_begin, t_end, w2r, w2_lds, sbest, ready);
 }
 
 template <class W, int NCB, int KC>
@@ -728,10 +742,11 @@ struct TileBuf {
 
 // `ready` is called by the whole workgroup after the first tiles are in flight
 // and before the activations are read; it returns false when the kernel must stop.
-template <class W, int NCB, int KC, class Ready>
-__device__ __forceinline__ bool logits_range(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest, Ready ready) {
+template <class W, int NCB, int KC, bool kWrite, class Ready>
+__device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest,
+                                              Ready ready) {
   constexpr int PF = DH_O_PREFETCH;
-  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
+  const int lane = opaque_lane(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15, kg = lane >> 4;
   const int B = a.B, r = a.r, V = a.V, P = a.P;
   const bool vec4 = (V & 3) == 0;
@@ -817,7 +832,7 @@ __device__ __forceinline__ bool logits_range(const ChainArgs& a, int p, int t_be
       float base[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) base[e] = a.b2 ? tb.lb[cb][e] + tb.b2[e] : tb.lb[cb][e];
-      tile_epilogue(a, vv, base, acc[cb], bok[cb], lrow[cb], lm[cb]);
+      tile_epilogue<kWrite>(a, vv, (t + 1) * 16 <= V, base, acc[cb], bok[cb], lrow[cb], lm[cb]);
     }
   };
 
@@ -836,6 +851,13 @@ __device__ __forceinline__ bool logits_range(const ChainArgs& a, int p, int t_be
   for (int cb = 0; cb < NCB; ++cb) best[cb] = lane_key(lm[cb]);
   publish_best<NCB>(a, p, best, sbest);
   return true;
+}
+
+template <class W, int NCB, int KC, class Ready>
+__device__ __forceinline__ bool logits_range(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest,
+                                             Ready ready) {
+  if (a.out_logits) return logits_range_<W, NCB, KC, true>(a, p, t_begin, t_end, sbest, ready);
+  return logits_range_<W, NCB, KC, false>(a, p, t_begin, t_end, sbest, ready);
 }
 
 // ---- kernels ------------------------------------------------------------------------
@@ -1069,14 +1091,6 @@ static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStr
   ChainArgs arg = a;
   void* params[] = {&arg};
   return hipLaunchCooperativeKernel(fn, dim3(cache.blocks), dim3(256), params, (unsigned)lds_bytes, s);
-}
-
-static int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    return 0;
-  return cus;
 }
 
 constexpr size_t kLdsBudget = 144 * 1024;  // dynamic LDS the persistent kernel may use (160 KB per CU)

@@ -86,6 +86,86 @@ __global__ __launch_bounds__(256) void gemm_stream(const W* __restrict__ A, int 
   }
 }
 
+#ifndef DH_R16_WAVES
+#define DH_R16_WAVES 8  // waves per workgroup of gemm_rows16
+#endif
+#ifndef DH_R16_U
+#define DH_R16_U 8      // k chunks per batch of loads in gemm_rows16
+#endif
+
+// At most 16 rows of A (one draft block of one sequence): the product is
+// bound by reading B once, and what limits the rate is how evenly that read
+// is spread.  Persistent: one workgroup per CU; A is staged once in LDS in
+// fragment order (k chunk c, lane l at 16-byte slot c*64 + l, so a fragment
+// read is 1 KB contiguous).  Workgroup g owns the 16-column tiles
+// [T g / G, T (g+1) / G); its waves split that range's (tile, k chunk) pairs
+// evenly, so every wave streams the same number of bytes of B.  A tile cut
+// between waves w and w+1 is finished by wave w as its lower-k part plus
+// wave w+1's higher-k part, a fixed order.  Needs at least WAVES tiles per
+// workgroup, so no tile is cut twice.
+template <int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void gemm_rows16(const uint16_t* __restrict__ A, int lda,
+                                                          const uint16_t* __restrict__ B, int ldb, float* __restrict__ C,
+                                                          int ldc, int M, int N, int K) {
+  extern __shared__ __attribute__((aligned(16))) uint4 sA[];  // [k chunks][64 lanes]
+  __shared__ __attribute__((aligned(16))) float4 part[WAVES][64];
+  const int nck = (K + 31) / 32;
+  for (int q = threadIdx.x; q < nck * 64; q += blockDim.x) {
+    const int c = q >> 6, l = q & 63, r = l & 15, k = c * 32 + (l >> 4) * 8;
+    sA[q] = (r < M && k < K) ? *reinterpret_cast<const uint4*>(A + (size_t)r * lda + k) : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane & 15, kg = lane >> 4;
+  const int T = (N + 15) / 16, G = gridDim.x, g = blockIdx.x;
+  const int tb = (int)((int64_t)T * g / G), te = (int)((int64_t)T * (g + 1) / G);
+  const int64_t total = (int64_t)(te - tb) * nck;
+  const int64_t lo = total * wv / WAVES, hi = total * (wv + 1) / WAVES;
+
+  auto store_tile = [&](int t, const f32x4& v) {
+    const int n = t * 16 + row;
+    if (n >= N) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (kg * 4 + i < M) C[(size_t)(kg * 4 + i) * ldc + n] = v[i];
+  };
+
+  f32x4 head = {0.f, 0.f, 0.f, 0.f};  // lower-k part of the tile cut at the end of this wave's range
+  int cut_tile = -1;
+  for (int64_t pos = lo; pos < hi;) {
+    const int t = tb + (int)(pos / nck), c0 = (int)(pos % nck);
+    const int c1 = (int)(c0 + (hi - pos) < nck ? c0 + (hi - pos) : nck);
+    const uint16_t* brow = B + (size_t)min(t * 16 + row, N - 1) * ldb + kg * 8;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = c0; c < c1; c += U) {
+      bf16x8 bfr[U], af[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int cc = c + u;
+        const bool ok = cc < c1 && cc * 32 + kg * 8 < K;
+        bfr[u] = load8_or_zero(brow + cc * 32, ok);
+        af[u] = ok ? __builtin_bit_cast(bf16x8, sA[cc * 64 + lane]) : zero8<uint16_t>();
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc = mma(af[u], bfr[u], acc);
+    }
+    if (c0 == 0 && c1 == nck) {
+      store_tile(t, acc);
+    } else if (c0 == 0) {  // the range ends inside tile t
+      head = acc;
+      cut_tile = t;
+    } else {  // the range starts inside tile t: its higher-k part
+      part[wv][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    pos += c1 - c0;
+  }
+  __syncthreads();
+  if (cut_tile >= 0) {
+    const float4 q = part[wv + 1][lane];
+    store_tile(cut_tile, f32x4{head[0] + q.x, head[1] + q.y, head[2] + q.z, head[3] + q.w});
+  }
+}
+
 // Small products (few columns, e.g. the 256 bottleneck units): one 16x16
 // output tile per workgroup, k split over its 4 waves (splitk_tile).
 template <class W>
@@ -224,6 +304,26 @@ hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int 
   }
   if (dtype == kF32)
     return launch_stream((const float*)A, lda, (const float*)B, ldb, C, ldc, M, N, K, s);
+  if (M <= 16) {
+    constexpr int WV = DH_R16_WAVES;
+    const int cus = device_cus();
+    const size_t lds = (size_t)((K + 31) / 32) * 64 * 16;
+    if (cus > 0 && (N + 15) / 16 >= WV * cus && lds <= 128 * 1024) {
+      static thread_local int attr_device = -1;
+      int dev = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) return e;
+      if (attr_device != dev) {
+        e = hipFuncSetAttribute((const void*)gemm_rows16<WV, DH_R16_U>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                128 * 1024);
+        if (e != hipSuccess) return e;
+        attr_device = dev;
+      }
+      hipLaunchKernelGGL((gemm_rows16<WV, DH_R16_U>), dim3(cus), dim3(64 * WV), lds, s, (const uint16_t*)A, lda,
+                         (const uint16_t*)B, ldb, C, ldc, M, N, K);
+      return hipGetLastError();
+    }
+  }
   if (!prefer_tiles || M <= 64)
     return launch_stream((const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, M, N, K, s);
   const int m_tiles = (M + TBM - 1) / TBM, n_tiles = (N + TBN - 1) / TBN;

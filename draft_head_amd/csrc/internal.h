@@ -11,6 +11,15 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kMaxChainGroup = 32;  // sequences per chain launch (two 16-column MFMA blocks)
 
+// compute units of the current device (0 if the query fails)
+inline int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 0;
+  return cus;
+}
+
 // C[m][n] = sum_k A[m][k] B[n][k], fp32 out.  prefer_tiles selects the
 // LDS-tiled kernel for many rows of A (bf16 only).
 hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int ldb, float* C, int ldc, int M, int N,

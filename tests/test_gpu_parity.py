@@ -86,6 +86,21 @@ def test_base_logits_ragged(dtype, d, V, B, P):
     _check_gemm(g, inp["H"], w["lm_head"], dtype, "ragged")
 
 
+# one sequence, many columns: the persistent balanced kernel (at least eight
+# 16-column tiles per CU), with ragged rows, columns and k tails
+@pytest.mark.parametrize("d,V,P", [(264, 33013, 5), (2568, 40009, 16), (40, 70001, 3), (1032, 36871, 1)])
+def test_base_logits_one_sequence_wide(d, V, P):
+    cfg = small_config(d=d, V=V, B=1, P=P, dtype="bf16")
+    say(f"case base logits one sequence wide d={d} V={V} P={P}")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    g = head.base_logits(head.upload(inp["H"])).cpu().numpy()
+    _check_gemm(g, inp["H"], w["lm_head"], "bf16", "one sequence wide")
+    g2 = head.base_logits(head.upload(inp["H"])).cpu().numpy()
+    assert np.array_equal(g, g2)  # fixed split and summation order
+
+
 @pytest.mark.parametrize("key,rows", [("qwen3_4b_b1", [(0, 0), (0, 15)]), ("qwen3_4b_b32", [(0, 0), (31, 9)]),
                                       ("qwen3_8b_b16", [(0, 3), (15, 15)])])
 def test_base_logits_full_size_sampled(key, rows):
