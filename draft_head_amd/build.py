@@ -12,6 +12,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU forms stay off: hipcc would otherwise fuse fp32 pairs by itself
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no fused multiply-adds unless written: every kernel variant then rounds
+    # the same expression the same way, and the schedules agree to the bit
+    "-ffp-contract=off",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -187,9 +187,15 @@ domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* 
     a.hb_step = L.hb_step;
     a.act = ws + L.act;
     a.keys = (uint64_t*)(ws + L.keys);
-    a.counters = (uint32_t*)(ws + L.counters);
     a.status = (int32_t*)(ws + L.status);
     a.h_step = L.h_step;
+    a.ll_h = (uint64_t*)(ws + L.ll_h);
+    a.ll_act = (uint64_t*)(ws + L.ll_act);
+    a.ll_part = (uint64_t*)(ws + L.ll_part);
+    a.ll_tok = (uint64_t*)(ws + L.ll_tok);
+    a.epoch = (uint32_t*)(ws + L.status + 4);
+    a.marker = (uint64_t*)(ws + L.status + 8);
+    a.ll_words = (L.trace - L.ll_h) / 8;
     a.act_step = L.act_step;
 #ifdef DH_TRACE_PHASES
     a.trace = (uint64_t*)(ws + L.trace);

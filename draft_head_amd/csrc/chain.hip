@@ -16,18 +16,20 @@
 //   W  bottleneck.  Work item = 16 rows of W1's state half; the H half,
 //      W1[:, :d] H_p, is computed for all positions before the chain.  The
 //      output is written as a bf16 hi + lo pair ready for phase O.
-//   O  W2 + base add + argmax.  Each workgroup streams a contiguous range of
+//   O  W2 + base add + argmax.  Each workgroup owns a contiguous range of
 //      16-row W2 tiles, keeps the bottleneck fragments in registers, adds the
 //      base-logit row in the MFMA epilogue and folds (value, index) into one
-//      64-bit key per sequence: wave shuffles, then LDS, then one device-wide
-//      atomic max per workgroup.  Full logits are written only on request.
-// The drafted token never leaves the device: phase G of the next step reads
-// the winning key.
+//      64-bit key per sequence: wave shuffles, then LDS, then one result per
+//      workgroup.  Full logits are written only on request.
+// The drafted token never leaves the device: phase G of the next step reduces
+// the workgroups' results.
 //
-// Two schedules compute identical values:
-//  * persistent: one cooperative launch for all P steps; phases are
-//    separated by arrival counters with bounded waits;
-//  * stepwise: three launches per step on the caller's stream.
+// Schedules that compute identical values:
+//  * persistent: one cooperative launch for all P steps.  Values cross
+//    workgroups as tagged hand-off words that readers poll (bounded waits);
+//    W2 either stays on chip for the whole launch or is streamed every step;
+//  * stepwise: three launches per step on the caller's stream, with a device
+//    wide atomic max per workgroup for the argmax.
 #include "device.h"
 #include "internal.h"
 
@@ -56,6 +58,8 @@ __device__ __forceinline__ int opaque_lane() {
 __device__ __forceinline__ float bias_at(const float* b, int i) { return b ? b[i] : 0.f; }
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
 
+__device__ __forceinline__ int32_t clamp_token(const ChainArgs& a, int32_t t) { return (t < 0 || t >= a.V) ? 0 : t; }
+
 __device__ __forceinline__ int32_t prev_token(const ChainArgs& a, int p, int b) {
   int32_t t = p == 0 ? a.t0[b]
                      : amax_index(__hip_atomic_load(&a.keys[(size_t)(p - 1) * a.B + b], __ATOMIC_RELAXED,
@@ -80,7 +84,7 @@ __device__ __forceinline__ void copy8(W* dst, const W* src) {
 __host__ __device__ inline size_t gru_slice_elems(int d, int Hs) { return (size_t)12 * (d + 8) + (size_t)12 * (Hs + 8); }
 
 template <class W>
-__device__ void stage_gru_slice(const ChainArgs& a, int item, W* lds) {
+__device__ __forceinline__ void stage_gru_slice(const ChainArgs& a, int item, W* lds) {
   const int d = a.d, Hs = a.Hs, j0 = item * 4;
   const int nx = d / 8, nh = Hs / 8;
   for (int i = threadIdx.x; i < 12 * nx; i += blockDim.x) {
@@ -134,9 +138,76 @@ __device__ __forceinline__ typename act<W>::type state_frag(const ChainArgs& a, 
   }
 }
 
+#ifndef DH_HIDDEN_SLEEP
+#define DH_HIDDEN_SLEEP 16
+#endif
+
+// Tag of the hand-off words a persistent launch writes at step p (P <= 64).
+__device__ __forceinline__ uint32_t ll_tag(uint32_t ep, int p) { return ep * 128u + (uint32_t)p + 1u; }
+
+// The same right operand from a hand-off slot with n elements per row
+// (bf16 weights: words [0, n/2) hold hi pairs, [n/2, n) lo pairs; fp32: one
+// value per word).  Returns whether every word read carries `tag`.
+template <class W>
+__device__ __forceinline__ bool ll_frag(const uint64_t* slot, int n, int b, int k, uint32_t tag, bool ok,
+                                        typename act<W>::type& out) {
+  if (!ok) {
+    out = act<W>::zero();
+    return true;
+  }
+  const uint64_t* row = slot + (size_t)b * n;
+  bool good = true;
+  if constexpr (sizeof(W) == 2) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t wh = ld_agent64(row + k / 2 + i), wl = ld_agent64(row + n / 2 + k / 2 + i);
+      good = good && ll_ok(wh, tag) && ll_ok(wl, tag);
+      h[i] = ll_data(wh);
+      l[i] = ll_data(wl);
+    }
+    out.hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+    out.lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+  } else {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint64_t w = ld_agent64(row + k + i);
+      good = good && ll_ok(w, tag);
+      v[i] = __uint_as_float(ll_data(w));
+    }
+    out.lo = make_float4(v[0], v[1], v[2], v[3]);
+    out.hi = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  return good;
+}
+
+// four consecutive values v of row b, elements k..k+3 (k a multiple of 4),
+// into a hand-off slot with n elements per row, as ll_frag reads them
+template <class W>
+__device__ __forceinline__ void ll_put4(uint64_t* slot, int n, int b, int k, const float (&v)[4], uint32_t tag) {
+  uint64_t* row = slot + (size_t)b * n;
+  if constexpr (sizeof(W) == 2) {
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hi[i] = f2bf(v[i]);
+      lo[i] = f2bf(v[i] - bf2f(hi[i]));
+    }
+    ll_put(row + k / 2, pack2(hi[0], hi[1]), tag);
+    ll_put(row + k / 2 + 1, pack2(hi[2], hi[3]), tag);
+    ll_put(row + n / 2 + k / 2, pack2(lo[0], lo[1]), tag);
+    ll_put(row + n / 2 + k / 2 + 1, pack2(lo[2], lo[3]), tag);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ll_put(row + k + i, __float_as_uint(v[i]), tag);
+  }
+}
+
 // per-wave partial sums of W_hh h(p) over this wave's k chunks
-template <class W, int NCB, bool kLds>
-__device__ void gru_hidden_part(const ChainArgs& a, int p, int item, const W* lds, f32x4 (&acc)[NCB]) {
+// kLL: the state comes as hand-off words of the persistent launch `ep`
+template <class W, int NCB, bool kLds, bool kLL = false>
+__device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int item, const W* lds, f32x4 (&acc)[NCB], uint32_t ep = 0) {
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (p == 0) return;  // h(0) = 0
@@ -164,8 +235,25 @@ __device__ void gru_hidden_part(const ChainArgs& a, int p, int item, const W* ld
       const int c = c0 + 4 * q, k = c * 32;
       const bool kok = c < nch && k + kg * 8 < Hs;
       A[q] = load8_or_zero(rh + k, kok && has_h);
+      if constexpr (!kLL) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) S[q][cb] = state_frag<W>(a, p, bb[cb], k + kg * 8, kok && bok[cb]);
+        for (int cb = 0; cb < NCB; ++cb) S[q][cb] = state_frag<W>(a, p, bb[cb], k + kg * 8, kok && bok[cb]);
+      }
+    }
+    if constexpr (kLL) {  // h(p) was written at step p - 1; off the critical path, so polled gently
+      const uint64_t* slot = a.ll_h + (size_t)p * B * Hs;
+      ll_wait<DH_HIDDEN_SLEEP>(a.status, [&] {
+        bool good = true;
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+          const int c = c0 + 4 * q, k = c * 32;
+          const bool kok = c < nch && k + kg * 8 < Hs;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            good = ll_frag<W>(slot, Hs, bb[cb], k + kg * 8, ll_tag(ep, p - 1), kok && bok[cb], S[q][cb]) && good;
+        }
+        return good;
+      });
     }
 #pragma unroll
     for (int q = 0; q < U; ++q)
@@ -174,12 +262,16 @@ __device__ void gru_hidden_part(const ChainArgs& a, int p, int item, const W* ld
   }
 }
 
-template <class W, int NCB>
-__device__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[NCB]);
+template <class W, int NCB, bool kLL>
+__device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[NCB], float& h_own,
+                          uint32_t ep);
 
 // input half on top of the hidden-half partials, then the gates: h(p+1)
-template <class W, int NCB, bool kLds>
-__device__ void gru_finish(const ChainArgs& a, int p, int item, float* red, const W* lds, const f32x4 (&acc_h)[NCB]) {
+// tok: this step's previous tokens by sequence (raw argmax indices), or
+// null to read them from the argmax keys / first tokens
+template <class W, int NCB, bool kLds, bool kLL = false>
+__device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, float* red, const W* lds, const f32x4 (&acc_h)[NCB],
+                           const int32_t* tok = nullptr, float* h_own = nullptr, uint32_t ep = 0) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int d = a.d, B = a.B;
@@ -193,8 +285,8 @@ __device__ void gru_finish(const ChainArgs& a, int p, int item, float* red, cons
   for (int cb = 0; cb < NCB; ++cb) {
     const int b = cb * 16 + row;
     bok[cb] = b < B;
-    const int tok = bok[cb] ? prev_token(a, p, b) : 0;
-    xe[cb] = (const W*)a.embed + (size_t)tok * d + kg * 8;
+    const int t_ = bok[cb] ? (tok ? clamp_token(a, tok[b]) : prev_token(a, p, b)) : 0;
+    xe[cb] = (const W*)a.embed + (size_t)t_ * d + kg * 8;
   }
   f32x4 acc[NCB];
 #pragma unroll
@@ -219,14 +311,18 @@ __device__ void gru_finish(const ChainArgs& a, int p, int item, float* red, cons
       for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(A[q], X[q][cb], acc[cb]);
   }
 
-  gru_gates<W, NCB>(a, p, item, red, acc);
+  float h_dummy = 0.f;
+  gru_gates<W, NCB, kLL>(a, p, item, red, acc, h_own ? *h_own : h_dummy, ep);
 }
 
-// sum the four waves' pre-activation partials and apply the gates: h(p+1),
-// stored fp32 and, for bf16 weights, also split into bf16 hi + lo once here
-// rather than by every reader
-template <class W, int NCB>
-__device__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[NCB]) {
+// Sum the four waves' pre-activation partials and apply the gates: h(p+1).
+// Stepwise: stored fp32 and, for bf16 weights, also split into bf16 hi + lo
+// once here rather than by every reader.  kLL (persistent): the lane keeps
+// its own unit's fp32 state in h_own across steps, and the state goes out as
+// hand-off words only.
+template <class W, int NCB, bool kLL>
+__device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[NCB], float& h_own,
+                          uint32_t ep) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int Hs = a.Hs, B = a.B, j0 = item * 4;
@@ -255,10 +351,21 @@ __device__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const
       const float rg = sigmoidf_(pre[0] + bias_at(a.b_ih, j) + bias_at(a.b_hh, j));
       const float zg = sigmoidf_(pre[1] + bias_at(a.b_ih, Hs + j) + bias_at(a.b_hh, Hs + j));
       const float ng = tanhf(pre[2] + bias_at(a.b_ih, 2 * Hs + j) + rg * (pre[3] + bias_at(a.b_hh, 2 * Hs + j)));
-      hn = (1.f - zg) * ng + zg * h_in[(size_t)b * Hs + j];
-      store_agent(&h_out[(size_t)b * Hs + j], hn);
+      if constexpr (kLL) {
+        hn = (1.f - zg) * ng + zg * h_own;
+        h_own = hn;
+      } else {
+        hn = (1.f - zg) * ng + zg * h_in[(size_t)b * Hs + j];
+        store_agent(&h_out[(size_t)b * Hs + j], hn);
+      }
     }
-    if constexpr (sizeof(W) == 2) {
+    if constexpr (kLL) {
+      // units j0..j0+3 of sequence b sit in lanes row, row+16, row+32, row+48
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = __shfl(hn, row + 16 * q);
+      if (kg == 0 && b < B) ll_put4<W>(a.ll_h + (size_t)(p + 1) * B * Hs, Hs, b, j0, v, ll_tag(ep, p));
+    } else if constexpr (sizeof(W) == 2) {
       // units j0..j0+3 of sequence b sit in lanes row, row+16, row+32, row+48
       float v[4];
 #pragma unroll
@@ -284,7 +391,8 @@ __device__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const
 // This wave's W_ih fragments (k chunks wv + 4j) do not depend on the token,
 // so they are fetched while the workgroup still waits for it; each workgroup
 // reads the same rows every step, so they stay in its XCD's L2.
-constexpr int kXPre = 20;  // chunks per wave fetched ahead: all of them for d <= 2560
+constexpr int kXPre = 12;  // chunks per wave fetched ahead (the register budget allows no more)
+constexpr int kXTail = 8;  // chunks per batch after them
 template <class W>
 __device__ __forceinline__ void gru_x_prefetch(const ChainArgs& a, int item, frag_t<W> (&xw)[kXPre]) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, kg = lane >> 4;
@@ -301,7 +409,8 @@ __device__ __forceinline__ void gru_x_prefetch(const ChainArgs& a, int item, fra
 
 template <class W, int NCB>
 __device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int item, float* red, const frag_t<W> (&xw)[kXPre],
-                               const f32x4 (&acc_h)[NCB]) {
+                                               const f32x4 (&acc_h)[NCB], const int32_t* tok, float& h_own,
+                                               uint32_t ep) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int d = a.d, B = a.B;
@@ -314,8 +423,8 @@ __device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int it
   for (int cb = 0; cb < NCB; ++cb) {
     const int b = cb * 16 + row;
     bok[cb] = b < B;
-    const int tok = bok[cb] ? prev_token(a, p, b) : 0;
-    xe[cb] = (const W*)a.embed + (size_t)tok * d + kg * 8;
+    const int t_ = bok[cb] ? (tok ? clamp_token(a, tok[b]) : prev_token(a, p, b)) : 0;
+    xe[cb] = (const W*)a.embed + (size_t)t_ * d + kg * 8;
   }
   f32x4 acc[NCB];
 #pragma unroll
@@ -335,11 +444,11 @@ __device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int it
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(xw[j], X[j][cb], acc[cb]);
   }
-  // chunks beyond the prefetched ones (d > 4 * 32 * kXPre), same order, four per batch
-  for (int c0 = wv + 4 * kXPre; c0 < ncx; c0 += 16) {
-    frag_t<W> A[4], X[4][NCB];
+  // chunks beyond the prefetched ones (d > 4 * 32 * kXPre), same order
+  for (int c0 = wv + 4 * kXPre; c0 < ncx; c0 += 4 * kXTail) {
+    frag_t<W> A[kXTail], X[kXTail][NCB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kXTail; ++q) {
       const int c = c0 + 4 * q, k = c * 32;
       const bool kok = c < ncx && k + kg * 8 < d;
       A[q] = load8_or_zero(rx + k, kok && has_x);
@@ -347,18 +456,18 @@ __device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int it
       for (int cb = 0; cb < NCB; ++cb) X[q][cb] = load8_or_zero(xe[cb] + k, kok && bok[cb]);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kXTail; ++q)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(A[q], X[q][cb], acc[cb]);
   }
   DH_STAMP(p, 8);
-  gru_gates<W, NCB>(a, p, item, red, acc);
+  gru_gates<W, NCB, true>(a, p, item, red, acc, h_own, ep);
 }
 
 // ---- phase W: 16 bottleneck units, all sequences ----------------------------------
 // The state half of W1 for a work item, 16 rows padded by 8, resident in LDS.
 template <class W>
-__device__ void stage_w1_slice(const ChainArgs& a, int item, W* lds) {
+__device__ __forceinline__ void stage_w1_slice(const ChainArgs& a, int item, W* lds) {
   const int Hs = a.Hs, nh = Hs / 8, k0 = item * 16;
   for (int i = threadIdx.x; i < 16 * nh; i += blockDim.x) {
     const int row = i / nh, c = i - row * nh;
@@ -389,9 +498,10 @@ __device__ __forceinline__ BottleneckPre bottleneck_pre(const ChainArgs& a, int 
   return q;
 }
 
-template <class W, int NCB, bool kLdsW>
-__device__ void bottleneck_item(const ChainArgs& a, int p, int item, float* red, const W* w1_lds,
-                                const BottleneckPre& pre_terms) {
+// kLL: state in and activations out as hand-off words of the persistent launch `ep`
+template <class W, int NCB, bool kLdsW, bool kLL = false>
+__device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int item, float* red, const W* w1_lds,
+                                const BottleneckPre& pre_terms, uint32_t ep = 0) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int Hs = a.Hs, B = a.B, r = a.r;
@@ -422,8 +532,26 @@ __device__ void bottleneck_item(const ChainArgs& a, int p, int item, float* red,
       const int c = c0 + 4 * q, k = c * 32;
       const bool kok = c < nch && k + kg * 8 < Hs;
       A[q] = load8_or_zero(rw + k, kok);
+      if constexpr (!kLL) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) S[q][cb] = state_frag<W>(a, p + 1, bb[cb], k + kg * 8, kok && bok[cb]);
+        for (int cb = 0; cb < NCB; ++cb) S[q][cb] = state_frag<W>(a, p + 1, bb[cb], k + kg * 8, kok && bok[cb]);
+      }
+    }
+    if constexpr (kLL) {
+      const uint64_t* slot = a.ll_h + (size_t)(p + 1) * B * Hs;
+      ll_wait(a.status, [&] {
+        bool good = true;
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+          const int c = c0 + 4 * q, k = c * 32;
+          const bool kok = c < nch && k + kg * 8 < Hs;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            good = ll_frag<W>(slot, Hs, bb[cb], k + kg * 8, ll_tag(ep, p), kok && bok[cb], S[q][cb]) && good;
+        }
+        return good;
+      });
+      DH_STAMP(p, 11);
     }
 #pragma unroll
     for (int q = 0; q < U; ++q)
@@ -454,7 +582,9 @@ __device__ void bottleneck_item(const ChainArgs& a, int p, int item, float* red,
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = pre[i] / (1.f + expf(-pre[i]));
       char* slot = (char*)a.act + (size_t)p * a.act_step;
-      if constexpr (sizeof(W) == 2) {
+      if constexpr (kLL) {
+        ll_put4<W>(a.ll_act + (size_t)p * B * r, r, b, k, s, ll_tag(ep, p));
+      } else if constexpr (sizeof(W) == 2) {
         uint16_t hi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -499,59 +629,6 @@ __device__ __forceinline__ void lane_max(LaneMax& m, float L, int32_t idx) {
 }
 __device__ __forceinline__ uint64_t lane_key(const LaneMax& m) { return m.i < 0 ? 0 : amax_key(m.v, (uint32_t)m.i); }
 
-// One lane's four logits of a tile, L = (Lb + b2) + (even k chunks + odd k
-// chunks), folded into its running argmax and, with kWrite, written out.
-// `full` (uniform): the whole tile lies inside the vocabulary.  Both phase-O
-// variants use this, so they agree to the bit.
-template <bool kWrite>
-__device__ __forceinline__ void tile_epilogue(const ChainArgs& a, int vv, bool full, const float (&base)[4],
-                                              const f32x4 (&acc)[2], bool bok, size_t lrow, LaneMax& m) {
-  const int V = a.V;
-  float L[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) L[e] = base[e] + (acc[0][e] + acc[1][e]);
-  if (full) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) lane_max(m, L[e], vv + e);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (vv + e < V) lane_max(m, L[e], vv + e);
-  }
-  if constexpr (kWrite) {
-    if (bok) {
-      float* dst = a.out_logits + lrow + vv;
-      if ((V & 3) == 0 && full) {
-        *reinterpret_cast<float4*>(dst) = make_float4(L[0], L[1], L[2], L[3]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (vv + e < V) dst[e] = L[e];
-      }
-    }
-  }
-}
-
-// Lb + b2 for one lane's four vocabulary entries vv.. of row lrow (zeros
-// past V or when !ok)
-__device__ __forceinline__ void load_base4(const ChainArgs& a, size_t lrow, int vv, bool ok, float (&out)[4]) {
-  const float* src = a.Lb + lrow + vv;
-  if (ok && (a.V & 3) == 0 && vv + 3 < a.V) {
-    const float4 q = *reinterpret_cast<const float4*>(src);
-    out[0] = q.x;
-    out[1] = q.y;
-    out[2] = q.z;
-    out[3] = q.w;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = (ok && vv + e < a.V) ? src[e] : 0.f;
-  }
-  if (a.b2) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] += (ok && vv + e < a.V) ? a.b2[vv + e] : 0.f;
-  }
-}
-
 // W2 tiles of workgroup `wg`: the bottleneck workgroups start phase O late,
 // so they take a smaller share (DH_W_SHARE / 8 of the others').
 __host__ __device__ inline void o_tile_range(int wg, int G, int nW, int T, int& t_begin, int& t_end) {
@@ -566,15 +643,15 @@ __host__ __device__ inline void o_tile_range(int wg, int G, int nW, int T, int& 
 
 // Resident W2.  Of a workgroup's tiles [t_begin, t_end) the first 4*NTW live
 // in registers for all P steps (wave wv owns t_begin + wv + 4i, i < NTW, as
-// MFMA left operands) and the rest, at most kLdsTiles, in LDS in fragment
+// MFMA right operands) and the rest, at most kLdsTiles, in LDS in fragment
 // order (tile j, k chunk c, lane l at 16-byte slot (j*KC + c)*64 + l, so a
 // wave's fragment read is 1 KB contiguous).  Slot i of wave wv is tile
 // t_begin + wv + 4i throughout.  Phase O then reads no weights from memory.
 constexpr int kLdsTilesPerWave = 5;
 constexpr int kLdsTiles = 4 * kLdsTilesPerWave;
 template <int KC>
-constexpr int resident_tiles() {  // 4 AGPRs per lane per k chunk: at most 192 of them
-  return KC >= 8 ? 6 : (KC >= 4 ? 12 : 8);
+constexpr int resident_tiles() {  // 4 AGPRs per lane per k chunk; at most 192 of them, so the rest fits
+  return KC >= 8 ? 6 : (KC >= 4 ? 10 : 8);
 }
 template <class W, int KC>
 constexpr bool resident_fits() {
@@ -585,6 +662,9 @@ __host__ __device__ inline size_t w2_lds_tile_bytes(int KC) { return (size_t)KC 
 // Loads from clamped, in-bounds addresses (no select).  Rows past V are never
 // stored; k positions past r meet zero activations, so the finite weights
 // read there add exactly zero.
+// LDS for the staged activations of a resident-W2 launch (256-byte multiple)
+__host__ __device__ inline size_t act_stage_bytes(int B, int r) { return ((size_t)B * r * 4 + 255) & ~size_t(255); }
+
 // (t may be -1 for a workgroup that owns no tile; such rows are never used)
 template <class W>
 __device__ __forceinline__ const W* w2_frag_ptr(const ChainArgs& a, int t, int row, int kg, int c) {
@@ -592,7 +672,7 @@ __device__ __forceinline__ const W* w2_frag_ptr(const ChainArgs& a, int t, int r
   return (const W*)a.w2 + (size_t)v * a.r + min(c * 32 + kg * 8, a.r - 8);
 }
 
-// The register tier is loaded straight into AGPRs (the MFMA reads its left
+// The register tier is loaded straight into AGPRs (the MFMA reads its right
 // operand from there), so it does not compete with the VGPRs the phases use.
 // The loads are not visible to the compiler's wait-count tracking, hence the
 // explicit wait for all of them; later compiler-issued waits are only ever
@@ -616,7 +696,7 @@ __device__ __forceinline__ void load_resident_w2(const ChainArgs& a, int t_begin
 
 // the LDS tier: tiles t_begin + 4*NTW + j, j < n_lds
 template <class W, int KC>
-__device__ void stage_w2_lds(const ChainArgs& a, int t_first, int n_lds, unsigned char* lds) {
+__device__ __forceinline__ void stage_w2_lds(const ChainArgs& a, int t_first, int n_lds, unsigned char* lds) {
   for (int q = threadIdx.x; q < n_lds * KC * 64; q += blockDim.x) {
     const int l = q & 63, c = (q >> 6) % KC, j = q / (KC * 64);
     *reinterpret_cast<uint4*>(lds + (size_t)q * 16) =
@@ -625,217 +705,278 @@ __device__ void stage_w2_lds(const ChainArgs& a, int t_first, int n_lds, unsigne
   __syncthreads();
 }
 
-// fold this workgroup's per-lane best keys into the device-wide keys of step p
-template <int NCB>
-__device__ __forceinline__ void publish_best(const ChainArgs& a, int p, uint64_t (&best)[NCB], uint64_t* sbest) {
-  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
-  const int row = lane & 15, kg = lane >> 4;
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 16));
-    best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 32));
-    if (kg == 0) sbest[(wv * NCB + cb) * 16 + row] = best[cb];
+// ---- phase O in paired-row form --------------------------------------------------
+// The MFMA's left operand holds the activations: row 2j of row group g is the
+// bf16 hi half of sequence 8g + j, row 2j + 1 its lo half (fp32 weights: the
+// value, and zeros).  The right operand is a 16-row W2 tile, so lane l holds,
+// for vocabulary entry t*16 + l % 16, result rows 4kg .. 4kg + 3 (kg = l / 16):
+// the hi and lo sums of sequences 8g + 2kg and 8g + 2kg + 1.  Eight sequences
+// share one MFMA per k chunk, and a lane's epilogue handles one entry.
+// L = (Lb + b2) + (hi + lo), hi and lo each the even k chunks' sum plus the
+// odd ones'; every phase-O variant computes exactly this.
+constexpr int kSeqPerRowGroup = 8;
+
+// left operand, elements k..k+7, for row `row` of row group g
+template <class W>
+__device__ __forceinline__ frag_t<W> act_row_frag(const uint32_t* act_s, int r, int B, int g, int row, int k) {
+  const int b = g * kSeqPerRowGroup + (row >> 1), part = row & 1;
+  if (b >= B || k >= r) return zero8<W>();
+  const uint32_t* src = act_s + (size_t)b * r;
+  if constexpr (sizeof(W) == 2) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + (part ? r / 2 : 0) + k / 2));
+  } else {
+    if (part) return zero8<float>();
+    f32x8 f;
+    f.lo = *reinterpret_cast<const float4*>(src + k);
+    f.hi = *reinterpret_cast<const float4*>(src + k + 4);
+    return f;
   }
+}
+
+// Lb of vocabulary entry v for this lane's sequences (8g + 2kg + j), and b2[v]
+template <int RG>
+__device__ __forceinline__ void load_base_rows(const ChainArgs& a, int p, int v, int kg, bool ok, float (&lb)[RG][2],
+                                               float& b2) {
+  const bool vok = ok && v < a.V;
+  b2 = (vok && a.b2) ? a.b2[v] : 0.f;
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int b = g * kSeqPerRowGroup + 2 * kg + j;
+      lb[g][j] = (vok && b < a.B) ? a.Lb[((size_t)b * a.P + p) * a.V + v] : 0.f;
+    }
+}
+
+// this lane's logits of a tile into its running argmaxes (and out, with kWrite)
+template <bool kWrite, int RG>
+__device__ __forceinline__ void rows_epilogue(const ChainArgs& a, int p, int v, int kg, const float (&lb)[RG][2],
+                                              float b2, const f32x4 (&acc)[RG][2], LaneMax (&lm)[RG][2]) {
+  if (v >= a.V) return;
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float hi = acc[g][0][2 * j] + acc[g][1][2 * j];
+      const float lo = acc[g][0][2 * j + 1] + acc[g][1][2 * j + 1];
+      const float base = a.b2 ? lb[g][j] + b2 : lb[g][j];
+      const float L = base + (hi + lo);
+      lane_max(lm[g][j], L, v);
+      if constexpr (kWrite) {
+        const int b = g * kSeqPerRowGroup + 2 * kg + j;
+        if (b < a.B) a.out_logits[((size_t)b * a.P + p) * a.V + v] = L;
+      }
+    }
+}
+
+// Fold the lanes' running argmaxes into one key per sequence for this
+// workgroup, then into the device-wide key of step p (atomic max), or, kLL,
+// publish it as this workgroup's (value, index) pair of hand-off words.
+template <int RG, bool kLL>
+__device__ __forceinline__ void publish_rows(const ChainArgs& a, int p, LaneMax (&lm)[RG][2], uint64_t* sbest,
+                                             uint32_t ep) {
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6, kg = lane >> 4;
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint64_t k = lane_key(lm[g][j]);
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) k = umax64(k, shfl_xor_u64(k, m));  // the 16 lanes of this kg
+      if ((lane & 15) == 0) sbest[wv * kMaxChainGroup + g * kSeqPerRowGroup + 2 * kg + j] = k;
+    }
   __syncthreads();
-  if (threadIdx.x < NCB * 16) {
-    const int cb = threadIdx.x >> 4, rr = threadIdx.x & 15, b = cb * 16 + rr;
+  if (threadIdx.x < RG * kSeqPerRowGroup) {
+    const int b = threadIdx.x;
     uint64_t m = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) m = umax64(m, sbest[(w * NCB + cb) * 16 + rr]);
-    if (b < a.B && m != 0) atomicMax((unsigned long long*)&a.keys[(size_t)p * a.B + b], (unsigned long long)m);
+    for (int w = 0; w < 4; ++w) m = umax64(m, sbest[w * kMaxChainGroup + b]);
+    if constexpr (kLL) {
+      if (b < a.B) {
+        uint64_t* w = a.ll_part + (((size_t)p * kMaxChainGrid + blockIdx.x) * a.B + b) * 2;
+        ll_put(w, (uint32_t)(m >> 32), ll_tag(ep, p));
+        ll_put(w + 1, (uint32_t)m, ll_tag(ep, p));
+      }
+    } else {
+      if (b < a.B && m != 0) atomicMax((unsigned long long*)&a.keys[(size_t)p * a.B + b], (unsigned long long)m);
+    }
   }
   __syncthreads();
 }
 
-// base logits, then the correction from resident W2 tiles, then the argmax;
-// same arithmetic and summation order as logits_range
-template <class W, int NCB, int KC, int NTW, bool kWrite, class Ready>
-__device__ __forceinline__ bool logits_resident_(const ChainArgs& a, int p, int t_begin, int t_end,
+// The bottleneck activations of step p, polled by the whole workgroup (a few
+// words per thread) and staged in LDS as the words' data: act_s[b * r + q]
+// holds word q of sequence b (bf16: hi pairs, then lo pairs; fp32: values).
+constexpr int kActWordsPerThread = 8;  // per poll round; B <= 8 at r = 256 takes one round
+__device__ __forceinline__ void stage_act_ll(const ChainArgs& a, int p, uint32_t ep, uint32_t* act_s) {
+  const int n = a.B * a.r;
+  const uint64_t* slot = a.ll_act + (size_t)p * n;
+  const uint32_t tag = ll_tag(ep, p);
+  for (int base = 0; base < n; base += kActWordsPerThread * (int)blockDim.x) {
+    uint32_t v[kActWordsPerThread];
+    ll_wait(a.status, [&] {
+      bool good = true;
+#pragma unroll
+      for (int i = 0; i < kActWordsPerThread; ++i) {
+        const int q = base + threadIdx.x + i * (int)blockDim.x;
+        if (q < n) {
+          const uint64_t w = ld_agent64(slot + q);
+          good = good && ll_ok(w, tag);
+          v[i] = ll_data(w);
+        }
+      }
+      return good;
+    });
+#pragma unroll
+    for (int i = 0; i < kActWordsPerThread; ++i) {
+      const int q = base + threadIdx.x + i * (int)blockDim.x;
+      if (q < n) act_s[q] = v[i];
+    }
+  }
+  __syncthreads();
+}
+// the same staging from the stepwise schedule's activation buffer (bf16: hi
+// [B][r] then lo [B][r]; fp32: [B][r])
+template <class W>
+__device__ __forceinline__ void stage_act_global(const ChainArgs& a, int p, uint32_t* act_s) {
+  const int B = a.B, r = a.r, n = B * r;
+  const uint32_t* slot = reinterpret_cast<const uint32_t*>((const char*)a.act + (size_t)p * a.act_step);
+  for (int q = threadIdx.x; q < n; q += blockDim.x) {
+    if constexpr (sizeof(W) == 2) {
+      const int b = q / r, w = q - b * r;
+      act_s[q] = w < r / 2 ? slot[(size_t)b * (r / 2) + w] : slot[(size_t)B * (r / 2) + (size_t)b * (r / 2) + w - r / 2];
+    } else {
+      act_s[q] = slot[q];
+    }
+  }
+  __syncthreads();
+}
+
+// phase O with resident W2 (persistent schedule): the base logits of every
+// owned tile are fetched before the activations exist
+template <class W, int RG, int KC, int NTW, bool kWrite>
+__device__ __forceinline__ void logits_resident_(const ChainArgs& a, int p, int t_begin, int t_end,
                                                  const frag_t<W> (&w2r)[NTW][KC], const unsigned char* w2_lds,
-                                                 uint64_t* sbest, Ready ready) {
+                                                 uint32_t* act_s, uint64_t* sbest, uint32_t ep) {
   constexpr int NT = NTW + kLdsTilesPerWave;  // slots below NTW: registers; then LDS
   const int lane = opaque_lane(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15, kg = lane >> 4;
-  const int B = a.B, r = a.r, V = a.V, P = a.P;
-  const char* act_p = (const char*)a.act + (size_t)p * a.act_step;
   auto tile_of = [&](int i) { return t_begin + wv + 4 * i; };
-  size_t lrow[NCB];
-  bool bok[NCB];
+  float lb[NT][RG][2], b2[NT];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int b = cb * 16 + row;
-    bok[cb] = b < B;
-    lrow[cb] = ((size_t)(bok[cb] ? b : 0) * P + p) * V;
-  }
-  // Lb + b2 of every owned tile: inputs, fetched before the activations exist
-  float lb[NCB][NT][4];
+  for (int i = 0; i < NT; ++i) load_base_rows<RG>(a, p, tile_of(i) * 16 + row, kg, tile_of(i) < t_end, lb[i], b2[i]);
+  stage_act_ll(a, p, ep, act_s);  // the activations of this step
+  DH_STAMP(p, 4);
+  frag_t<W> af[RG][KC];
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int c = 0; c < KC; ++c) af[g][c] = act_row_frag<W>(act_s, a.r, a.B, g, row, c * 32 + kg * 8);
+  LaneMax lm[RG][2];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) lm[g][0] = lm[g][1] = LaneMax{0.f, -1};
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    const int t = tile_of(i);
+    if (tile_of(i) >= t_end) break;
+    f32x4 acc[RG][2];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) load_base4(a, lrow[cb], t * 16 + kg * 4, t < t_end, lb[cb][i]);
-  }
-  if (!ready()) return false;
-
-  uint64_t best[NCB];
+    for (int g = 0; g < RG; ++g) acc[g][0] = acc[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i < NTW) {
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    LaneMax lm{0.f, -1};
-    const int b = cb * 16 + row;
-    typename act<W>::type bf[KC];
+      for (int c = 0; c < KC; ++c)
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const int k = c * 32 + kg * 8;
-      const bool ok = bok[cb] && k < r;
-      if constexpr (sizeof(W) == 2) {
-        const uint16_t* hi = (const uint16_t*)act_p + (size_t)b * r + k;
-        bf[c].hi = load8_or_zero(hi, ok);
-        bf[c].lo = load8_or_zero(hi + (size_t)B * r, ok);
-      } else {
-        bf[c] = load8_or_zero((const float*)act_p + (size_t)b * r + k, ok);
+        for (int g = 0; g < RG; ++g) acc[g][c & 1] = mma(af[g][c], w2r[i < NTW ? i : 0][c], acc[g][c & 1]);
+    } else {
+      const unsigned char* src = w2_lds + ((size_t)(4 * (i - NTW) + wv) * KC * 64 + lane) * 16;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const frag_t<W> w = *reinterpret_cast<const frag_t<W>*>(src + (size_t)c * 64 * 16);
+#pragma unroll
+        for (int g = 0; g < RG; ++g) acc[g][c & 1] = mma(af[g][c], w, acc[g][c & 1]);
       }
     }
-#ifdef DH_TRACE_PHASES
-    __builtin_amdgcn_s_waitcnt(0);
-    if (cb == 0) DH_STAMP(p, 10);
-#endif
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      if (tile_of(i) >= t_end) break;
-      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      if (i < NTW) {
-#pragma unroll
-        for (int c = 0; c < KC; ++c) acc[c & 1] = mma(w2r[i < NTW ? i : 0][c], bf[c], acc[c & 1]);
-      } else {
-        const unsigned char* src = w2_lds + ((size_t)(4 * (i - NTW) + wv) * KC * 64 + lane) * 16;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const frag_t<W> w = *reinterpret_cast<const frag_t<W>*>(src + (size_t)c * 64 * 16);
-          acc[c & 1] = mma(w, bf[c], acc[c & 1]);
-        }
-      }
-      tile_epilogue<kWrite>(a, tile_of(i) * 16 + kg * 4, (tile_of(i) + 1) * 16 <= V, lb[cb][i], acc, bok[cb], lrow[cb],
-                            lm);
-    }
-    best[cb] = lane_key(lm);
+    rows_epilogue<kWrite, RG>(a, p, tile_of(i) * 16 + row, kg, lb[i], b2[i], acc, lm);
   }
   DH_STAMP(p, 6);
-  publish_best<NCB>(a, p, best, sbest);
+  publish_rows<RG, true>(a, p, lm, sbest, ep);
   DH_STAMP(p, 7);
-  return true;
 }
 
-template <class W, int NCB, int KC, int NTW, class Ready>
-__device__ __forceinline__ bool logits_resident(const ChainArgs& a, int p, int t_begin, int t_end,
+template <class W, int RG, int KC, int NTW>
+__device__ __forceinline__ void logits_resident(const ChainArgs& a, int p, int t_begin, int t_end,
                                                 const frag_t<W> (&w2r)[NTW][KC], const unsigned char* w2_lds,
-                                                uint64_t* sbest, Ready ready) {
-  if (a.out_logits) return logits_resident_<W, NCB, KC, NTW, true>(a, p, t_begin, t_end, w2r, w2_lds, sbest, ready);
-  return logits_resident_<W, NCB, KC, NTW, false>(a, p, t_begin, t_end, w2r, w2_lds, sbest, ready);
+                                                uint32_t* act_s, uint64_t* sbest, uint32_t ep) {
+  if (a.out_logits)
+    logits_resident_<W, RG, KC, NTW, true>(a, p, t_begin, t_end, w2r, w2_lds, act_s, sbest, ep);
+  else
+    logits_resident_<W, RG, KC, NTW, false>(a, p, t_begin, t_end, w2r, w2_lds, act_s, sbest, ep);
 }
 
-template <class W, int NCB, int KC>
+template <class W, int RG, int KC>
 struct TileBuf {
-  frag_t<W> w[KC];    // 16 W2 rows x all of k, MFMA left operand
-  float lb[NCB][4];   // base logits of this lane's 4 rows, per column block
-  float b2[4];
+  frag_t<W> w[KC];  // 16 W2 rows x all of k, MFMA right operand
+  float lb[RG][2];  // base logits of this lane's entry for its sequences
+  float b2;
 };
 
-// `ready` is called by the whole workgroup after the first tiles are in flight
-// and before the activations are read; it returns false when the kernel must stop.
-template <class W, int NCB, int KC, bool kWrite, class Ready>
+// phase O with W2 streamed from memory: each wave walks tiles t_begin + wv,
+// + 4, ... with a ring of PF + 1 tile buffers; the first DH_O_EARLY tiles are
+// issued before the activations exist (after `ready` in the stepwise schedule)
+template <class W, int RG, int KC, bool kWrite, bool kLL, class Ready>
 __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest,
-                                              Ready ready) {
+                                              Ready ready, uint32_t ep, uint32_t* act_s) {
   constexpr int PF = DH_O_PREFETCH;
   const int lane = opaque_lane(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15, kg = lane >> 4;
-  const int B = a.B, r = a.r, V = a.V, P = a.P;
-  const bool vec4 = (V & 3) == 0;
-
-  const char* act_p = (const char*)a.act + (size_t)p * a.act_step;
-  typename act<W>::type bf[NCB][KC];
-  size_t lrow[NCB];
-  bool bok[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int b = cb * 16 + row;
-    bok[cb] = b < B;
-    lrow[cb] = ((size_t)(bok[cb] ? b : 0) * P + p) * V;
-  }
-
-  LaneMax lm[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) lm[cb] = LaneMax{0.f, -1};
-
+  const int r = a.r, V = a.V;
   const W* w2 = (const W*)a.w2;
-  auto issue = [&](int t, TileBuf<W, NCB, KC>& tb) {
+  auto issue = [&](int t, TileBuf<W, RG, KC>& tb) {
     if (t >= t_end) return;
     const W* wr = w2 + (size_t)min(t * 16 + row, V - 1) * r + kg * 8;
 #pragma unroll
     for (int c = 0; c < KC; ++c) tb.w[c] = load8_or_zero(wr + c * 32, c * 32 + kg * 8 < r);
-    const int vv = t * 16 + kg * 4;  // this lane's 4 vocabulary rows
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const float* src = a.Lb + lrow[cb] + vv;
-      if (vec4 && vv + 3 < V) {
-        const float4 q = *reinterpret_cast<const float4*>(src);
-        tb.lb[cb][0] = q.x;
-        tb.lb[cb][1] = q.y;
-        tb.lb[cb][2] = q.z;
-        tb.lb[cb][3] = q.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tb.lb[cb][i] = vv + i < V ? src[i] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tb.b2[i] = (a.b2 && vv + i < V) ? a.b2[vv + i] : 0.f;
+    load_base_rows<RG>(a, p, t * 16 + row, kg, true, tb.lb, tb.b2);
   };
-
-  // first tiles go out before the activations exist
-  TileBuf<W, NCB, KC> ring[PF + 1];
+  TileBuf<W, RG, KC> ring[PF + 1];
   int t = t_begin + wv;
 #pragma unroll
   for (int i = 0; i < DH_O_EARLY; ++i) issue(t + 4 * i, ring[i]);
-  if (!ready()) return false;
+  if constexpr (!kLL) {
+    if (!ready()) return false;
+  }
 #pragma unroll
   for (int i = DH_O_EARLY; i < PF; ++i) issue(t + 4 * i, ring[i]);
-
-  // right operands: the bottleneck activations of every sequence, all of k
+  if constexpr (kLL)
+    stage_act_ll(a, p, ep, act_s);
+  else
+    stage_act_global<W>(a, p, act_s);
+  // left operands kept in registers when they fit in 64, else read per tile from LDS
+  constexpr bool kAfRegs = RG * KC * (int)(sizeof(frag_t<W>) / 4) <= 64;
+  frag_t<W> af[kAfRegs ? RG : 1][kAfRegs ? KC : 1];
+  if constexpr (kAfRegs) {
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int b = cb * 16 + row;
+    for (int g = 0; g < RG; ++g)
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const int k = c * 32 + kg * 8;
-      const bool ok = bok[cb] && k < r;
-      if constexpr (sizeof(W) == 2) {
-        const uint16_t* hi = (const uint16_t*)act_p + (size_t)b * r + k;
-        bf[cb][c].hi = load8_or_zero(hi, ok);
-        bf[cb][c].lo = load8_or_zero(hi + (size_t)B * r, ok);
-      } else {
-        bf[cb][c] = load8_or_zero((const float*)act_p + (size_t)b * r + k, ok);
-      }
-    }
+      for (int c = 0; c < KC; ++c) af[g][c] = act_row_frag<W>(act_s, r, a.B, g, row, c * 32 + kg * 8);
   }
-
-  auto consume = [&](int t, const TileBuf<W, NCB, KC>& tb) {
-    const int vv = t * 16 + kg * 4;
-    f32x4 acc[NCB][2];  // even and odd k chunks: two independent MFMA chains
+  LaneMax lm[RG][2];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[cb][0] = acc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < RG; ++g) lm[g][0] = lm[g][1] = LaneMax{0.f, -1};
+  auto consume = [&](int t, const TileBuf<W, RG, KC>& tb) {
+    f32x4 acc[RG][2];  // even and odd k chunks: two independent MFMA chains per row group
+#pragma unroll
+    for (int g = 0; g < RG; ++g) acc[g][0] = acc[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KC; ++c)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) acc[cb][c & 1] = mma(tb.w[c], bf[cb][c], acc[cb][c & 1]);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      float base[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) base[e] = a.b2 ? tb.lb[cb][e] + tb.b2[e] : tb.lb[cb][e];
-      tile_epilogue<kWrite>(a, vv, (t + 1) * 16 <= V, base, acc[cb], bok[cb], lrow[cb], lm[cb]);
-    }
+      for (int g = 0; g < RG; ++g) {
+        if constexpr (kAfRegs)
+          acc[g][c & 1] = mma(af[g][c], tb.w[c], acc[g][c & 1]);
+        else
+          acc[g][c & 1] = mma(act_row_frag<W>(act_s, r, a.B, g, row, c * 32 + kg * 8), tb.w[c], acc[g][c & 1]);
+      }
+    rows_epilogue<kWrite, RG>(a, p, t * 16 + row, kg, tb.lb, tb.b2, acc, lm);
   };
-
   // ring of PF + 1 tile buffers; slot indices are compile-time after unrolling
   while (t < t_end) {
 #pragma unroll
@@ -845,25 +986,88 @@ __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_b
       t += 4;
     }
   }
-
-  uint64_t best[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) best[cb] = lane_key(lm[cb]);
-  publish_best<NCB>(a, p, best, sbest);
+  publish_rows<RG, kLL>(a, p, lm, sbest, ep);
   return true;
 }
 
-template <class W, int NCB, int KC, class Ready>
+template <class W, int RG, int KC, bool kLL, class Ready>
 __device__ __forceinline__ bool logits_range(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest,
-                                             Ready ready) {
-  if (a.out_logits) return logits_range_<W, NCB, KC, true>(a, p, t_begin, t_end, sbest, ready);
-  return logits_range_<W, NCB, KC, false>(a, p, t_begin, t_end, sbest, ready);
+                                             Ready ready, uint32_t ep, uint32_t* act_s) {
+  if (a.out_logits) return logits_range_<W, RG, KC, true, kLL>(a, p, t_begin, t_end, sbest, ready, ep, act_s);
+  return logits_range_<W, RG, KC, false, kLL>(a, p, t_begin, t_end, sbest, ready, ep, act_s);
+}
+
+// ---- the tokens of a step from the workgroups' argmax pairs ---------------------
+// Every workgroup publishes, per sequence, its best (value, index) as a pair
+// of hand-off words.  One workgroup per sequence reduces it over the grid and
+// publishes the result as one more pair, which the readers poll: two
+// hand-offs, but each reader polls B pairs instead of grid x B (letting every
+// reader reduce all pairs itself measured slower: the polling traffic of 256
+// readers delays everyone).  Tokens are raw argmax indices, as the packed key
+// gives them.
+__device__ __forceinline__ uint64_t pair_key(uint64_t hi, uint64_t lo) {
+  return ((uint64_t)ll_data(hi) << 32) | ll_data(lo);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = umax64(v, shfl_xor_u64(v, m));
+  return v;
+}
+
+// The last B workgroups of the grid (no bottleneck work, so they reach this
+// first) reduce one sequence each of step p and publish it.
+__device__ __forceinline__ void ll_tokens_reduce(const ChainArgs& a, int p, uint32_t ep, uint64_t* sred) {
+  const int B = a.B, b = (int)gridDim.x - 1 - (int)blockIdx.x;
+  if (b < 0 || b >= B) return;
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const uint32_t tag = ll_tag(ep, p);
+  const uint64_t* part = a.ll_part + (size_t)p * kMaxChainGrid * B * 2;
+  uint64_t key = 0;
+  ll_wait(a.status, [&] {
+    bool good = true;
+    key = 0;
+    for (int w = tid; w < (int)gridDim.x; w += blockDim.x) {
+      const uint64_t hi = ld_agent64(part + ((size_t)w * B + b) * 2), lo = ld_agent64(part + ((size_t)w * B + b) * 2 + 1);
+      good = good && ll_ok(hi, tag) && ll_ok(lo, tag);
+      key = umax64(key, pair_key(hi, lo));
+    }
+    return good;
+  });
+  key = wave_max_u64(key);
+  if ((tid & 63) == 0) sred[wv] = key;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t m = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = umax64(m, sred[w]);
+    ll_put(a.ll_tok + ((size_t)p * B + b) * 2, (uint32_t)(m >> 32), tag);
+    ll_put(a.ll_tok + ((size_t)p * B + b) * 2 + 1, (uint32_t)m, tag);
+  }
+  __syncthreads();
+}
+
+// tok[b] (LDS) = the token drafted at step p for every sequence b
+__device__ __forceinline__ void ll_tokens_read(const ChainArgs& a, int p, uint32_t ep, int32_t* tok) {
+  const int B = a.B, lane = threadIdx.x & 63;
+  const uint32_t tag = ll_tag(ep, p);
+  if (threadIdx.x < 64) {  // B <= kMaxChainGroup <= 64
+    uint64_t m = 0;
+    ll_wait(a.status, [&] {
+      if (lane >= B) return true;
+      const uint64_t hi = ld_agent64(a.ll_tok + ((size_t)p * B + lane) * 2);
+      const uint64_t lo = ld_agent64(a.ll_tok + ((size_t)p * B + lane) * 2 + 1);
+      m = pair_key(hi, lo);
+      return ll_ok(hi, tag) && ll_ok(lo, tag);
+    });
+    if (lane < B) tok[lane] = amax_index(m);
+  }
+  __syncthreads();
 }
 
 // ---- kernels ------------------------------------------------------------------------
+constexpr uint64_t kLLMarker = 0x6c6c2d646f6d696eull;
 // Before the steps: the H half of the bottleneck for every position,
 // zh[b][p][k] = sum_i H[b][p][i] W1[k][i] (one 16x16 tile per workgroup, k
-// split over the waves), and the zeroed keys, counters and initial state.
+// split over the waves), and the zeroed keys and initial state.
 template <class W>
 __global__ __launch_bounds__(256) void chain_prologue(ChainArgs a, const void* H, int reset_status) {
   __shared__ __attribute__((aligned(16))) float red[4 * 64 * 4];
@@ -872,22 +1076,31 @@ __global__ __launch_bounds__(256) void chain_prologue(ChainArgs a, const void* H
                  red);
   const int nblk = gridDim.x * gridDim.y, blk = blockIdx.y * gridDim.x + blockIdx.x;
   const int tid = blk * blockDim.x + threadIdx.x, stride = nblk * blockDim.x;
+  if (blk == 0) {
+    // first launch on this workspace: clear the hand-off words once, so that
+    // no leftover bits can carry a current tag; afterwards the launch counter
+    // alone keeps earlier launches' words from passing
+    __shared__ int fresh;
+    if (threadIdx.x == 0) fresh = *a.marker != kLLMarker;
+    __syncthreads();
+    if (fresh) {
+      uint4* w = reinterpret_cast<uint4*>(a.ll_h);
+      for (size_t i = threadIdx.x; i < a.ll_words / 2; i += blockDim.x) w[i] = make_uint4(0, 0, 0, 0);
+      if (threadIdx.x == 0) {
+        *a.epoch = 0;
+        *a.marker = kLLMarker;
+      }
+    }
+  }
   for (int i = tid; i < a.P * a.B; i += stride) a.keys[i] = 0;
   for (int i = tid; i < a.B * a.Hs; i += stride) a.h[i] = 0.f;  // state slot 0
-  for (int i = tid; i < 4 * kSubCounters * kCounterStride; i += stride) a.counters[i] = 0;
   if (tid == 0) {
+    *a.epoch += 1;  // tags of this launch's hand-off words
     int32_t s = reset_status ? 0 : *a.status;
     for (int b = 0; b < a.B; ++b)
       if ((a.t0[b] < 0 || a.t0[b] >= a.V) && s == 0) s = 1;
     *a.status = s;
   }
-}
-
-// drafted tokens of step p from the packed argmax keys
-__device__ __forceinline__ void write_tokens(const ChainArgs& a, int p) {
-  for (int b = threadIdx.x; b < a.B; b += blockDim.x)
-    a.out_tokens[(size_t)b * a.P + p] =
-        amax_index(__hip_atomic_load(&a.keys[(size_t)p * a.B + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 __global__ void chain_finalize(ChainArgs a) {
@@ -915,12 +1128,13 @@ __global__ __launch_bounds__(256) void chain_bottleneck_k(ChainArgs a, int p) {
     bottleneck_item<W, NCB, false>(a, p, it, red, nullptr, bottleneck_pre<NCB>(a, p, it));
 }
 
-template <class W, int NCB, int KC>
+template <class W, int RG, int KC>
 __global__ __launch_bounds__(256) void chain_logits_k(ChainArgs a, int p) {
-  __shared__ uint64_t sbest[4 * NCB * 16];
+  __shared__ uint64_t sbest[4 * kMaxChainGroup];
+  __shared__ __attribute__((aligned(16))) uint32_t act_s[kMaxChainGroup * 256];  // r <= 256
   const int T = (a.V + 15) / 16, G = gridDim.x, w = blockIdx.x;
-  logits_range<W, NCB, KC>(a, p, (int)((int64_t)T * w / G), (int)((int64_t)T * (w + 1) / G), sbest,
-                           [] { return true; });
+  logits_range<W, RG, KC, false>(a, p, (int)((int64_t)T * w / G), (int)((int64_t)T * (w + 1) / G), sbest,
+                                 [] { return true; }, 0u, act_s);
 }
 
 // All P steps in one cooperative launch; every workgroup owns one GRU work
@@ -929,19 +1143,20 @@ __global__ __launch_bounds__(256) void chain_logits_k(ChainArgs a, int p) {
 // W1 in LDS.  NTW > 0 (W2 resident on chip): the GRU weights come from
 // memory, W_ih fetched ahead of the token; kLds 2 puts the W1 slice in LDS;
 // the LDS tier of W2 follows it.
-template <class W, int NCB, int KC, int kLds, int NTW>
+template <class W, int RG, int KC, int kLds, int NTW>
 __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
+  constexpr int NCB = RG <= 2 ? 1 : 2;  // 16-sequence column blocks of phases G and W
   constexpr bool kGruLds = kLds >= 1 && NTW == 0;
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
   __shared__ __attribute__((aligned(16))) float red[4 * NCB * 64 * 4];
-  __shared__ uint64_t sbest[4 * NCB * 16];
-  W* gl = reinterpret_cast<W*>(dyn_lds);
+  __shared__ uint64_t sbest[4 * kMaxChainGroup];
+  // dynamic LDS: [staged activations][GRU slice (streamed W2)][W1 slice][LDS
+  // tier of W2 (resident W2)]
+  uint32_t* act_s = reinterpret_cast<uint32_t*>(dyn_lds);
+  W* gl = reinterpret_cast<W*>(dyn_lds + act_stage_bytes(a.B, a.r));
   W* wl = gl + (kGruLds ? gru_slice_elems(a.d, a.Hs) : 0);
   const int G = gridDim.x, wg = blockIdx.x;
   const int nG = a.Hs / 4, nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
-  uint32_t* cG = a.counters + 0 * kSubCounters * kCounterStride;
-  uint32_t* cW = a.counters + 1 * kSubCounters * kCounterStride;
-  uint32_t* cO = a.counters + 2 * kSubCounters * kCounterStride;
   int t_begin, t_end;
   o_tile_range(wg, G, nW, T, t_begin, t_end);
   frag_t<W> w2r[NTW > 0 ? NTW : 1][KC];
@@ -956,51 +1171,74 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
   f32x4 acc_h[NCB];  // hidden half of this workgroup's next GRU step
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc_h[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __shared__ int32_t tok_s[kMaxChainGroup];
+  __shared__ uint64_t sred_t[4 * kMaxChainGroup];
+  const uint32_t ep = *a.epoch;  // advanced by the prologue launch
+  float h_own = 0.f;             // this lane's own unit of the GRU state, h(0) = 0
   for (int p = 0; p < a.P; ++p) {
+    // G: the previous token of every sequence, then one GRU step for this workgroup's units
+    if (p > 0) ll_tokens_reduce(a, p - 1, ep, sred_t);
+    BottleneckPre pre{};  // bottleneck terms known before the state: fetched during the GRU step
     if (wg < nG) {
+      const int32_t* tk = nullptr;  // step 0 reads the first tokens
       if constexpr (NTW > 0) {
+        // the token first: loads issued before its poll would delay it (wait
+        // counts retire in order); W_ih then comes from L2 while the
+        // embedding row comes from HBM
+        if (p > 0) {
+          ll_tokens_read(a, p - 1, ep, tok_s);
+          tk = tok_s;
+        }
+        if (wg < nW) pre = bottleneck_pre<NCB>(a, p, wg);
         frag_t<W> xw[kXPre];
         gru_x_prefetch<W>(a, wg, xw);
-        if (p > 0 && !wg_wait_geq(cO, (uint32_t)(p * G), a.status)) return;
         DH_STAMP(p, 0);
-        if (wg == 0 && p > 0) write_tokens(a, p - 1);
-        gru_finish_pre<W, NCB>(a, p, wg, red, xw, acc_h);
+        if (wg == 0 && p > 0)
+          for (int b = threadIdx.x; b < a.B; b += blockDim.x) a.out_tokens[(size_t)b * a.P + p - 1] = tok_s[b];
+        gru_finish_pre<W, NCB>(a, p, wg, red, xw, acc_h, tk, h_own, ep);
       } else {
-        if (p > 0 && !wg_wait_geq(cO, (uint32_t)(p * G), a.status)) return;
+        if (p > 0) {
+          ll_tokens_read(a, p - 1, ep, tok_s);
+          tk = tok_s;
+        }
+        if (wg < nW) pre = bottleneck_pre<NCB>(a, p, wg);
         DH_STAMP(p, 0);
-        if (wg == 0 && p > 0) write_tokens(a, p - 1);
-        gru_finish<W, NCB, kGruLds>(a, p, wg, red, gl, acc_h);
+        if (wg == 0 && p > 0)
+          for (int b = threadIdx.x; b < a.B; b += blockDim.x) a.out_tokens[(size_t)b * a.P + p - 1] = tok_s[b];
+        gru_finish<W, NCB, kGruLds, true>(a, p, wg, red, gl, acc_h, tk, &h_own, ep);
       }
     }
-    wg_arrive(cG);
     DH_STAMP(p, 1);
+    // W: the bottleneck of this step from h(p+1)
     if (wg < nW) {
-      const BottleneckPre pre = bottleneck_pre<NCB>(a, p, wg);
-      if (!wg_wait_geq(cG, (uint32_t)((p + 1) * G), a.status)) return;
+      if (wg >= nG) pre = bottleneck_pre<NCB>(a, p, wg);
       DH_STAMP(p, 2);
-      bottleneck_item<W, NCB, (kLds >= 2)>(a, p, wg, red, wl, pre);
+      bottleneck_item<W, NCB, (kLds >= 2), true>(a, p, wg, red, wl, pre, ep);
     }
-    wg_arrive(cW);
     DH_STAMP(p, 3);
-    if (wg < nG && p + 1 < a.P) {  // W_hh h(p+1) while the bottleneck runs
-      if (!wg_wait_geq(cG, (uint32_t)((p + 1) * G), a.status)) return;
-      gru_hidden_part<W, NCB, kGruLds>(a, p + 1, wg, gl, acc_h);
-    }
-    auto ready = [&] {
-      const bool ok = wg_wait_geq(cW, (uint32_t)((p + 1) * G), a.status);
-      DH_STAMP(p, 4);
-      return ok;
-    };
-    bool go;
+    // W_hh h(p+1) for the next step: in the wait for the bottleneck, or, in
+    // the bottleneck workgroups, after phase O
+    const bool hidden = wg < nG && p + 1 < a.P;
+#ifndef DH_HIDDEN_LATE
+    if (hidden && wg >= nW) gru_hidden_part<W, NCB, kGruLds, true>(a, p + 1, wg, gl, acc_h, ep);
+#endif
+    // O: this workgroup's vocabulary tiles, then its argmax pairs
     if constexpr (NTW > 0)
-      go = logits_resident<W, NCB, KC, NTW>(a, p, t_begin, t_end, w2r, w2l, sbest, ready);
+      logits_resident<W, RG, KC, NTW>(a, p, t_begin, t_end, w2r, w2l, act_s, sbest, ep);
     else
-      go = logits_range<W, NCB, KC>(a, p, t_begin, t_end, sbest, ready);
-    if (!go) return;
-    wg_arrive(cO);
+      logits_range<W, RG, KC, true>(a, p, t_begin, t_end, sbest, [] { return true; }, ep, act_s);
     DH_STAMP(p, 5);
+#ifndef DH_HIDDEN_LATE
+    if (hidden && wg < nW) gru_hidden_part<W, NCB, kGruLds, true>(a, p + 1, wg, gl, acc_h, ep);
+#else
+    if (hidden) gru_hidden_part<W, NCB, kGruLds, true>(a, p + 1, wg, gl, acc_h, ep);
+#endif
   }
-  if (wg == 0 && wg_wait_geq(cO, (uint32_t)(a.P * G), a.status)) write_tokens(a, a.P - 1);
+  ll_tokens_reduce(a, a.P - 1, ep, sred_t);
+  if (wg == 0) {
+    ll_tokens_read(a, a.P - 1, ep, tok_s);
+    for (int b = threadIdx.x; b < a.B; b += blockDim.x) a.out_tokens[(size_t)b * a.P + a.P - 1] = tok_s[b];
+  }
 }
 
 // ---- host side ------------------------------------------------------------------------
@@ -1012,8 +1250,6 @@ ChainLayout chain_layout(int d, int Hs, int r, int P, int group) {
   size_t off = 0;
   L.status = off;
   off += 256;
-  L.counters = off;
-  off += (size_t)4 * kSubCounters * kCounterStride * 4;
   L.keys = off;
   off += align256((size_t)P * group * 8);
   L.zh = off;
@@ -1029,6 +1265,14 @@ ChainLayout chain_layout(int d, int Hs, int r, int P, int group) {
   L.act_step = (int)align256((size_t)group * r * 4);
   L.act = off;
   off += (size_t)P * L.act_step;
+  L.ll_h = off;
+  off += (size_t)(P + 1) * group * Hs * 8;
+  L.ll_act = off;
+  off += align256((size_t)P * group * r * 8);
+  L.ll_part = off;
+  off += (size_t)P * kMaxChainGrid * group * 16;
+  L.ll_tok = off;
+  off += align256((size_t)P * group * 16);
   L.trace = off;
 #ifdef DH_TRACE_PHASES
   off += (size_t)P * 1024 * kTraceSlots * 8;
@@ -1042,14 +1286,15 @@ ChainLayout chain_layout(int d, int Hs, int r, int P, int group) {
 // its register and LDS slots hold.
 static size_t resident_lds(int G, const ChainArgs& a, int ntw, int kc, size_t w1_bytes) {
   const int nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
-  size_t need = w1_bytes;
+  const size_t act = act_stage_bytes(a.B, a.r);
+  size_t need = act + w1_bytes;
   for (int w = 0; w < G; ++w) {
     int b, e;
     o_tile_range(w, G, nW, T, b, e);
     const int n_lds = e - b - 4 * ntw;
     if (n_lds > kLdsTiles) return 0;
     if (n_lds > 0) {
-      const size_t at = (w < nW ? w1_bytes : 0) + (size_t)n_lds * w2_lds_tile_bytes(kc);
+      const size_t at = act + (w < nW ? w1_bytes : 0) + (size_t)n_lds * w2_lds_tile_bytes(kc);
       need = at > need ? at : need;
     }
   }
@@ -1063,10 +1308,10 @@ struct CoopGrid {
   int blocks = 0;
 };
 
-template <class W, int NCB, int KC, int kLds, int NTW>
+template <class W, int RG, int KC, int kLds, int NTW>
 static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStream_t s) {
   static thread_local CoopGrid cache;
-  const void* fn = (const void*)chain_persistent<W, NCB, KC, kLds, NTW>;
+  const void* fn = (const void*)chain_persistent<W, RG, KC, kLds, NTW>;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -1088,6 +1333,7 @@ static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStr
     cache.blocks = NTW > 0 ? cus : cus * (per_cu > 2 ? 2 : per_cu);
   }
   if (cache.blocks < a.Hs / 4) return hipErrorInvalidConfiguration;  // one GRU item per workgroup
+  if (cache.blocks > kMaxChainGrid || cache.blocks < a.B) return hipErrorInvalidConfiguration;  // hand-off slots
   ChainArgs arg = a;
   void* params[] = {&arg};
   return hipLaunchCooperativeKernel(fn, dim3(cache.blocks), dim3(256), params, (unsigned)lds_bytes, s);
@@ -1095,8 +1341,9 @@ static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStr
 
 constexpr size_t kLdsBudget = 144 * 1024;  // dynamic LDS the persistent kernel may use (160 KB per CU)
 
-template <class W, int NCB, int KC>
+template <class W, int RG, int KC>
 static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& persistent) {
+  constexpr int NCB = RG <= 2 ? 1 : 2;
   const int cus = device_cus();
   // the persistent schedule needs one GRU work item per workgroup
   persistent = mode != 1 && cus > 0 && a.Hs / 4 <= cus;
@@ -1109,31 +1356,32 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
       constexpr int NTW = resident_tiles<KC>();
       if (mode == 0) {
         const size_t l2 = resident_lds(cus, a, NTW, KC, w);
-        if (l2 > 0 && l2 <= kLdsBudget) return launch_persistent<W, NCB, KC, 2, NTW>(a, l2, s);
+        if (l2 > 0 && l2 <= kLdsBudget) return launch_persistent<W, RG, KC, 2, NTW>(a, l2, s);
       }
     }
-    if (g + w <= kLdsBudget) return launch_persistent<W, NCB, KC, 2, 0>(a, g + w, s);
-    if (g <= kLdsBudget) return launch_persistent<W, NCB, KC, 1, 0>(a, g, s);
-    return launch_persistent<W, NCB, KC, 0, 0>(a, 0, s);
+    const size_t act = act_stage_bytes(a.B, a.r);
+    if (act + g + w <= kLdsBudget) return launch_persistent<W, RG, KC, 2, 0>(a, act + g + w, s);
+    if (act + g <= kLdsBudget) return launch_persistent<W, RG, KC, 1, 0>(a, act + g, s);
+    return launch_persistent<W, RG, KC, 0, 0>(a, act, s);
   }
   const int nG = a.Hs / 4, nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
   const int nO = T < cus ? T : (cus > 0 ? cus : 256);
   for (int p = 0; p < a.P; ++p) {
     hipLaunchKernelGGL((chain_gru_k<W, NCB>), dim3(nG), dim3(256), 0, s, a, p);
     hipLaunchKernelGGL((chain_bottleneck_k<W, NCB>), dim3(nW), dim3(256), 0, s, a, p);
-    hipLaunchKernelGGL((chain_logits_k<W, NCB, KC>), dim3(nO), dim3(256), 0, s, a, p);
+    hipLaunchKernelGGL((chain_logits_k<W, RG, KC>), dim3(nO), dim3(256), 0, s, a, p);
   }
   return hipGetLastError();
 }
 
 // k chunks of 32 in the bottleneck, rounded up to 1, 2, 4 or 8 (zero padded)
-template <class W, int NCB>
+template <class W, int RG>
 static hipError_t run_chain_kc(const ChainArgs& a, int mode, hipStream_t s, bool& persistent) {
   const int kc = (a.r + 31) / 32;
-  if (kc <= 1) return run_chain<W, NCB, 1>(a, mode, s, persistent);
-  if (kc <= 2) return run_chain<W, NCB, 2>(a, mode, s, persistent);
-  if (kc <= 4) return run_chain<W, NCB, 4>(a, mode, s, persistent);
-  if (kc <= 8) return run_chain<W, NCB, 8>(a, mode, s, persistent);
+  if (kc <= 1) return run_chain<W, RG, 1>(a, mode, s, persistent);
+  if (kc <= 2) return run_chain<W, RG, 2>(a, mode, s, persistent);
+  if (kc <= 4) return run_chain<W, RG, 4>(a, mode, s, persistent);
+  if (kc <= 8) return run_chain<W, RG, 8>(a, mode, s, persistent);
   return hipErrorInvalidValue;
 }
 
@@ -1147,16 +1395,19 @@ hipError_t launch_chain(int dtype, const ChainArgs& a, const void* H, int mode, 
     hipLaunchKernelGGL(chain_prologue<float>, pro, dim3(256), 0, s, a, H, reset_status ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const bool two = a.B > 16;
+  // row groups of 8 sequences in phase O
+  const int rg = a.B <= 8 ? 1 : (a.B <= 16 ? 2 : 4);
   bool persistent = false;
   if (ev_start && ev_stop) {
     e = hipEventRecord(ev_start, s);
     if (e != hipSuccess) return e;
   }
   if (dtype == kBF16)
-    e = two ? run_chain_kc<uint16_t, 2>(a, mode, s, persistent) : run_chain_kc<uint16_t, 1>(a, mode, s, persistent);
+    e = rg == 1 ? run_chain_kc<uint16_t, 1>(a, mode, s, persistent)
+                : (rg == 2 ? run_chain_kc<uint16_t, 2>(a, mode, s, persistent) : run_chain_kc<uint16_t, 4>(a, mode, s, persistent));
   else
-    e = two ? run_chain_kc<float, 2>(a, mode, s, persistent) : run_chain_kc<float, 1>(a, mode, s, persistent);
+    e = rg == 1 ? run_chain_kc<float, 1>(a, mode, s, persistent)
+                : (rg == 2 ? run_chain_kc<float, 2>(a, mode, s, persistent) : run_chain_kc<float, 4>(a, mode, s, persistent));
   if (e != hipSuccess) return e;
   if (ev_start && ev_stop) {
     e = hipEventRecord(ev_stop, s);

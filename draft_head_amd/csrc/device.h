@@ -216,63 +216,53 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 // ---- bounded waits between workgroups of one persistent launch ------------------
-// Every wait ends: on success, on an error already flagged by another
-// workgroup, or after kWaitTicks of the 100 MHz constant clock (then the
-// status word is set to 2 and the caller leaves the kernel).
+// Every wait ends: on success, on a timeout already flagged by another wave,
+// or after kWaitTicks of the 100 MHz constant clock (then it sets the status
+// word to 2 itself).
 constexpr uint64_t kWaitTicks = 200000000ull;  // 2 s
 constexpr int kStatusTimeout = 2;
 
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+// ---- tagged hand-off words ---------------------------------------------------------
+// A value handed from one workgroup to others inside a persistent launch
+// travels as one 64-bit word, 32 data bits under a 32-bit tag that names the
+// launch and the step, written with a single agent-coherent 8-byte store
+// (single-copy atomic) and read with agent-coherent loads.  Readers poll the
+// words themselves until every tag is current: the data arrive with the
+// signal, and a writer never waits for its stores to land.
+__device__ __forceinline__ uint64_t ld_agent64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void ll_put(uint64_t* w, uint32_t data, uint32_t tag) {
+  __hip_atomic_store(w, ((uint64_t)tag << 32) | data, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool ll_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+__device__ __forceinline__ uint32_t ll_data(uint64_t w) { return (uint32_t)w; }
 
-// Arrival counters are split into kSubCounters lines (workgroup w counts into
-// line w % kSubCounters) so that hundreds of workgroups finishing together do
-// not serialize on one atomic; a waiter sums the lines.
-constexpr int kSubCounters = 8;
-constexpr int kCounterStride = 64;  // uint32 per line: 256 bytes
-
-// whole workgroup calls; returns false when the kernel must stop.
-// Data handed between workgroups is written with agent-coherent stores (see
-// store_agent) into buffers that no workgroup reads before they are
-// written within the launch, so a reader can hold no stale copy and no
-// cache writeback or invalidate is needed around the counters.
-__device__ __forceinline__ bool wg_wait_geq(const uint32_t* counter, uint32_t target, int32_t* status) {
-  __shared__ int ok_flag;
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    const uint64_t t0 = wall_clock64();
-    while (true) {
-      uint32_t sum = 0;
-#pragma unroll
-      for (int i = 0; i < kSubCounters; ++i) sum += ld_agent(counter + i * kCounterStride);
-      if (sum >= target) break;
-      if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kStatusTimeout) {
-        ok = 0;
-        break;
-      }
+// Repeat `attempt` (it issues the loads and tells, per lane, whether every
+// word it read carries the expected tag) until it succeeds in every lane of
+// the wave.  Gives up when another wave has flagged a timeout or after
+// kWaitTicks (then flags one itself) and returns false; the caller carries on
+// with what it read, so every wave still reaches the end of the kernel.
+// kSleep: s_sleep units (64 clocks each) between attempts; waits off the
+// critical path use longer ones so they add less polling traffic.
+template <int kSleep = 1, class F>
+__device__ __forceinline__ bool ll_wait(int32_t* status, F&& attempt) {
+  uint64_t t0 = 0;
+  for (int tries = 0;; ++tries) {  // one call site, so `attempt` is inlined
+    if (__all(attempt())) return true;
+    if (tries == 0) {
+      t0 = wall_clock64();
+    } else {
+      if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kStatusTimeout) return false;
       if (wall_clock64() - t0 > kWaitTicks) {
         __hip_atomic_store(status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
+        return false;
       }
     }
-    ok_flag = ok;
+    __builtin_amdgcn_s_sleep(kSleep);
   }
-  __syncthreads();
-  return ok_flag != 0;
 }
 
-// whole workgroup calls after its last hand-off store of a phase: every wave
-// waits for its own stores to complete before the barrier, then one thread
-// counts the workgroup in
-__device__ __forceinline__ void wg_arrive(uint32_t* counter) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(counter + (blockIdx.x % kSubCounters) * kCounterStride, 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // stores that are visible device-wide once complete (they bypass the
 // per-XCD L2 write-back)

@@ -10,6 +10,7 @@ namespace dh {
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kMaxChainGroup = 32;  // sequences per chain launch (two 16-column MFMA blocks)
+constexpr int kMaxChainGrid = 1024; // workgroups of a persistent chain launch at most
 
 // compute units of the current device (0 if the query fails)
 inline int device_cus() {
@@ -47,17 +48,24 @@ struct ChainArgs {
   void* act;               // [P][act_step bytes] bottleneck activations of each step:
                            //   bf16 hi [B][r] then lo [B][r], or fp32 [B][r]
   uint64_t* keys;          // [P][B] packed argmax keys
-  uint32_t* counters;      // [4][sub-counters][line] phase arrival counters
   int32_t* status;         // device status word
   int h_step;              // floats between consecutive state slots (256-byte multiple)
   int hb_step;             // bf16 elements between consecutive split-state slots (256-byte multiple)
   int act_step;            // bytes between consecutive activation slots (256-byte multiple)
   uint64_t* trace;         // phase timestamps [P][grid][slots] when built with DH_TRACE_PHASES, else null
+  // tagged hand-off words of the persistent schedule
+  uint64_t* ll_h;          // [P+1][B][Hs] state after each step (bf16: hi pairs, then lo pairs; fp32: one per word)
+  uint64_t* ll_act;        // [P][B][r] bottleneck activations, same packing
+  uint64_t* ll_part;       // [P][kMaxChainGrid][B][2] each workgroup's argmax (value, index) per sequence
+  uint64_t* ll_tok;        // [P][B][2] per-sequence argmax when reduced in two levels
+  uint32_t* epoch;         // launch counter, advanced by the prologue
+  uint64_t* marker;        // kLLMarker once the hand-off words have been cleared
+  size_t ll_words;         // hand-off words from ll_h on (all four regions)
 };
 
 // workspace carving for a chain launch of up to `group` sequences
 struct ChainLayout {
-  size_t status, counters, keys, zh, h, hb, act, trace, total;
+  size_t status, keys, zh, h, hb, act, ll_h, ll_act, ll_part, ll_tok, trace, total;
   int h_step, hb_step, act_step;
 };
 ChainLayout chain_layout(int d, int Hs, int r, int P, int group);

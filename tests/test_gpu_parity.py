@@ -183,9 +183,10 @@ def test_chain_deterministic_and_prefix_stable():
     assert np.array_equal(t8, t1[:, :8]) and np.array_equal(L8, L1[:, :8])
 
 
-# B <= 16 with bf16 weights keeps W2 on chip in mode 0; every mode splits k
-# over the waves in the same order, so all three agree to the bit
-@pytest.mark.parametrize("B,r", [(20, 32), (9, 32), (16, 256), (1, 256)])
+# B <= 16 with bf16 weights keeps W2 on chip in mode 0; phase O takes 8
+# sequences per MFMA row group (B 1, 8 | 9, 16 | 17 .. 32: 1, 2, 4 groups);
+# every mode sums in the same order, so all three agree to the bit
+@pytest.mark.parametrize("B,r", [(20, 32), (9, 32), (16, 256), (1, 256), (8, 256), (32, 64)])
 def test_chain_modes_agree_bitwise(B, r):
     cfg = small_config(d=96, V=1501, Hs=48, r=r, P=12, B=B, dtype="bf16", biases=True)
     say(f"case chain modes agree B={B} r={r}")
