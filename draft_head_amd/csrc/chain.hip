@@ -182,6 +182,60 @@ __device__ __forceinline__ bool ll_frag(const uint64_t* slot, int n, int b, int 
   return good;
 }
 
+// The same right operand from hand-off words already staged in LDS as their
+// data (dst[b * n + q] = word q of row b).
+template <class W>
+__device__ __forceinline__ typename act<W>::type staged_frag(const uint32_t* st, int n, int b, int k, bool ok) {
+  if (!ok) return act<W>::zero();
+  const uint32_t* row = st + (size_t)b * n;
+  if constexpr (sizeof(W) == 2) {
+    bf16pair f;
+    f.hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + k / 2));
+    f.lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + n / 2 + k / 2));
+    return f;
+  } else {
+    f32x8 f;
+    f.lo = *reinterpret_cast<const float4*>(row + k);
+    f.hi = *reinterpret_cast<const float4*>(row + k + 4);
+    return f;
+  }
+}
+
+__host__ __device__ inline bool stage_state(int B, int Hs) { return B * Hs <= 8 * 256; }
+
+// n hand-off words of `slot` carrying `tag`, polled by the whole workgroup (a
+// few words per thread per round) and staged in LDS as their data.
+constexpr int kStageWordsPerThread = 8;
+struct IdentityIndex {
+  __device__ int operator()(int q) const { return q; }
+};
+template <class Index = IdentityIndex>
+__device__ __forceinline__ void stage_words_ll(int32_t* status, const uint64_t* slot, int n, uint32_t tag,
+                                               uint32_t* dst, Index index = Index()) {
+  for (int base = 0; base < n; base += kStageWordsPerThread * (int)blockDim.x) {
+    uint32_t v[kStageWordsPerThread];
+    ll_wait(status, [&] {
+      bool good = true;
+#pragma unroll
+      for (int i = 0; i < kStageWordsPerThread; ++i) {
+        const int q = base + threadIdx.x + i * (int)blockDim.x;
+        if (q < n) {
+          const uint64_t w = ld_agent64(slot + q);
+          good = good && ll_ok(w, tag);
+          v[i] = ll_data(w);
+        }
+      }
+      return good;
+    });
+#pragma unroll
+    for (int i = 0; i < kStageWordsPerThread; ++i) {
+      const int q = base + threadIdx.x + i * (int)blockDim.x;
+      if (q < n) dst[index(q)] = v[i];
+    }
+  }
+  __syncthreads();
+}
+
 // four consecutive values v of row b, elements k..k+3 (k a multiple of 4),
 // into a hand-off slot with n elements per row, as ll_frag reads them
 template <class W>
@@ -392,7 +446,7 @@ __device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, f
 // so they are fetched while the workgroup still waits for it; each workgroup
 // reads the same rows every step, so they stay in its XCD's L2.
 constexpr int kXPre = 12;  // chunks per wave fetched ahead (the register budget allows no more)
-constexpr int kXTail = 8;  // chunks per batch after them
+constexpr int kXTail = 20;  // chunks per batch after them (d <= 5120 in one more round)
 template <class W>
 __device__ __forceinline__ void gru_x_prefetch(const ChainArgs& a, int item, frag_t<W> (&xw)[kXPre]) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, kg = lane >> 4;
@@ -498,10 +552,12 @@ __device__ __forceinline__ BottleneckPre bottleneck_pre(const ChainArgs& a, int 
   return q;
 }
 
-// kLL: state in and activations out as hand-off words of the persistent launch `ep`
+// kLL: state in and activations out as hand-off words of the persistent launch
+// `ep`; with h_s (LDS, B * Hs words) the whole workgroup polls the state
+// words once and the waves read their fragments from there.
 template <class W, int NCB, bool kLdsW, bool kLL = false>
 __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int item, float* red, const W* w1_lds,
-                                const BottleneckPre& pre_terms, uint32_t ep = 0) {
+                                const BottleneckPre& pre_terms, uint32_t ep = 0, uint32_t* h_s = nullptr) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int Hs = a.Hs, B = a.B, r = a.r;
@@ -524,6 +580,7 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int U = NCB == 1 ? 8 : 4;
   const int nch = (Hs + 31) / 32;
+  if (kLL && h_s) stage_words_ll(a.status, a.ll_h + (size_t)(p + 1) * B * Hs, B * Hs, ll_tag(ep, p), h_s);
   for (int c0 = wv; c0 < nch; c0 += 4 * U) {  // this wave's chunks wv, wv + 4, ... in order
     frag_t<W> A[U];
     typename act<W>::type S[U][NCB];
@@ -532,12 +589,15 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
       const int c = c0 + 4 * q, k = c * 32;
       const bool kok = c < nch && k + kg * 8 < Hs;
       A[q] = load8_or_zero(rw + k, kok);
-      if constexpr (!kLL) {
+      if (kLL && h_s) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) S[q][cb] = staged_frag<W>(h_s, Hs, bb[cb], k + kg * 8, kok && bok[cb]);
+      } else if constexpr (!kLL) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) S[q][cb] = state_frag<W>(a, p + 1, bb[cb], k + kg * 8, kok && bok[cb]);
       }
     }
-    if constexpr (kLL) {
+    if (kLL && !h_s) {
       const uint64_t* slot = a.ll_h + (size_t)(p + 1) * B * Hs;
       ll_wait(a.status, [&] {
         bool good = true;
@@ -662,8 +722,14 @@ __host__ __device__ inline size_t w2_lds_tile_bytes(int KC) { return (size_t)KC 
 // Loads from clamped, in-bounds addresses (no select).  Rows past V are never
 // stored; k positions past r meet zero activations, so the finite weights
 // read there add exactly zero.
-// LDS for the staged activations of a resident-W2 launch (256-byte multiple)
-__host__ __device__ inline size_t act_stage_bytes(int B, int r) { return ((size_t)B * r * 4 + 255) & ~size_t(255); }
+// Staged activations in LDS: sequence b's words at b*(r+8) + q, and with bf16
+// weights the lo half (words q >= r/2) shifted by 4 more words, so that the
+// 16 (sequence, half) rows one fragment read touches fall in distinct banks.
+__host__ __device__ inline size_t act_stage_bytes(int B, int r) { return ((size_t)B * (r + 8) * 4 + 255) & ~size_t(255); }
+template <class W>
+__device__ __forceinline__ int act_stage_index(int q, int b, int r) {
+  return b * (r + 8) + ((sizeof(W) == 2 && q >= r / 2) ? q + 4 : q);
+}
 
 // (t may be -1 for a workgroup that owns no tile; such rows are never used)
 template <class W>
@@ -721,9 +787,9 @@ template <class W>
 __device__ __forceinline__ frag_t<W> act_row_frag(const uint32_t* act_s, int r, int B, int g, int row, int k) {
   const int b = g * kSeqPerRowGroup + (row >> 1), part = row & 1;
   if (b >= B || k >= r) return zero8<W>();
-  const uint32_t* src = act_s + (size_t)b * r;
+  const uint32_t* src = act_s + (size_t)b * (r + 8);
   if constexpr (sizeof(W) == 2) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + (part ? r / 2 : 0) + k / 2));
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + (part ? r / 2 + 4 : 0) + k / 2));
   } else {
     if (part) return zero8<float>();
     f32x8 f;
@@ -804,36 +870,12 @@ __device__ __forceinline__ void publish_rows(const ChainArgs& a, int p, LaneMax 
   __syncthreads();
 }
 
-// The bottleneck activations of step p, polled by the whole workgroup (a few
-// words per thread) and staged in LDS as the words' data: act_s[b * r + q]
-// holds word q of sequence b (bf16: hi pairs, then lo pairs; fp32: values).
-constexpr int kActWordsPerThread = 8;  // per poll round; B <= 8 at r = 256 takes one round
+// The bottleneck activations of step p, staged in LDS (act_stage_index).
+template <class W>
 __device__ __forceinline__ void stage_act_ll(const ChainArgs& a, int p, uint32_t ep, uint32_t* act_s) {
-  const int n = a.B * a.r;
-  const uint64_t* slot = a.ll_act + (size_t)p * n;
-  const uint32_t tag = ll_tag(ep, p);
-  for (int base = 0; base < n; base += kActWordsPerThread * (int)blockDim.x) {
-    uint32_t v[kActWordsPerThread];
-    ll_wait(a.status, [&] {
-      bool good = true;
-#pragma unroll
-      for (int i = 0; i < kActWordsPerThread; ++i) {
-        const int q = base + threadIdx.x + i * (int)blockDim.x;
-        if (q < n) {
-          const uint64_t w = ld_agent64(slot + q);
-          good = good && ll_ok(w, tag);
-          v[i] = ll_data(w);
-        }
-      }
-      return good;
-    });
-#pragma unroll
-    for (int i = 0; i < kActWordsPerThread; ++i) {
-      const int q = base + threadIdx.x + i * (int)blockDim.x;
-      if (q < n) act_s[q] = v[i];
-    }
-  }
-  __syncthreads();
+  const int r = a.r;
+  stage_words_ll(a.status, a.ll_act + (size_t)p * a.B * r, a.B * r, ll_tag(ep, p), act_s,
+                 [r](int q) { return act_stage_index<W>(q % r, q / r, r); });
 }
 // the same staging from the stepwise schedule's activation buffer (bf16: hi
 // [B][r] then lo [B][r]; fp32: [B][r])
@@ -842,11 +884,12 @@ __device__ __forceinline__ void stage_act_global(const ChainArgs& a, int p, uint
   const int B = a.B, r = a.r, n = B * r;
   const uint32_t* slot = reinterpret_cast<const uint32_t*>((const char*)a.act + (size_t)p * a.act_step);
   for (int q = threadIdx.x; q < n; q += blockDim.x) {
+    const int b = q / r, w = q - b * r;
     if constexpr (sizeof(W) == 2) {
-      const int b = q / r, w = q - b * r;
-      act_s[q] = w < r / 2 ? slot[(size_t)b * (r / 2) + w] : slot[(size_t)B * (r / 2) + (size_t)b * (r / 2) + w - r / 2];
+      act_s[act_stage_index<W>(w, b, r)] =
+          w < r / 2 ? slot[(size_t)b * (r / 2) + w] : slot[(size_t)B * (r / 2) + (size_t)b * (r / 2) + w - r / 2];
     } else {
-      act_s[q] = slot[q];
+      act_s[act_stage_index<W>(w, b, r)] = slot[q];
     }
   }
   __syncthreads();
@@ -865,7 +908,7 @@ __device__ __forceinline__ void logits_resident_(const ChainArgs& a, int p, int 
   float lb[NT][RG][2], b2[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) load_base_rows<RG>(a, p, tile_of(i) * 16 + row, kg, tile_of(i) < t_end, lb[i], b2[i]);
-  stage_act_ll(a, p, ep, act_s);  // the activations of this step
+  stage_act_ll<W>(a, p, ep, act_s);  // the activations of this step
   DH_STAMP(p, 4);
   frag_t<W> af[RG][KC];
 #pragma unroll
@@ -947,7 +990,7 @@ __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_b
 #pragma unroll
   for (int i = DH_O_EARLY; i < PF; ++i) issue(t + 4 * i, ring[i]);
   if constexpr (kLL)
-    stage_act_ll(a, p, ep, act_s);
+    stage_act_ll<W>(a, p, ep, act_s);
   else
     stage_act_global<W>(a, p, act_s);
   // left operands kept in registers when they fit in 64, else read per tile from LDS
@@ -1131,7 +1174,7 @@ __global__ __launch_bounds__(256) void chain_bottleneck_k(ChainArgs a, int p) {
 template <class W, int RG, int KC>
 __global__ __launch_bounds__(256) void chain_logits_k(ChainArgs a, int p) {
   __shared__ uint64_t sbest[4 * kMaxChainGroup];
-  __shared__ __attribute__((aligned(16))) uint32_t act_s[kMaxChainGroup * 256];  // r <= 256
+  __shared__ __attribute__((aligned(16))) uint32_t act_s[kMaxChainGroup * (256 + 8)];  // r <= 256
   const int T = (a.V + 15) / 16, G = gridDim.x, w = blockIdx.x;
   logits_range<W, RG, KC, false>(a, p, (int)((int64_t)T * w / G), (int)((int64_t)T * (w + 1) / G), sbest,
                                  [] { return true; }, 0u, act_s);
@@ -1168,6 +1211,12 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
   if (kGruLds && wg < nG) stage_gru_slice<W>(a, wg, gl);
   if (kLds >= 2 && wg < nW) stage_w1_slice<W>(a, wg, wl);
   if constexpr (NTW > 0) stage_w2_lds<W, KC>(a, t_begin + 4 * NTW, max(0, t_end - t_begin - 4 * NTW), w2l);
+  // resident W2: the bottleneck workgroups stage the state words after their
+  // LDS tiles when one poll round covers them (more rounds cost a memory
+  // round trip each, more than per-lane polling)
+  uint32_t* h_s = NTW > 0 && wg < nW && stage_state(a.B, a.Hs)
+                      ? reinterpret_cast<uint32_t*>(w2l + (size_t)max(0, t_end - t_begin - 4 * NTW) * w2_lds_tile_bytes(KC))
+                      : nullptr;
   f32x4 acc_h[NCB];  // hidden half of this workgroup's next GRU step
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc_h[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1213,7 +1262,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
     if (wg < nW) {
       if (wg >= nG) pre = bottleneck_pre<NCB>(a, p, wg);
       DH_STAMP(p, 2);
-      bottleneck_item<W, NCB, (kLds >= 2), true>(a, p, wg, red, wl, pre, ep);
+      bottleneck_item<W, NCB, (kLds >= 2), true>(a, p, wg, red, wl, pre, ep, h_s);
     }
     DH_STAMP(p, 3);
     // W_hh h(p+1) for the next step: in the wait for the bottleneck, or, in
@@ -1281,22 +1330,22 @@ ChainLayout chain_layout(int d, int Hs, int r, int P, int group) {
   return L;
 }
 
-// Dynamic LDS a resident-W2 launch on G workgroups needs (the W1 slice
-// region, then the LDS tiles), or 0 if some workgroup owns more tiles than
-// its register and LDS slots hold.
+// Dynamic LDS a resident-W2 launch on G workgroups needs (staged
+// activations; in bottleneck workgroups the W1 slice; the LDS tiles; in
+// bottleneck workgroups the staged state), or 0 if some workgroup owns more
+// tiles than its register and LDS slots hold.
 static size_t resident_lds(int G, const ChainArgs& a, int ntw, int kc, size_t w1_bytes) {
   const int nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
   const size_t act = act_stage_bytes(a.B, a.r);
-  size_t need = act + w1_bytes;
+  const size_t hst = stage_state(a.B, a.Hs) ? act_stage_bytes(a.B, a.Hs) : 0;  // staged state
+  size_t need = act + w1_bytes + hst;
   for (int w = 0; w < G; ++w) {
     int b, e;
     o_tile_range(w, G, nW, T, b, e);
     const int n_lds = e - b - 4 * ntw;
     if (n_lds > kLdsTiles) return 0;
-    if (n_lds > 0) {
-      const size_t at = act + (w < nW ? w1_bytes : 0) + (size_t)n_lds * w2_lds_tile_bytes(kc);
-      need = at > need ? at : need;
-    }
+    const size_t at = act + (w < nW ? w1_bytes + hst : 0) + (size_t)(n_lds > 0 ? n_lds : 0) * w2_lds_tile_bytes(kc);
+    need = at > need ? at : need;
   }
   return need;
 }
