@@ -665,11 +665,8 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
 }
 
 // ---- phase O: W2 tiles [t_begin, t_end), base add, argmax ---------------------------
-#ifndef DH_O_PREFETCH
-#define DH_O_PREFETCH 2  // tiles in flight per wave beyond the one being consumed
-#endif
 #ifndef DH_O_EARLY
-#define DH_O_EARLY 2     // of those, issued before the activations are ready
+#define DH_O_EARLY 2     // tiles of phase O issued before the activations are ready
 #endif
 #ifndef DH_W_SHARE
 #define DH_W_SHARE 3     // W2 share of a bottleneck workgroup, in eighths of the others'
@@ -722,13 +719,39 @@ __host__ __device__ inline size_t w2_lds_tile_bytes(int KC) { return (size_t)KC 
 // Loads from clamped, in-bounds addresses (no select).  Rows past V are never
 // stored; k positions past r meet zero activations, so the finite weights
 // read there add exactly zero.
-// Staged activations in LDS: sequence b's words at b*(r+8) + q, and with bf16
-// weights the lo half (words q >= r/2) shifted by 4 more words, so that the
-// 16 (sequence, half) rows one fragment read touches fall in distinct banks.
-__host__ __device__ inline size_t act_stage_bytes(int B, int r) { return ((size_t)B * (r + 8) * 4 + 255) & ~size_t(255); }
-template <class W>
+// Staged activations in LDS, one row of act_row_words words per sequence.
+// bf16 weights: the hi words (bf16 pairs) of sequence b at b*S + q, q < r/2,
+// its lo words at b*S + P + 4 + q, where P = 16 KC >= r/2 and S = 2P + 8; the
+// 4-word shift puts the 16 (sequence, half) rows of one fragment read in
+// distinct banks.  fp32 weights: the values at b*S + q, S = 32 KC + 8.  Words
+// from r/2 (fp32: r) up to the k chunks' end hold zeros, so fragment reads
+// need no bounds: the pads are cleared once per launch (act_clear_pads).
+__host__ __device__ constexpr int act_half_words(int kc, int wsize) { return wsize == 2 ? 16 * kc : 32 * kc; }
+__host__ __device__ constexpr int act_row_words(int kc, int wsize) {
+  return wsize == 2 ? 2 * act_half_words(kc, 2) + 8 : act_half_words(kc, 4) + 8;
+}
+__host__ __device__ inline size_t act_stage_bytes(int B, int kc, int wsize) {
+  return ((size_t)B * act_row_words(kc, wsize) * 4 + 255) & ~size_t(255);
+}
+// LDS bytes of B * n staged 32-bit words
+__host__ __device__ inline size_t stage_words_bytes(int B, int n) { return ((size_t)B * n * 4 + 255) & ~size_t(255); }
+// word q (< r for fp32; bf16: hi words q < r/2, then lo words) of sequence b
+template <class W, int KC>
 __device__ __forceinline__ int act_stage_index(int q, int b, int r) {
-  return b * (r + 8) + ((sizeof(W) == 2 && q >= r / 2) ? q + 4 : q);
+  constexpr int P = act_half_words(KC, sizeof(W)), S = act_row_words(KC, sizeof(W));
+  if constexpr (sizeof(W) == 2) return b * S + (q < r / 2 ? q : q - r / 2 + P + 4);
+  return b * S + q;
+}
+template <class W, int KC>
+__device__ __forceinline__ void act_clear_pads(uint32_t* act_s, int B, int r) {
+  constexpr int P = act_half_words(KC, sizeof(W)), S = act_row_words(KC, sizeof(W));
+  const int used = sizeof(W) == 2 ? r / 2 : r, pad = P - used;
+  if (pad <= 0) return;
+  for (int q = threadIdx.x; q < B * pad; q += blockDim.x) {
+    const int b = q / pad, w = used + q % pad;
+    act_s[b * S + w] = 0u;
+    if constexpr (sizeof(W) == 2) act_s[b * S + P + 4 + w] = 0u;
+  }
 }
 
 // (t may be -1 for a workgroup that owns no tile; such rows are never used)
@@ -782,35 +805,49 @@ __device__ __forceinline__ void stage_w2_lds(const ChainArgs& a, int t_first, in
 // odd ones'; every phase-O variant computes exactly this.
 constexpr int kSeqPerRowGroup = 8;
 
-// left operand, elements k..k+7, for row `row` of row group g
-template <class W>
-__device__ __forceinline__ frag_t<W> act_row_frag(const uint32_t* act_s, int r, int B, int g, int row, int k) {
-  const int b = g * kSeqPerRowGroup + (row >> 1), part = row & 1;
-  if (b >= B || k >= r) return zero8<W>();
-  const uint32_t* src = act_s + (size_t)b * (r + 8);
+// left operand, elements k..k+7 (k < 32 KC), for row `row` of row group g.
+// Rows of sequences past B read sequence B - 1: their results are never used.
+template <class W, int KC>
+__device__ __forceinline__ frag_t<W> act_row_frag(const uint32_t* act_s, int B, int g, int row, int k) {
+  constexpr int P = act_half_words(KC, sizeof(W)), S = act_row_words(KC, sizeof(W));
+  const int b = min(g * kSeqPerRowGroup + (row >> 1), B - 1), part = row & 1;
+  const uint32_t* src = act_s + b * S;
   if constexpr (sizeof(W) == 2) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + (part ? r / 2 + 4 : 0) + k / 2));
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + (part ? P + 4 : 0) + k / 2));
   } else {
-    if (part) return zero8<float>();
     f32x8 f;
     f.lo = *reinterpret_cast<const float4*>(src + k);
     f.hi = *reinterpret_cast<const float4*>(src + k + 4);
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (part) f.lo = z, f.hi = z;  // the odd rows stay zero for fp32 weights
     return f;
   }
 }
 
 // Lb of vocabulary entry v for this lane's sequences (8g + 2kg + j), and b2[v]
-template <int RG>
-__device__ __forceinline__ void load_base_rows(const ChainArgs& a, int p, int v, int kg, bool ok, float (&lb)[RG][2],
+// Loads from clamped addresses with no per-lane condition (a lane-dependent
+// select here would turn into a masked region that waits for the load, and
+// with it for every load issued earlier).  Entries past V are skipped by
+// rows_epilogue, rows of sequences past B are never published.  kSkipEmpty:
+// rows (g, j) with no sequence in any lane are skipped by a uniform branch;
+// inside a software-pipelined loop every load is issued instead, so that the
+// number of loads after any given one is fixed and the waits stay exact.
+template <int RG, bool kSkipEmpty>
+__device__ __forceinline__ void load_base_rows(const ChainArgs& a, int p, int v, int kg, float (&lb)[RG][2],
                                                float& b2) {
-  const bool vok = ok && v < a.V;
-  b2 = (vok && a.b2) ? a.b2[v] : 0.f;
+  const int vc = min(v, a.V - 1);
+  const float bias = (a.b2 ? a.b2 : a.Lb)[vc];  // always loaded (a uniform select of the address)
+  b2 = a.b2 ? bias : 0.f;
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int b = g * kSeqPerRowGroup + 2 * kg + j;
-      lb[g][j] = (vok && b < a.B) ? a.Lb[((size_t)b * a.P + p) * a.V + v] : 0.f;
+      const float* src = a.Lb + ((size_t)min(b, a.B - 1) * a.P + p) * a.V + vc;
+      if constexpr (kSkipEmpty)
+        lb[g][j] = g * kSeqPerRowGroup + j < a.B ? *src : 0.f;
+      else
+        lb[g][j] = *src;
     }
 }
 
@@ -871,25 +908,25 @@ __device__ __forceinline__ void publish_rows(const ChainArgs& a, int p, LaneMax 
 }
 
 // The bottleneck activations of step p, staged in LDS (act_stage_index).
-template <class W>
+template <class W, int KC>
 __device__ __forceinline__ void stage_act_ll(const ChainArgs& a, int p, uint32_t ep, uint32_t* act_s) {
   const int r = a.r;
   stage_words_ll(a.status, a.ll_act + (size_t)p * a.B * r, a.B * r, ll_tag(ep, p), act_s,
-                 [r](int q) { return act_stage_index<W>(q % r, q / r, r); });
+                 [r](int q) { return act_stage_index<W, KC>(q % r, q / r, r); });
 }
 // the same staging from the stepwise schedule's activation buffer (bf16: hi
 // [B][r] then lo [B][r]; fp32: [B][r])
-template <class W>
+template <class W, int KC>
 __device__ __forceinline__ void stage_act_global(const ChainArgs& a, int p, uint32_t* act_s) {
   const int B = a.B, r = a.r, n = B * r;
   const uint32_t* slot = reinterpret_cast<const uint32_t*>((const char*)a.act + (size_t)p * a.act_step);
   for (int q = threadIdx.x; q < n; q += blockDim.x) {
     const int b = q / r, w = q - b * r;
     if constexpr (sizeof(W) == 2) {
-      act_s[act_stage_index<W>(w, b, r)] =
+      act_s[act_stage_index<W, KC>(w, b, r)] =
           w < r / 2 ? slot[(size_t)b * (r / 2) + w] : slot[(size_t)B * (r / 2) + (size_t)b * (r / 2) + w - r / 2];
     } else {
-      act_s[act_stage_index<W>(w, b, r)] = slot[q];
+      act_s[act_stage_index<W, KC>(w, b, r)] = slot[q];
     }
   }
   __syncthreads();
@@ -907,14 +944,14 @@ __device__ __forceinline__ void logits_resident_(const ChainArgs& a, int p, int 
   auto tile_of = [&](int i) { return t_begin + wv + 4 * i; };
   float lb[NT][RG][2], b2[NT];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) load_base_rows<RG>(a, p, tile_of(i) * 16 + row, kg, tile_of(i) < t_end, lb[i], b2[i]);
-  stage_act_ll<W>(a, p, ep, act_s);  // the activations of this step
+  for (int i = 0; i < NT; ++i) load_base_rows<RG, true>(a, p, tile_of(i) * 16 + row, kg, lb[i], b2[i]);
+  stage_act_ll<W, KC>(a, p, ep, act_s);  // the activations of this step
   DH_STAMP(p, 4);
   frag_t<W> af[RG][KC];
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
-    for (int c = 0; c < KC; ++c) af[g][c] = act_row_frag<W>(act_s, a.r, a.B, g, row, c * 32 + kg * 8);
+    for (int c = 0; c < KC; ++c) af[g][c] = act_row_frag<W, KC>(act_s, a.B, g, row, c * 32 + kg * 8);
   LaneMax lm[RG][2];
 #pragma unroll
   for (int g = 0; g < RG; ++g) lm[g][0] = lm[g][1] = LaneMax{0.f, -1};
@@ -962,37 +999,41 @@ struct TileBuf {
   float b2;
 };
 
-// phase O with W2 streamed from memory: each wave walks tiles t_begin + wv,
-// + 4, ... with a ring of PF + 1 tile buffers; the first DH_O_EARLY tiles are
-// issued before the activations exist (after `ready` in the stepwise schedule)
+// phase O with W2 streamed from memory: each wave walks its tiles t_begin +
+// wv, + 4, ... with three named tile buffers, two tiles ahead of the one it
+// multiplies.  Every pass issues the same loads (past the wave's last tile
+// they repeat a valid tile, never used), so the number of loads issued after
+// any given one is fixed and the compiler's wait counts cover exactly the
+// tile being consumed; a buffer array indexed in a loop would instead be
+// rotated through register copies, each of which waits for its load.  The
+// first DH_O_EARLY tiles are issued before the activations exist (before
+// `ready` in the stepwise schedule).
 template <class W, int RG, int KC, bool kWrite, bool kLL, class Ready>
 __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest,
                                               Ready ready, uint32_t ep, uint32_t* act_s) {
-  constexpr int PF = DH_O_PREFETCH;
+  static_assert(DH_O_EARLY >= 0 && DH_O_EARLY <= 2, "two tiles ahead");
   const int lane = opaque_lane(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15, kg = lane >> 4;
-  const int r = a.r, V = a.V;
-  const W* w2 = (const W*)a.w2;
-  auto issue = [&](int t, TileBuf<W, RG, KC>& tb) {
-    if (t >= t_end) return;
-    const W* wr = w2 + (size_t)min(t * 16 + row, V - 1) * r + kg * 8;
+  const int t0 = t_begin + wv, n = t_end > t0 ? (t_end - t0 + 3) / 4 : 0;  // tiles of this wave
+  const int t_last = t_end > t_begin ? t_end - 1 : max(t_begin, 0);
+  auto issue = [&](int i, TileBuf<W, RG, KC>& tb) {
+    const int t = min(t0 + 4 * i, t_last);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) tb.w[c] = load8_or_zero(wr + c * 32, c * 32 + kg * 8 < r);
-    load_base_rows<RG>(a, p, t * 16 + row, kg, true, tb.lb, tb.b2);
+    for (int c = 0; c < KC; ++c) tb.w[c] = load8(w2_frag_ptr<W>(a, t, row, kg, c));
+    load_base_rows<RG, false>(a, p, t * 16 + row, kg, tb.lb, tb.b2);
   };
-  TileBuf<W, RG, KC> ring[PF + 1];
-  int t = t_begin + wv;
-#pragma unroll
-  for (int i = 0; i < DH_O_EARLY; ++i) issue(t + 4 * i, ring[i]);
+  TileBuf<W, RG, KC> s0, s1, s2;
+  if (DH_O_EARLY >= 1) issue(0, s0);
+  if (DH_O_EARLY >= 2) issue(1, s1);
   if constexpr (!kLL) {
     if (!ready()) return false;
   }
-#pragma unroll
-  for (int i = DH_O_EARLY; i < PF; ++i) issue(t + 4 * i, ring[i]);
+  if (DH_O_EARLY < 1) issue(0, s0);
+  if (DH_O_EARLY < 2) issue(1, s1);
   if constexpr (kLL)
-    stage_act_ll<W>(a, p, ep, act_s);
+    stage_act_ll<W, KC>(a, p, ep, act_s);
   else
-    stage_act_global<W>(a, p, act_s);
+    stage_act_global<W, KC>(a, p, act_s);
   // left operands kept in registers when they fit in 64, else read per tile from LDS
   constexpr bool kAfRegs = RG * KC * (int)(sizeof(frag_t<W>) / 4) <= 64;
   frag_t<W> af[kAfRegs ? RG : 1][kAfRegs ? KC : 1];
@@ -1000,12 +1041,12 @@ __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_b
 #pragma unroll
     for (int g = 0; g < RG; ++g)
 #pragma unroll
-      for (int c = 0; c < KC; ++c) af[g][c] = act_row_frag<W>(act_s, r, a.B, g, row, c * 32 + kg * 8);
+      for (int c = 0; c < KC; ++c) af[g][c] = act_row_frag<W, KC>(act_s, a.B, g, row, c * 32 + kg * 8);
   }
   LaneMax lm[RG][2];
 #pragma unroll
   for (int g = 0; g < RG; ++g) lm[g][0] = lm[g][1] = LaneMax{0.f, -1};
-  auto consume = [&](int t, const TileBuf<W, RG, KC>& tb) {
+  auto consume = [&](int i, const TileBuf<W, RG, KC>& tb) {
     f32x4 acc[RG][2];  // even and odd k chunks: two independent MFMA chains per row group
 #pragma unroll
     for (int g = 0; g < RG; ++g) acc[g][0] = acc[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1016,19 +1057,21 @@ __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_b
         if constexpr (kAfRegs)
           acc[g][c & 1] = mma(af[g][c], tb.w[c], acc[g][c & 1]);
         else
-          acc[g][c & 1] = mma(act_row_frag<W>(act_s, r, a.B, g, row, c * 32 + kg * 8), tb.w[c], acc[g][c & 1]);
+          acc[g][c & 1] = mma(act_row_frag<W, KC>(act_s, a.B, g, row, c * 32 + kg * 8), tb.w[c], acc[g][c & 1]);
       }
-    rows_epilogue<kWrite, RG>(a, p, t * 16 + row, kg, tb.lb, tb.b2, acc, lm);
+    rows_epilogue<kWrite, RG>(a, p, (t0 + 4 * i) * 16 + row, kg, tb.lb, tb.b2, acc, lm);
   };
-  // ring of PF + 1 tile buffers; slot indices are compile-time after unrolling
-  while (t < t_end) {
-#pragma unroll
-    for (int s = 0; s < PF + 1; ++s) {
-      issue(t + 4 * PF, ring[(s + PF) % (PF + 1)]);
-      if (t < t_end) consume(t, ring[s]);
-      t += 4;
-    }
+  int i = 0;
+  for (; i + 3 <= n; i += 3) {
+    issue(i + 2, s2);
+    consume(i, s0);
+    issue(i + 3, s0);
+    consume(i + 1, s1);
+    issue(i + 4, s1);
+    consume(i + 2, s2);
   }
+  if (i < n) consume(i, s0);
+  if (i + 1 < n) consume(i + 1, s1);
   publish_rows<RG, kLL>(a, p, lm, sbest, ep);
   return true;
 }
@@ -1176,6 +1219,7 @@ __global__ __launch_bounds__(256) void chain_logits_k(ChainArgs a, int p) {
   __shared__ uint64_t sbest[4 * kMaxChainGroup];
   __shared__ __attribute__((aligned(16))) uint32_t act_s[kMaxChainGroup * (256 + 8)];  // r <= 256
   const int T = (a.V + 15) / 16, G = gridDim.x, w = blockIdx.x;
+  act_clear_pads<W, KC>(act_s, a.B, a.r);  // made visible by the staging's barrier
   logits_range<W, RG, KC, false>(a, p, (int)((int64_t)T * w / G), (int)((int64_t)T * (w + 1) / G), sbest,
                                  [] { return true; }, 0u, act_s);
 }
@@ -1196,7 +1240,8 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
   // dynamic LDS: [staged activations][GRU slice (streamed W2)][W1 slice][LDS
   // tier of W2 (resident W2)]
   uint32_t* act_s = reinterpret_cast<uint32_t*>(dyn_lds);
-  W* gl = reinterpret_cast<W*>(dyn_lds + act_stage_bytes(a.B, a.r));
+  act_clear_pads<W, KC>(act_s, a.B, a.r);  // made visible by the first staging's barrier
+  W* gl = reinterpret_cast<W*>(dyn_lds + act_stage_bytes(a.B, KC, sizeof(W)));
   W* wl = gl + (kGruLds ? gru_slice_elems(a.d, a.Hs) : 0);
   const int G = gridDim.x, wg = blockIdx.x;
   const int nG = a.Hs / 4, nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
@@ -1336,8 +1381,8 @@ ChainLayout chain_layout(int d, int Hs, int r, int P, int group) {
 // tiles than its register and LDS slots hold.
 static size_t resident_lds(int G, const ChainArgs& a, int ntw, int kc, size_t w1_bytes) {
   const int nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
-  const size_t act = act_stage_bytes(a.B, a.r);
-  const size_t hst = stage_state(a.B, a.Hs) ? act_stage_bytes(a.B, a.Hs) : 0;  // staged state
+  const size_t act = act_stage_bytes(a.B, kc, 2);  // resident W2 is bf16
+  const size_t hst = stage_state(a.B, a.Hs) ? stage_words_bytes(a.B, a.Hs) : 0;  // staged state
   size_t need = act + w1_bytes + hst;
   for (int w = 0; w < G; ++w) {
     int b, e;
@@ -1408,7 +1453,7 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
         if (l2 > 0 && l2 <= kLdsBudget) return launch_persistent<W, RG, KC, 2, NTW>(a, l2, s);
       }
     }
-    const size_t act = act_stage_bytes(a.B, a.r);
+    const size_t act = act_stage_bytes(a.B, KC, sizeof(W));
     if (act + g + w <= kLdsBudget) return launch_persistent<W, RG, KC, 2, 0>(a, act + g + w, s);
     if (act + g <= kLdsBudget) return launch_persistent<W, RG, KC, 1, 0>(a, act + g, s);
     return launch_persistent<W, RG, KC, 0, 0>(a, act, s);

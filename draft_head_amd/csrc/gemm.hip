@@ -6,14 +6,16 @@
 // head (Dutch Domino summary, "Methodologie", part 1; 163.com explainer,
 // section 3) and for the H-half of the bottleneck projection, W1[:, :d] H_i.
 //
-// Two kernels:
-//  * gemm_stream: every wave owns 16 columns (16 weight rows) and streams
-//    their full k range from HBM straight into MFMA fragments; each
-//    workgroup row covers MT 16-row tiles of A.  For few activation rows
-//    the product is bound by reading B once, so nothing is staged in LDS.
-//  * gemm_tiled: 128x128 output tiles, k staged through LDS in 64-deep
-//    slabs (double buffered), 2x2 waves of 64x64, bf16 only.  Tiles that
-//    share B columns are issued to the same XCD so they meet in its L2.
+// Kernels, by the number of rows of A:
+//  * gemm_rows16 (at most 16 rows, one draft block): persistent, B streamed
+//    once from HBM straight into MFMA fragments, A in LDS.
+//  * gemm_stream (few rows, or fp32): every wave owns 16-column tiles and
+//    streams their full k range; nothing is staged in LDS.
+//  * gemm_tiled (up to 128 rows): 128x128 tiles, k staged through LDS.
+//  * gemm_wide (more than 128 rows): persistent 256x256 tiles, direct
+//    global->LDS loads; the product is then bound by how fast a CU can pull
+//    operands from L2, so the tile is as large as the register file allows.
+// Tiles that share B columns are given to the same XCD so they meet in its L2.
 #include "device.h"
 #include "internal.h"
 
@@ -166,6 +168,167 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_rows16(const uint16_t* __rest
   }
 }
 
+#ifndef DH_WIDE_BK
+#define DH_WIDE_BK 64   // k depth of a stage of gemm_wide
+#endif
+#ifndef DH_WIDE_NBUF
+#define DH_WIDE_NBUF 2  // LDS stage buffers of gemm_wide
+#endif
+
+// Many rows of A, bf16, K a multiple of BK.
+// Workgroup tile BM x 256 (BM = 32 MT), eight waves in 2 x 4, each MT x 4
+// 16x16 tiles; k runs in BK-deep stages through a ring of NBUF LDS buffers.
+// What bounds this product on MI355X is how fast a CU pulls operands from
+// L2, so the tile is as large as the register file allows (fewer bytes per
+// flop).  Loads go straight from global memory into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at slot l of a 1 KB
+// block); a load covers 1024 / (2 BK) rows, lane l taking row l / (BK / 8)
+// and 16-byte unit l % (BK / 8).  Row r's unit u is stored at position
+// u ^ sw(r) of the row, sw chosen so that the 16 rows of a fragment read
+// fall in distinct banks.  Persistent, one workgroup per CU, tiles dealt
+// per XCD (below).  Stage q's loads are issued during stage
+// q - (NBUF - 1) into the buffer that stage q - 1 used; the barrier at the
+// end of every stage publishes the next one and frees the oldest.
+template <int BK>
+__device__ __forceinline__ int wide_swizzle(int r) {
+  return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3;
+}
+
+template <int MT, int BK, int NBUF>
+__global__ __launch_bounds__(512) void gemm_wide(const uint16_t* __restrict__ A, int lda,
+                                                 const uint16_t* __restrict__ B, int ldb, float* __restrict__ C,
+                                                 int ldc, int M, int N, int K, int m_tiles, int n_tiles) {
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  constexpr int NT = 4, BM = 2 * MT * 16, BN = 256;
+  constexpr int ROWB = BK * 2, UPR = BK / 8, RPL = 64 / UPR;  // bytes, units per row; rows per load
+  constexpr int A_BYTES = BM * ROWB, STAGE = A_BYTES + BN * ROWB;
+  constexpr int A_LOADS = BM / RPL, LOADS = A_LOADS + BN / RPL;
+  static_assert(LOADS % 8 == 0, "loads split evenly over the waves");
+  constexpr int D = LOADS / 8, LA = NBUF - 1;
+  static_assert((LA - 1) * D < 64, "vmcnt range");
+  constexpr int KC = BK / 32;  // MFMA k chunks per stage
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // [NBUF][STAGE]
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wv >> 2, wn = wv & 3;
+  const int nks = K / BK;
+
+  const int G = gridDim.x, nx = G < 8 ? G : 8, g = blockIdx.x, x = g % nx, y = g / nx;
+  const int Gx = (G - x + nx - 1) / nx;
+  const int total = m_tiles * n_tiles;
+  const int tx0 = (int)((int64_t)total * x / nx), tx1 = (int)((int64_t)total * (x + 1) / nx);
+  const int n_my = tx1 - tx0 > y ? (tx1 - tx0 - y + Gx - 1) / Gx : 0;
+  if (n_my == 0) return;
+  const int S = n_my * nks;
+
+  // the loads of stage q; past the last stage they repeat it (in bounds, never read)
+  const int lrow = lane / UPR, lunit = lane % UPR;
+  int ld_q = 0, ld_tile = 0, ld_ks = 0, ld_buf = 0;
+  const uint16_t* srcA = nullptr;
+  const uint16_t* srcB = nullptr;
+  auto aim = [&]() {
+    const int t = tx0 + y + ld_tile * Gx, mt = t % m_tiles, nt = t / m_tiles;
+    srcA = A + (size_t)mt * BM * lda;
+    srcB = B + (size_t)nt * BN * ldb;
+    return mt;
+  };
+  int ld_mt = aim();
+  int ld_nt = (tx0 + y) / m_tiles;
+  auto issue_one = [&](int d) {
+    const int L = wv * D + d;
+    const bool isA = L < A_LOADS;
+    const int r = (isA ? L : L - A_LOADS) * RPL + lrow;
+    const int unit = lunit ^ wide_swizzle<BK>(r);
+    const uint16_t* src = isA ? srcA + (size_t)min(r, M - 1 - ld_mt * BM) * lda
+                              : srcB + (size_t)min(r, N - 1 - ld_nt * BN) * ldb;
+    __builtin_amdgcn_global_load_lds((const void*)(src + ld_ks * BK + unit * 8),
+                                     (__attribute__((address_space(3))) void*)(lds + (size_t)ld_buf * STAGE + L * 1024),
+                                     16, 0, 0);
+  };
+  auto advance = [&]() {
+    ld_buf = ld_buf + 1 == NBUF ? 0 : ld_buf + 1;
+    if (ld_q + 1 < S) {
+      ++ld_q;
+      if (++ld_ks == nks) {
+        ld_ks = 0;
+        ++ld_tile;
+        ld_mt = aim();
+        ld_nt = (tx0 + y + ld_tile * Gx) / m_tiles;
+      }
+    }
+  };
+  auto issue = [&]() {
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue_one(d);
+    advance();
+  };
+  auto sync = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // fragment reads: row l % 16 of a 16-row tile, unit UPR-chunk c: 4c + l / 16
+  const int fr = lane & 15, sw = wide_swizzle<BK>(fr);
+  int off[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) off[c] = fr * ROWB + (((4 * c + (lane >> 4)) ^ sw) * 16);
+  f32x4 acc[MT][NT];
+  int rd_buf = 0;
+  auto stage = [&](bool first) {
+    const unsigned char* a0 = lds + rd_buf * STAGE + wm * MT * 16 * ROWB;
+    const unsigned char* b0 = lds + rd_buf * STAGE + A_BYTES + wn * NT * 16 * ROWB;
+    rd_buf = rd_buf + 1 == NBUF ? 0 : rd_buf + 1;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      bf16x8 fa[MT], fb[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(b0 + j * 16 * ROWB + off[c]);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(a0 + i * 16 * ROWB + off[c]);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = mma(fa[i], fb[j], (first && c == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i][j]);
+      }
+    }
+  };
+  // end of stage q: stage q + 1 in (loads of q + 2 .. q + LA still out), then the barrier
+  auto finish = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((LA - 1) * D) : "memory");
+    sync();
+  };
+
+  for (int q = 0; q < LA; ++q) issue();
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((LA - 1) * D) : "memory");
+  sync();
+  for (int i = 0; i < n_my; ++i) {
+    issue();
+    stage(true);
+    finish();
+    for (int ks = 1; ks < nks; ++ks) {
+      issue();
+      stage(false);
+      finish();
+    }
+    const int t = tx0 + y + i * Gx, mt = t % m_tiles, nt = t / m_tiles;
+    const int m0 = mt * BM + wm * MT * 16 + (lane >> 4) * 4, n0 = nt * BN + wn * NT * 16 + fr;
+    if (mt * BM + BM <= M && nt * BN + BN <= N) {
+#pragma unroll
+      for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int b = 0; b < NT; ++b) C[(size_t)(m0 + a * 16 + e) * ldc + n0 + b * 16] = acc[a][b][e];
+    } else {
+#pragma unroll
+      for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int b = 0; b < NT; ++b)
+            if (m0 + a * 16 + e < M && n0 + b * 16 < N) C[(size_t)(m0 + a * 16 + e) * ldc + n0 + b * 16] = acc[a][b][e];
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Small products (few columns, e.g. the 256 bottleneck units): one 16x16
 // output tile per workgroup, k split over its 4 waves (splitk_tile).
 template <class W>
@@ -289,6 +452,42 @@ static hipError_t launch_stream(const W* A, int lda, const W* B, int ldb, float*
   return hipGetLastError();
 }
 
+// LDS beyond 64 KB per workgroup has to be asked for once per kernel and device
+static hipError_t allow_lds(const void* fn, size_t bytes) {
+  static thread_local const void* done_fn[8];
+  static thread_local int done_dev[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < 8; ++i)
+    if (done_fn[i] == fn && done_dev[i] == dev) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < 8; ++i)
+    if (done_dev[i] < 0) {
+      done_fn[i] = fn;
+      done_dev[i] = dev;
+      break;
+    }
+  return hipSuccess;
+}
+
+template <int MT>
+static hipError_t launch_wide(const uint16_t* A, int lda, const uint16_t* B, int ldb, float* C, int ldc, int M, int N,
+                              int K, int cus, hipStream_t s) {
+  constexpr int BK = DH_WIDE_BK, NBUF = DH_WIDE_NBUF, BM = 2 * MT * 16, BN = 256;
+  constexpr size_t lds = (size_t)NBUF * (BM + BN) * BK * 2;
+  static_assert(lds <= 160 * 1024, "LDS of a CU");
+  const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
+  const int64_t total = (int64_t)m_tiles * n_tiles;
+  const int grid = total < cus ? (int)total : cus;
+  hipError_t e = allow_lds((const void*)gemm_wide<MT, BK, NBUF>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_wide<MT, BK, NBUF>), dim3(grid), dim3(512), lds, s, A, lda, B, ldb, C, ldc, M, N, K, m_tiles,
+                     n_tiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int ldb, float* C, int ldc, int M, int N,
                           int K, bool prefer_tiles, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
@@ -323,6 +522,10 @@ hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int 
                          (const uint16_t*)B, ldb, C, ldc, M, N, K);
       return hipGetLastError();
     }
+  }
+  if (prefer_tiles && M > 128 && K % DH_WIDE_BK == 0 && lda % 8 == 0 && ldb % 8 == 0) {
+    const int cus = device_cus();
+    if (cus > 0) return launch_wide<8>((const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, M, N, K, cus, s);
   }
   if (!prefer_tiles || M <= 64)
     return launch_stream((const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, M, N, K, s);

@@ -101,6 +101,24 @@ def test_base_logits_one_sequence_wide(d, V, P):
     assert np.array_equal(g, g2)  # fixed split and summation order
 
 
+# many rows (several sequences' blocks): the LDS-ring MFMA kernel for k a
+# multiple of 64, both tile shapes, ragged rows and columns, several tiles per
+# workgroup, and the look-ahead loads crossing tile boundaries
+@pytest.mark.parametrize("d,V,B,P", [(320, 40009, 19, 16), (576, 9001, 8, 16), (1024, 70001, 3, 11),
+                                     (384, 5003, 1, 7), (640, 33331, 40, 13), (2560, 12007, 32, 16)])
+def test_base_logits_many_rows(d, V, B, P):
+    cfg = small_config(d=d, V=V, B=B, P=P, dtype="bf16")
+    say(f"case base logits many rows d={d} V={V} B={B} P={P}")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    Hd = head.upload(inp["H"])
+    g = head.base_logits(Hd).cpu().numpy()
+    _check_gemm(g, inp["H"], w["lm_head"], "bf16", "many rows")
+    g2 = head.base_logits(Hd).cpu().numpy()
+    assert np.array_equal(g, g2)
+
+
 @pytest.mark.parametrize("key,rows", [("qwen3_4b_b1", [(0, 0), (0, 15)]), ("qwen3_4b_b32", [(0, 0), (31, 9)]),
                                       ("qwen3_8b_b16", [(0, 3), (15, 15)])])
 def test_base_logits_full_size_sampled(key, rows):
