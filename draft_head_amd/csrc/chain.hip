@@ -875,7 +875,7 @@ __device__ __forceinline__ void rows_epilogue(const ChainArgs& a, int p, int v, 
 // Fold the lanes' running argmaxes into one key per sequence for this
 // workgroup, then into the device-wide key of step p (atomic max), or, kLL,
 // publish it as this workgroup's (value, index) pair of hand-off words.
-template <int RG, bool kLL>
+template <int RG, bool kLL, int NWV = 4>
 __device__ __forceinline__ void publish_rows(const ChainArgs& a, int p, LaneMax (&lm)[RG][2], uint64_t* sbest,
                                              uint32_t ep) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6, kg = lane >> 4;
@@ -893,7 +893,7 @@ __device__ __forceinline__ void publish_rows(const ChainArgs& a, int p, LaneMax 
     const int b = threadIdx.x;
     uint64_t m = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) m = umax64(m, sbest[w * kMaxChainGroup + b]);
+    for (int w = 0; w < NWV; ++w) m = umax64(m, sbest[w * kMaxChainGroup + b]);
     if constexpr (kLL) {
       if (b < a.B) {
         uint64_t* w = a.ll_part + (((size_t)p * kMaxChainGrid + blockIdx.x) * a.B + b) * 2;
@@ -1076,6 +1076,62 @@ __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_b
   return true;
 }
 
+// an int the compiler cannot see through (keeps a loop-invariant LDS read
+// inside the loop, where it costs a few registers instead of many)
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+// phase O of the stepwise schedule with many waves: each of NWV waves takes
+// the workgroup's tiles t_begin + wv, + NWV, ... with the next tile's loads in
+// flight while it multiplies one (two named buffers, loads always issued from
+// clamped addresses so the waits stay exact), and re-reads the staged
+// activations from LDS per tile, so it needs few registers and the other
+// waves hide what latency is left.
+template <class W, int RG, int KC, int NWV, bool kWrite>
+__device__ __forceinline__ void logits_wide_(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest,
+                                             uint32_t* act_s) {
+  const int lane = opaque_lane(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane & 15, kg = lane >> 4;
+  const int t0 = t_begin + wv, n = t_end > t0 ? (t_end - t0 + NWV - 1) / NWV : 0;
+  const int t_last = t_end > t_begin ? t_end - 1 : max(t_begin, 0);
+  auto issue = [&](int i, TileBuf<W, RG, KC>& tb) {
+    const int t = min(t0 + NWV * i, t_last);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) tb.w[c] = load8(w2_frag_ptr<W>(a, t, row, kg, c));
+    load_base_rows<RG, false>(a, p, t * 16 + row, kg, tb.lb, tb.b2);
+  };
+  TileBuf<W, RG, KC> s0, s1;
+  issue(0, s0);
+  stage_act_global<W, KC>(a, p, act_s);
+  LaneMax lm[RG][2];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) lm[g][0] = lm[g][1] = LaneMax{0.f, -1};
+  auto consume = [&](int i, const TileBuf<W, RG, KC>& tb) {
+    const uint32_t* as = act_s + opaque_zero();
+    f32x4 acc[RG][2];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) acc[g][0] = acc[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+        acc[g][c & 1] = mma(act_row_frag<W, KC>(as, a.B, g, row, c * 32 + kg * 8), tb.w[c], acc[g][c & 1]);
+    rows_epilogue<kWrite, RG>(a, p, (t0 + NWV * i) * 16 + row, kg, tb.lb, tb.b2, acc, lm);
+  };
+  int i = 0;
+  for (; i + 2 <= n; i += 2) {
+    issue(i + 1, s1);
+    consume(i, s0);
+    issue(i + 2, s0);
+    consume(i + 1, s1);
+  }
+  if (i < n) consume(i, s0);
+  publish_rows<RG, false, NWV>(a, p, lm, sbest, 0u);
+}
+
 template <class W, int RG, int KC, bool kLL, class Ready>
 __device__ __forceinline__ bool logits_range(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest,
                                              Ready ready, uint32_t ep, uint32_t* act_s) {
@@ -1222,6 +1278,20 @@ __global__ __launch_bounds__(256) void chain_logits_k(ChainArgs a, int p) {
   act_clear_pads<W, KC>(act_s, a.B, a.r);  // made visible by the staging's barrier
   logits_range<W, RG, KC, false>(a, p, (int)((int64_t)T * w / G), (int)((int64_t)T * (w + 1) / G), sbest,
                                  [] { return true; }, 0u, act_s);
+}
+
+// stepwise phase O with NWV waves per workgroup (one workgroup per CU)
+template <class W, int RG, int KC, int NWV>
+__global__ __launch_bounds__(64 * NWV) void chain_logits_wide_k(ChainArgs a, int p) {
+  __shared__ uint64_t sbest[NWV * kMaxChainGroup];
+  __shared__ __attribute__((aligned(16))) uint32_t act_s[kMaxChainGroup * (256 + 8)];  // r <= 256
+  const int T = (a.V + 15) / 16, G = gridDim.x, w = blockIdx.x;
+  const int t_begin = (int)((int64_t)T * w / G), t_end = (int)((int64_t)T * (w + 1) / G);
+  act_clear_pads<W, KC>(act_s, a.B, a.r);  // made visible by the staging's barrier
+  if (a.out_logits)
+    logits_wide_<W, RG, KC, NWV, true>(a, p, t_begin, t_end, sbest, act_s);
+  else
+    logits_wide_<W, RG, KC, NWV, false>(a, p, t_begin, t_end, sbest, act_s);
 }
 
 // All P steps in one cooperative launch; every workgroup owns one GRU work
@@ -1439,8 +1509,12 @@ template <class W, int RG, int KC>
 static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& persistent) {
   constexpr int NCB = RG <= 2 ? 1 : 2;
   const int cus = device_cus();
-  // the persistent schedule needs one GRU work item per workgroup
-  persistent = mode != 1 && cus > 0 && a.Hs / 4 <= cus;
+  // the persistent schedule needs one GRU work item per workgroup.  By
+  // default it runs for up to 8 sequences (one row group), where the
+  // hand-offs between its phases are what bounds a step; with more
+  // sequences the three launches per step, each with all the waves a CU
+  // holds for its phase, are faster.
+  persistent = (mode == 2 || (mode == 0 && RG == 1)) && cus > 0 && a.Hs / 4 <= cus;
   if (persistent) {
     const size_t g = gru_slice_elems(a.d, a.Hs) * sizeof(W);
     const size_t w = (size_t)16 * (a.Hs + 8) * sizeof(W);
@@ -1463,7 +1537,11 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
   for (int p = 0; p < a.P; ++p) {
     hipLaunchKernelGGL((chain_gru_k<W, NCB>), dim3(nG), dim3(256), 0, s, a, p);
     hipLaunchKernelGGL((chain_bottleneck_k<W, NCB>), dim3(nW), dim3(256), 0, s, a, p);
-    hipLaunchKernelGGL((chain_logits_k<W, RG, KC>), dim3(nO), dim3(256), 0, s, a, p);
+    constexpr int NWV = RG * KC >= 16 ? 8 : 16;  // waves per CU, as registers allow
+    if constexpr (sizeof(W) == 2)  // bf16: many light waves per CU
+      hipLaunchKernelGGL((chain_logits_wide_k<W, RG, KC, NWV>), dim3(nO), dim3(64 * NWV), 0, s, a, p);
+    else
+      hipLaunchKernelGGL((chain_logits_k<W, RG, KC>), dim3(nO), dim3(256), 0, s, a, p);
   }
   return hipGetLastError();
 }

@@ -190,13 +190,14 @@ domino_status domino_tree_draft(const domino_dims *dims, const domino_weights *w
 void domino_set_timing_events(void *base_start, void *base_stop, void *chain_start, void *chain_stop);
 
 /*
- * Chain scheduling.  0 (default): one persistent cooperative launch runs
- * all P steps and, for bf16 weights and batch <= 16 where it fits, keeps W2
- * on chip (registers and LDS) for all of them; 2: the same launch with W2
- * read from memory every step; 1: three kernel launches per step.  All
- * compute the same function; they may differ in the last bits of fp32 sums
- * (different k-split orders).  Returns the previous mode; any other value is
- * rejected with -1.  Process-wide setting.
+ * Chain scheduling.  0 (default): the library picks; for up to 8 sequences
+ * one persistent cooperative launch runs all P steps and, for bf16 weights
+ * where it fits, keeps W2 on chip (registers and LDS) for all of them; for
+ * more sequences, three kernel launches per step.  1: three launches per
+ * step.  2: the persistent launch with W2 read from memory every step.  All
+ * compute the same function with the same summation order, so their outputs
+ * agree to the bit.  Returns the previous mode; any other value is rejected
+ * with -1.  Process-wide setting.
  */
 int32_t domino_set_chain_mode(int32_t mode);
 
