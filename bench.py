@@ -254,8 +254,10 @@ def main():
     if cfg.tree:
         roof["kernel"] = "tree launches (domino_tree_draft)" if dom == "chain" else "LM-head GEMM (domino_base_logits)"
     else:
-        roof["kernel"] = ("chain_persistent (domino_draft_chain steps)" if dom == "chain"
-                          else "LM-head GEMM (domino_base_logits)")
+        one_launch = args.chain_mode == 2 or (args.chain_mode == 0 and B <= 8)
+        roof["kernel"] = (("domino_draft_chain steps (" + ("chain_persistent, one launch" if one_launch
+                                                           else "three launches per step") + ")")
+                          if dom == "chain" else "LM-head GEMM (domino_base_logits)")
 
     value = B / (ms_per_step * 1e-3)
     out = {
