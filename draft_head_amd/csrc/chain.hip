@@ -25,11 +25,13 @@
 // the workgroups' results.
 //
 // Schedules that compute identical values:
-//  * persistent: one cooperative launch for all P steps.  Values cross
+//  * persistent: one launch for all P steps (all workgroups resident).  Values cross
 //    workgroups as tagged hand-off words that readers poll (bounded waits);
 //    W2 either stays on chip for the whole launch or is streamed every step;
 //  * stepwise: three launches per step on the caller's stream, with a device
 //    wide atomic max per workgroup for the argmax.
+#include <mutex>
+
 #include "device.h"
 #include "internal.h"
 
@@ -1294,7 +1296,7 @@ __global__ __launch_bounds__(64 * NWV) void chain_logits_wide_k(ChainArgs a, int
     logits_wide_<W, RG, KC, NWV, false>(a, p, t_begin, t_end, sbest, act_s);
 }
 
-// All P steps in one cooperative launch; every workgroup owns one GRU work
+// All P steps in one launch (every workgroup resident); each owns one GRU work
 // item (Hs/4 <= grid).  NTW == 0 (W2 streamed every step), kLds: 0 weights
 // from global memory, 1 the GRU slice in LDS, 2 also the bottleneck slice of
 // W1 in LDS.  NTW > 0 (W2 resident on chip): the GRU weights come from
@@ -1472,6 +1474,23 @@ struct CoopGrid {
   int blocks = 0;
 };
 
+// The persistent kernel needs all of its workgroups resident at the same
+// time (they hand data to each other).  It is sized to one or two workgroups
+// per CU and dispatched as an ordinary launch: a cooperative launch, which
+// would guarantee residency, costs about 20 us of queue hand-over per call on
+// this runtime.  Two persistent launches sharing the CUs could each wait for
+// the other, so every persistent launch on a device first waits for the
+// previous one, on whatever stream it ran.  Waits inside the kernel are
+// bounded in any case (status 2).
+struct PersistentGate {
+  std::mutex m;
+  hipEvent_t last = nullptr;
+};
+static PersistentGate& persistent_gate(int dev) {
+  static PersistentGate gates[64];
+  return gates[dev & 63];
+}
+
 template <class W, int RG, int KC, int kLds, int NTW>
 static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStream_t s) {
   static thread_local CoopGrid cache;
@@ -1498,9 +1517,20 @@ static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStr
   }
   if (cache.blocks < a.Hs / 4) return hipErrorInvalidConfiguration;  // one GRU item per workgroup
   if (cache.blocks > kMaxChainGrid || cache.blocks < a.B) return hipErrorInvalidConfiguration;  // hand-off slots
-  ChainArgs arg = a;
-  void* params[] = {&arg};
-  return hipLaunchCooperativeKernel(fn, dim3(cache.blocks), dim3(256), params, (unsigned)lds_bytes, s);
+  // every workgroup must be resident at once: the grid is sized to what the
+  // device holds, and launches are ordered per device (PersistentGate)
+  PersistentGate& g = persistent_gate(dev);
+  std::lock_guard<std::mutex> lock(g.m);
+  if (g.last) {
+    e = hipStreamWaitEvent(s, g.last, 0);
+  } else {
+    e = hipEventCreateWithFlags(&g.last, hipEventDisableTiming);
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((chain_persistent<W, RG, KC, kLds, NTW>), dim3(cache.blocks), dim3(256), lds_bytes, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return hipEventRecord(g.last, s);
 }
 
 constexpr size_t kLdsBudget = 144 * 1024;  // dynamic LDS the persistent kernel may use (160 KB per CU)

@@ -36,7 +36,9 @@
  *   - Errors: a non-zero domino_status is returned and domino_last_error()
  *     (per thread) describes it.  No C++ exception crosses the ABI.
  *   - Calls are stateless and may run concurrently on distinct streams with
- *     distinct workspaces and outputs.
+ *     distinct workspaces and outputs.  The persistent chain schedule keeps a
+ *     workgroup on every CU for the whole call; the library orders such
+ *     launches one after another on each device, whatever their streams.
  */
 #ifndef DOMINO_H
 #define DOMINO_H
@@ -191,7 +193,7 @@ void domino_set_timing_events(void *base_start, void *base_stop, void *chain_sta
 
 /*
  * Chain scheduling.  0 (default): the library picks; for up to 8 sequences
- * one persistent cooperative launch runs all P steps and, for bf16 weights
+ * one persistent launch runs all P steps and, for bf16 weights
  * where it fits, keeps W2 on chip (registers and LDS) for all of them; for
  * more sequences, three kernel launches per step.  1: three launches per
  * step.  2: the persistent launch with W2 read from memory every step.  All
