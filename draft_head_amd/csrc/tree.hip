@@ -234,23 +234,44 @@ __global__ __launch_bounds__(256) void tree_gru(TreeArgs t, int b0) {
   unsigned char* xl = lds + (size_t)kTreeSeqs * Hs * sizeof(double);  // [kTreeSeqs][d] stored type
   if (threadIdx.x < nb) sc[threadIdx.x] = reinterpret_cast<const TreeCur*>(t.cur)[b0 + threadIdx.x];
   __syncthreads();
-  // stage every sequence's parent state and embedding row in one flat pass
+  // stage every sequence's parent state and embedding row: batches of kStage
+  // 16-byte pieces per thread are loaded before any is stored, so their
+  // latencies overlap (a load-store loop would pay one round trip per piece)
   {
+    constexpr int kStage = 8;
     const int hchunks = Hs / 2, xchunks = d * es / 16;  // 16-byte pieces
-    const int per = hchunks + xchunks;
-    for (int i = threadIdx.x; i < nb * per; i += blockDim.x) {
+    const int per = hchunks + xchunks, n = nb * per;
+    auto src_of = [&](int i) -> const uint4* {
       const int s = i / per, q = i - s * per;
       const TreeCur& c = sc[s];
       if (q < hchunks) {
-        double2 v = make_double2(0.0, 0.0);
-        if (c.expand && c.parent_slot >= 0)
-          v = reinterpret_cast<const double2*>(t.states + ((size_t)(b0 + s) * (t.N + 1) + c.parent_slot) * Hs)[q];
-        reinterpret_cast<double2*>(hl + (size_t)s * Hs)[q] = v;
-      } else {
-        const int x = q - hchunks;
-        const unsigned char* xe = (const unsigned char*)t.embed + (size_t)c.token * d * es;
-        *reinterpret_cast<uint4*>(xl + (size_t)s * d * es + (size_t)x * 16) =
-            *reinterpret_cast<const uint4*>(xe + (size_t)x * 16);
+        // a node with no parent state reads slot 0 of its own sequence (zeros are stored instead)
+        const int slot = c.parent_slot >= 0 ? c.parent_slot : 0;
+        return reinterpret_cast<const uint4*>(t.states + ((size_t)(b0 + s) * (t.N + 1) + slot) * Hs) + q;
+      }
+      return reinterpret_cast<const uint4*>((const unsigned char*)t.embed + (size_t)c.token * d * es) + (q - hchunks);
+    };
+    auto dst_of = [&](int i) -> uint4* {
+      const int s = i / per, q = i - s * per;
+      if (q < hchunks) return reinterpret_cast<uint4*>(hl + (size_t)s * Hs) + q;
+      return reinterpret_cast<uint4*>(xl + (size_t)s * d * es) + (q - hchunks);
+    };
+    for (int base = 0; base < n; base += kStage * (int)blockDim.x) {
+      uint4 v[kStage];
+#pragma unroll
+      for (int k = 0; k < kStage; ++k) {
+        const int i = base + k * (int)blockDim.x + threadIdx.x;
+        v[k] = i < n ? *src_of(i) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < kStage; ++k) {
+        const int i = base + k * (int)blockDim.x + threadIdx.x;
+        if (i < n) {
+          const int s = i / per, q = i - s * per;
+          const TreeCur& c = sc[s];
+          const bool zero = q < hchunks && !(c.expand && c.parent_slot >= 0);
+          *dst_of(i) = zero ? make_uint4(0, 0, 0, 0) : v[k];
+        }
       }
     }
   }
@@ -346,7 +367,19 @@ __global__ __launch_bounds__(256) void tree_bottleneck(TreeArgs t) {
   if (!c.expand) return;
   const int Hs = t.Hs;
   const double* st = t.states + ((size_t)b * (t.N + 1) + c.slot) * Hs;
-  for (int i = threadIdx.x; i < Hs; i += blockDim.x) S[i] = st[i];
+  for (int i0 = 0; i0 < Hs; i0 += 4 * (int)blockDim.x) {  // four loads in flight per thread
+    double v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + q * (int)blockDim.x + threadIdx.x;
+      v[q] = i < Hs ? st[i] : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + q * (int)blockDim.x + threadIdx.x;
+      if (i < Hs) S[i] = v[q];
+    }
+  }
   __syncthreads();
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   for (int jj = lane * 8; jj < Hs; jj += 512) {
