@@ -39,11 +39,11 @@ __device__ __forceinline__ float key_value(uint64_t k) {
   return __uint_as_float(u);
 }
 
-// descending bitonic sort of buf[0..kTopCap) by the whole workgroup
-__device__ void bitonic_desc(uint64_t* buf) {
-  for (int size = 2; size <= kTopCap; size <<= 1) {
+// descending bitonic sort of buf[0..n) (n a power of two) by the whole workgroup
+__device__ void bitonic_desc(uint64_t* buf, int n = kTopCap) {
+  for (int size = 2; size <= n; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < kTopCap / 2; i += blockDim.x) {
+      for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
         const bool desc = (lo & size) == 0;
@@ -58,64 +58,130 @@ __device__ void bitonic_desc(uint64_t* buf) {
   }
 }
 
-// Top M keys (value bits, inverted index; key 0 = none) of one row segment.
-// A single pass: keys above the running threshold (the M-th best so far) are
-// appended to an LDS buffer, which is sorted and cut back to M whenever fewer
-// than 1024 slots remain.  The next 1024 elements are loaded while the
-// current ones are filtered.
-__global__ __launch_bounds__(256) void topm_segment(const float* __restrict__ Lb, int V, int M, uint64_t* seg_keys,
-                                                    int32_t* status, int reset_status) {
-  __shared__ uint64_t buf[kTopCap];
-  __shared__ int count;
-  __shared__ uint64_t thresh;
-  const int seg = blockIdx.x, row = blockIdx.y;
-  if (reset_status && seg == 0 && row == 0 && threadIdx.x == 0) *status = 0;
-  const int per = (V + kTopSegs - 1) / kTopSegs;
-  const int v_begin = seg * per, v_end = min(V, v_begin + per);
-  const float* x = Lb + (size_t)row * V;
+// Top M keys (value bits, inverted index; key 0 = none) of the elements
+// [v_begin, v_end) of row x, into out[0..M), in a single pass: keys above the
+// running threshold (the M-th best so far) are appended to an LDS buffer,
+// which is sorted and cut back to M whenever fewer than 1024 slots remain.
+// The fallback of topm_segment for inputs whose threshold estimate admits
+// too many candidates.
+__device__ void topm_scan_iterative(const float* __restrict__ x, int v_begin, int v_end, int M, uint64_t* buf,
+                                    int* count, uint64_t* thresh, uint64_t* out) {
+  __syncthreads();
   if (threadIdx.x == 0) {
-    count = 0;
-    thresh = 0;
+    *count = 0;
+    *thresh = 0;
   }
   for (int i = threadIdx.x; i < kTopCap; i += blockDim.x) buf[i] = 0;
   __syncthreads();
-  float cur[4], nxt[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int v = v_begin + q * 256 + threadIdx.x;
-    cur[q] = v < v_end ? x[v] : 0.f;
-  }
   for (int c0 = v_begin; c0 < v_end; c0 += 1024) {
+    float cur[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int v = c0 + 1024 + q * 256 + threadIdx.x;
-      nxt[q] = v < v_end ? x[v] : 0.f;
+      const int v = c0 + q * 256 + threadIdx.x;
+      cur[q] = x[min(v, v_end - 1)];
     }
-    const uint64_t th = thresh;
+    const uint64_t th = *thresh;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int v = c0 + q * 256 + threadIdx.x;
       if (v < v_end) {
         const uint64_t k = amax_key(cur[q], (uint32_t)v);
-        if (k > th) buf[atomicAdd(&count, 1)] = k;
+        if (k > th) buf[atomicAdd(count, 1)] = k;
       }
     }
     __syncthreads();
-    if (count > kTopCap - 1024) {
+    if (*count > kTopCap - 1024) {
       bitonic_desc(buf);
       if (threadIdx.x == 0) {
-        count = M;
-        thresh = buf[M - 1];
+        *count = M;
+        *thresh = buf[M - 1];
       }
       __syncthreads();
       for (int i = M + threadIdx.x; i < kTopCap; i += blockDim.x) buf[i] = 0;
       __syncthreads();
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
   }
   bitonic_desc(buf);
+  for (int j = threadIdx.x; j < M; j += blockDim.x) out[j] = buf[j];
+}
+
+// Top M keys of one row segment, sorted, key 0 = none.  Two passes over the
+// segment.  Pass 1: every thread's largest key; within each wave the
+// ceil(M/4)-th largest of these maxima is reached by at least ceil(M/4)
+// distinct elements, so the smallest of the four waves' values, tau, is
+// reached by at least M elements and cannot exceed the segment's M-th key.
+// Pass 2 collects every key >= tau (for typical data a few times M), which
+// are then sorted.  More candidates than the LDS buffer holds send the
+// segment to topm_scan_iterative.
+__global__ __launch_bounds__(256) void topm_segment(const float* __restrict__ Lb, int V, int M, uint64_t* seg_keys,
+                                                    int32_t* status, int reset_status) {
+  __shared__ uint64_t buf[kTopCap];
+  __shared__ int count;
+  __shared__ uint64_t thresh;
+  __shared__ uint64_t wq[4];
+  const int seg = blockIdx.x, row = blockIdx.y;
+  if (reset_status && seg == 0 && row == 0 && threadIdx.x == 0) *status = 0;
+  const int per = (V + kTopSegs - 1) / kTopSegs;
+  const int v_begin = seg * per, v_end = min(V, v_begin + per);
+  const float* x = Lb + (size_t)row * V;
   uint64_t* out = seg_keys + ((size_t)row * kTopSegs + seg) * M;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (v_end <= v_begin) {  // empty segment
+    for (int j = threadIdx.x; j < M; j += blockDim.x) out[j] = 0;
+    return;
+  }
+  // pass 1 (loads from clamped addresses, four in flight per thread)
+  uint64_t mk = 0;
+  for (int v0 = v_begin; v0 < v_end; v0 += 4 * 256) {
+    float f[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) f[q] = x[min(v0 + q * 256 + (int)threadIdx.x, v_end - 1)];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v = v0 + q * 256 + threadIdx.x;
+      if (v < v_end) mk = umax64(mk, amax_key(f[q], (uint32_t)v));
+    }
+  }
+  // descending bitonic sort of the 64 maxima across the wave
+  for (int size = 2; size <= 64; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint64_t o = shfl_xor_u64(mk, stride);
+      const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
+      mk = keep_max ? umax64(mk, o) : (mk < o ? mk : o);
+    }
+  const int qm = (M + 3) / 4;  // <= 64
+  const uint64_t wk = ((uint64_t)__shfl((uint32_t)(mk >> 32), qm - 1) << 32) | __shfl((uint32_t)mk, qm - 1);
+  if (lane == 0) wq[wv] = wk;
+  if (threadIdx.x == 0) count = 0;
+  __syncthreads();
+  uint64_t tau = wq[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) tau = wq[w] < tau ? wq[w] : tau;
+  // pass 2: every key >= tau
+  for (int v0 = v_begin; v0 < v_end; v0 += 4 * 256) {
+    float f[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) f[q] = x[min(v0 + q * 256 + (int)threadIdx.x, v_end - 1)];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v = v0 + q * 256 + threadIdx.x;
+      const uint64_t k = amax_key(f[q], (uint32_t)v);
+      if (v < v_end && k >= tau && k != 0) {
+        const int pos = atomicAdd(&count, 1);
+        if (pos < kTopCap) buf[pos] = k;
+      }
+    }
+  }
+  __syncthreads();
+  const int n = count;
+  if (n > kTopCap) {
+    topm_scan_iterative(x, v_begin, v_end, M, buf, &count, &thresh, out);
+    return;
+  }
+  int p2 = 64;
+  while (p2 < n || p2 < M) p2 <<= 1;
+  for (int i = n + threadIdx.x; i < p2; i += blockDim.x) buf[i] = 0;
+  __syncthreads();
+  bitonic_desc(buf, p2);
   for (int j = threadIdx.x; j < M; j += blockDim.x) out[j] = buf[j];
 }
 
@@ -124,9 +190,11 @@ __global__ __launch_bounds__(256) void topm_merge(const uint64_t* seg_keys, int 
   __shared__ uint64_t buf[kTopCap];
   const int row = blockIdx.x;
   const uint64_t* src = seg_keys + (size_t)row * kTopSegs * M;
-  for (int i = threadIdx.x; i < kTopCap; i += blockDim.x) buf[i] = i < kTopSegs * M ? src[i] : 0;
+  int n = 64;  // the segment lists, padded to a power of two
+  while (n < kTopSegs * M) n <<= 1;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) buf[i] = i < kTopSegs * M ? src[i] : 0;
   __syncthreads();
-  bitonic_desc(buf);
+  bitonic_desc(buf, n);
   for (int j = threadIdx.x; j < M; j += blockDim.x) {
     const uint64_t k = buf[j];
     cand_idx[(size_t)row * M + j] = amax_index(k);

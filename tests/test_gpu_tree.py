@@ -111,12 +111,24 @@ def test_tree_full_size():
     _compare(g, o, key)
 
 
-@pytest.mark.parametrize("kind", ["random", "ties", "constant", "ascending", "small_v"])
+@pytest.mark.parametrize("kind", ["random", "ties", "constant", "ascending", "small_v", "wide", "wide_m256",
+                                  "wide_m1", "one_wave_heavy"])
 def test_candidates_match_oracle_topm(kind):
     say(f"case top-M {kind}")
     B, P, V, M = 2, 3, 5003, 64
     rng = np.random.default_rng(5)
-    if kind == "random":
+    if kind.startswith("wide") or kind == "one_wave_heavy":
+        B, P, V = 1, 2, 151936
+        M = {"wide_m256": 256, "wide_m1": 1}.get(kind, 64)
+        Lb = rng.standard_normal((B, P, V)).astype(np.float32)
+        if kind == "one_wave_heavy":
+            # every segment's large values sit on the elements its first wave
+            # scans, so the other waves' thresholds admit too many candidates
+            # and the kernel takes its iterative path
+            per = (V + 7) // 8
+            v = np.arange(V)
+            Lb[:, :, (v - (v // per) * per) % 256 < 64] += 10.0
+    elif kind == "random":
         Lb = rng.standard_normal((B, P, V)).astype(np.float32)
     elif kind == "ties":
         Lb = (np.round(rng.standard_normal((B, P, V)) * 2) / 2).astype(np.float32)
