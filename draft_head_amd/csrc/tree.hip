@@ -284,14 +284,16 @@ __global__ void tree_init(TreeArgs t) {
 }
 
 // ---- fp64 GRU step of each sequence's current node -----------------------------------------
-// Workgroup = 4 GRU units, wave w = unit 4*blockIdx + w.  The current nodes'
-// embedding rows (stored type) and parent states (fp64) of up to kTreeSeqs
-// sequences are staged in LDS; lanes split k in runs of 8 and the 6 partial
-// sums (gi_r, gi_z, gi_n, gh_r, gh_z, gh_n) per sequence are reduced across
-// the wave; lane s finishes sequence s.
+// Workgroup = 4 GRU units and 8 waves: wave w takes unit 4*blockIdx + w % 4
+// for half of the sequences (w / 4 selects which), so a SIMD runs two waves.
+// The current nodes' embedding rows (stored type) and parent states (fp64) of
+// up to kTreeSeqs sequences are staged in LDS; lanes split k in runs of 8 and
+// the 6 partial sums (gi_r, gi_z, gi_n, gh_r, gh_z, gh_n) per sequence are
+// reduced across the wave; lane s finishes the wave's sequence s.
 constexpr int kTreeSeqs = 8;
+constexpr int kSeqPerWave = 4;  // two waves per GRU unit, each with half of the sequences
 
-__global__ __launch_bounds__(256) void tree_gru(TreeArgs t, int b0) {
+__global__ __launch_bounds__(512) void tree_gru(TreeArgs t, int b0) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ TreeCur sc[kTreeSeqs];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -344,18 +346,19 @@ __global__ __launch_bounds__(256) void tree_gru(TreeArgs t, int b0) {
     }
   }
   __syncthreads();
-  const int j = blockIdx.x * 4 + wv;
+  // wave wv: unit blockIdx * 4 + wv % 4, sequences s0 .. s0 + kSeqPerWave - 1
+  const int j = blockIdx.x * 4 + (wv & 3), s0 = (wv >> 2) * kSeqPerWave;
   if (j >= Hs) return;
-  int expand[kTreeSeqs];
+  int expand[kSeqPerWave];
 #pragma unroll
-  for (int s = 0; s < kTreeSeqs; ++s) expand[s] = s < nb ? sc[s].expand : 0;
-  double acc[kTreeSeqs][6];
+  for (int s = 0; s < kSeqPerWave; ++s) expand[s] = s0 + s < nb ? sc[s0 + s].expand : 0;
+  double acc[kSeqPerWave][6];
 #pragma unroll
-  for (int s = 0; s < kTreeSeqs; ++s)
+  for (int s = 0; s < kSeqPerWave; ++s)
 #pragma unroll
     for (int g = 0; g < 6; ++g) acc[s][g] = 0.0;
-  // input half, four 8-wide runs of every gate row in flight at a time
-  constexpr int R = 4;
+  // input half, R 8-wide runs of every gate row in flight at a time
+  constexpr int R = 2;
   for (int k0 = lane * 8; k0 < d; k0 += 512 * R) {
     double w[R][3][8];
 #pragma unroll
@@ -367,10 +370,10 @@ __global__ __launch_bounds__(256) void tree_gru(TreeArgs t, int b0) {
     for (int u = 0; u < R; ++u) {
       if (k0 + u * 512 >= d) break;
 #pragma unroll
-      for (int s = 0; s < kTreeSeqs; ++s) {
+      for (int s = 0; s < kSeqPerWave; ++s) {
         if (!expand[s]) continue;
         double x[8];
-        load8_f64(xl + (size_t)s * d * es, t.dtype, k0 + u * 512, x);
+        load8_f64(xl + (size_t)(s0 + s) * d * es, t.dtype, k0 + u * 512, x);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
 #pragma unroll
@@ -389,11 +392,11 @@ __global__ __launch_bounds__(256) void tree_gru(TreeArgs t, int b0) {
     for (int u = 0; u < R; ++u) {
       if (k0 + u * 512 >= Hs) break;
 #pragma unroll
-      for (int s = 0; s < kTreeSeqs; ++s) {
+      for (int s = 0; s < kSeqPerWave; ++s) {
         if (!expand[s]) continue;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const double h = hl[(size_t)s * Hs + k0 + u * 512 + e];
+          const double h = hl[(size_t)(s0 + s) * Hs + k0 + u * 512 + e];
 #pragma unroll
           for (int g = 0; g < 3; ++g) acc[s][3 + g] += w[u][g][e] * h;
         }
@@ -401,27 +404,28 @@ __global__ __launch_bounds__(256) void tree_gru(TreeArgs t, int b0) {
     }
   }
 #pragma unroll
-  for (int s = 0; s < kTreeSeqs; ++s)
+  for (int s = 0; s < kSeqPerWave; ++s)
 #pragma unroll
     for (int g = 0; g < 6; ++g) acc[s][g] = wave_sum(acc[s][g]);
   double a6[6] = {0, 0, 0, 0, 0, 0};
   int mine = 0;
 #pragma unroll
-  for (int s = 0; s < kTreeSeqs; ++s)
+  for (int s = 0; s < kSeqPerWave; ++s)
     if (s == lane) {
       mine = expand[s];
 #pragma unroll
       for (int g = 0; g < 6; ++g) a6[g] = acc[s][g];
     }
-  if (lane < nb && mine) {
-    const TreeCur c = sc[lane];
+  const int sq = s0 + lane;  // the sequence this lane finishes
+  if (lane < kSeqPerWave && sq < nb && mine) {
+    const TreeCur c = sc[sq];
     auto bi = [&](int row) { return t.b_ih ? (double)t.b_ih[row] : 0.0; };
     auto bh = [&](int row) { return t.b_hh ? (double)t.b_hh[row] : 0.0; };
     const double r = 1.0 / (1.0 + exp(-(a6[0] + bi(j) + a6[3] + bh(j))));
     const double z = 1.0 / (1.0 + exp(-(a6[1] + bi(Hs + j) + a6[4] + bh(Hs + j))));
     const double nn = tanh(a6[2] + bi(2 * Hs + j) + r * (a6[5] + bh(2 * Hs + j)));
-    const double hprev = hl[(size_t)lane * Hs + j];
-    t.states[((size_t)(b0 + lane) * (t.N + 1) + c.slot) * Hs + j] = (1.0 - z) * nn + z * hprev;
+    const double hprev = hl[(size_t)sq * Hs + j];
+    t.states[((size_t)(b0 + sq) * (t.N + 1) + c.slot) * Hs + j] = (1.0 - z) * nn + z * hprev;
   }
 }
 
@@ -697,7 +701,7 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
   }
   for (int k = 0; k < t.N; ++k) {
     for (int b0 = 0; b0 < t.B; b0 += kTreeSeqs)
-      hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(256), lds, s, t, b0);
+      hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(64 * 4 * (kTreeSeqs / kSeqPerWave)), lds, s, t, b0);
     hipLaunchKernelGGL(tree_bottleneck, dim3((t.r + 15) / 16, t.B), dim3(256), 0, s, t);
     hipLaunchKernelGGL(tree_score_pop, dim3(t.B), dim3(256), 0, s, t, k);
   }
