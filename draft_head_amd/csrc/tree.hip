@@ -284,16 +284,17 @@ __global__ void tree_init(TreeArgs t) {
 }
 
 // ---- fp64 GRU step of each sequence's current node -----------------------------------------
-// Workgroup = 4 GRU units and 8 waves: wave w takes unit 4*blockIdx + w % 4
-// for half of the sequences (w / 4 selects which), so a SIMD runs two waves.
+// Workgroup = 4 GRU units and 16 waves: wave w takes unit 4*blockIdx + w % 4
+// for a quarter of the sequences (w / 4 selects which), so a SIMD runs four
+// waves.
 // The current nodes' embedding rows (stored type) and parent states (fp64) of
 // up to kTreeSeqs sequences are staged in LDS; lanes split k in runs of 8 and
 // the 6 partial sums (gi_r, gi_z, gi_n, gh_r, gh_z, gh_n) per sequence are
 // reduced across the wave; lane s finishes the wave's sequence s.
 constexpr int kTreeSeqs = 8;
-constexpr int kSeqPerWave = 4;  // two waves per GRU unit, each with half of the sequences
+constexpr int kSeqPerWave = 2;  // four waves per GRU unit, each with a quarter of the sequences
 
-__global__ __launch_bounds__(512) void tree_gru(TreeArgs t, int b0) {
+__global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ TreeCur sc[kTreeSeqs];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(512) void tree_gru(TreeArgs t, int b0) {
   }
   __syncthreads();
   // wave wv: unit blockIdx * 4 + wv % 4, sequences s0 .. s0 + kSeqPerWave - 1
-  const int j = blockIdx.x * 4 + (wv & 3), s0 = (wv >> 2) * kSeqPerWave;
+  const int j = blockIdx.x * 4 + (wv & 3), s0 = (wv >> 2) * kSeqPerWave;  // waves 4q .. 4q+3: quarter q
   if (j >= Hs) return;
   int expand[kSeqPerWave];
 #pragma unroll
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(512) void tree_gru(TreeArgs t, int b0) {
 #pragma unroll
     for (int g = 0; g < 6; ++g) acc[s][g] = 0.0;
   // input half, R 8-wide runs of every gate row in flight at a time
-  constexpr int R = 2;
+  constexpr int R = 1;
   for (int k0 = lane * 8; k0 < d; k0 += 512 * R) {
     double w[R][3][8];
 #pragma unroll
