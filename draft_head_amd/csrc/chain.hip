@@ -539,14 +539,15 @@ __device__ __forceinline__ void stage_w1_slice(const ChainArgs& a, int item, W* 
 struct BottleneckPre {
   float4 zh, b1;
 };
+// (sequences seq0 .. seq0 + 16 NCB - 1)
 template <int NCB>
-__device__ __forceinline__ BottleneckPre bottleneck_pre(const ChainArgs& a, int p, int item) {
+__device__ __forceinline__ BottleneckPre bottleneck_pre(const ChainArgs& a, int p, int item, int seq0 = 0) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   BottleneckPre q;
   q.zh = make_float4(0.f, 0.f, 0.f, 0.f);
   q.b1 = q.zh;
-  const int b = wv * 16 + row, k = item * 16 + kg * 4;
+  const int b = seq0 + wv * 16 + row, k = item * 16 + kg * 4;
   if (wv < NCB && b < a.B && k < a.r) {  // r is a multiple of 8: k..k+3 are valid together
     q.zh = *reinterpret_cast<const float4*>(&a.zh[((size_t)b * a.P + p) * a.r + k]);
     if (a.b1) q.b1 = *reinterpret_cast<const float4*>(&a.b1[k]);
@@ -559,7 +560,8 @@ __device__ __forceinline__ BottleneckPre bottleneck_pre(const ChainArgs& a, int 
 // words once and the waves read their fragments from there.
 template <class W, int NCB, bool kLdsW, bool kLL = false>
 __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int item, float* red, const W* w1_lds,
-                                const BottleneckPre& pre_terms, uint32_t ep = 0, uint32_t* h_s = nullptr) {
+                                const BottleneckPre& pre_terms, uint32_t ep = 0, uint32_t* h_s = nullptr,
+                                int seq0 = 0) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int Hs = a.Hs, B = a.B, r = a.r;
@@ -573,7 +575,7 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
   bool bok[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    const int b = cb * 16 + row;
+    const int b = seq0 + cb * 16 + row;
     bok[cb] = b < B;
     bb[cb] = bok[cb] ? b : 0;
   }
@@ -638,7 +640,7 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
       pre[2] += v.z;
       pre[3] += v.w;
     }
-    const int b = cb * 16 + row, k = k0 + kg * 4;
+    const int b = seq0 + cb * 16 + row, k = k0 + kg * 4;
     if (b < B && k < r) {  // r is a multiple of 8, so k..k+3 are all valid
       float s[4];
 #pragma unroll
@@ -1266,10 +1268,12 @@ __global__ __launch_bounds__(256) void chain_gru_k(ChainArgs a, int p) {
 }
 
 template <class W, int NCB>
+// (blockIdx.y: the block of 16 NCB sequences)
 __global__ __launch_bounds__(256) void chain_bottleneck_k(ChainArgs a, int p) {
   __shared__ __attribute__((aligned(16))) float red[4 * NCB * 64 * 4];
+  const int seq0 = blockIdx.y * 16 * NCB;
   for (int it = blockIdx.x; it < (a.r + 15) / 16; it += gridDim.x)
-    bottleneck_item<W, NCB, false>(a, p, it, red, nullptr, bottleneck_pre<NCB>(a, p, it));
+    bottleneck_item<W, NCB, false>(a, p, it, red, nullptr, bottleneck_pre<NCB>(a, p, it, seq0), 0u, nullptr, seq0);
 }
 
 template <class W, int RG, int KC>
@@ -1566,7 +1570,8 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
   const int nO = T < cus ? T : (cus > 0 ? cus : 256);
   for (int p = 0; p < a.P; ++p) {
     hipLaunchKernelGGL((chain_gru_k<W, NCB>), dim3(nG), dim3(256), 0, s, a, p);
-    hipLaunchKernelGGL((chain_bottleneck_k<W, NCB>), dim3(nW), dim3(256), 0, s, a, p);
+    // one workgroup per 16 rows and 16 sequences: more CUs share the state reads
+    hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 15) / 16), dim3(256), 0, s, a, p);
     constexpr int NWV = RG * KC >= 16 ? 8 : 16;  // waves per CU, as registers allow
     if constexpr (sizeof(W) == 2)  // bf16: many light waves per CU
       hipLaunchKernelGGL((chain_logits_wide_k<W, RG, KC, NWV>), dim3(nO), dim3(64 * NWV), 0, s, a, p);
