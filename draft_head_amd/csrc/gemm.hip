@@ -89,10 +89,10 @@ __global__ __launch_bounds__(256) void gemm_stream(const W* __restrict__ A, int 
 }
 
 #ifndef DH_R16_WAVES
-#define DH_R16_WAVES 8  // waves per workgroup of gemm_rows16
+#define DH_R16_WAVES 16  // waves per workgroup of gemm_rows16
 #endif
 #ifndef DH_R16_U
-#define DH_R16_U 8      // k chunks per batch of loads in gemm_rows16
+#define DH_R16_U 2       // k chunks per batch of loads in gemm_rows16
 #endif
 
 // At most 16 rows of A (one draft block of one sequence): the product is
