@@ -254,7 +254,7 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   if (topm < 1 || topm > 256) return fail(DOMINO_ERR_INVALID_ARGUMENT, "topm %d must be in [1, 256]", topm);
   if (topm > dims->vocab) return fail(DOMINO_ERR_INVALID_ARGUMENT, "topm %d exceeds the vocabulary", topm);
   if (dims->gru_hidden > 4096) return fail(DOMINO_ERR_UNSUPPORTED, "gru_hidden %d exceeds 4096 for the tree", dims->gru_hidden);
-  if (dh::tree_gru_lds(dims->hidden, dims->gru_hidden, dims->dtype) > 156 * 1024)
+  if (dh::tree_gru_lds_total(dims->hidden, dims->gru_hidden, dims->dtype) > 160 * 1024)
     return fail(DOMINO_ERR_UNSUPPORTED, "hidden %d with gru_hidden %d exceeds the tree's LDS budget", dims->hidden,
                 dims->gru_hidden);
   if (batch == 0) return ok();

@@ -116,6 +116,7 @@ TreeLayout tree_layout(int d, int Hs, int r, int P, int group, int N, int M);
 hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 // dynamic LDS of the tree's GRU kernel (must stay within the CU's 160 KB)
 size_t tree_gru_lds(int d, int Hs, int dtype);
+size_t tree_gru_lds_total(int d, int Hs, int dtype);  // the GRU step's whole LDS (160 KB per CU)
 // top-M of each of `rows` rows of length V, ordered (value desc, index asc);
 // scratch holds topm_scratch_bytes(rows, M)
 size_t topm_scratch_bytes(int rows, int M);

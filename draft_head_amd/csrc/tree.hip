@@ -430,6 +430,175 @@ __global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0) {
   }
 }
 
+// ---- the same GRU step on the fp64 matrix cores (bf16 weights) ----------------------------
+// Workgroup = 4 GRU units.  The MFMA's 16 rows are the r, z and n rows of
+// those units (rows 12..15 repeat row 11; their results are not used) and its
+// 16 columns the sequences (columns past the last repeat it, unused).  The k
+// range runs in 32-wide blocks dealt to the 8 waves in turn; in a block, lane
+// l holds 8 consecutive k values, 8 (l / 16) + 0..7, of its row and column,
+// and MFMA i of the block takes value i of every lane, so the 8 MFMAs cover
+// the block's 32 k values (4 each).  The input half (W_ih E[token]) and the
+// hidden half (W_hh h) have their own accumulators; the waves' partial sums
+// meet in LDS, in wave order, and 32 threads finish (unit, sequence) pairs.
+// Staged rows are padded (16 bytes per embedding row, 64 per state row) so
+// that the 16 columns of one fragment read fall in distinct banks.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__host__ __device__ inline int tree_x_stride(int d) { return d + 8; }     // bf16 elements
+__host__ __device__ inline int tree_h_stride(int Hs) { return Hs + 8; }   // doubles
+
+__device__ __forceinline__ void bf16x8_to_f64(const uint4& r, double (&o)[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[2 * e] = (double)__uint_as_float(w[e] << 16);
+    o[2 * e + 1] = (double)__uint_as_float(w[e] & 0xFFFF0000u);
+  }
+}
+
+constexpr int kGruWaves = 8;  // waves of tree_gru_mfma, splitting the k blocks
+
+__global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int b0) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  __shared__ TreeCur sc[kTreeSeqs];
+  __shared__ double red[kGruWaves][2][12][kTreeSeqs];  // [wave][input, hidden][gate row][sequence]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int d = t.d, Hs = t.Hs;
+  const int nb = min(kTreeSeqs, t.B - b0);
+  const int xs = tree_x_stride(d), hs = tree_h_stride(Hs);
+  double* hl = reinterpret_cast<double*>(lds);                                  // [kTreeSeqs][hs]
+  uint16_t* xl = reinterpret_cast<uint16_t*>(lds + (size_t)kTreeSeqs * hs * 8);  // [kTreeSeqs][xs]
+  if (threadIdx.x < nb) sc[threadIdx.x] = reinterpret_cast<const TreeCur*>(t.cur)[b0 + threadIdx.x];
+  __syncthreads();
+  // stage the parent states (zeros where there is none) and the embedding rows
+  {
+    constexpr int kStage = 8;
+    const int hchunks = Hs / 2, xchunks = d / 8;  // 16-byte pieces
+    const int per = hchunks + xchunks, n = nb * per;
+    for (int base = 0; base < n; base += kStage * (int)blockDim.x) {
+      uint4 v[kStage];
+#pragma unroll
+      for (int k = 0; k < kStage; ++k) {
+        const int i = min(base + k * (int)blockDim.x + (int)threadIdx.x, n - 1);
+        const int sq = i / per, q = i - sq * per;
+        const TreeCur& c = sc[sq];
+        const uint4* src;
+        if (q < hchunks) {
+          const int slot = c.parent_slot >= 0 ? c.parent_slot : 0;
+          src = reinterpret_cast<const uint4*>(t.states + ((size_t)(b0 + sq) * (t.N + 1) + slot) * Hs) + q;
+        } else {
+          src = reinterpret_cast<const uint4*>((const uint16_t*)t.embed + (size_t)c.token * d) + (q - hchunks);
+        }
+        v[k] = *src;
+      }
+#pragma unroll
+      for (int k = 0; k < kStage; ++k) {
+        const int i = base + k * (int)blockDim.x + threadIdx.x;
+        if (i < n) {
+          const int sq = i / per, q = i - sq * per;
+          const TreeCur& c = sc[sq];
+          if (q < hchunks) {
+            const bool zero = !(c.expand && c.parent_slot >= 0);
+            *reinterpret_cast<uint4*>(hl + (size_t)sq * hs + 2 * q) = zero ? make_uint4(0, 0, 0, 0) : v[k];
+          } else {
+            *reinterpret_cast<uint4*>(xl + (size_t)sq * xs + 8 * (q - hchunks)) = v[k];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int j0 = blockIdx.x * 4;
+  const int rr = lane & 15, kq = lane >> 4;  // A row and B column; k group
+  const int g = rr < 12 ? rr >> 2 : 2, u = rr < 12 ? rr & 3 : 3;
+  const size_t wrow = (size_t)g * Hs + min(j0 + u, Hs - 1);
+  const int sq = min(rr, nb - 1);
+  // two accumulators per half (even and odd blocks of a batch), summed at the end
+  f64x4 acc_i[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  f64x4 acc_h[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  constexpr int NB = 4;  // blocks whose weights are in flight together
+  const uint16_t* wi = (const uint16_t*)t.w_ih + wrow * d;
+  const uint16_t* xr = xl + (size_t)sq * xs;
+  const int nbi = (d + 31) / 32, nbh = (Hs + 31) / 32;
+  for (int b0k = wv; b0k < nbi; b0k += kGruWaves * NB) {
+    uint4 wr[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int k = (b0k + kGruWaves * q) * 32 + 8 * kq;
+      wr[q] = *reinterpret_cast<const uint4*>(wi + min(k, d - 8));
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int k = (b0k + kGruWaves * q) * 32 + 8 * kq;
+      const bool ok = k < d;
+      double w8[8], x8[8];
+      bf16x8_to_f64(wr[q], w8);
+      bf16x8_to_f64(*reinterpret_cast<const uint4*>(xr + (ok ? k : 0)), x8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc_i[q & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w8[i], ok ? x8[i] : 0.0, acc_i[q & 1], 0, 0, 0);
+    }
+  }
+  const uint16_t* wh = (const uint16_t*)t.w_hh + wrow * Hs;
+  const double* hr = hl + (size_t)sq * hs;
+  for (int b0k = wv; b0k < nbh; b0k += kGruWaves * NB) {
+    uint4 wr[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int k = (b0k + kGruWaves * q) * 32 + 8 * kq;
+      wr[q] = *reinterpret_cast<const uint4*>(wh + min(k, Hs - 8));
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int k = (b0k + kGruWaves * q) * 32 + 8 * kq;
+      const bool ok = k < Hs;
+      const int kc = ok ? k : 0;
+      double w8[8];
+      bf16x8_to_f64(wr[q], w8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc_h[q & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w8[i], ok ? hr[kc + i] : 0.0, acc_h[q & 1], 0, 0, 0);
+    }
+  }
+  // result layout of the fp64 MFMA: register i of lane l holds row 4 i + l / 16 of column l % 16
+  if (rr < kTreeSeqs) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {  // rows 12..15 (i = 3) are padding
+      red[wv][0][4 * i + kq][rr] = acc_i[0][i] + acc_i[1][i];
+      red[wv][1][4 * i + kq][rr] = acc_h[0][i] + acc_h[1][i];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 4 * kTreeSeqs) {
+    const int uu = threadIdx.x / kTreeSeqs, s = threadIdx.x % kTreeSeqs, j = j0 + uu;
+    if (s < nb && j < Hs && sc[s].expand) {
+      double gi[3], gh[3];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        gi[q] = red[0][0][4 * q + uu][s];
+        gh[q] = red[0][1][4 * q + uu][s];
+#pragma unroll
+        for (int w = 1; w < kGruWaves; ++w) {
+          gi[q] += red[w][0][4 * q + uu][s];
+          gh[q] += red[w][1][4 * q + uu][s];
+        }
+      }
+      const TreeCur c = sc[s];
+      auto bi = [&](int row) { return t.b_ih ? (double)t.b_ih[row] : 0.0; };
+      auto bh = [&](int row) { return t.b_hh ? (double)t.b_hh[row] : 0.0; };
+      const double r = 1.0 / (1.0 + exp(-(gi[0] + bi(j) + gh[0] + bh(j))));
+      const double z = 1.0 / (1.0 + exp(-(gi[1] + bi(Hs + j) + gh[1] + bh(Hs + j))));
+      const double nn = tanh(gi[2] + bi(2 * Hs + j) + r * (gh[2] + bh(2 * Hs + j)));
+      const double hprev = hl[(size_t)s * hs + j];
+      t.states[((size_t)(b0 + s) * (t.N + 1) + c.slot) * Hs + j] = (1.0 - z) * nn + z * hprev;
+    }
+  }
+}
+
+size_t tree_gru_mfma_lds(int d, int Hs) {
+  return (size_t)kTreeSeqs * tree_h_stride(Hs) * 8 + (size_t)kTreeSeqs * tree_x_stride(d) * 2;
+}
+
 // ---- fp64 bottleneck of each sequence's current node: a = SiLU(W1 [H_delta ; S] + b1) -------
 // Workgroup = 16 bottleneck units of one sequence; wave w takes 4, lanes split Hs.
 __global__ __launch_bounds__(256) void tree_bottleneck(TreeArgs t) {
@@ -681,6 +850,13 @@ hipError_t launch_topm(const float* Lb, int rows, int V, int M, void* scratch, i
   return launch_topm_impl(Lb, rows, V, M, (uint64_t*)scratch, idx, val, nullptr, false, s);
 }
 
+// LDS of the GRU-step kernel that runs for this storage type, static part included
+size_t tree_gru_lds_total(int d, int Hs, int dtype) {
+  if (dtype == kBF16)
+    return tree_gru_mfma_lds(d, Hs) + sizeof(double) * kGruWaves * 2 * 12 * kTreeSeqs + sizeof(TreeCur) * kTreeSeqs;
+  return tree_gru_lds(d, Hs, dtype) + sizeof(TreeCur) * kTreeSeqs;
+}
+
 size_t tree_gru_lds(int d, int Hs, int dtype) {
   return (size_t)kTreeSeqs * Hs * sizeof(double) + (size_t)kTreeSeqs * d * (dtype == kBF16 ? 2 : 4);
 }
@@ -693,16 +869,23 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(tree_zh, dim3((t.r + 15) / 16, t.B * t.P), dim3(256), 0, s, t);
   hipLaunchKernelGGL(tree_init, dim3((t.B + 255) / 256), dim3(256), 0, s, t);
-  const size_t lds = tree_gru_lds(t.d, t.Hs, t.dtype);
-  static thread_local size_t attr_lds = 0;
-  if (lds > attr_lds) {
-    e = hipFuncSetAttribute((const void*)tree_gru, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // bf16 weights: the GRU step on the fp64 matrix cores
+  const bool mfma = t.dtype == kBF16;
+  const size_t lds = mfma ? tree_gru_mfma_lds(t.d, t.Hs) : tree_gru_lds(t.d, t.Hs, t.dtype);
+  static thread_local size_t attr_lds[2] = {0, 0};
+  if (lds > attr_lds[mfma]) {
+    e = hipFuncSetAttribute(mfma ? (const void*)tree_gru_mfma : (const void*)tree_gru,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_lds = lds;
+    attr_lds[mfma] = lds;
   }
   for (int k = 0; k < t.N; ++k) {
-    for (int b0 = 0; b0 < t.B; b0 += kTreeSeqs)
-      hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(64 * 4 * (kTreeSeqs / kSeqPerWave)), lds, s, t, b0);
+    for (int b0 = 0; b0 < t.B; b0 += kTreeSeqs) {
+      if (mfma)
+        hipLaunchKernelGGL(tree_gru_mfma, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), lds, s, t, b0);
+      else
+        hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(64 * 4 * (kTreeSeqs / kSeqPerWave)), lds, s, t, b0);
+    }
     hipLaunchKernelGGL(tree_bottleneck, dim3((t.r + 15) / 16, t.B), dim3(256), 0, s, t);
     hipLaunchKernelGGL(tree_score_pop, dim3(t.B), dim3(256), 0, s, t, k);
   }
