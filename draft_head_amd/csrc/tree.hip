@@ -646,10 +646,35 @@ __global__ __launch_bounds__(256) void tree_bottleneck(TreeArgs t) {
 }
 
 // ---- score the current node's children, push them, pop the best entry ----------------------
-__device__ __forceinline__ bool entry_before(double sa, int4 ma, double sb, int4 mb) {
-  if (sa != sb) return sa > sb;
-  if (ma.x != mb.x) return ma.x < mb.x;  // parent index
-  return ma.y < mb.y;                    // candidate rank
+// Heap order: higher score first, then lower parent index, then lower
+// candidate rank.  The running best of a scan is kept without branches: the
+// comparison is evaluated with bitwise logic and every field is replaced
+// through a select.  The empty state (score -inf, parent and rank INT_MAX) loses to any real entry.  A
+// divergent `if (first || before) { copy the whole entry }` was compiled into
+// code that kept the old token and depth on one of the two paths into the
+// copy, so the form below is used wherever the entry's meta is consumed.
+struct BestEntry {
+  int slot;
+  double s;
+  int4 m;
+};
+
+__device__ __forceinline__ BestEntry best_empty() {
+  BestEntry e;
+  e.slot = -1;
+  e.s = -INFINITY;
+  e.m = make_int4(INT_MAX, INT_MAX, 0, 0);
+  return e;
+}
+
+__device__ __forceinline__ void best_offer(BestEntry& e, int slot, double s, int4 m) {
+  const bool take = (s > e.s) | ((s == e.s) & ((m.x < e.m.x) | ((m.x == e.m.x) & (m.y < e.m.y))));
+  e.slot = take ? slot : e.slot;
+  e.s = take ? s : e.s;
+  e.m.x = take ? m.x : e.m.x;
+  e.m.y = take ? m.y : e.m.y;
+  e.m.z = take ? m.z : e.m.z;
+  e.m.w = take ? m.w : e.m.w;
 }
 
 // One workgroup per sequence.  Wave w scores candidates w, w+4, ...: lanes
@@ -660,6 +685,7 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
   __shared__ double l[256];    // corrected candidate logits (M <= 256)
   __shared__ double red_s[256];
   __shared__ int red_i[256];
+  __shared__ int4 red_m[256];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = t.r, M = t.M, P = t.P;
   TreeCur* curp = reinterpret_cast<TreeCur*>(t.cur) + b;
@@ -667,6 +693,11 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
   double* hs = t.heap_score + (size_t)b * t.heap_cap;
   int4* hm = t.heap_meta + (size_t)b * t.heap_cap;
   int count = t.heap_count[b];
+  // each thread's best among the entries already on the heap, read before the
+  // scoring so that no read has to follow the pushes (the heap order is a strict
+  // total order, so the scan order does not matter)
+  BestEntry best = best_empty();
+  for (int i = tid; i < count; i += blockDim.x) best_offer(best, i, hs[i], hm[i]);
 
   if (c.expand) {
     const int delta = c.depth;
@@ -729,39 +760,32 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
     __syncthreads();
     const double lse = red_s[0];
     for (int j = tid; j < M; j += blockDim.x) {
-      hs[count + j] = c.score + (l[j] - lse);
-      hm[count + j] = make_int4(c.node, j, cidx[j], delta + 1);
+      const double sj = c.score + (l[j] - lse);
+      const int4 mj = make_int4(c.node, j, cidx[j], delta + 1);
+      hs[count + j] = sj;
+      hm[count + j] = mj;
+      best_offer(best, count + j, sj, mj);
     }
     count += M;
-    __syncthreads();
+    __syncthreads();  // every thread has read lse (red_s[0]) before the reduction reuses red_s
   }
 
   // pop: best entry under (score desc, parent asc, rank asc)
-  int best = -1;
-  double bs = 0.0;
-  int4 bm = make_int4(0, 0, 0, 0);
-  for (int i = tid; i < count; i += blockDim.x) {
-    const double s = hs[i];
-    const int4 m = hm[i];
-    if (best < 0 || entry_before(s, m, bs, bm)) {
-      best = i;
-      bs = s;
-      bm = m;
-    }
-  }
-  red_i[tid] = best;
-  red_s[tid] = bs;
+  // tree reduction over the threads' bests, entirely in LDS (score, meta, slot)
+  red_i[tid] = best.slot;
+  red_s[tid] = best.s;
+  red_m[tid] = best.m;
   __syncthreads();
   for (int half = blockDim.x / 2; half > 0; half >>= 1) {
     if (tid < half) {
-      const int o = red_i[tid + half];
-      if (o >= 0) {
-        const int me = red_i[tid];
-        if (me < 0 || entry_before(red_s[tid + half], hm[o], red_s[tid], hm[me])) {
-          red_i[tid] = o;
-          red_s[tid] = red_s[tid + half];
-        }
-      }
+      BestEntry e;
+      e.slot = red_i[tid];
+      e.s = red_s[tid];
+      e.m = red_m[tid];
+      best_offer(e, red_i[tid + half], red_s[tid + half], red_m[tid + half]);
+      red_i[tid] = e.slot;
+      red_s[tid] = e.s;
+      red_m[tid] = e.m;
     }
     __syncthreads();
   }
@@ -782,8 +806,8 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
       if (t.out_depth) t.out_depth[o] = 0;
       if (t.out_scores) t.out_scores[o] = -INFINITY;
     } else {
-      const double s = hs[bi];
-      const int4 m = hm[bi];
+      const double s = red_s[0];
+      const int4 m = red_m[0];
       t.out_parents[o] = m.x;
       t.out_tokens[o] = m.z;
       if (t.out_depth) t.out_depth[o] = m.w;
