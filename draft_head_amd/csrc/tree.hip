@@ -437,15 +437,14 @@ __global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0) {
 // range runs in 32-wide blocks dealt to the 8 waves in turn; in a block, lane
 // l holds 8 consecutive k values, 8 (l / 16) + 0..7, of its row and column,
 // and MFMA i of the block takes value i of every lane, so the 8 MFMAs cover
-// the block's 32 k values (4 each).  The input half (W_ih E[token]) and the
-// hidden half (W_hh h) have their own accumulators; the waves' partial sums
-// meet in LDS, in wave order, and 32 threads finish (unit, sequence) pairs.
-// Staged rows are padded (16 bytes per embedding row, 64 per state row) so
-// that the 16 columns of one fragment read fall in distinct banks.
+// the block's 32 k values (4 each).  Each lane reads its own operands (weight
+// row, embedding row or parent state of its column) straight from memory:
+// nothing is staged, so the matrix cores start as soon as the first block
+// lands and the only barrier is the one before the cross-wave sum.  The
+// input half (W_ih E[token]) and the hidden half (W_hh h) have their own
+// accumulators; the waves' partial sums meet in LDS, in wave order, and 32
+// threads finish (unit, sequence) pairs.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
-
-__host__ __device__ inline int tree_x_stride(int d) { return d + 8; }     // bf16 elements
-__host__ __device__ inline int tree_h_stride(int Hs) { return Hs + 8; }   // doubles
 
 __device__ __forceinline__ void bf16x8_to_f64(const uint4& r, double (&o)[8]) {
   const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -456,108 +455,128 @@ __device__ __forceinline__ void bf16x8_to_f64(const uint4& r, double (&o)[8]) {
   }
 }
 
+struct F64x8 {
+  double v[8];
+};
+
+__device__ __forceinline__ F64x8 load_f64x8(const double* p) {
+  F64x8 r;
+  const double4* q = reinterpret_cast<const double4*>(p);
+  const double4 a = q[0], b = q[1];
+  r.v[0] = a.x, r.v[1] = a.y, r.v[2] = a.z, r.v[3] = a.w;
+  r.v[4] = b.x, r.v[5] = b.y, r.v[6] = b.z, r.v[7] = b.w;
+  return r;
+}
+
 constexpr int kGruWaves = 8;  // waves of tree_gru_mfma, splitting the k blocks
+constexpr int kGruPreI = 10;  // input-half blocks per wave whose loads are all issued up front
+constexpr int kGruPreH = 4;   // hidden-half blocks per wave whose loads are all issued up front
 
 __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int b0) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  __shared__ TreeCur sc[kTreeSeqs];
   __shared__ double red[kGruWaves][2][12][kTreeSeqs];  // [wave][input, hidden][gate row][sequence]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int d = t.d, Hs = t.Hs;
   const int nb = min(kTreeSeqs, t.B - b0);
-  const int xs = tree_x_stride(d), hs = tree_h_stride(Hs);
-  double* hl = reinterpret_cast<double*>(lds);                                  // [kTreeSeqs][hs]
-  uint16_t* xl = reinterpret_cast<uint16_t*>(lds + (size_t)kTreeSeqs * hs * 8);  // [kTreeSeqs][xs]
-  if (threadIdx.x < nb) sc[threadIdx.x] = reinterpret_cast<const TreeCur*>(t.cur)[b0 + threadIdx.x];
-  __syncthreads();
-  // stage the parent states (zeros where there is none) and the embedding rows
-  {
-    constexpr int kStage = 8;
-    const int hchunks = Hs / 2, xchunks = d / 8;  // 16-byte pieces
-    const int per = hchunks + xchunks, n = nb * per;
-    for (int base = 0; base < n; base += kStage * (int)blockDim.x) {
-      uint4 v[kStage];
-#pragma unroll
-      for (int k = 0; k < kStage; ++k) {
-        const int i = min(base + k * (int)blockDim.x + (int)threadIdx.x, n - 1);
-        const int sq = i / per, q = i - sq * per;
-        const TreeCur& c = sc[sq];
-        const uint4* src;
-        if (q < hchunks) {
-          const int slot = c.parent_slot >= 0 ? c.parent_slot : 0;
-          src = reinterpret_cast<const uint4*>(t.states + ((size_t)(b0 + sq) * (t.N + 1) + slot) * Hs) + q;
-        } else {
-          src = reinterpret_cast<const uint4*>((const uint16_t*)t.embed + (size_t)c.token * d) + (q - hchunks);
-        }
-        v[k] = *src;
-      }
-#pragma unroll
-      for (int k = 0; k < kStage; ++k) {
-        const int i = base + k * (int)blockDim.x + threadIdx.x;
-        if (i < n) {
-          const int sq = i / per, q = i - sq * per;
-          const TreeCur& c = sc[sq];
-          if (q < hchunks) {
-            const bool zero = !(c.expand && c.parent_slot >= 0);
-            *reinterpret_cast<uint4*>(hl + (size_t)sq * hs + 2 * q) = zero ? make_uint4(0, 0, 0, 0) : v[k];
-          } else {
-            *reinterpret_cast<uint4*>(xl + (size_t)sq * xs + 8 * (q - hchunks)) = v[k];
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
   const int j0 = blockIdx.x * 4;
   const int rr = lane & 15, kq = lane >> 4;  // A row and B column; k group
   const int g = rr < 12 ? rr >> 2 : 2, u = rr < 12 ? rr & 3 : 3;
   const size_t wrow = (size_t)g * Hs + min(j0 + u, Hs - 1);
+  const uint16_t* wi = (const uint16_t*)t.w_ih + wrow * d;
+  const uint16_t* wh = (const uint16_t*)t.w_hh + wrow * Hs;
+  const TreeCur* curs = reinterpret_cast<const TreeCur*>(t.cur) + b0;
+  // the weights do not depend on the tree: their loads go out first
+  uint4 wpi[kGruPreI], wph[kGruPreH];
+#pragma unroll
+  for (int q = 0; q < kGruPreI; ++q)
+    wpi[q] = *reinterpret_cast<const uint4*>(wi + min((wv + kGruWaves * q) * 32 + 8 * kq, d - 8));
+#pragma unroll
+  for (int q = 0; q < kGruPreH; ++q)
+    wph[q] = *reinterpret_cast<const uint4*>(wh + min((wv + kGruWaves * q) * 32 + 8 * kq, Hs - 8));
+  // this lane's column: sequence sq's token row and parent state (zeros without a parent)
   const int sq = min(rr, nb - 1);
-  // two accumulators per half (even and odd blocks of a batch), summed at the end
+  const TreeCur c = curs[sq];
+  const bool has_h = c.expand && c.parent_slot >= 0;
+  const uint16_t* xr = (const uint16_t*)t.embed + (size_t)min(max(c.token, 0), t.V - 1) * d;
+  const double* hr = t.states + ((size_t)(b0 + sq) * (t.N + 1) + max(c.parent_slot, 0)) * Hs;
+  // the finishing lanes (wave 0, lanes 0..31: unit lane / 8, sequence lane % 8)
+  // take their sequence's cursor from lane lane % 8, whose column it is
+  const int fs = lane & 7, fu = (lane >> 3) & 3;
+  const int f_slot = __shfl(c.slot, fs), f_ps = __shfl(c.parent_slot, fs);
+  const int f_exp = __shfl(c.expand, fs);
+  uint4 xp[kGruPreI];
+#pragma unroll
+  for (int q = 0; q < kGruPreI; ++q)
+    xp[q] = *reinterpret_cast<const uint4*>(xr + min((wv + kGruWaves * q) * 32 + 8 * kq, d - 8));
+  F64x8 hp[kGruPreH];
+#pragma unroll
+  for (int q = 0; q < kGruPreH; ++q) hp[q] = load_f64x8(hr + min((wv + kGruWaves * q) * 32 + 8 * kq, Hs - 8));
+  const double hprev_raw =
+      t.states[((size_t)(b0 + min(fs, nb - 1)) * (t.N + 1) + max(f_ps, 0)) * Hs + min(j0 + fu, Hs - 1)];
+  // every load above is issued before the first MFMA (the scheduler would
+  // otherwise move them next to their uses and wait on each in turn)
+  __builtin_amdgcn_sched_barrier(0);
+
+  // two accumulators per half (even and odd blocks), summed at the end
   f64x4 acc_i[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
   f64x4 acc_h[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
-  constexpr int NB = 4;  // blocks whose weights are in flight together
-  const uint16_t* wi = (const uint16_t*)t.w_ih + wrow * d;
-  const uint16_t* xr = xl + (size_t)sq * xs;
+#pragma unroll
+  for (int q = 0; q < kGruPreI; ++q) {
+    const bool ok = (wv + kGruWaves * q) * 32 + 8 * kq < d;
+    double w8[8], x8[8];
+    bf16x8_to_f64(wpi[q], w8);
+    bf16x8_to_f64(xp[q], x8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc_i[q & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w8[i], ok ? x8[i] : 0.0, acc_i[q & 1], 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < kGruPreH; ++q) {
+    const bool ok = has_h && (wv + kGruWaves * q) * 32 + 8 * kq < Hs;
+    double w8[8];
+    bf16x8_to_f64(wph[q], w8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc_h[q & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w8[i], ok ? hp[q].v[i] : 0.0, acc_h[q & 1], 0, 0, 0);
+  }
+  // blocks past those (wider hidden sizes), four in flight at a time
+  constexpr int NB = 4;
   const int nbi = (d + 31) / 32, nbh = (Hs + 31) / 32;
-  for (int b0k = wv; b0k < nbi; b0k += kGruWaves * NB) {
-    uint4 wr[NB];
+  for (int bk = wv + kGruWaves * kGruPreI; bk < nbi; bk += kGruWaves * NB) {
+    uint4 wr[NB], xv[NB];
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      const int k = (b0k + kGruWaves * q) * 32 + 8 * kq;
-      wr[q] = *reinterpret_cast<const uint4*>(wi + min(k, d - 8));
+      const int k = min((bk + kGruWaves * q) * 32 + 8 * kq, d - 8);
+      wr[q] = *reinterpret_cast<const uint4*>(wi + k);
+      xv[q] = *reinterpret_cast<const uint4*>(xr + k);
     }
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      const int k = (b0k + kGruWaves * q) * 32 + 8 * kq;
-      const bool ok = k < d;
+      const bool ok = (bk + kGruWaves * q) * 32 + 8 * kq < d;
       double w8[8], x8[8];
       bf16x8_to_f64(wr[q], w8);
-      bf16x8_to_f64(*reinterpret_cast<const uint4*>(xr + (ok ? k : 0)), x8);
+      bf16x8_to_f64(xv[q], x8);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         acc_i[q & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w8[i], ok ? x8[i] : 0.0, acc_i[q & 1], 0, 0, 0);
     }
   }
-  const uint16_t* wh = (const uint16_t*)t.w_hh + wrow * Hs;
-  const double* hr = hl + (size_t)sq * hs;
-  for (int b0k = wv; b0k < nbh; b0k += kGruWaves * NB) {
+  for (int bk = wv + kGruWaves * kGruPreH; bk < nbh; bk += kGruWaves * NB) {
     uint4 wr[NB];
+    F64x8 hv[NB];
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      const int k = (b0k + kGruWaves * q) * 32 + 8 * kq;
-      wr[q] = *reinterpret_cast<const uint4*>(wh + min(k, Hs - 8));
+      const int k = min((bk + kGruWaves * q) * 32 + 8 * kq, Hs - 8);
+      wr[q] = *reinterpret_cast<const uint4*>(wh + k);
+      hv[q] = load_f64x8(hr + k);
     }
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      const int k = (b0k + kGruWaves * q) * 32 + 8 * kq;
-      const bool ok = k < Hs;
-      const int kc = ok ? k : 0;
+      const bool ok = has_h && (bk + kGruWaves * q) * 32 + 8 * kq < Hs;
       double w8[8];
       bf16x8_to_f64(wr[q], w8);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        acc_h[q & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w8[i], ok ? hr[kc + i] : 0.0, acc_h[q & 1], 0, 0, 0);
+        acc_h[q & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w8[i], ok ? hv[q].v[i] : 0.0, acc_h[q & 1], 0, 0, 0);
     }
   }
   // result layout of the fp64 MFMA: register i of lane l holds row 4 i + l / 16 of column l % 16
@@ -570,33 +589,28 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int 
   }
   __syncthreads();
   if (threadIdx.x < 4 * kTreeSeqs) {
-    const int uu = threadIdx.x / kTreeSeqs, s = threadIdx.x % kTreeSeqs, j = j0 + uu;
-    if (s < nb && j < Hs && sc[s].expand) {
+    const int j = j0 + fu;
+    if (fs < nb && j < Hs && f_exp) {
       double gi[3], gh[3];
 #pragma unroll
       for (int q = 0; q < 3; ++q) {
-        gi[q] = red[0][0][4 * q + uu][s];
-        gh[q] = red[0][1][4 * q + uu][s];
+        gi[q] = red[0][0][4 * q + fu][fs];
+        gh[q] = red[0][1][4 * q + fu][fs];
 #pragma unroll
         for (int w = 1; w < kGruWaves; ++w) {
-          gi[q] += red[w][0][4 * q + uu][s];
-          gh[q] += red[w][1][4 * q + uu][s];
+          gi[q] += red[w][0][4 * q + fu][fs];
+          gh[q] += red[w][1][4 * q + fu][fs];
         }
       }
-      const TreeCur c = sc[s];
       auto bi = [&](int row) { return t.b_ih ? (double)t.b_ih[row] : 0.0; };
       auto bh = [&](int row) { return t.b_hh ? (double)t.b_hh[row] : 0.0; };
       const double r = 1.0 / (1.0 + exp(-(gi[0] + bi(j) + gh[0] + bh(j))));
       const double z = 1.0 / (1.0 + exp(-(gi[1] + bi(Hs + j) + gh[1] + bh(Hs + j))));
       const double nn = tanh(gi[2] + bi(2 * Hs + j) + r * (gh[2] + bh(2 * Hs + j)));
-      const double hprev = hl[(size_t)s * hs + j];
-      t.states[((size_t)(b0 + s) * (t.N + 1) + c.slot) * Hs + j] = (1.0 - z) * nn + z * hprev;
+      const double hprev = f_ps >= 0 ? hprev_raw : 0.0;
+      t.states[((size_t)(b0 + fs) * (t.N + 1) + f_slot) * Hs + j] = (1.0 - z) * nn + z * hprev;
     }
   }
-}
-
-size_t tree_gru_mfma_lds(int d, int Hs) {
-  return (size_t)kTreeSeqs * tree_h_stride(Hs) * 8 + (size_t)kTreeSeqs * tree_x_stride(d) * 2;
 }
 
 // ---- fp64 bottleneck of each sequence's current node: a = SiLU(W1 [H_delta ; S] + b1) -------
@@ -876,8 +890,7 @@ hipError_t launch_topm(const float* Lb, int rows, int V, int M, void* scratch, i
 
 // LDS of the GRU-step kernel that runs for this storage type, static part included
 size_t tree_gru_lds_total(int d, int Hs, int dtype) {
-  if (dtype == kBF16)
-    return tree_gru_mfma_lds(d, Hs) + sizeof(double) * kGruWaves * 2 * 12 * kTreeSeqs + sizeof(TreeCur) * kTreeSeqs;
+  if (dtype == kBF16) return sizeof(double) * kGruWaves * 2 * 12 * kTreeSeqs;  // static only, any shape
   return tree_gru_lds(d, Hs, dtype) + sizeof(TreeCur) * kTreeSeqs;
 }
 
@@ -893,20 +906,19 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(tree_zh, dim3((t.r + 15) / 16, t.B * t.P), dim3(256), 0, s, t);
   hipLaunchKernelGGL(tree_init, dim3((t.B + 255) / 256), dim3(256), 0, s, t);
-  // bf16 weights: the GRU step on the fp64 matrix cores
+  // bf16 weights: the GRU step on the fp64 matrix cores (static LDS only)
   const bool mfma = t.dtype == kBF16;
-  const size_t lds = mfma ? tree_gru_mfma_lds(t.d, t.Hs) : tree_gru_lds(t.d, t.Hs, t.dtype);
-  static thread_local size_t attr_lds[2] = {0, 0};
-  if (lds > attr_lds[mfma]) {
-    e = hipFuncSetAttribute(mfma ? (const void*)tree_gru_mfma : (const void*)tree_gru,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const size_t lds = mfma ? 0 : tree_gru_lds(t.d, t.Hs, t.dtype);
+  static thread_local size_t attr_lds = 0;
+  if (!mfma && lds > attr_lds) {
+    e = hipFuncSetAttribute((const void*)tree_gru, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_lds[mfma] = lds;
+    attr_lds = lds;
   }
   for (int k = 0; k < t.N; ++k) {
     for (int b0 = 0; b0 < t.B; b0 += kTreeSeqs) {
       if (mfma)
-        hipLaunchKernelGGL(tree_gru_mfma, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), lds, s, t, b0);
+        hipLaunchKernelGGL(tree_gru_mfma, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), 0, s, t, b0);
       else
         hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(64 * 4 * (kTreeSeqs / kSeqPerWave)), lds, s, t, b0);
     }

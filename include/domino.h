@@ -170,10 +170,10 @@ size_t domino_tree_workspace_size(const domino_dims *dims, int32_t batch, int32_
  *   when the tree runs out of nodes hold parent -1, token -1, depth 0,
  *   score -inf.
  * Limits: 1 <= nodes <= 64, 1 <= topm <= min(256, vocab), gru_hidden <= 4096,
- * and the GRU step's LDS within 160 KB: eight fp64 state rows and eight
- * embedding rows, each padded by 8 elements, plus 12.3 KB for bf16
- * (64*(gru_hidden+8) + 16*(hidden+8) + 12544 bytes), or
- * 64*gru_hidden + 32*hidden + 256 bytes for fp32.
+ * and, for fp32 weights only, the GRU step's LDS within 160 KB: eight fp64
+ * state rows and eight embedding rows (64*gru_hidden + 32*hidden + 256
+ * bytes).  The bf16 GRU step reads its operands directly and has no such
+ * limit.
  * The int32 at workspace offset 0 holds the device status after the call
  * (1 = a first token was outside [0, V) and token 0 was used).
  */

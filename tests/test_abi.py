@@ -170,5 +170,7 @@ def test_tree_arguments_rejected_before_launch():
     assert L.domino_tree_candidates(ctypes.byref(d), None, 2, 8, FAKE, FAKE, FAKE, cw, None) == dh.ERR_INVALID_ARGUMENT
     assert L.domino_tree_candidates(ctypes.byref(d), FAKE, 2, 8, FAKE, FAKE, FAKE, cw - 1, None) == dh.ERR_WORKSPACE
     assert L.domino_tree_candidates(ctypes.byref(d), FAKE, 0, 8, None, None, None, 0, None) == dh.OK
-    big = _dims(hidden=8192, gru_hidden=2048)
+    # fp32 weights: the GRU step stages eight states and embedding rows in LDS,
+    # which these sizes overflow (the bf16 step stages nothing)
+    big = _dims(hidden=8192, gru_hidden=2048, dtype="f32")
     assert call(dims=ctypes.byref(big), wsb=1 << 40) == dh.ERR_UNSUPPORTED

@@ -50,6 +50,7 @@ def _compare(g, o, label):
     (48, 515, 16, 16, 5, 9, 40, 5, "bf16"),      # more sequences than one GRU pass
     (32, 300, 8, 32, 3, 2, 64, 256, "f32"),      # largest budget and candidate count
     (32, 64, 8, 8, 1, 2, 10, 4, "bf16"),         # one position: the tree runs out of nodes
+    (3080, 1000, 1288, 64, 2, 3, 8, 16, "bf16"),  # GRU k blocks past the preloaded ones, ragged last block
 ])
 def test_tree_matches_oracle(d, V, Hs, r, P, B, N, M, dtype):
     cfg = small_config(d=d, V=V, Hs=Hs, r=r, P=P, B=B, dtype=dtype, biases=True)
