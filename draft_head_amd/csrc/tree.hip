@@ -681,8 +681,8 @@ __device__ __forceinline__ BestEntry best_empty() {
   return e;
 }
 
-__device__ __forceinline__ void best_offer(BestEntry& e, int slot, double s, int4 m) {
-  const bool take = (s > e.s) | ((s == e.s) & ((m.x < e.m.x) | ((m.x == e.m.x) & (m.y < e.m.y))));
+__device__ __forceinline__ void best_offer(BestEntry& e, int slot, double s, int4 m, bool valid = true) {
+  const bool take = valid & ((s > e.s) | ((s == e.s) & ((m.x < e.m.x) | ((m.x == e.m.x) & (m.y < e.m.y)))));
   e.slot = take ? slot : e.slot;
   e.s = take ? s : e.s;
   e.m.x = take ? m.x : e.m.x;
@@ -694,14 +694,29 @@ __device__ __forceinline__ void best_offer(BestEntry& e, int slot, double s, int
 // One workgroup per sequence.  Wave w scores candidates w, w+4, ...: lanes
 // split the bottleneck in runs of 4 and the partial dot products are reduced
 // across the wave.
+__device__ __forceinline__ void best_offer_lane(BestEntry& e, int src_lane_xor) {
+  BestEntry o;
+  o.slot = __shfl_xor(e.slot, src_lane_xor);
+  o.s = __shfl_xor(e.s, src_lane_xor);
+  o.m.x = __shfl_xor(e.m.x, src_lane_xor);
+  o.m.y = __shfl_xor(e.m.y, src_lane_xor);
+  o.m.z = __shfl_xor(e.m.z, src_lane_xor);
+  o.m.w = __shfl_xor(e.m.w, src_lane_xor);
+  best_offer(e, o.slot, o.s, o.m);
+}
+
 __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
   __shared__ double a[256];    // bottleneck (r <= 256)
   __shared__ double l[256];    // corrected candidate logits (M <= 256)
-  __shared__ double red_s[256];
-  __shared__ int red_i[256];
-  __shared__ int4 red_m[256];
+  __shared__ int lid[256];     // their token ids
+  __shared__ double lse_s;
+  __shared__ BestEntry wbest[4];
+  __shared__ double last_s;    // the last entry pushed
+  __shared__ int4 last_m;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = t.r, M = t.M, P = t.P;
+  // the bottleneck does not depend on the cursor: its read goes out first
+  const double av = t.act[(size_t)b * r + min(tid, r - 1)];
   TreeCur* curp = reinterpret_cast<TreeCur*>(t.cur) + b;
   const TreeCur c = *curp;
   double* hs = t.heap_score + (size_t)b * t.heap_cap;
@@ -709,54 +724,91 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
   int count = t.heap_count[b];
   // each thread's best among the entries already on the heap, read before the
   // scoring so that no read has to follow the pushes (the heap order is a strict
-  // total order, so the scan order does not matter)
+  // total order, so the scan order does not matter); thread 0 also keeps the
+  // last entry, which refills the popped slot when nothing is pushed
   BestEntry best = best_empty();
-  for (int i = tid; i < count; i += blockDim.x) best_offer(best, i, hs[i], hm[i]);
+  for (int i0 = tid; i0 < count; i0 += 4 * (int)blockDim.x) {  // four reads in flight per thread
+    double sv[4];
+    int4 mv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = min(i0 + q * (int)blockDim.x, count - 1);
+      sv[q] = hs[i];
+      mv[q] = hm[i];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + q * (int)blockDim.x;
+      best_offer(best, i, sv[q], mv[q], i < count);
+    }
+  }
+  double tail_s = 0.0;
+  int4 tail_m = make_int4(0, 0, 0, 0);
+  if (tid == 0 && count > 0) {
+    tail_s = hs[count - 1];
+    tail_m = hm[count - 1];
+  }
 
   if (c.expand) {
     const int delta = c.depth;
-    for (int i = tid; i < r; i += blockDim.x) a[i] = t.act[(size_t)b * r + i];
+    if (tid < r) a[tid] = av;
     __syncthreads();
     const int32_t* cidx = t.cand_idx + ((size_t)b * P + delta) * M;
     const float* cval = t.cand_val + ((size_t)b * P + delta) * M;
-    const int kk = lane * 4;
+    const int kk = min(lane * 4, r - 4);
+    const bool kin = lane * 4 < r;
     // wave w scores candidates w, w+4, ...; 16 W2 rows per batch in flight
     constexpr int CB = 16;
     for (int j0 = wv; j0 < M; j0 += 4 * CB) {
       double w[CB][4];
       int vv[CB];
+      float cv[CB];
 #pragma unroll
       for (int q = 0; q < CB; ++q) {
-        const int j = j0 + 4 * q;
-        vv[q] = j < M ? cidx[j] : 0;
+        const int j = min(j0 + 4 * q, M - 1);
+        vv[q] = cidx[j];
+        cv[q] = cval[j];
       }
+      // the storage-type and bias tests sit outside the row loops, so that the
+      // CB row reads go out back to back
+      double bv[CB];
+      float bf[CB];
+      if (t.b2) {
 #pragma unroll
-      for (int q = 0; q < CB; ++q) {
-        const int j = j0 + 4 * q;
-        if (j < M && kk < r) {
-          if (t.dtype == kBF16) {
-            const uint2 u = *reinterpret_cast<const uint2*>((const uint16_t*)t.w2 + (size_t)vv[q] * r + kk);
-            w[q][0] = (double)__uint_as_float(u.x << 16);
-            w[q][1] = (double)__uint_as_float(u.x & 0xFFFF0000u);
-            w[q][2] = (double)__uint_as_float(u.y << 16);
-            w[q][3] = (double)__uint_as_float(u.y & 0xFFFF0000u);
-          } else {
-            const float4 u = *reinterpret_cast<const float4*>((const float*)t.w2 + (size_t)vv[q] * r + kk);
-            w[q][0] = u.x, w[q][1] = u.y, w[q][2] = u.z, w[q][3] = u.w;
-          }
-        } else {
-          w[q][0] = w[q][1] = w[q][2] = w[q][3] = 0.0;
+        for (int q = 0; q < CB; ++q) bf[q] = t.b2[vv[q]];
+      }
+      if (t.dtype == kBF16) {
+        uint2 u[CB];
+#pragma unroll
+        for (int q = 0; q < CB; ++q) u[q] = *reinterpret_cast<const uint2*>((const uint16_t*)t.w2 + (size_t)vv[q] * r + kk);
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+          w[q][0] = (double)__uint_as_float(u[q].x << 16);
+          w[q][1] = (double)__uint_as_float(u[q].x & 0xFFFF0000u);
+          w[q][2] = (double)__uint_as_float(u[q].y << 16);
+          w[q][3] = (double)__uint_as_float(u[q].y & 0xFFFF0000u);
         }
+      } else {
+        float4 u[CB];
+#pragma unroll
+        for (int q = 0; q < CB; ++q) u[q] = *reinterpret_cast<const float4*>((const float*)t.w2 + (size_t)vv[q] * r + kk);
+#pragma unroll
+        for (int q = 0; q < CB; ++q) w[q][0] = u[q].x, w[q][1] = u[q].y, w[q][2] = u[q].z, w[q][3] = u[q].w;
       }
+#pragma unroll
+      for (int q = 0; q < CB; ++q) bv[q] = t.b2 ? (double)bf[q] : 0.0;
 #pragma unroll
       for (int q = 0; q < CB; ++q) {
         const int j = j0 + 4 * q;
         double sdot = 0.0;
-        if (kk < r)
+        if (kin)
 #pragma unroll
           for (int e = 0; e < 4; ++e) sdot += w[q][e] * a[kk + e];
         sdot = wave_sum(sdot);
-        if (lane == 0 && j < M) l[j] = (double)cval[j] + (t.b2 ? (double)t.b2[vv[q]] : 0.0) + sdot;
+        if (lane == 0 && j < M) {
+          l[j] = (double)cv[q] + bv[q] + sdot;
+          lid[j] = vv[q];
+        }
       }
     }
     __syncthreads();
@@ -769,43 +821,36 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
       double se = 0.0;
       for (int j = lane; j < M; j += 64) se += exp(l[j] - mx);
       se = wave_sum(se);
-      if (lane == 0) red_s[0] = mx + log(se);
+      if (lane == 0) lse_s = mx + log(se);
     }
     __syncthreads();
-    const double lse = red_s[0];
+    const double lse = lse_s;
     for (int j = tid; j < M; j += blockDim.x) {
       const double sj = c.score + (l[j] - lse);
-      const int4 mj = make_int4(c.node, j, cidx[j], delta + 1);
+      const int4 mj = make_int4(c.node, j, lid[j], delta + 1);
       hs[count + j] = sj;
       hm[count + j] = mj;
       best_offer(best, count + j, sj, mj);
+      if (j == M - 1) {
+        last_s = sj;
+        last_m = mj;
+      }
     }
     count += M;
-    __syncthreads();  // every thread has read lse (red_s[0]) before the reduction reuses red_s
   }
 
-  // pop: best entry under (score desc, parent asc, rank asc)
-  // tree reduction over the threads' bests, entirely in LDS (score, meta, slot)
-  red_i[tid] = best.slot;
-  red_s[tid] = best.s;
-  red_m[tid] = best.m;
+  // pop: best entry under (score desc, parent asc, rank asc): within each
+  // wave by shuffles, then over the four waves
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) best_offer_lane(best, m);
+  if (lane == 0) wbest[wv] = best;
   __syncthreads();
-  for (int half = blockDim.x / 2; half > 0; half >>= 1) {
-    if (tid < half) {
-      BestEntry e;
-      e.slot = red_i[tid];
-      e.s = red_s[tid];
-      e.m = red_m[tid];
-      best_offer(e, red_i[tid + half], red_s[tid + half], red_m[tid + half]);
-      red_i[tid] = e.slot;
-      red_s[tid] = e.s;
-      red_m[tid] = e.m;
-    }
-    __syncthreads();
-  }
   if (tid == 0) {
+    BestEntry e = wbest[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) best_offer(e, wbest[w].slot, wbest[w].s, wbest[w].m);
     const size_t o = (size_t)b * t.N + k;
-    const int bi = red_i[0];
+    const int bi = e.slot;
     TreeCur n;
     n.expand = 0;
     n.slot = k + 1;
@@ -820,14 +865,20 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
       if (t.out_depth) t.out_depth[o] = 0;
       if (t.out_scores) t.out_scores[o] = -INFINITY;
     } else {
-      const double s = red_s[0];
-      const int4 m = red_m[0];
+      const double s = e.s;
+      const int4 m = e.m;
       t.out_parents[o] = m.x;
       t.out_tokens[o] = m.z;
       if (t.out_depth) t.out_depth[o] = m.w;
       if (t.out_scores) t.out_scores[o] = s;
-      hs[bi] = hs[count - 1];
-      hm[bi] = hm[count - 1];
+      // the last entry moves into the popped slot
+      if (c.expand) {
+        hs[bi] = last_s;
+        hm[bi] = last_m;
+      } else {
+        hs[bi] = tail_s;
+        hm[bi] = tail_m;
+      }
       count -= 1;
       n.expand = (m.w < P && k + 1 < t.N) ? 1 : 0;
       n.parent_slot = m.x + 1;  // node index -> state slot; the anchor's slot is 0
