@@ -613,49 +613,85 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int 
   }
 }
 
+// eight consecutive weights of one row, as stored, and their fp64 values
+template <class W>
+struct Run8;
+template <>
+struct Run8<uint16_t> {
+  uint4 u;
+  __device__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ void get(double (&o)[8]) const { bf16x8_to_f64(u, o); }
+};
+template <>
+struct Run8<float> {
+  float4 a, b;
+  __device__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ void get(double (&o)[8]) const {
+    o[0] = a.x, o[1] = a.y, o[2] = a.z, o[3] = a.w, o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
+  }
+};
+
 // ---- fp64 bottleneck of each sequence's current node: a = SiLU(W1 [H_delta ; S] + b1) -------
 // Workgroup = 16 bottleneck units of one sequence; wave w takes 4, lanes split Hs.
+template <class W>
 __global__ __launch_bounds__(256) void tree_bottleneck(TreeArgs t) {
-  __shared__ double S[4096];
+  constexpr int U = 2;  // runs of 8 per lane and row whose reads go out first (state width <= 1024)
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int b = blockIdx.y, k0 = blockIdx.x * 16 + wv * 4;
+  const int Hs = t.Hs, r = t.r;
+  const size_t ld = (size_t)t.d + Hs;
+  const W* w1s = reinterpret_cast<const W*>(t.w1) + t.d;  // state half of W1
+  // the weights do not depend on the tree: their reads go out before the cursor's
+  Run8<W> wr[U][4];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wr[u][q].load(w1s + (size_t)min(k0 + q, r - 1) * ld + min(lane * 8 + 512 * u, Hs - 8));
   const TreeCur c = reinterpret_cast<const TreeCur*>(t.cur)[b];
   if (!c.expand) return;
-  const int Hs = t.Hs;
   const double* st = t.states + ((size_t)b * (t.N + 1) + c.slot) * Hs;
-  for (int i0 = 0; i0 < Hs; i0 += 4 * (int)blockDim.x) {  // four loads in flight per thread
-    double v[4];
+  F64x8 sv[U];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = i0 + q * (int)blockDim.x + threadIdx.x;
-      v[q] = i < Hs ? st[i] : 0.0;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = i0 + q * (int)blockDim.x + threadIdx.x;
-      if (i < Hs) S[i] = v[q];
-    }
-  }
-  __syncthreads();
+  for (int u = 0; u < U; ++u) sv[u] = load_f64x8(st + min(lane * 8 + 512 * u, Hs - 8));
+  // lane q < 4 finishes row k0 + q: its W1_H half and bias
+  const int kq = min(k0 + (lane & 3), r - 1);
+  const double zq = t.zh[((size_t)b * t.P + c.depth) * r + kq];
+  const double bq = t.b1 ? (double)t.b1[kq] : 0.0;
+  __builtin_amdgcn_sched_barrier(0);
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int jj = lane * 8; jj < Hs; jj += 512) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (lane * 8 + 512 * u >= Hs) break;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (k0 + q >= t.r) break;
       double w[8];
-      load8_f64(t.w1, t.dtype, (size_t)(k0 + q) * (t.d + Hs) + t.d + jj, w);
+      wr[u][q].get(w);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[q] += w[e] * S[jj + e];
+      for (int e = 0; e < 8; ++e) acc[q] += w[e] * sv[u].v[e];
     }
   }
+  for (int jj = lane * 8 + 512 * U; jj < Hs; jj += 512) {  // wider states
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const double v = wave_sum(acc[q]);
-    const int k = k0 + q;
-    if (lane == 0 && k < t.r) {
-      const double z = v + t.zh[((size_t)b * t.P + c.depth) * t.r + k] + (t.b1 ? (double)t.b1[k] : 0.0);
-      t.act[(size_t)b * t.r + k] = z / (1.0 + exp(-z));
+    for (int q = 0; q < 4; ++q) {
+      Run8<W> x;
+      x.load(w1s + (size_t)min(k0 + q, r - 1) * ld + jj);
+      double w[8];
+      x.get(w);
+      const F64x8 sx = load_f64x8(st + jj);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q] += w[e] * sx.v[e];
     }
+  }
+  double v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = wave_sum(acc[q]);
+  const int k = k0 + lane;
+  if (lane < 4 && k < r) {
+    const double z = (lane == 0 ? v[0] : lane == 1 ? v[1] : lane == 2 ? v[2] : v[3]) + zq + bq;
+    t.act[(size_t)b * r + k] = z / (1.0 + exp(-z));
   }
 }
 
@@ -973,7 +1009,10 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
       else
         hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(64 * 4 * (kTreeSeqs / kSeqPerWave)), lds, s, t, b0);
     }
-    hipLaunchKernelGGL(tree_bottleneck, dim3((t.r + 15) / 16, t.B), dim3(256), 0, s, t);
+    if (t.dtype == kBF16)
+      hipLaunchKernelGGL(tree_bottleneck<uint16_t>, dim3((t.r + 15) / 16, t.B), dim3(256), 0, s, t);
+    else
+      hipLaunchKernelGGL(tree_bottleneck<float>, dim3((t.r + 15) / 16, t.B), dim3(256), 0, s, t);
     hipLaunchKernelGGL(tree_score_pop, dim3(t.B), dim3(256), 0, s, t, k);
   }
   e = hipGetLastError();
