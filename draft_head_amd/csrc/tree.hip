@@ -236,30 +236,101 @@ __device__ __forceinline__ void load8_f64(const void* base, int dtype, size_t i,
   }
 }
 
-// W1[:, :d] H[b][p] in fp64.  Workgroup = one row of H and 16 rows of W1;
-// wave w takes 4 W1 rows, lanes split d in runs of 8.
+__device__ __forceinline__ void bf16x8_to_f64(const uint4& r, double (&o)[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[2 * e] = (double)__uint_as_float(w[e] << 16);
+    o[2 * e + 1] = (double)__uint_as_float(w[e] & 0xFFFF0000u);
+  }
+}
+
+struct F64x8 {
+  double v[8];
+};
+
+__device__ __forceinline__ F64x8 load_f64x8(const double* p) {
+  F64x8 r;
+  const double4* q = reinterpret_cast<const double4*>(p);
+  const double4 a = q[0], b = q[1];
+  r.v[0] = a.x, r.v[1] = a.y, r.v[2] = a.z, r.v[3] = a.w;
+  r.v[4] = b.x, r.v[5] = b.y, r.v[6] = b.z, r.v[7] = b.w;
+  return r;
+}
+
+// eight consecutive weights of one row, as stored, and their fp64 values
+template <class W>
+struct Run8;
+template <>
+struct Run8<uint16_t> {
+  uint4 u;
+  __device__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ void get(double (&o)[8]) const { bf16x8_to_f64(u, o); }
+};
+template <>
+struct Run8<float> {
+  float4 a, b;
+  __device__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ void get(double (&o)[8]) const {
+    o[0] = a.x, o[1] = a.y, o[2] = a.z, o[3] = a.w, o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
+  }
+};
+
+// W1[:, :d] H[b][p] in fp64 for every (sequence, position) row.  Workgroup =
+// 16 rows of W1 and 8 rows of H, so that each W1 run read serves eight H rows;
+// wave w takes 4 W1 rows, lanes split d in runs of 8, two runs per lane in
+// flight.  The per-lane sums follow k in the same order as a plain loop.
+template <class W>
 __global__ __launch_bounds__(256) void tree_zh(TreeArgs t) {
+  constexpr int MR = 8;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int m = blockIdx.y, k0 = blockIdx.x * 16 + wv * 4;
-  const int d = t.d;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int j = lane * 8; j < d; j += 512) {
-    double h[8];
-    load8_f64(t.H, t.dtype, (size_t)m * d + j, h);
+  const int m0 = blockIdx.y * MR, k0 = blockIdx.x * 16 + wv * 4;
+  const int d = t.d, r = t.r, rows = t.B * t.P;
+  const size_t ld = (size_t)d + t.Hs;
+  const W* w1 = reinterpret_cast<const W*>(t.w1);
+  const W* H = reinterpret_cast<const W*>(t.H);
+  double acc[4][MR];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (k0 + q >= t.r) break;
-      double w[8];
-      load8_f64(t.w1, t.dtype, (size_t)(k0 + q) * (d + t.Hs) + j, w);
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[q] += w[e] * h[e];
+    for (int i = 0; i < MR; ++i) acc[q][i] = 0.0;
+  for (int j0 = lane * 8; j0 < d; j0 += 1024) {
+    Run8<W> wr[2][4], hr[2][MR];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = min(j0 + 512 * u, d - 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wr[u][q].load(w1 + (size_t)min(k0 + q, r - 1) * ld + j);
+#pragma unroll
+      for (int i = 0; i < MR; ++i) hr[u][i].load(H + (size_t)min(m0 + i, rows - 1) * d + j);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (j0 + 512 * u >= d) break;
+      double w[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wr[u][q].get(w[q]);
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        double h[8];
+        hr[u][i].get(h);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[q][i] += w[q][e] * h[e];
+      }
     }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const double v = wave_sum(acc[q]);
-    if (lane == 0 && k0 + q < t.r) t.zh[(size_t)m * t.r + k0 + q] = v;
-  }
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      const double v = wave_sum(acc[q][i]);
+      if (lane == 0 && k0 + q < r && m0 + i < rows) t.zh[(size_t)(m0 + i) * r + k0 + q] = v;
+    }
 }
 
 // empty heaps; the anchor as each sequence's first node to expand
@@ -446,27 +517,8 @@ __global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0) {
 // threads finish (unit, sequence) pairs.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void bf16x8_to_f64(const uint4& r, double (&o)[8]) {
-  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    o[2 * e] = (double)__uint_as_float(w[e] << 16);
-    o[2 * e + 1] = (double)__uint_as_float(w[e] & 0xFFFF0000u);
-  }
-}
 
-struct F64x8 {
-  double v[8];
-};
 
-__device__ __forceinline__ F64x8 load_f64x8(const double* p) {
-  F64x8 r;
-  const double4* q = reinterpret_cast<const double4*>(p);
-  const double4 a = q[0], b = q[1];
-  r.v[0] = a.x, r.v[1] = a.y, r.v[2] = a.z, r.v[3] = a.w;
-  r.v[4] = b.x, r.v[5] = b.y, r.v[6] = b.z, r.v[7] = b.w;
-  return r;
-}
 
 constexpr int kGruWaves = 8;  // waves of tree_gru_mfma, splitting the k blocks
 constexpr int kGruPreI = 10;  // input-half blocks per wave whose loads are all issued up front
@@ -613,26 +665,6 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int 
   }
 }
 
-// eight consecutive weights of one row, as stored, and their fp64 values
-template <class W>
-struct Run8;
-template <>
-struct Run8<uint16_t> {
-  uint4 u;
-  __device__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
-  __device__ void get(double (&o)[8]) const { bf16x8_to_f64(u, o); }
-};
-template <>
-struct Run8<float> {
-  float4 a, b;
-  __device__ void load(const float* p) {
-    a = reinterpret_cast<const float4*>(p)[0];
-    b = reinterpret_cast<const float4*>(p)[1];
-  }
-  __device__ void get(double (&o)[8]) const {
-    o[0] = a.x, o[1] = a.y, o[2] = a.z, o[3] = a.w, o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
-  }
-};
 
 // ---- fp64 bottleneck of each sequence's current node: a = SiLU(W1 [H_delta ; S] + b1) -------
 // Workgroup = 16 bottleneck units of one sequence; wave w takes 4, lanes split Hs.
@@ -991,7 +1023,10 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
   if (ev_start && ev_stop && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;
   e = launch_topm_impl(t.Lb, t.B * t.P, t.V, t.M, t.seg_keys, t.cand_idx, t.cand_val, t.status, reset_status, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tree_zh, dim3((t.r + 15) / 16, t.B * t.P), dim3(256), 0, s, t);
+  if (t.dtype == kBF16)
+    hipLaunchKernelGGL(tree_zh<uint16_t>, dim3((t.r + 15) / 16, (t.B * t.P + 7) / 8), dim3(256), 0, s, t);
+  else
+    hipLaunchKernelGGL(tree_zh<float>, dim3((t.r + 15) / 16, (t.B * t.P + 7) / 8), dim3(256), 0, s, t);
   hipLaunchKernelGGL(tree_init, dim3((t.B + 255) / 256), dim3(256), 0, s, t);
   // bf16 weights: the GRU step on the fp64 matrix cores (static LDS only)
   const bool mfma = t.dtype == kBF16;
