@@ -32,6 +32,7 @@ namespace dh {
 // segment's top M, then one workgroup per row merges the segment lists.
 constexpr int kTopCap = 2048;  // LDS key buffer; M <= kTopCap / kTopSegs
 constexpr int kTopSegs = 8;
+constexpr int kTopInFlight = 16;  // row reads in flight per thread in each pass of topm_segment
 
 __device__ __forceinline__ float key_value(uint64_t k) {
   uint32_t u = (uint32_t)(k >> 32);
@@ -130,14 +131,14 @@ __global__ __launch_bounds__(256) void topm_segment(const float* __restrict__ Lb
     for (int j = threadIdx.x; j < M; j += blockDim.x) out[j] = 0;
     return;
   }
-  // pass 1 (loads from clamped addresses, four in flight per thread)
+  // pass 1 (loads from clamped addresses, kTopInFlight in flight per thread)
   uint64_t mk = 0;
-  for (int v0 = v_begin; v0 < v_end; v0 += 4 * 256) {
-    float f[4];
+  for (int v0 = v_begin; v0 < v_end; v0 += kTopInFlight * 256) {
+    float f[kTopInFlight];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) f[q] = x[min(v0 + q * 256 + (int)threadIdx.x, v_end - 1)];
+    for (int q = 0; q < kTopInFlight; ++q) f[q] = x[min(v0 + q * 256 + (int)threadIdx.x, v_end - 1)];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kTopInFlight; ++q) {
       const int v = v0 + q * 256 + threadIdx.x;
       if (v < v_end) mk = umax64(mk, amax_key(f[q], (uint32_t)v));
     }
@@ -157,12 +158,12 @@ __global__ __launch_bounds__(256) void topm_segment(const float* __restrict__ Lb
   uint64_t tau = wq[0];
   for (int w = 1; w < (int)(blockDim.x >> 6); ++w) tau = wq[w] < tau ? wq[w] : tau;
   // pass 2: every key >= tau
-  for (int v0 = v_begin; v0 < v_end; v0 += 4 * 256) {
-    float f[4];
+  for (int v0 = v_begin; v0 < v_end; v0 += kTopInFlight * 256) {
+    float f[kTopInFlight];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) f[q] = x[min(v0 + q * 256 + (int)threadIdx.x, v_end - 1)];
+    for (int q = 0; q < kTopInFlight; ++q) f[q] = x[min(v0 + q * 256 + (int)threadIdx.x, v_end - 1)];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kTopInFlight; ++q) {
       const int v = v0 + q * 256 + threadIdx.x;
       const uint64_t k = amax_key(f[q], (uint32_t)v);
       if (v < v_end && k >= tau && k != 0) {
