@@ -194,12 +194,12 @@ __device__ __forceinline__ int wide_swizzle(int r) {
   return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3;
 }
 
-template <int MT, int BK, int NBUF>
+template <int MT, int BK, int NBUF, int NT>
 __global__ __launch_bounds__(512) void gemm_wide(const uint16_t* __restrict__ A, int lda,
                                                  const uint16_t* __restrict__ B, int ldb, float* __restrict__ C,
                                                  int ldc, int M, int N, int K, int m_tiles, int n_tiles) {
   static_assert(BK == 32 || BK == 64, "stage depth");
-  constexpr int NT = 4, BM = 2 * MT * 16, BN = 256;
+  constexpr int BM = 2 * MT * 16, BN = 4 * NT * 16;
   constexpr int ROWB = BK * 2, UPR = BK / 8, RPL = 64 / UPR;  // bytes, units per row; rows per load
   constexpr int A_BYTES = BM * ROWB, STAGE = A_BYTES + BN * ROWB;
   constexpr int A_LOADS = BM / RPL, LOADS = A_LOADS + BN / RPL;
@@ -472,18 +472,18 @@ static hipError_t allow_lds(const void* fn, size_t bytes) {
   return hipSuccess;
 }
 
-template <int MT>
+template <int MT, int NT>
 static hipError_t launch_wide(const uint16_t* A, int lda, const uint16_t* B, int ldb, float* C, int ldc, int M, int N,
                               int K, int cus, hipStream_t s) {
-  constexpr int BK = DH_WIDE_BK, NBUF = DH_WIDE_NBUF, BM = 2 * MT * 16, BN = 256;
+  constexpr int BK = DH_WIDE_BK, NBUF = DH_WIDE_NBUF, BM = 2 * MT * 16, BN = 4 * NT * 16;
   constexpr size_t lds = (size_t)NBUF * (BM + BN) * BK * 2;
   static_assert(lds <= 160 * 1024, "LDS of a CU");
   const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
   const int64_t total = (int64_t)m_tiles * n_tiles;
   const int grid = total < cus ? (int)total : cus;
-  hipError_t e = allow_lds((const void*)gemm_wide<MT, BK, NBUF>, lds);
+  hipError_t e = allow_lds((const void*)gemm_wide<MT, BK, NBUF, NT>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_wide<MT, BK, NBUF>), dim3(grid), dim3(512), lds, s, A, lda, B, ldb, C, ldc, M, N, K, m_tiles,
+  hipLaunchKernelGGL((gemm_wide<MT, BK, NBUF, NT>), dim3(grid), dim3(512), lds, s, A, lda, B, ldb, C, ldc, M, N, K, m_tiles,
                      n_tiles);
   return hipGetLastError();
 }
@@ -523,9 +523,16 @@ hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int 
       return hipGetLastError();
     }
   }
-  if (prefer_tiles && M > 128 && K % DH_WIDE_BK == 0 && lda % 8 == 0 && ldb % 8 == 0) {
+  // Tile shapes by row count (measured at V = 151936): one row tile of 128 or
+  // 256 rows takes 320 columns, so that the 475 column tiles need at most two
+  // rounds of the CUs (256 columns leave a third, partial round); above 256
+  // rows the 256 x 256 tile is faster.
+  if (prefer_tiles && M > 16 && K % DH_WIDE_BK == 0 && lda % 8 == 0 && ldb % 8 == 0) {
     const int cus = device_cus();
-    if (cus > 0) return launch_wide<8>((const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, M, N, K, cus, s);
+    const uint16_t *a16 = (const uint16_t*)A, *b16 = (const uint16_t*)B;
+    if (cus > 0 && M > 256) return launch_wide<8, 4>(a16, lda, b16, ldb, C, ldc, M, N, K, cus, s);
+    if (cus > 0 && M > 128) return launch_wide<8, 5>(a16, lda, b16, ldb, C, ldc, M, N, K, cus, s);
+    if (cus > 0) return launch_wide<4, 5>(a16, lda, b16, ldb, C, ldc, M, N, K, cus, s);
   }
   if (!prefer_tiles || M <= 64)
     return launch_stream((const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, M, N, K, s);

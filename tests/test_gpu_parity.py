@@ -102,10 +102,12 @@ def test_base_logits_one_sequence_wide(d, V, P):
 
 
 # many rows (several sequences' blocks): the LDS-ring MFMA kernel for k a
-# multiple of 64, both tile shapes, ragged rows and columns, several tiles per
+# multiple of 64, all three tile shapes (128 x 320 up to 128 rows, 256 x 320 up
+# to 256, 256 x 256 above), ragged rows and columns, several tiles per
 # workgroup, and the look-ahead loads crossing tile boundaries
 @pytest.mark.parametrize("d,V,B,P", [(320, 40009, 19, 16), (576, 9001, 8, 16), (1024, 70001, 3, 11),
-                                     (384, 5003, 1, 7), (640, 33331, 40, 13), (2560, 12007, 32, 16)])
+                                     (384, 5003, 1, 7), (640, 33331, 40, 13), (2560, 12007, 32, 16),
+                                     (1280, 20011, 13, 16), (768, 30011, 16, 16), (128, 4099, 2, 9)])
 def test_base_logits_many_rows(d, V, B, P):
     cfg = small_config(d=d, V=V, B=B, P=P, dtype="bf16")
     say(f"case base logits many rows d={d} V={V} B={B} P={P}")
