@@ -280,58 +280,77 @@ struct Run8<float> {
   }
 };
 
-// W1[:, :d] H[b][p] in fp64 for every (sequence, position) row.  Workgroup =
-// 16 rows of W1 and 8 rows of H, so that each W1 run read serves eight H rows;
-// wave w takes 4 W1 rows, lanes split d in runs of 8, two runs per lane in
-// flight.  The per-lane sums follow k in the same order as a plain loop.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// W1[:, :d] H[b][p] in fp64 for every (sequence, position) row, on the fp64
+// matrix cores.  Workgroup = one 16 x 16 output tile: MFMA rows are 16 rows of
+// W1 (bottleneck units), columns 16 rows of H.  The k range (d) runs in
+// 32-wide blocks dealt to the 8 waves in turn; in a block, lane l holds 8
+// consecutive k values, 8 (l / 16) + 0..7, of its row and column, and MFMA i
+// takes value i of every lane.  The first kZhPre blocks of every wave are read
+// before the first MFMA; the waves' sums meet in LDS in wave order.
+constexpr int kZhWaves = 8, kZhPre = 10;
+
 template <class W>
-__global__ __launch_bounds__(256) void tree_zh(TreeArgs t) {
-  constexpr int MR = 8;
+__global__ __launch_bounds__(64 * kZhWaves) void tree_zh(TreeArgs t) {
+  __shared__ double red[kZhWaves][4][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int m0 = blockIdx.y * MR, k0 = blockIdx.x * 16 + wv * 4;
+  const int rr = lane & 15, kq = lane >> 4;
+  const int k0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
   const int d = t.d, r = t.r, rows = t.B * t.P;
-  const size_t ld = (size_t)d + t.Hs;
-  const W* w1 = reinterpret_cast<const W*>(t.w1);
-  const W* H = reinterpret_cast<const W*>(t.H);
-  double acc[4][MR];
+  const W* wrow = reinterpret_cast<const W*>(t.w1) + (size_t)min(k0 + rr, r - 1) * ((size_t)d + t.Hs);
+  const W* hrow = reinterpret_cast<const W*>(t.H) + (size_t)min(m0 + rr, rows - 1) * d;
+  Run8<W> wa[kZhPre], ha[kZhPre];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < kZhPre; ++q) {
+    const int j = min((wv + kZhWaves * q) * 32 + 8 * kq, d - 8);
+    wa[q].load(wrow + j);
+    ha[q].load(hrow + j);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f64x4 acc[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
 #pragma unroll
-    for (int i = 0; i < MR; ++i) acc[q][i] = 0.0;
-  for (int j0 = lane * 8; j0 < d; j0 += 1024) {
-    Run8<W> wr[2][4], hr[2][MR];
+  for (int q = 0; q < kZhPre; ++q) {
+    const bool ok = (wv + kZhWaves * q) * 32 + 8 * kq < d;
+    double w8[8], h8[8];
+    wa[q].get(w8);
+    ha[q].get(h8);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = min(j0 + 512 * u, d - 8);
+    for (int i = 0; i < 8; ++i)
+      acc[q & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w8[i], ok ? h8[i] : 0.0, acc[q & 1], 0, 0, 0);
+  }
+  const int nbk = (d + 31) / 32;
+  for (int bk = wv + kZhWaves * kZhPre; bk < nbk; bk += kZhWaves * 4) {  // wider H rows
+    Run8<W> wb[4], hb[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wr[u][q].load(w1 + (size_t)min(k0 + q, r - 1) * ld + j);
-#pragma unroll
-      for (int i = 0; i < MR; ++i) hr[u][i].load(H + (size_t)min(m0 + i, rows - 1) * d + j);
+    for (int q = 0; q < 4; ++q) {
+      const int j = min((bk + kZhWaves * q) * 32 + 8 * kq, d - 8);
+      wb[q].load(wrow + j);
+      hb[q].load(hrow + j);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (j0 + 512 * u >= d) break;
-      double w[4][8];
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = (bk + kZhWaves * q) * 32 + 8 * kq < d;
+      double w8[8], h8[8];
+      wb[q].get(w8);
+      hb[q].get(h8);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wr[u][q].get(w[q]);
-#pragma unroll
-      for (int i = 0; i < MR; ++i) {
-        double h[8];
-        hr[u][i].get(h);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[q][i] += w[q][e] * h[e];
-      }
+      for (int i = 0; i < 8; ++i)
+        acc[q & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w8[i], ok ? h8[i] : 0.0, acc[q & 1], 0, 0, 0);
     }
   }
+  // result layout of the fp64 MFMA: register i of lane l holds row 4 i + l / 16 of column l % 16
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int i = 0; i < 4; ++i) red[wv][i][lane] = acc[0][i] + acc[1][i];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int i = threadIdx.x >> 6, l = threadIdx.x & 63;
+    double v = red[0][i][l];
 #pragma unroll
-    for (int i = 0; i < MR; ++i) {
-      const double v = wave_sum(acc[q][i]);
-      if (lane == 0 && k0 + q < r && m0 + i < rows) t.zh[(size_t)(m0 + i) * r + k0 + q] = v;
-    }
+    for (int w = 1; w < kZhWaves; ++w) v += red[w][i][l];
+    const int k = k0 + 4 * i + (l >> 4), m = m0 + (l & 15);
+    if (k < r && m < rows) t.zh[(size_t)m * r + k] = v;
+  }
 }
 
 // empty heaps; the anchor as each sequence's first node to expand
@@ -516,7 +535,6 @@ __global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0) {
 // input half (W_ih E[token]) and the hidden half (W_hh h) have their own
 // accumulators; the waves' partial sums meet in LDS, in wave order, and 32
 // threads finish (unit, sequence) pairs.
-typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 
 
@@ -1024,10 +1042,11 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
   if (ev_start && ev_stop && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;
   e = launch_topm_impl(t.Lb, t.B * t.P, t.V, t.M, t.seg_keys, t.cand_idx, t.cand_val, t.status, reset_status, s);
   if (e != hipSuccess) return e;
+  const dim3 zh_grid((t.r + 15) / 16, (t.B * t.P + 15) / 16);
   if (t.dtype == kBF16)
-    hipLaunchKernelGGL(tree_zh<uint16_t>, dim3((t.r + 15) / 16, (t.B * t.P + 7) / 8), dim3(256), 0, s, t);
+    hipLaunchKernelGGL(tree_zh<uint16_t>, zh_grid, dim3(64 * kZhWaves), 0, s, t);
   else
-    hipLaunchKernelGGL(tree_zh<float>, dim3((t.r + 15) / 16, (t.B * t.P + 7) / 8), dim3(256), 0, s, t);
+    hipLaunchKernelGGL(tree_zh<float>, zh_grid, dim3(64 * kZhWaves), 0, s, t);
   hipLaunchKernelGGL(tree_init, dim3((t.B + 255) / 256), dim3(256), 0, s, t);
   // bf16 weights: the GRU step on the fp64 matrix cores (static LDS only)
   const bool mfma = t.dtype == kBF16;
