@@ -242,7 +242,10 @@ __device__ __forceinline__ uint32_t ll_data(uint64_t w) { return (uint32_t)w; }
 // word it read carries the expected tag) until it succeeds in every lane of
 // the wave.  Gives up when another wave has flagged a timeout or after
 // kWaitTicks (then flags one itself) and returns false; the caller carries on
-// with what it read, so every wave still reaches the end of the kernel.
+// with what it read, so every wave still reaches the end of the kernel.  The
+// shared flag and the clock are read on every 8th retry only: the flag read is
+// a round trip to memory, and between two attempts it would double the time
+// a wave takes to see words that have just landed.
 // kSleep: s_sleep units (64 clocks each) between attempts; waits off the
 // critical path use longer ones so they add less polling traffic.
 template <int kSleep = 1, class F>
@@ -252,7 +255,7 @@ __device__ __forceinline__ bool ll_wait(int32_t* status, F&& attempt) {
     if (__all(attempt())) return true;
     if (tries == 0) {
       t0 = wall_clock64();
-    } else {
+    } else if ((tries & 7) == 0) {
       if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kStatusTimeout) return false;
       if (wall_clock64() - t0 > kWaitTicks) {
         __hip_atomic_store(status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
