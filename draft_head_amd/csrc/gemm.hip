@@ -176,8 +176,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_rows16(const uint16_t* __rest
 #endif
 
 // Many rows of A, bf16, K a multiple of BK.
-// Workgroup tile BM x 256 (BM = 32 MT), eight waves in 2 x 4, each MT x 4
-// 16x16 tiles; k runs in BK-deep stages through a ring of NBUF LDS buffers.
+// Workgroup tile BM x BN (BM = 32 MT, BN = 64 NT), eight waves in 2 x 4, each
+// MT x NT 16x16 tiles; k runs in BK-deep stages through a ring of NBUF LDS
+// buffers.
 // What bounds this product on MI355X is how fast a CU pulls operands from
 // L2, so the tile is as large as the register file allows (fewer bytes per
 // flop).  Loads go straight from global memory into LDS

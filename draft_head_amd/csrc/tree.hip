@@ -11,13 +11,15 @@
 //
 // Kernels, in launch order for one call:
 //  topm_segment     T1: top-M of each segment of each base-logit row, ordered
-//                   (value desc, index asc): a single pass with a running
-//                   threshold and an LDS buffer trimmed by a bitonic sort
+//                   (value desc, index asc): a bound from the waves' maxima,
+//                   then a bitonic sort of the keys at or above it (a single
+//                   pass with a running threshold when too many pass)
 //  topm_merge       the row's top-M from its segment lists
-//  tree_zh          W1[:, :d] H for every position, fp64
+//  tree_zh          W1[:, :d] H for every position, fp64 matrix cores
 //  tree_init        empty heaps; the anchor as each sequence's first node
 //  per round (N rounds):
-//   tree_gru        fp64 GRU step of each sequence's current node
+//   tree_gru_mfma   fp64 GRU step of each sequence's current node (bf16
+//                   weights, matrix cores; tree_gru for fp32 weights)
 //   tree_bottleneck fp64 a = SiLU(W1 [H ; S] + b1) of those nodes
 //   tree_score_pop  score and push the node's M children, then pop the best entry
 #include <math.h>
