@@ -51,6 +51,8 @@ def _compare(g, o, label):
     (32, 300, 8, 32, 3, 2, 64, 256, "f32"),      # largest budget and candidate count
     (32, 64, 8, 8, 1, 2, 10, 4, "bf16"),         # one position: the tree runs out of nodes
     (3080, 1000, 1288, 64, 2, 3, 8, 16, "bf16"),  # GRU k blocks past the preloaded ones, ragged last block
+    (64, 777, 24, 16, 3, 17, 12, 6, "bf16"),      # three GRU passes (sequences 16..)
+    (128, 1500, 32, 256, 4, 3, 12, 16, "bf16"),   # the largest rank: full bottleneck vector in the pop
 ])
 def test_tree_matches_oracle(d, V, Hs, r, P, B, N, M, dtype):
     cfg = small_config(d=d, V=V, Hs=Hs, r=r, P=P, B=B, dtype=dtype, biases=True)
