@@ -122,7 +122,7 @@ def test_base_logits_many_rows(d, V, B, P):
 
 
 @pytest.mark.parametrize("key,rows", [("qwen3_4b_b1", [(0, 0), (0, 15)]), ("qwen3_4b_b32", [(0, 0), (31, 9)]),
-                                      ("qwen3_8b_b16", [(0, 3), (15, 15)])])
+                                      ("qwen3_8b_b16", [(0, 3), (15, 15)]), ("qwen3_4b_tree", [(0, 0), (7, 15)])])
 def test_base_logits_full_size_sampled(key, rows):
     cfg = synth.CONFIGS[key]
     say(f"case base logits full {key}")
