@@ -16,13 +16,18 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdomino.so")
 
-OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE = 0, 1, 2, 3, 4
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE = 0, -1, -2, -3, -4
+ERR_TIMEOUT, ERR_FIRST_TOKEN = -5, -6
 F32, BF16 = 0, 1
+OP_BASE, OP_CHAIN, OP_TREE, OP_CANDIDATES = 0, 1, 2, 3
+# raw device-side status word at offset 0 of a workspace
 STATUS_FINE, STATUS_BAD_FIRST_TOKEN, STATUS_TIMEOUT = 0, 1, 2
 
-EXPORTS = ("domino_version", "domino_last_error", "domino_base_logits", "domino_chain_workspace_size",
-           "domino_draft_chain", "domino_set_chain_mode", "domino_set_timing_events", "domino_tree_workspace_size",
-           "domino_tree_draft", "domino_tree_candidates", "domino_tree_candidates_workspace_size")
+# include/domino.h (the contract) and include/domino_bench.h (bench and test hooks)
+EXPORTS = ("domino_version", "domino_last_error", "domino_workspace_size", "domino_device_status",
+           "domino_release_cache", "domino_base_logits", "domino_draft_chain", "domino_tree_candidates",
+           "domino_tree_draft")
+BENCH_EXPORTS = ("domino_set_timing_events", "domino_set_chain_mode", "domino_chain_stamp_offset")
 
 
 class DominoError(RuntimeError):
@@ -56,24 +61,26 @@ def lib():
         L.domino_version.argtypes = []
         L.domino_last_error.restype = ctypes.c_char_p
         L.domino_last_error.argtypes = []
+        L.domino_workspace_size.restype = sz
+        L.domino_workspace_size.argtypes = [P, i32, i32, i32, i32]
+        L.domino_device_status.restype = ctypes.c_int
+        L.domino_device_status.argtypes = [P, P]
+        L.domino_release_cache.restype = None
+        L.domino_release_cache.argtypes = []
         L.domino_base_logits.restype = ctypes.c_int
         L.domino_base_logits.argtypes = [P, P, P, i32, P, P]
-        L.domino_chain_workspace_size.restype = sz
-        L.domino_chain_workspace_size.argtypes = [P, i32]
         L.domino_draft_chain.restype = ctypes.c_int
         L.domino_draft_chain.argtypes = [P, P, P, P, P, i32, P, P, P, sz, P]
+        L.domino_tree_candidates.restype = ctypes.c_int
+        L.domino_tree_candidates.argtypes = [P, P, i32, i32, P, P, P, sz, P]
+        L.domino_tree_draft.restype = ctypes.c_int
+        L.domino_tree_draft.argtypes = [P, P, P, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
         L.domino_set_chain_mode.restype = i32
         L.domino_set_chain_mode.argtypes = [i32]
         L.domino_set_timing_events.restype = None
         L.domino_set_timing_events.argtypes = [P, P, P, P]
-        L.domino_tree_workspace_size.restype = sz
-        L.domino_tree_workspace_size.argtypes = [P, i32, i32, i32]
-        L.domino_tree_candidates.restype = ctypes.c_int
-        L.domino_tree_candidates.argtypes = [P, P, i32, i32, P, P, P, sz, P]
-        L.domino_tree_candidates_workspace_size.restype = sz
-        L.domino_tree_candidates_workspace_size.argtypes = [P, i32, i32]
-        L.domino_tree_draft.restype = ctypes.c_int
-        L.domino_tree_draft.argtypes = [P, P, P, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
+        L.domino_chain_stamp_offset.restype = sz
+        L.domino_chain_stamp_offset.argtypes = [P, i32]
         _lib = L
     return _lib
 
@@ -127,13 +134,26 @@ def make_weights(t: dict) -> Weights:
     return Weights(**{k: (t[k].data_ptr() if t.get(k) is not None else None) for k in names})
 
 
+def domino_workspace_size(dims: Dims, batch: int, op: int, nodes: int = 0, topm: int = 0) -> int:
+    return int(lib().domino_workspace_size(ctypes.byref(dims), int(batch), int(op), int(nodes), int(topm)))
+
+
+def domino_device_status(workspace, stream=None):
+    """Waits for the stream and raises DominoError if the last call on `workspace` flagged a device status."""
+    _check(lib().domino_device_status(_ptr(workspace), _stream(stream)))
+
+
+def domino_release_cache():
+    lib().domino_release_cache()
+
+
+def domino_chain_stamp_offset(dims: Dims, batch: int) -> int:
+    return int(lib().domino_chain_stamp_offset(ctypes.byref(dims), int(batch)))
+
+
 def domino_base_logits(dims: Dims, weights: Weights, H, batch: int, base_logits, stream=None):
     _check(lib().domino_base_logits(ctypes.byref(dims), ctypes.byref(weights), _ptr(H), int(batch),
                                     _ptr(base_logits), _stream(stream)))
-
-
-def domino_chain_workspace_size(dims: Dims, batch: int) -> int:
-    return int(lib().domino_chain_workspace_size(ctypes.byref(dims), int(batch)))
 
 
 def domino_draft_chain(dims: Dims, weights: Weights, H, base_logits, first_tokens, batch: int, out_tokens,
@@ -143,18 +163,10 @@ def domino_draft_chain(dims: Dims, weights: Weights, H, base_logits, first_token
                                     _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
-def domino_tree_candidates_workspace_size(dims: Dims, batch: int, topm: int) -> int:
-    return int(lib().domino_tree_candidates_workspace_size(ctypes.byref(dims), int(batch), int(topm)))
-
-
 def domino_tree_candidates(dims: Dims, base_logits, batch: int, topm: int, out_index, out_value, workspace,
                            workspace_bytes: int, stream=None):
     _check(lib().domino_tree_candidates(ctypes.byref(dims), _ptr(base_logits), int(batch), int(topm), _ptr(out_index),
                                         _ptr(out_value), _ptr(workspace), int(workspace_bytes), _stream(stream)))
-
-
-def domino_tree_workspace_size(dims: Dims, batch: int, nodes: int, topm: int) -> int:
-    return int(lib().domino_tree_workspace_size(ctypes.byref(dims), int(batch), int(nodes), int(topm)))
 
 
 def domino_tree_draft(dims: Dims, weights: Weights, H, base_logits, first_tokens, batch: int, nodes: int, topm: int,
@@ -209,13 +221,15 @@ class DraftHead:
         domino_base_logits(self.dims, self.weights, H, B, out, stream)
         return out
 
-    def workspace(self, batch):
+    def workspace(self, batch, op=OP_CHAIN, nodes=0, topm=0):
         import torch
-        n = domino_chain_workspace_size(self.dims, batch)
+        n = domino_workspace_size(self.dims, batch, op, nodes, topm)
         return torch.zeros(max(n, 16), dtype=torch.uint8, device=self.device)
 
     def draft_chain(self, H, base_logits, first_tokens, want_logits=True, out_tokens=None, out_logits=None,
-                    workspace=None, stream=None):
+                    workspace=None, stream=None, check=True):
+        """Enqueue the chain; with `check`, wait for it and raise DominoError on a device status
+        (a timed-out wait, or a first token outside the vocabulary)."""
         import torch
         B = H.shape[0]
         if out_tokens is None:
@@ -226,19 +240,22 @@ class DraftHead:
             workspace = self.workspace(B)
         domino_draft_chain(self.dims, self.weights, H, base_logits, first_tokens, B, out_tokens,
                            out_logits if want_logits else None, workspace, workspace.numel(), stream)
+        if check:
+            domino_device_status(workspace, stream)
         return out_tokens, (out_logits if want_logits else None), workspace
 
-    def tree_draft(self, H, base_logits, first_tokens, nodes, topm, workspace=None, stream=None):
+    def tree_draft(self, H, base_logits, first_tokens, nodes, topm, workspace=None, stream=None, check=True):
         """-> dict of device tensors parents, tokens, depth [B][N] int32 and scores [B][N] fp64, and the workspace."""
         import torch
         B = H.shape[0]
         out = {k: torch.empty((B, nodes), dtype=torch.int32, device=self.device) for k in ("parents", "tokens", "depth")}
         out["scores"] = torch.empty((B, nodes), dtype=torch.float64, device=self.device)
         if workspace is None:
-            n = domino_tree_workspace_size(self.dims, B, nodes, topm)
-            workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=self.device)
+            workspace = self.workspace(B, OP_TREE, nodes, topm)
         domino_tree_draft(self.dims, self.weights, H, base_logits, first_tokens, B, nodes, topm, out["parents"],
                           out["tokens"], out["depth"], out["scores"], workspace, workspace.numel(), stream)
+        if check:
+            domino_device_status(workspace, stream)
         return out, workspace
 
     @staticmethod

@@ -5,16 +5,19 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "../../include/domino.h"
+#include "../../include/domino_bench.h"
 #include "internal.h"
 
 namespace {
 
 thread_local std::string g_error;
-int g_chain_mode = 0;
-hipEvent_t g_base_start = nullptr, g_base_stop = nullptr, g_chain_start = nullptr, g_chain_stop = nullptr;
+// process-wide bench settings (domino_bench.h)
+std::atomic<int> g_chain_mode{0};
+std::atomic<hipEvent_t> g_base_start{nullptr}, g_base_stop{nullptr}, g_chain_start{nullptr}, g_chain_stop{nullptr};
 
 domino_status fail(domino_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 domino_status fail(domino_status s, const char* fmt, ...) {
@@ -88,10 +91,56 @@ void domino_set_timing_events(void* base_start, void* base_stop, void* chain_sta
 
 int32_t domino_set_chain_mode(int32_t mode) {
   if (mode < 0 || mode > 2) return -1;
-  const int32_t prev = g_chain_mode;
-  g_chain_mode = mode;
-  return prev;
+  return g_chain_mode.exchange(mode);
 }
+
+size_t domino_workspace_size(const domino_dims* dims, int32_t batch, int32_t op, int32_t nodes, int32_t topm) {
+  if (check_dims(dims) != DOMINO_OK) return 0;
+  if (batch < 0) return fail(DOMINO_ERR_INVALID_ARGUMENT, "batch %d is negative", batch), 0;
+  const int bs = batch > 0 ? batch : 1;
+  switch (op) {
+    case DOMINO_OP_BASE:
+      return 0;
+    case DOMINO_OP_CHAIN: {
+      const int group = bs < dh::kMaxChainGroup ? bs : dh::kMaxChainGroup;
+      return dh::chain_layout(dims->hidden, dims->gru_hidden, dims->rank, dims->block, group).total;
+    }
+    case DOMINO_OP_TREE:
+      if (nodes < 1 || nodes > 64) return fail(DOMINO_ERR_INVALID_ARGUMENT, "nodes %d must be in [1, 64]", nodes), 0;
+      if (topm < 1 || topm > 256) return fail(DOMINO_ERR_INVALID_ARGUMENT, "topm %d must be in [1, 256]", topm), 0;
+      return dh::tree_layout(dims->hidden, dims->gru_hidden, dims->rank, dims->block, bs, nodes, topm).total;
+    case DOMINO_OP_CANDIDATES:
+      if (topm < 1 || topm > 256) return fail(DOMINO_ERR_INVALID_ARGUMENT, "topm %d must be in [1, 256]", topm), 0;
+      return dh::topm_scratch_bytes(bs * dims->block, topm);
+    default:
+      return fail(DOMINO_ERR_INVALID_ARGUMENT, "op %d is not a domino_op", op), 0;
+  }
+}
+
+size_t domino_chain_stamp_offset(const domino_dims* dims, int32_t batch) {
+  if (domino_workspace_size(dims, batch, DOMINO_OP_CHAIN, 0, 0) == 0) return 0;
+  const int bs = batch > 0 ? batch : 1;
+  const int group = bs < dh::kMaxChainGroup ? bs : dh::kMaxChainGroup;
+  return dh::chain_layout(dims->hidden, dims->gru_hidden, dims->rank, dims->block, group).stamps;
+}
+
+domino_status domino_device_status(const void* workspace, void* stream) {
+  if (!workspace) return fail(DOMINO_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(DOMINO_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+  int32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "reading the device status");
+  if (word == 0) return ok();
+  if (word == dh::kDeviceStatusFirstToken)
+    return fail(DOMINO_ERR_FIRST_TOKEN, "a first token was outside [0, vocab); that sequence was drafted from token 0");
+  if (word == dh::kDeviceStatusTimeout)
+    return fail(DOMINO_ERR_TIMEOUT, "a wait between workgroups gave up after 2 s; the outputs are undefined "
+                                    "(were the device's CUs shared with other work?)");
+  return fail(DOMINO_ERR_DEVICE, "unknown device status %d", word);
+}
+
+void domino_release_cache(void) { dh::release_chain_cache(); }
 
 domino_status domino_base_logits(const domino_dims* dims, const domino_weights* w, const void* H, int32_t batch,
                                  float* base_logits, void* stream) {
@@ -106,20 +155,13 @@ domino_status domino_base_logits(const domino_dims* dims, const domino_weights* 
   if ((int64_t)batch * dims->block > INT32_MAX / 2) return fail(DOMINO_ERR_UNSUPPORTED, "batch too large");
   const int M = batch * dims->block;
   hipError_t e = hipSuccess;
-  if (g_base_start && (e = hipEventRecord(g_base_start, (hipStream_t)stream)) != hipSuccess)
-    return device_fail(e, "timing event");
+  const hipEvent_t ev0 = g_base_start.load(), ev1 = g_base_stop.load();
+  if (ev0 && (e = hipEventRecord(ev0, (hipStream_t)stream)) != hipSuccess) return device_fail(e, "timing event");
   e = dh::launch_gemm_nt(dims->dtype, H, dims->hidden, w->lm_head, dims->hidden, base_logits, dims->vocab, M,
                          dims->vocab, dims->hidden, true, (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "base-logit GEMM launch");
-  if (g_base_stop && (e = hipEventRecord(g_base_stop, (hipStream_t)stream)) != hipSuccess)
-    return device_fail(e, "timing event");
+  if (ev1 && (e = hipEventRecord(ev1, (hipStream_t)stream)) != hipSuccess) return device_fail(e, "timing event");
   return ok();
-}
-
-size_t domino_chain_workspace_size(const domino_dims* dims, int32_t batch) {
-  if (check_dims(dims) != DOMINO_OK || batch < 0) return 0;
-  const int group = batch < dh::kMaxChainGroup ? (batch > 0 ? batch : 1) : dh::kMaxChainGroup;
-  return dh::chain_layout(dims->hidden, dims->gru_hidden, dims->rank, dims->block, group).total;
 }
 
 domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* w, const void* H,
@@ -146,7 +188,7 @@ domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* 
   REQUIRE_PTR(out_tokens, "out_tokens");
   OPTIONAL_PTR(out_logits, "out_logits");
   REQUIRE_PTR(workspace, "workspace");
-  const size_t need = domino_chain_workspace_size(dims, batch);
+  const size_t need = domino_workspace_size(dims, batch, DOMINO_OP_CHAIN, 0, 0);
   if (workspace_bytes < need)
     return fail(DOMINO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes,
                 need);
@@ -195,22 +237,22 @@ domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* 
     a.ll_tok = (uint64_t*)(ws + L.ll_tok);
     a.epoch = (uint32_t*)(ws + L.status + 4);
     a.marker = (uint64_t*)(ws + L.status + 8);
+    a.sig = (uint64_t*)(ws + L.status + 16);
     a.ll_words = (L.trace - L.ll_h) / 8;
+    // the hand-off words are cleared again whenever the region they occupy changes
+    a.sig_value = ((uint64_t)L.ll_h << 32) ^ (uint64_t)a.ll_words ^ ((uint64_t)P << 56) ^ ((uint64_t)Bg << 48);
+    a.stamps = (uint64_t*)(ws + L.stamps);
     a.act_step = L.act_step;
 #ifdef DH_TRACE_PHASES
     a.trace = (uint64_t*)(ws + L.trace);
 #else
     a.trace = nullptr;
 #endif
-    hipError_t e = dh::launch_chain(dims->dtype, a, Hg, g_chain_mode, g0 == 0, s, g_chain_start, g_chain_stop);
+    hipError_t e = dh::launch_chain(dims->dtype, a, Hg, g_chain_mode.load(), g0 == 0, s, g_chain_start.load(),
+                                     g_chain_stop.load());
     if (e != hipSuccess) return device_fail(e, "chain launch");
   }
   return ok();
-}
-
-size_t domino_tree_candidates_workspace_size(const domino_dims* dims, int32_t batch, int32_t topm) {
-  if (check_dims(dims) != DOMINO_OK || batch < 0 || topm < 1 || topm > 256) return 0;
-  return dh::topm_scratch_bytes((batch > 0 ? batch : 1) * dims->block, topm);
 }
 
 domino_status domino_tree_candidates(const domino_dims* dims, const float* base_logits, int32_t batch, int32_t topm,
@@ -226,7 +268,7 @@ domino_status domino_tree_candidates(const domino_dims* dims, const float* base_
   REQUIRE_PTR(out_index, "out_index");
   REQUIRE_PTR(out_value, "out_value");
   REQUIRE_PTR(workspace, "workspace");
-  const size_t need = domino_tree_candidates_workspace_size(dims, batch, topm);
+  const size_t need = domino_workspace_size(dims, batch, DOMINO_OP_CANDIDATES, 0, topm);
   if (workspace_bytes < need)
     return fail(DOMINO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes,
                 need);
@@ -234,12 +276,6 @@ domino_status domino_tree_candidates(const domino_dims* dims, const float* base_
                                  (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "top-M launch");
   return ok();
-}
-
-size_t domino_tree_workspace_size(const domino_dims* dims, int32_t batch, int32_t nodes, int32_t topm) {
-  if (check_dims(dims) != DOMINO_OK || batch < 0 || nodes < 1 || nodes > 64 || topm < 1 || topm > 256) return 0;
-  return dh::tree_layout(dims->hidden, dims->gru_hidden, dims->rank, dims->block, batch > 0 ? batch : 1, nodes, topm)
-      .total;
 }
 
 domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w, const void* H,
@@ -275,7 +311,7 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   OPTIONAL_PTR(out_depth, "out_depth");
   OPTIONAL_PTR(out_scores, "out_scores");
   REQUIRE_PTR(workspace, "workspace");
-  const size_t need = domino_tree_workspace_size(dims, batch, nodes, topm);
+  const size_t need = domino_workspace_size(dims, batch, DOMINO_OP_TREE, nodes, topm);
   if (workspace_bytes < need)
     return fail(DOMINO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes,
                 need);
@@ -320,7 +356,7 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   t.cur = ws + L.cur;
   t.status = (int32_t*)(ws + L.status);
   t.heap_cap = L.heap_cap;
-  hipError_t e = dh::launch_tree(t, true, (hipStream_t)stream, g_chain_start, g_chain_stop);
+  hipError_t e = dh::launch_tree(t, true, (hipStream_t)stream, g_chain_start.load(), g_chain_stop.load());
   if (e != hipSuccess) return device_fail(e, "tree launch");
   return ok();
 }

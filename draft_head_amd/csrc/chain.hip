@@ -770,21 +770,47 @@ __device__ __forceinline__ const W* w2_frag_ptr(const ChainArgs& a, int t, int r
 // The loads are not visible to the compiler's wait-count tracking, hence the
 // explicit wait for all of them; later compiler-issued waits are only ever
 // stricter while these are outstanding, since loads retire in order.
+// Eight 16-byte loads straight into AGPRs; the wait for them is part of the
+// same asm statement, so no output register is seen by the compiler before
+// its data has landed.
+__device__ __forceinline__ void agpr_load8(bf16x8* o, const void* const (&p)[8]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %8, off\n\t"
+      "global_load_dwordx4 %1, %9, off\n\t"
+      "global_load_dwordx4 %2, %10, off\n\t"
+      "global_load_dwordx4 %3, %11, off\n\t"
+      "global_load_dwordx4 %4, %12, off\n\t"
+      "global_load_dwordx4 %5, %13, off\n\t"
+      "global_load_dwordx4 %6, %14, off\n\t"
+      "global_load_dwordx4 %7, %15, off\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&a"(o[0]), "=&a"(o[1]), "=&a"(o[2]), "=&a"(o[3]), "=&a"(o[4]), "=&a"(o[5]), "=&a"(o[6]), "=&a"(o[7])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+      : "memory");
+}
+__device__ __forceinline__ void agpr_load1(bf16x8& o, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=&a"(o) : "v"(p) : "memory");
+}
+
 template <class W, int KC, int NTW>
 __device__ __forceinline__ void load_resident_w2(const ChainArgs& a, int t_begin, int t_end, frag_t<W> (&w2r)[NTW][KC]) {
   static_assert(sizeof(W) == 2, "resident W2 is bf16");
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
+  constexpr int N = NTW * KC;  // fragments of this wave, in groups of 8 per asm statement
+  auto ptr_of = [&](int f) -> const void* {
+    const int i = f / KC, c = f % KC;
+    return w2_frag_ptr<W>(a, min(t_begin + wv + 4 * i, t_end - 1), row, kg, c);
+  };
+  frag_t<W>* flat = &w2r[0][0];
 #pragma unroll
-  for (int i = 0; i < NTW; ++i) {
-    const int t = min(t_begin + wv + 4 * i, t_end - 1);
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const W* ptr = w2_frag_ptr<W>(a, t, row, kg, c);
-      asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(w2r[i][c]) : "v"(ptr) : "memory");
-    }
+  for (int f0 = 0; f0 + 8 <= N; f0 += 8) {
+    const void* const p[8] = {ptr_of(f0), ptr_of(f0 + 1), ptr_of(f0 + 2), ptr_of(f0 + 3),
+                              ptr_of(f0 + 4), ptr_of(f0 + 5), ptr_of(f0 + 6), ptr_of(f0 + 7)};
+    agpr_load8(flat + f0, p);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int f = N - N % 8; f < N; ++f) agpr_load1(flat[f], ptr_of(f));
 }
 
 // the LDS tier: tiles t_begin + 4*NTW + j, j < n_lds
@@ -1211,6 +1237,8 @@ __device__ __forceinline__ void ll_tokens_read(const ChainArgs& a, int p, uint32
 
 // ---- kernels ------------------------------------------------------------------------
 constexpr uint64_t kLLMarker = 0x6c6c2d646f6d696eull;
+// tags are epoch * 128 + step + 1 in 32 bits (steps < 64)
+constexpr uint32_t kEpochLimit = 1u << 25;
 // Before the steps: the H half of the bottleneck for every position,
 // zh[b][p][k] = sum_i H[b][p][i] W1[k][i] (one 16x16 tile per workgroup, k
 // split over the waves), and the zeroed keys and initial state.
@@ -1223,11 +1251,12 @@ __global__ __launch_bounds__(256) void chain_prologue(ChainArgs a, const void* H
   const int nblk = gridDim.x * gridDim.y, blk = blockIdx.y * gridDim.x + blockIdx.x;
   const int tid = blk * blockDim.x + threadIdx.x, stride = nblk * blockDim.x;
   if (blk == 0) {
-    // first launch on this workspace: clear the hand-off words once, so that
-    // no leftover bits can carry a current tag; afterwards the launch counter
-    // alone keeps earlier launches' words from passing
+    // First launch on this workspace, or on a different layout of it, or the
+    // launch counter about to overflow the tags: clear the hand-off words, so
+    // that no leftover bits can carry a current tag; between clears the launch
+    // counter alone keeps earlier launches' words from passing.
     __shared__ int fresh;
-    if (threadIdx.x == 0) fresh = *a.marker != kLLMarker;
+    if (threadIdx.x == 0) fresh = *a.marker != kLLMarker || *a.sig != a.sig_value || *a.epoch + 1 >= kEpochLimit;
     __syncthreads();
     if (fresh) {
       uint4* w = reinterpret_cast<uint4*>(a.ll_h);
@@ -1235,6 +1264,7 @@ __global__ __launch_bounds__(256) void chain_prologue(ChainArgs a, const void* H
       if (threadIdx.x == 0) {
         *a.epoch = 0;
         *a.marker = kLLMarker;
+        *a.sig = a.sig_value;
       }
     }
   }
@@ -1346,6 +1376,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
   const uint32_t ep = *a.epoch;  // advanced by the prologue launch
   float h_own = 0.f;             // this lane's own unit of the GRU state, h(0) = 0
   for (int p = 0; p < a.P; ++p) {
+    if (wg == 0 && threadIdx.x == 0) a.stamps[p] = wall_clock64();
     // G: the previous token of every sequence, then one GRU step for this workgroup's units
     if (p > 0) ll_tokens_reduce(a, p - 1, ep, sred_t);
     BottleneckPre pre{};  // bottleneck terms known before the state: fetched during the GRU step
@@ -1408,6 +1439,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
   if (wg == 0) {
     ll_tokens_read(a, a.P - 1, ep, tok_s);
     for (int b = threadIdx.x; b < a.B; b += blockDim.x) a.out_tokens[(size_t)b * a.P + a.P - 1] = tok_s[b];
+    if (threadIdx.x == 0) a.stamps[a.P] = wall_clock64();
   }
 }
 
@@ -1420,6 +1452,8 @@ ChainLayout chain_layout(int d, int Hs, int r, int P, int group) {
   size_t off = 0;
   L.status = off;
   off += 256;
+  L.stamps = off;
+  off += align256((size_t)(P + 1) * 8);
   L.keys = off;
   off += align256((size_t)P * group * 8);
   L.zh = off;
@@ -1490,9 +1524,24 @@ struct PersistentGate {
   std::mutex m;
   hipEvent_t last = nullptr;
 };
-static PersistentGate& persistent_gate(int dev) {
-  static PersistentGate gates[64];
-  return gates[dev & 63];
+static PersistentGate g_gates[64];
+static PersistentGate& persistent_gate(int dev) { return g_gates[dev & 63]; }
+
+void release_chain_cache() {
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (int dev = 0; dev < 64; ++dev) {
+    PersistentGate& g = g_gates[dev];
+    std::lock_guard<std::mutex> lock(g.m);
+    if (!g.last) continue;
+    // the event belongs to device `dev`: wait for the last launch it marks, then free it
+    if (hipSetDevice(dev) == hipSuccess) {
+      (void)hipEventSynchronize(g.last);
+      (void)hipEventDestroy(g.last);
+    }
+    g.last = nullptr;
+  }
+  if (have_cur) (void)hipSetDevice(cur);
 }
 
 template <class W, int RG, int KC, int kLds, int NTW>
@@ -1548,23 +1597,26 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
   // hand-offs between its phases are what bounds a step; with more
   // sequences the three launches per step, each with all the waves a CU
   // holds for its phase, are faster.
-  persistent = (mode == 2 || (mode == 0 && RG == 1)) && cus > 0 && a.Hs / 4 <= cus;
-  if (persistent) {
-    const size_t g = gru_slice_elems(a.d, a.Hs) * sizeof(W);
-    const size_t w = (size_t)16 * (a.Hs + 8) * sizeof(W);
-    // W2 stays on chip (registers + LDS) when every workgroup's share fits;
-    // the grid is then one workgroup per CU
-    if constexpr (NCB == 1 && resident_fits<W, KC>()) {
-      constexpr int NTW = resident_tiles<KC>();
-      if (mode == 0) {
-        const size_t l2 = resident_lds(cus, a, NTW, KC, w);
-        if (l2 > 0 && l2 <= kLdsBudget) return launch_persistent<W, RG, KC, 2, NTW>(a, l2, s);
+  // fp32 weights (small models) always run the three launches per step
+  persistent = sizeof(W) == 2 && (mode == 2 || (mode == 0 && RG == 1)) && cus > 0 && a.Hs / 4 <= cus;
+  if constexpr (sizeof(W) == 2) {
+    if (persistent) {
+      const size_t g = gru_slice_elems(a.d, a.Hs) * sizeof(W);
+      const size_t w = (size_t)16 * (a.Hs + 8) * sizeof(W);
+      // W2 stays on chip (registers + LDS) when every workgroup's share fits;
+      // the grid is then one workgroup per CU
+      if constexpr (NCB == 1 && resident_fits<W, KC>()) {
+        constexpr int NTW = resident_tiles<KC>();
+        if (mode == 0) {
+          const size_t l2 = resident_lds(cus, a, NTW, KC, w);
+          if (l2 > 0 && l2 <= kLdsBudget) return launch_persistent<W, RG, KC, 2, NTW>(a, l2, s);
+        }
       }
+      const size_t act = act_stage_bytes(a.B, KC, sizeof(W));
+      if (act + g + w <= kLdsBudget) return launch_persistent<W, RG, KC, 2, 0>(a, act + g + w, s);
+      if (act + g <= kLdsBudget) return launch_persistent<W, RG, KC, 1, 0>(a, act + g, s);
+      return launch_persistent<W, RG, KC, 0, 0>(a, act, s);
     }
-    const size_t act = act_stage_bytes(a.B, KC, sizeof(W));
-    if (act + g + w <= kLdsBudget) return launch_persistent<W, RG, KC, 2, 0>(a, act + g + w, s);
-    if (act + g <= kLdsBudget) return launch_persistent<W, RG, KC, 1, 0>(a, act + g, s);
-    return launch_persistent<W, RG, KC, 0, 0>(a, act, s);
   }
   const int nG = a.Hs / 4, nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
   const int nO = T < cus ? T : (cus > 0 ? cus : 256);
@@ -1581,15 +1633,13 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
   return hipGetLastError();
 }
 
-// k chunks of 32 in the bottleneck, rounded up to 1, 2, 4 or 8 (zero padded)
+// Phase O always runs 8 k chunks of 32 (r <= 256): chunks past r meet zero
+// activations (the staged rows are zero padded) and add exact zeros, so a
+// smaller rank gives the same values as a kernel sized for it.
 template <class W, int RG>
 static hipError_t run_chain_kc(const ChainArgs& a, int mode, hipStream_t s, bool& persistent) {
-  const int kc = (a.r + 31) / 32;
-  if (kc <= 1) return run_chain<W, RG, 1>(a, mode, s, persistent);
-  if (kc <= 2) return run_chain<W, RG, 2>(a, mode, s, persistent);
-  if (kc <= 4) return run_chain<W, RG, 4>(a, mode, s, persistent);
-  if (kc <= 8) return run_chain<W, RG, 8>(a, mode, s, persistent);
-  return hipErrorInvalidValue;
+  if (a.r > 8 * 32) return hipErrorInvalidValue;
+  return run_chain<W, RG, 8>(a, mode, s, persistent);
 }
 
 hipError_t launch_chain(int dtype, const ChainArgs& a, const void* H, int mode, bool reset_status, hipStream_t s,

@@ -220,7 +220,7 @@ __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > 
 // or after kWaitTicks of the 100 MHz constant clock (then it sets the status
 // word to 2 itself).
 constexpr uint64_t kWaitTicks = 200000000ull;  // 2 s
-constexpr int kStatusTimeout = 2;
+constexpr int kStatusTimeout = 2;  // same value as kDeviceStatusTimeout
 
 // ---- tagged hand-off words ---------------------------------------------------------
 // A value handed from one workgroup to others inside a persistent launch

@@ -11,6 +11,9 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kMaxChainGroup = 32;  // sequences per chain launch (two 16-column MFMA blocks)
 constexpr int kMaxChainGrid = 1024; // workgroups of a persistent chain launch at most
+// device-side status word at offset 0 of a workspace
+constexpr int kDeviceStatusFirstToken = 1;  // a first token outside [0, V) was replaced by 0
+constexpr int kDeviceStatusTimeout = 2;     // a wait between workgroups gave up
 
 // compute units of the current device (0 if the query fails)
 inline int device_cus() {
@@ -60,15 +63,20 @@ struct ChainArgs {
   uint64_t* ll_tok;        // [P][B][2] per-sequence argmax when reduced in two levels
   uint32_t* epoch;         // launch counter, advanced by the prologue
   uint64_t* marker;        // kLLMarker once the hand-off words have been cleared
+  uint64_t* sig;           // layout signature the hand-off words were cleared for
+  uint64_t sig_value;      // this launch's layout signature
   size_t ll_words;         // hand-off words from ll_h on (all four regions)
+  uint64_t* stamps;        // [P+1] step start clocks of the persistent schedule (first workgroup)
 };
 
 // workspace carving for a chain launch of up to `group` sequences
 struct ChainLayout {
-  size_t status, keys, zh, h, hb, act, ll_h, ll_act, ll_part, ll_tok, trace, total;
+  size_t status, stamps, keys, zh, h, hb, act, ll_h, ll_act, ll_part, ll_tok, trace, total;
   int h_step, hb_step, act_step;
 };
 ChainLayout chain_layout(int d, int Hs, int r, int P, int group);
+// frees the per-device events that order persistent launches
+void release_chain_cache();
 
 // prologue (H half of the bottleneck, zeroed state) then the P steps
 hipError_t launch_chain(int dtype, const ChainArgs& a, const void* H, int mode, bool reset_status, hipStream_t s,

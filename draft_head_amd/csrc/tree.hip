@@ -89,11 +89,20 @@ __device__ void topm_scan_iterative(const float* __restrict__ x, int v_begin, in
       const int v = c0 + q * 256 + threadIdx.x;
       if (v < v_end) {
         const uint64_t k = amax_key(cur[q], (uint32_t)v);
-        if (k > th) buf[atomicAdd(count, 1)] = k;
+        if (k > th) {
+          // at most kTopCap - 1024 keys are kept between rounds and a round
+          // appends at most 1024, so the bound only guards the invariant
+          const int pos = atomicAdd(count, 1);
+          if (pos < kTopCap) buf[pos] = k;
+        }
       }
     }
     __syncthreads();
-    if (*count > kTopCap - 1024) {
+    // every thread takes the branch on the same snapshot of the count, and
+    // no thread appends again before all have read it
+    const int n_now = *count;
+    __syncthreads();
+    if (n_now > kTopCap - 1024) {
       bitonic_desc(buf);
       if (threadIdx.x == 0) {
         *count = M;

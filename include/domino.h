@@ -33,12 +33,26 @@
  *       r = s(W_ir x + b_ir + W_hr h + b_hr), z = s(W_iz x + b_iz + W_hz h + b_hz),
  *       n = tanh(W_in x + b_in + r (W_hn h + b_hn)), h' = (1 - z) n + z h,
  *     starting from h = 0 and reading the anchor token first.
- *   - Errors: a non-zero domino_status is returned and domino_last_error()
+ *   - Errors: a negative domino_status is returned and domino_last_error()
  *     (per thread) describes it.  No C++ exception crosses the ABI.
- *   - Calls are stateless and may run concurrently on distinct streams with
- *     distinct workspaces and outputs.  The persistent chain schedule keeps a
- *     workgroup on every CU for the whole call; the library orders such
- *     launches one after another on each device, whatever their streams.
+ *   - Device-side status.  Conditions found while the kernels run (a first
+ *     token outside [0, V), a wait between workgroups that gave up) cannot be
+ *     returned by the enqueueing call.  The kernels write them to the int32 at
+ *     offset 0 of the call's workspace; domino_device_status() waits for the
+ *     stream and turns that word into a domino_status.  A caller that skips
+ *     it must treat the outputs of a call whose word reads 2 as undefined.
+ *   - Concurrency.  The library keeps no state that changes the results of a
+ *     call.  Calls may run concurrently on distinct streams with distinct
+ *     workspaces and outputs.  The chain's one-launch schedule keeps a
+ *     workgroup on every CU for the whole call and its workgroups wait for
+ *     each other; the library orders such launches one after another on each
+ *     device, whatever their streams (one HIP event per device, kept until
+ *     domino_release_cache).  A device whose CUs are partly held by other
+ *     work (another process, a CU-masked stream) can make those waits give
+ *     up after 2 s: the call then reports DOMINO_ERR_TIMEOUT through
+ *     domino_device_status.
+ *   - Benchmark and test hooks that change process-wide settings live in
+ *     domino_bench.h, outside this contract.
  */
 #ifndef DOMINO_H
 #define DOMINO_H
@@ -52,11 +66,23 @@ extern "C" {
 
 typedef enum {
   DOMINO_OK = 0,
-  DOMINO_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, bad dimension or count */
-  DOMINO_ERR_UNSUPPORTED = 2,      /* valid but outside what the kernels implement     */
-  DOMINO_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required        */
-  DOMINO_ERR_DEVICE = 4            /* a HIP runtime call failed; see domino_last_error  */
+  DOMINO_ERR_INVALID_ARGUMENT = -1, /* null / misaligned pointer, bad dimension or count  */
+  DOMINO_ERR_UNSUPPORTED = -2,      /* valid but outside what the kernels implement      */
+  DOMINO_ERR_WORKSPACE = -3,        /* workspace missing or smaller than required         */
+  DOMINO_ERR_DEVICE = -4,           /* a HIP runtime call failed; see domino_last_error   */
+  DOMINO_ERR_TIMEOUT = -5,          /* (domino_device_status) a wait between workgroups
+                                       gave up: the outputs of that call are undefined   */
+  DOMINO_ERR_FIRST_TOKEN = -6       /* (domino_device_status) a first token was outside
+                                       [0, V); that sequence was drafted from token 0    */
 } domino_status;
+
+/* The call domino_workspace_size is asked about. */
+typedef enum {
+  DOMINO_OP_BASE = 0,      /* domino_base_logits: needs no workspace (size 0)        */
+  DOMINO_OP_CHAIN = 1,     /* domino_draft_chain and domino_draft_chain_sampled       */
+  DOMINO_OP_TREE = 2,      /* domino_tree_draft                                       */
+  DOMINO_OP_CANDIDATES = 3 /* domino_tree_candidates                                  */
+} domino_op;
 
 typedef enum { DOMINO_F32 = 0, DOMINO_BF16 = 1 } domino_dtype;
 
@@ -93,6 +119,33 @@ const char *domino_version(void);
 const char *domino_last_error(void);
 
 /*
+ * Bytes of device workspace a call needs: `op` is a domino_op; `nodes` and
+ * `topm` matter for DOMINO_OP_TREE (both) and DOMINO_OP_CANDIDATES (topm)
+ * only.  Returns 0 for DOMINO_OP_BASE and for arguments the call would reject
+ * (then domino_last_error says why).  A workspace sized for `batch`
+ * sequences serves any smaller batch of the same dims.
+ */
+size_t domino_workspace_size(const domino_dims *dims, int32_t batch, int32_t op, int32_t nodes, int32_t topm);
+
+/*
+ * Device status of the last call that used `workspace` (device): waits for
+ * `stream` (which must be the stream of that call, or one ordered after it),
+ * reads the int32 at offset 0 and returns DOMINO_OK (0), DOMINO_ERR_FIRST_TOKEN
+ * (1) or DOMINO_ERR_TIMEOUT (2); DOMINO_ERR_DEVICE if the wait or the read
+ * fails.  The word is reset by the next call that uses the workspace.
+ */
+domino_status domino_device_status(const void *workspace, void *stream);
+
+/*
+ * Releases what the library keeps for the life of the process: the event that
+ * orders one-launch chain schedules on each device, and the cached launch
+ * settings of the calling thread.  Waits for that event first.  Safe to call
+ * at any time when no call is being enqueued; later calls recreate what they
+ * need.
+ */
+void domino_release_cache(void);
+
+/*
  * Base logits (device):  base_logits[b][p][v] = sum_k H[b][p][k] * lm_head[v][k]
  * for b < batch, p < block, v < vocab, computed with fp32 accumulation and
  * stored fp32.  H is [batch][block][hidden] in dims.dtype.  batch == 0 is a
@@ -100,9 +153,6 @@ const char *domino_last_error(void);
  */
 domino_status domino_base_logits(const domino_dims *dims, const domino_weights *weights, const void *H,
                                  int32_t batch, float *base_logits, void *stream);
-
-/* Bytes of workspace domino_draft_chain needs for `batch` sequences. */
-size_t domino_chain_workspace_size(const domino_dims *dims, int32_t batch);
 
 /*
  * The sequential correction chain over one draft block for `batch`
@@ -116,11 +166,11 @@ size_t domino_chain_workspace_size(const domino_dims *dims, int32_t batch);
  * Outputs (device): out_tokens [batch][P] int32; out_logits [batch][P][V]
  *   fp32 final logits, or NULL to skip them (may equal base_logits for an
  *   in-place update).
- * workspace (device): at least domino_chain_workspace_size(dims, batch)
- *   bytes.  After the call completes, the int32 at offset 0 of the workspace
- *   holds a device-side status: 0 = fine, 1 = a first token was outside
- *   [0, V) (that sequence was drafted from token 0 instead), 2 = an internal
- *   wait timed out (outputs undefined).
+ * workspace (device): at least domino_workspace_size(dims, batch,
+ *   DOMINO_OP_CHAIN, 0, 0) bytes; its device status (domino_device_status):
+ *   1 = a first token was outside [0, V) (that sequence was drafted from
+ *   token 0 instead), 2 = a wait between workgroups gave up (outputs
+ *   undefined).
  * batch == 0 is a no-op.  Calls that share a workspace must not overlap.
  */
 domino_status domino_draft_chain(const domino_dims *dims, const domino_weights *weights, const void *H,
@@ -128,23 +178,18 @@ domino_status domino_draft_chain(const domino_dims *dims, const domino_weights *
                                  int32_t *out_tokens, float *out_logits, void *workspace, size_t workspace_bytes,
                                  void *stream);
 
-/* Bytes of workspace domino_tree_candidates needs (0 for invalid arguments). */
-size_t domino_tree_candidates_workspace_size(const domino_dims *dims, int32_t batch, int32_t topm);
-
 /*
  * Top-M candidates of every base-logit row (the tree's candidate lists,
  * DominoTree summary, "Top-M" restriction): for each of batch*block rows of
  * base_logits [batch][block][vocab] (device, fp32), out_index/out_value
  * [batch][block][topm] (device) hold the topm largest entries ordered by
  * (value desc, index asc); -0.0 counts as +0.0.  1 <= topm <= min(256, vocab).
- * workspace (device): domino_tree_candidates_workspace_size bytes of scratch.
+ * workspace (device): domino_workspace_size(dims, batch,
+ * DOMINO_OP_CANDIDATES, 0, topm) bytes of scratch.
  */
 domino_status domino_tree_candidates(const domino_dims *dims, const float *base_logits, int32_t batch, int32_t topm,
                                      int32_t *out_index, float *out_value, void *workspace, size_t workspace_bytes,
                                      void *stream);
-
-/* Bytes of workspace domino_tree_draft needs (0 for invalid arguments). */
-size_t domino_tree_workspace_size(const domino_dims *dims, int32_t batch, int32_t nodes, int32_t topm);
 
 /*
  * Best-first draft tree with path-conditioned scoring (DominoTree summary,
@@ -174,37 +219,14 @@ size_t domino_tree_workspace_size(const domino_dims *dims, int32_t batch, int32_
  * state rows and eight embedding rows (64*gru_hidden + 32*hidden + 256
  * bytes).  The bf16 GRU step reads its operands directly and has no such
  * limit.
- * The int32 at workspace offset 0 holds the device status after the call
- * (1 = a first token was outside [0, V) and token 0 was used).
+ * workspace (device): domino_workspace_size(dims, batch, DOMINO_OP_TREE,
+ * nodes, topm) bytes; device status 1 = a first token was outside [0, V)
+ * and token 0 was used.
  */
 domino_status domino_tree_draft(const domino_dims *dims, const domino_weights *weights, const void *H,
                                 const float *base_logits, const int32_t *first_tokens, int32_t batch, int32_t nodes,
                                 int32_t topm, int32_t *out_parents, int32_t *out_tokens, int32_t *out_depth,
                                 double *out_scores, void *workspace, size_t workspace_bytes, void *stream);
-
-/*
- * Timing hooks for benchmarks and profilers (hipEvent_t handles passed as
- * void*).  While set, each later domino_base_logits call records base_start
- * on its stream right before its GEMM launch and base_stop right after it,
- * and each domino_draft_chain call records chain_start right before the
- * launch(es) that run the P steps (after the short prologue) and chain_stop
- * right after them; each domino_tree_draft call records the chain pair around
- * all of its launches.  A NULL pair disables that pair.  The events stay owned
- * by the caller.  Process-wide setting; not for concurrent callers.
- */
-void domino_set_timing_events(void *base_start, void *base_stop, void *chain_start, void *chain_stop);
-
-/*
- * Chain scheduling.  0 (default): the library picks; for up to 8 sequences
- * one persistent launch runs all P steps and, for bf16 weights
- * where it fits, keeps W2 on chip (registers and LDS) for all of them; for
- * more sequences, three kernel launches per step.  1: three launches per
- * step.  2: the persistent launch with W2 read from memory every step.  All
- * compute the same function with the same summation order, so their outputs
- * agree to the bit.  Returns the previous mode; any other value is rejected
- * with -1.  Process-wide setting.
- */
-int32_t domino_set_chain_mode(int32_t mode);
 
 #ifdef __cplusplus
 }

@@ -10,25 +10,46 @@ import draft_head_amd as dh
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "domino.h")
+BENCH_HEADER = os.path.join(ROOT, "include", "domino_bench.h")
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(path=HEADER):
+    src = open(path).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(domino_[a-z_0-9]+)\s*\(", src)))
 
 
-def test_header_declares_the_calls():
+def test_header_declares_the_contract_calls():
     names = declared_functions()
-    for n in ("domino_base_logits", "domino_draft_chain", "domino_chain_workspace_size", "domino_last_error"):
+    # the calls of the boundary: the three operations, workspace sizing,
+    # error reporting and cache release
+    for n in ("domino_base_logits", "domino_draft_chain", "domino_tree_draft", "domino_workspace_size",
+              "domino_last_error", "domino_release_cache", "domino_device_status"):
         assert n in names
+    # process-wide hooks stay out of the contract header
+    for n in ("domino_set_chain_mode", "domino_set_timing_events"):
+        assert n not in names and n in declared_functions(BENCH_HEADER)
 
 
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(dh.LIB_PATH)
-    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    declared = declared_functions()
+    bench = declared_functions(BENCH_HEADER)
+    missing = [n for n in declared + bench if not hasattr(lib, n)]
     assert not missing, missing
-    assert set(dh.EXPORTS) >= set(declared_functions())
+    assert set(dh.EXPORTS) == set(declared)
+    assert set(dh.BENCH_EXPORTS) == set(bench)
+
+
+def test_status_codes_are_negative():
+    src = open(HEADER).read()
+    vals = dict((k, int(v)) for k, v in re.findall(r"(DOMINO_(?:OK|ERR_[A-Z_]+))\s*=\s*(-?\d+)", src))
+    assert vals["DOMINO_OK"] == 0
+    assert all(v < 0 for k, v in vals.items() if k != "DOMINO_OK")
+    assert (dh.ERR_INVALID_ARGUMENT, dh.ERR_UNSUPPORTED, dh.ERR_WORKSPACE, dh.ERR_DEVICE, dh.ERR_TIMEOUT,
+            dh.ERR_FIRST_TOKEN) == tuple(vals[k] for k in (
+                "DOMINO_ERR_INVALID_ARGUMENT", "DOMINO_ERR_UNSUPPORTED", "DOMINO_ERR_WORKSPACE", "DOMINO_ERR_DEVICE",
+                "DOMINO_ERR_TIMEOUT", "DOMINO_ERR_FIRST_TOKEN"))
 
 
 def test_version_and_empty_error():
@@ -79,7 +100,7 @@ def test_null_and_misaligned_pointers_rejected():
     assert "aligned" in dh.last_error()
     assert L.domino_base_logits(None, ctypes.byref(_weights()), FAKE, 1, FAKE, None) == dh.ERR_INVALID_ARGUMENT
     assert L.domino_base_logits(ctypes.byref(d), None, FAKE, 1, FAKE, None) == dh.ERR_INVALID_ARGUMENT
-    ws = dh.domino_chain_workspace_size(d, 4)
+    ws = dh.domino_workspace_size(d, 4, dh.OP_CHAIN)
     # every call below is short of workspace or has one bad argument, so none reaches a launch
     args = (ctypes.byref(d), ctypes.byref(_weights()), FAKE, FAKE, FAKE, 4, FAKE, None, FAKE, ws - 1, None)
     assert L.domino_draft_chain(*args) == dh.ERR_WORKSPACE
@@ -104,7 +125,7 @@ def test_null_and_misaligned_pointers_rejected():
 def test_workspace_too_small():
     L = dh.lib()
     d = _dims()
-    need = dh.domino_chain_workspace_size(d, 8)
+    need = dh.domino_workspace_size(d, 8, dh.OP_CHAIN)
     st = L.domino_draft_chain(ctypes.byref(d), ctypes.byref(_weights()), FAKE, FAKE, FAKE, 8, FAKE, None, FAKE,
                               need - 1, None)
     assert st == dh.ERR_WORKSPACE
@@ -124,10 +145,32 @@ def test_negative_and_zero_batch():
 
 def test_workspace_size_grows_then_saturates():
     d = _dims()
-    s = [dh.domino_chain_workspace_size(d, b) for b in (1, 2, 16, 32, 33, 1000)]
+    s = [dh.domino_workspace_size(d, b, dh.OP_CHAIN) for b in (1, 2, 16, 32, 33, 1000)]
     assert s[0] < s[1] < s[2] < s[3]
     assert s[3] == s[4] == s[5]  # sequences run in groups of at most 32
-    assert dh.domino_chain_workspace_size(_dims(hidden=3), 1) == 0
+    assert dh.domino_workspace_size(_dims(hidden=3), 1, dh.OP_CHAIN) == 0
+    assert "hidden" in dh.last_error()
+
+
+def test_workspace_size_by_op():
+    d = _dims()
+    assert dh.domino_workspace_size(d, 8, dh.OP_BASE) == 0
+    assert dh.domino_workspace_size(d, 8, dh.OP_TREE, 16, 64) > 0
+    assert dh.domino_workspace_size(d, 8, dh.OP_CANDIDATES, 0, 64) > 0
+    assert dh.domino_workspace_size(d, 8, 9) == 0
+    assert "op" in dh.last_error()
+    assert dh.domino_workspace_size(d, -1, dh.OP_CHAIN) == 0
+    assert "batch" in dh.last_error()
+    # the step clocks sit inside the chain workspace
+    off = dh.domino_chain_stamp_offset(d, 8)
+    assert 0 < off and off + (d.block + 1) * 8 <= dh.domino_workspace_size(d, 8, dh.OP_CHAIN)
+
+
+def test_device_status_and_release_without_launch():
+    L = dh.lib()
+    assert L.domino_device_status(None, None) == dh.ERR_INVALID_ARGUMENT
+    assert L.domino_device_status(FAKE + 4, None) == dh.ERR_INVALID_ARGUMENT
+    dh.domino_release_cache()  # nothing cached yet: a no-op that needs no device
 
 
 def test_chain_mode_switch():
@@ -142,11 +185,11 @@ def test_chain_mode_switch():
 def test_tree_arguments_rejected_before_launch():
     L = dh.lib()
     d = _dims()
-    ws = dh.domino_tree_workspace_size(d, 8, 16, 64)
+    ws = dh.domino_workspace_size(d, 8, dh.OP_TREE, 16, 64)
     assert ws > 0
-    assert dh.domino_tree_workspace_size(d, 8, 0, 64) == 0
-    assert dh.domino_tree_workspace_size(d, 8, 65, 64) == 0
-    assert dh.domino_tree_workspace_size(d, 8, 16, 257) == 0
+    assert dh.domino_workspace_size(d, 8, dh.OP_TREE, 0, 64) == 0
+    assert dh.domino_workspace_size(d, 8, dh.OP_TREE, 65, 64) == 0
+    assert dh.domino_workspace_size(d, 8, dh.OP_TREE, 16, 257) == 0
     good = dict(dims=ctypes.byref(d), w=ctypes.byref(_weights()), H=FAKE, Lb=FAKE, t0=FAKE, B=8, N=16, M=64,
                 par=FAKE, tok=FAKE, dep=None, sc=None, ws=FAKE, wsb=ws - 1, s=None)
 
@@ -164,7 +207,7 @@ def test_tree_arguments_rejected_before_launch():
     small_v = _dims(vocab=50)
     assert call(dims=ctypes.byref(small_v), M=64, wsb=1 << 40) == dh.ERR_INVALID_ARGUMENT
     assert "vocabulary" in dh.last_error()
-    cw = dh.domino_tree_candidates_workspace_size(d, 2, 8)
+    cw = dh.domino_workspace_size(d, 2, dh.OP_CANDIDATES, 0, 8)
     assert cw > 0
     assert L.domino_tree_candidates(ctypes.byref(d), FAKE, 2, 0, FAKE, FAKE, FAKE, cw, None) == dh.ERR_INVALID_ARGUMENT
     assert L.domino_tree_candidates(ctypes.byref(d), None, 2, 8, FAKE, FAKE, FAKE, cw, None) == dh.ERR_INVALID_ARGUMENT

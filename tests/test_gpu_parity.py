@@ -13,8 +13,8 @@ import torch
 import draft_head_amd as dh
 import oracle
 import synth
-from gpu_common import compare_chain, gemm_bound, say, weights_for
-from helpers import small_config, widen
+from gpu_common import LOGIT_TOL, compare_chain, gemm_bound, say, weights_for
+from helpers import row_rel_err, small_config, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -45,10 +45,17 @@ def _run(cfg, w, inp, want_logits=True, head=None):
     H = head.upload(inp["H"])
     t0 = head.upload(inp["t0"])
     Lb = head.base_logits(H)
-    toks, L, ws = head.draft_chain(H, Lb, t0, want_logits=want_logits)
+    toks, L, ws = head.draft_chain(H, Lb, t0, want_logits=want_logits, check=False)
     torch.cuda.synchronize()
     status = dh.DraftHead.device_status(ws)
     return head, Lb.cpu().numpy(), toks.cpu().numpy(), None if L is None else L.cpu().numpy(), status
+
+
+def _check_base_rel(g, ref, label):
+    """The benchmark spec bar on L^base: row-relative error <= 1e-3 against the oracle."""
+    err = row_rel_err(g, ref)
+    assert err.max() <= LOGIT_TOL, f"{label}: base-logit error {err.max():.3e}"
+    return float(err.max())
 
 
 # ---- base logits ------------------------------------------------------------------
@@ -84,6 +91,7 @@ def test_base_logits_ragged(dtype, d, V, B, P):
     head = dh.DraftHead.from_config(cfg, w)
     g = head.base_logits(head.upload(inp["H"])).cpu().numpy()
     _check_gemm(g, inp["H"], w["lm_head"], dtype, "ragged")
+    _check_base_rel(g, oracle.Model.from_config(cfg, w).base_logits(inp["H"]), "ragged")
 
 
 # one sequence, many columns: the persistent balanced kernel (at least eight
@@ -132,9 +140,11 @@ def test_base_logits_full_size_sampled(key, rows):
     torch.cuda.synchronize()
     assert torch.isfinite(g).all().item()
     w = weights_for(key)
+    m = oracle.Model.from_config(cfg, w)
     for b, p in rows:
         row = g[b, p].cpu().numpy()
         _check_gemm(row[None], inp["H"][b, p][None], w["lm_head"], cfg.dtype, f"{key} row {(b, p)}")
+        _check_base_rel(row[None], m.base_logits(inp["H"][b, p][None]), f"{key} row {(b, p)}")
 
 
 # ---- chain ---------------------------------------------------------------------------
@@ -226,15 +236,22 @@ def test_chain_modes_agree_bitwise(B, r):
     assert np.array_equal(t0_, t2_) and np.array_equal(L0, L2)
 
 
-def test_chain_bad_first_token_flagged():
+def test_chain_bad_first_token_flagged(chain_mode):
     cfg = small_config(d=32, V=101, Hs=16, r=16, P=4, B=3, dtype="bf16")
-    say("case chain bad first token")
+    say(f"case chain bad first token mode={chain_mode}")
     w = synth.make_weights(cfg)
     inp = synth.make_inputs(cfg)
     inp["t0"] = np.array([5, cfg.vocab + 7, -3], np.int32)
-    _, _, toks, _, status = _run(cfg, w, inp, want_logits=False)
+    head, _, toks, _, status = _run(cfg, w, inp, want_logits=False)
     assert status == dh.STATUS_BAD_FIRST_TOKEN
-    assert toks.min() >= 0 and toks.max() < cfg.vocab
+    # the flagged sequences were drafted from token 0: tokens as the oracle drafts them from there
+    m = oracle.Model.from_config(cfg, w)
+    compare_chain(m, inp["H"], m.base_logits(inp["H"]), np.array([5, 0, 0], np.int32), toks, None, "bad t0")
+    # the checked binding call raises on the device status
+    H, t0 = head.upload(inp["H"]), head.upload(inp["t0"])
+    with pytest.raises(dh.DominoError) as ei:
+        head.draft_chain(H, head.base_logits(H), t0, want_logits=False)
+    assert ei.value.status == dh.ERR_FIRST_TOKEN
 
 
 def test_chain_in_place_logits_and_guard_bytes():
@@ -281,12 +298,16 @@ def test_chain_on_side_stream():
     assert torch.equal(toks, ref_t) and torch.equal(L, ref_logits)
 
 
-@pytest.mark.parametrize("key,sample,mode", [("qwen3_4b_b1", [0], 0), ("qwen3_4b_b1", [0], 1),
-                                             ("qwen3_4b_b1", [0], 2), ("qwen3_4b_b32", [0, 13, 31], 0),
-                                             ("qwen3_8b_b16", [0, 15], 0), ("qwen3_8b_b16", [3], 2)])
-def test_chain_full_size_sampled(key, sample, mode):
+# logits: True writes the final logits (compared within 1e-3); False is the
+# tokens-only launch, exactly the call and kernel that bench.py times
+@pytest.mark.parametrize("key,sample,mode,logits", [
+    ("qwen3_4b_b1", [0], 0, True), ("qwen3_4b_b1", [0], 1, True), ("qwen3_4b_b1", [0], 2, True),
+    ("qwen3_4b_b1", [0], 0, False), ("qwen3_4b_b1", [0], 2, False),
+    ("qwen3_4b_b32", [0, 13, 31], 0, True), ("qwen3_4b_b32", [0, 20, 31], 0, False),
+    ("qwen3_8b_b16", [0, 15], 0, True), ("qwen3_8b_b16", [3, 9], 0, False), ("qwen3_8b_b16", [3], 2, True)])
+def test_chain_full_size_sampled(key, sample, mode, logits):
     cfg = synth.CONFIGS[key]
-    say(f"case chain full {key} mode={mode} sample={sample}")
+    say(f"case chain full {key} mode={mode} logits={logits} sample={sample}")
     prev = dh.set_chain_mode(mode)
     try:
         head = device_head(key)
@@ -294,19 +315,135 @@ def test_chain_full_size_sampled(key, sample, mode):
         H = head.upload(inp["H"])
         t0 = head.upload(inp["t0"])
         Lb = head.base_logits(H)
-        toks, L, ws = head.draft_chain(H, Lb, t0)
+        toks, L, ws = head.draft_chain(H, Lb, t0, want_logits=logits)  # raises on a device status
         torch.cuda.synchronize()
-        assert dh.DraftHead.device_status(ws) == 0
     finally:
         dh.set_chain_mode(prev)
     w = weights_for(key)
     m = oracle.Model.from_config(cfg, w)
     Hs_ = np.ascontiguousarray(inp["H"][sample])
     Lb_ref = m.base_logits(Hs_)
-    info = compare_chain(m, Hs_, Lb_ref, inp["t0"][sample], toks.cpu().numpy()[sample], L.cpu().numpy()[sample], key)
+    info = compare_chain(m, Hs_, Lb_ref, inp["t0"][sample], toks.cpu().numpy()[sample],
+                         L.cpu().numpy()[sample] if logits else None, key)
     say("  ", info)
     t = toks.cpu().numpy()
     assert t.min() >= 0 and t.max() < cfg.vocab
+
+
+# ---- exact ties and signed zeros across workgroups ----------------------------------
+def _tie_case(V, zero_w2):
+    """Hand-built base logits (the chain takes them as an input) with exact ties whose
+    copies sit in the tile ranges of the first and of the last workgroups, and rows
+    whose maximum is a signed zero.  With W2 != 0 the tied entries get identical W2
+    rows, so their corrections are identical too."""
+    cfg = small_config(d=64, V=V, Hs=32, r=32, P=5, B=4, dtype="bf16", biases=False)
+    w = synth.make_weights(cfg)
+    if zero_w2:
+        w["w2"] = np.zeros_like(w["w2"])
+    inp = synth.make_inputs(cfg)
+    B, P = cfg.batch, cfg.block
+    rng = np.random.default_rng(11)
+    Lb = (rng.standard_normal((B, P, V)) * 0.5 - 3.0).astype(np.float32)
+    lo, mid, hi = 5, V // 2 + 3, V - 3  # first workgroup's range, the middle, the last one's
+    ties = {  # (b, p): entries holding the row's maximum
+        (0, 0): [lo, hi], (0, 2): [mid, hi], (1, 1): [lo, mid, hi], (2, 3): [hi - 1, hi],
+        (3, 0): [lo, lo + 1], (3, 4): [lo, hi],
+    }
+    for (b, p), idx in ties.items():
+        Lb[b, p, idx] = 40.0
+    zeros = {(1, 3): (lo + 2, -0.0, hi, 0.0), (2, 1): (lo + 2, 0.0, hi, -0.0), (3, 2): (mid, -0.0, hi - 2, 0.0)}
+    for (b, p), (i, vi, j, vj) in zeros.items():
+        Lb[b, p] = -np.abs(Lb[b, p]) - 1.0
+        Lb[b, p, i] = vi
+        Lb[b, p, j] = vj
+    if not zero_w2:
+        for idx in ties.values():
+            for v in idx[1:]:
+                w["w2"][v] = w["w2"][idx[0]]
+    return cfg, w, inp, Lb, ties, zeros
+
+
+@pytest.mark.parametrize("zero_w2", [True, False])
+def test_chain_exact_ties_across_workgroups(chain_mode, zero_w2):
+    V = 60013
+    say(f"case chain ties mode={chain_mode} zero_w2={zero_w2}")
+    cfg, w, inp, Lb, ties, zeros = _tie_case(V, zero_w2)
+    head = dh.DraftHead.from_config(cfg, w)
+    H, t0, Lbd = head.upload(inp["H"]), head.upload(inp["t0"]), head.upload(Lb)
+    for logits in (True, False):
+        toks, L, _ = head.draft_chain(H, Lbd, t0, want_logits=logits)
+        g = toks.cpu().numpy()
+        for (b, p), idx in ties.items():
+            assert g[b, p] == min(idx), ((b, p), g[b, p], idx)
+        if zero_w2:  # zero correction: L = L^base bitwise, both signed zeros count as the maximum
+            for (b, p), (i, _, j, _) in zeros.items():
+                assert g[b, p] == min(i, j), ((b, p), g[b, p])
+            assert np.array_equal(g, np.argmax(Lb + np.float32(0.0), axis=-1))
+            if logits:
+                assert np.array_equal(L.cpu().numpy(), Lb)
+        m = oracle.Model.from_config(cfg, w)
+        compare_chain(m, inp["H"], Lb, inp["t0"], g, L.cpu().numpy() if logits else None, "ties")
+
+
+# ---- the worked micro example, zero padded ---------------------------------------------
+# V=4, d=2, Hs=1, r=1, P=2 (written out below); padded to d = Hs = r = 8 with
+# zeros, which leaves every value unchanged: padded GRU units keep h = 0
+# (h' = h/2 with all their weights zero), padded bottleneck units give SiLU(0) = 0.
+MICRO_EXPECT = {  # t0 -> (tokens, logits at p=0, logits at p=1), closed forms of the definitions
+    0: ([0, 1], [1, 0, 1, -1], [0, 1, 1, 0]),
+    1: ([1, 1], [1, 1.2505490219, -0.2505490219, -1], [0, 3.0736888186, -1.0736888186, 0]),
+    2: ([2, 2], [1, -0.2447974530, 1.2447974530, -1], [0, 0.8480316599, 1.1519683401, 0]),
+    3: ([2, 2], [1, -0.2726392900, 1.2726392900, -1], [0, 0.8289735483, 1.1710264517, 0]),
+}
+
+
+def _micro_weights(dtype):
+    d = Hs = r = 8
+    V = 4
+    f = np.float32
+    lm = np.zeros((V, d), f)
+    lm[:, :2] = [[1, 0], [0, 1], [1, 1], [-1, 0]]
+    E = np.zeros((V, d), f)
+    E[:, :2] = [[0, 0], [1, 0], [0, 1], [1, 1]]
+    w_ih = np.zeros((3 * Hs, d), f)
+    w_ih[2 * Hs + 0, :2] = [1, -2]          # only the n gate of unit 0 reads x
+    w_hh = np.zeros((3 * Hs, Hs), f)
+    w1 = np.zeros((r, d + Hs), f)
+    w1[0, d + 0] = 4.0                       # bottleneck unit 0 reads state unit 0
+    w2 = np.zeros((V, r), f)
+    w2[:, 0] = [0, 1, -1, 0]
+    w = {"lm_head": lm, "embed": E, "w_ih": w_ih, "w_hh": w_hh, "w1": w1, "w2": w2}
+    if dtype == "bf16":  # every value above is exact in bf16
+        w = {k: (v.view(np.uint32) >> 16).astype(np.uint16) for k, v in w.items()}
+    H = np.zeros((4, 2, d), f)
+    H[:, 0, 0] = 1.0
+    H[:, 1, 1] = 1.0
+    if dtype == "bf16":
+        H = (H.view(np.uint32) >> 16).astype(np.uint16)
+    return w, H
+
+
+@pytest.mark.parametrize("dtype,tol", [("f32", 1e-6), ("bf16", 2e-5)])
+def test_chain_micro_example(chain_mode, dtype, tol):
+    """All four anchors at once (one sequence each).  fp32 weights: logits within 1e-6 of the
+    closed forms.  bf16: the fp32 activations meet the weights as bf16 hi + lo, which keeps
+    them to 2^-17 relative, so the bound is 2e-5 at these magnitudes."""
+    say(f"case chain micro example mode={chain_mode} {dtype}")
+    w, H = _micro_weights(dtype)
+    head = dh.DraftHead(8, 4, 8, 8, 2, dtype, w)
+    Hd = head.upload(H)
+    t0 = head.upload(np.arange(4, dtype=np.int32))
+    Lb = head.base_logits(Hd)
+    assert np.array_equal(Lb.cpu().numpy()[0], np.array([[1, 0, 1, -1], [0, 1, 1, 0]], np.float32))
+    for logits in (True, False):
+        toks, L, _ = head.draft_chain(Hd, Lb, t0, want_logits=logits)
+        g = toks.cpu().numpy()
+        for t in range(4):
+            exp_tok, l0, l1 = MICRO_EXPECT[t]
+            assert g[t].tolist() == exp_tok, (t, g[t])
+            if logits:
+                Lt = L.cpu().numpy()[t].astype(np.float64)
+                assert np.max(np.abs(Lt - np.array([l0, l1]))) <= tol, (t, Lt)
 
 
 def test_timing_events_bracket_main_launches():

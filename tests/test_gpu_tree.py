@@ -30,7 +30,7 @@ def _device():
 
 def _gpu_tree(cfg, w, H, Lb, t0, N, M):
     head = dh.DraftHead.from_config(cfg, w)
-    out, ws = head.tree_draft(head.upload(H), head.upload(Lb), head.upload(t0), N, M)
+    out, ws = head.tree_draft(head.upload(H), head.upload(Lb), head.upload(t0), N, M, check=False)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}, dh.DraftHead.device_status(ws)
 
@@ -95,6 +95,10 @@ def test_tree_bad_first_token_flagged():
     assert st == dh.STATUS_BAD_FIRST_TOKEN
     o = m.tree(inp["H"], Lb, np.array([0, 3], np.int32), 8, 4)  # drafted from token 0 instead
     _compare(g, o, "bad first token")
+    head = dh.DraftHead.from_config(cfg, w)
+    with pytest.raises(dh.DominoError) as ei:
+        head.tree_draft(head.upload(inp["H"]), head.upload(Lb), head.upload(np.array([-1, 3], np.int32)), 8, 4)
+    assert ei.value.status == dh.ERR_FIRST_TOKEN
 
 
 def test_tree_full_size():
@@ -108,10 +112,28 @@ def test_tree_full_size():
     head = dh.DraftHead.from_config(cfg, w)
     out, ws = head.tree_draft(head.upload(inp["H"]), head.upload(Lb), head.upload(inp["t0"]), cfg.nodes, cfg.topm)
     torch.cuda.synchronize()
-    assert dh.DraftHead.device_status(ws) == 0
     g = {k: v.cpu().numpy() for k, v in out.items()}
     o = oracle.Model.from_config(cfg, w).tree(inp["H"], Lb, inp["t0"], cfg.nodes, cfg.topm)
     _compare(g, o, key)
+
+
+def test_tree_full_size_after_gpu_base_logits():
+    """The whole tree path at full size: the GPU's LM-head GEMM gives L^base, and both the
+    GPU tree and the oracle tree take exactly those fp32 values (the tree is a function of
+    its L^base input), at the bench's batch, budget and candidate count."""
+    key = "qwen3_4b_tree"
+    cfg = synth.CONFIGS[key]
+    say(f"case tree full {key} with the GPU's own base logits")
+    w = weights_for("qwen3_4b_b1")
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    H = head.upload(inp["H"])
+    Lb = head.base_logits(H)
+    out, _ = head.tree_draft(H, Lb, head.upload(inp["t0"]), cfg.nodes, cfg.topm)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    o = oracle.Model.from_config(cfg, w).tree(inp["H"], Lb.cpu().numpy(), inp["t0"], cfg.nodes, cfg.topm)
+    _compare(g, o, key + " (GPU base logits)")
 
 
 @pytest.mark.parametrize("kind", ["random", "ties", "constant", "ascending", "small_v", "wide", "wide_m256",
@@ -148,7 +170,7 @@ def test_candidates_match_oracle_topm(kind):
     x = torch.from_numpy(np.ascontiguousarray(Lb)).cuda()
     idx = torch.empty((B, P, M), dtype=torch.int32, device="cuda")
     val = torch.empty((B, P, M), dtype=torch.float32, device="cuda")
-    ws = torch.zeros(dh.domino_tree_candidates_workspace_size(dims, B, M), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(dh.domino_workspace_size(dims, B, dh.OP_CANDIDATES, 0, M), dtype=torch.uint8, device="cuda")
     dh.domino_tree_candidates(dims, x, B, M, idx, val, ws, ws.numel())
     torch.cuda.synchronize()
     gi, gv = idx.cpu().numpy(), val.cpu().numpy()
