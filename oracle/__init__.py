@@ -47,6 +47,10 @@ def _load():
             "oracle_chain": ([P, P, i32, P, P, P, P, P, P, P], None),
             "oracle_topm": ([P, i32, i32, P, P], None),
             "oracle_tree": ([P, P, i32, P, P, P, i32, i32, P, P, P, P], None),
+            "oracle_philox4x32_10": ([P, P, P], None),
+            "oracle_gumbel": ([ctypes.c_uint64, i32, i32, i32], f64),
+            "oracle_chain_sampled": ([P, P, i32, i32, P, P, P, P, f64, ctypes.c_uint64, P, P, P], None),
+            "oracle_tree_verify_inputs": ([i32, i32, P, P, P, P, P, P, P], None),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -151,6 +155,24 @@ class Model:
                              _ptr(forced), _ptr(tokens), _ptr(logits), _ptr(margins))
         return tokens, logits, margins
 
+    def chain_sampled(self, H, Lb, t0, temperature, seed, seq0=0, forced=None, want_logits=True):
+        """Gumbel-max chain at `temperature` -> (tokens, logits|None, perturbed margins)."""
+        H = self._store(H)
+        Lb = np.ascontiguousarray(Lb, dtype=np.float32)
+        t0 = np.ascontiguousarray(t0, dtype=np.int32)
+        B, P, V = t0.size, self.dims.block, self.dims.vocab
+        assert H.size == B * P * self.dims.hidden and Lb.size == B * P * V
+        if forced is not None:
+            forced = np.ascontiguousarray(forced, dtype=np.int32)
+            assert forced.size == B * P
+        tokens = np.empty((B, P), dtype=np.int32)
+        margins = np.empty((B, P), dtype=np.float64)
+        logits = np.empty((B, P, V), dtype=np.float64) if want_logits else None
+        _load().oracle_chain_sampled(ctypes.byref(self.dims), ctypes.byref(self.weights), B, int(seq0), _ptr(H),
+                                     _ptr(Lb), _ptr(t0), _ptr(forced), float(temperature), int(seed), _ptr(tokens),
+                                     _ptr(logits), _ptr(margins))
+        return tokens, logits, margins
+
     def tree(self, H, Lb, t0, nodes, topm):
         """-> dict(parents, tokens, depth, scores), each [B][N]."""
         H = self._store(H)
@@ -190,3 +212,30 @@ def topm(row, M):
     val = np.empty(M, dtype=np.float32)
     _load().oracle_topm(_ptr(row), row.size, M, _ptr(idx), _ptr(val))
     return idx, val
+
+
+def philox4x32_10(counter, key):
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, dtype=np.uint32)
+    _load().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def gumbel(seed, b, p, v) -> float:
+    return _load().oracle_gumbel(int(seed), int(b), int(p), int(v))
+
+
+def tree_verify_inputs(parents, tokens, first_tokens, start_positions=None):
+    """parents, tokens [B][N] -> (mask [B][N+1][N+1] uint8, positions [B][N+1], tokens [B][N+1])."""
+    parents = np.ascontiguousarray(parents, dtype=np.int32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    first_tokens = np.ascontiguousarray(first_tokens, dtype=np.int32)
+    B, N = parents.shape
+    sp = None if start_positions is None else np.ascontiguousarray(start_positions, dtype=np.int32)
+    mask = np.empty((B, N + 1, N + 1), dtype=np.uint8)
+    pos = np.empty((B, N + 1), dtype=np.int32)
+    tok = np.empty((B, N + 1), dtype=np.int32)
+    _load().oracle_tree_verify_inputs(B, N, _ptr(parents), _ptr(tokens), _ptr(first_tokens), _ptr(sp), _ptr(mask),
+                                      _ptr(pos), _ptr(tok))
+    return mask, pos, tok

@@ -26,8 +26,23 @@
  * children scored by a log-softmax over the M corrected candidate logits,
  * heap key (score desc, parent index asc, candidate rank asc).
  *
+ * Sampling at temperature T > 0 (the pages report decoding at T = 1 next
+ * to greedy decoding: 163.com explainer, section 6; DominoTree summary,
+ * experiments at T in {0, 0.5, 1}) is written as the Gumbel-max trick:
+ * argmax_v (L_v + T g_v) with g_v standard Gumbel noise, which draws v with
+ * probability softmax(L / T)_v.  The noise comes from the counter-based
+ * generator Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011), written here from that
+ * definition; its counter layout is fixed below so the GPU path can draw
+ * the same numbers from its own implementation.
+ *
+ * Verification inputs of a drafted tree follow the standard tree-attention
+ * verification that DominoTree reuses unchanged (DominoTree summary,
+ * "方法论 / 核心组件", verification: an ancestor-only causal mask).
+ *
  * Parity pins: tests/test_oracle_*.py (hand values, torch float64
- * library routines, brute-force tree enumeration, closed forms).
+ * library routines, brute-force tree enumeration, closed forms, the
+ * generator's published known-answer vectors, distribution tests).
  */
 #include <math.h>
 #include <stdint.h>
@@ -361,4 +376,152 @@ void oracle_tree(const od_dims *D, const od_weights *W, int32_t B, const void *H
   free(a);
   free(l);
   free(heap);
+}
+
+/* ---- sampling at temperature T ------------------------------------------------ */
+
+/*
+ * Philox4x32-10: 10 rounds on a 128-bit counter (c0..c3) under a 64-bit key
+ * (k0, k1).  A round multiplies c0 and c2 by the constants 0xD2511F53 and
+ * 0xCD9E8D57 into 64-bit products (hi, lo) and returns
+ *   (hi(c2 M1) ^ c1 ^ k0, lo(c2 M1), hi(c0 M0) ^ c3 ^ k1, lo(c0 M0));
+ * before every round after the first the key is advanced by the Weyl
+ * constants (0x9E3779B9, 0xBB67AE85).
+ */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+    c0 = n0;
+    c1 = n1;
+    c2 = n2;
+    c3 = n3;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+/*
+ * The standard Gumbel noise of sequence b (its index in the whole batch),
+ * block position p and vocabulary entry v under `seed`:
+ *   x = word (b & 1) of Philox4x32-10(counter (v, p, b >> 1, 0), key (seed lo, seed hi)),
+ *   u = (2 (x >> 9) + 1) / 2^24          (in (0, 1), exact in fp32),
+ *   g = -log(-log(u)).
+ */
+double oracle_gumbel(uint64_t seed, int32_t b, int32_t p, int32_t v) {
+  const uint32_t ctr[4] = {(uint32_t)v, (uint32_t)p, (uint32_t)b >> 1, 0u};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t x[4];
+  oracle_philox4x32_10(ctr, key, x);
+  const double u = (2.0 * (double)(x[b & 1] >> 9) + 1.0) / 16777216.0;
+  return -log(-log(u));
+}
+
+/*
+ * The correction chain with the token of every position drawn at
+ * temperature T >= 0 (Gumbel-max): the chain of oracle_chain, except that
+ *   tokens[b][p] = argmax_v (L[b][p][v] + T g(seed, b, p, v))
+ * (first index on exact ties) and the token fed back is that draw (or
+ * forced[b][p]).  T = 0 is the greedy chain.  logits are the unperturbed L;
+ * margins are the top-2 margins of the perturbed values.  b counts from
+ * `seq0` in the whole batch (the noise depends on it).
+ */
+void oracle_chain_sampled(const od_dims *D, const od_weights *W, int32_t B, int32_t seq0, const void *H,
+                          const float *Lb, const int32_t *t0, const int32_t *forced, double temperature,
+                          uint64_t seed, int32_t *tokens, double *logits, double *margins) {
+  const int d = D->hidden, V = D->vocab, Hs = D->gru_hidden, r = D->rank, P = D->block, dt = D->dtype;
+  double *x = malloc(sizeof(double) * d);
+  double *h = malloc(sizeof(double) * Hs);
+  double *hn = malloc(sizeof(double) * Hs);
+  double *a = malloc(sizeof(double) * r);
+  double *L = malloc(sizeof(double) * V);
+  double *Lp = malloc(sizeof(double) * V);
+  const size_t hrow_bytes = dt == 0 ? 4 : 2;
+  for (int b = 0; b < B; ++b) {
+    for (int j = 0; j < Hs; ++j) h[j] = 0.0;
+    int32_t prev = t0[b];
+    for (int p = 0; p < P; ++p) {
+      for (int k = 0; k < d; ++k) x[k] = elem(W->embed, dt, (size_t)prev * d + k);
+      oracle_gru_cell(D, W, x, h, hn);
+      memcpy(h, hn, sizeof(double) * Hs);
+      const size_t row = (size_t)b * P + p;
+      oracle_head_bottleneck(D, W, (const char *)H + row * d * hrow_bytes, h, a);
+      oracle_final_logits(D, W, Lb + row * V, a, L);
+#pragma omp parallel for schedule(static)
+      for (int v = 0; v < V; ++v) Lp[v] = temperature > 0.0 ? L[v] + temperature * oracle_gumbel(seed, seq0 + b, p, v) : L[v];
+      double m;
+      const int32_t t = oracle_argmax(Lp, V, &m);
+      tokens[row] = t;
+      if (margins) margins[row] = m;
+      if (logits) memcpy(logits + row * V, L, sizeof(double) * V);
+      prev = forced ? forced[row] : t;
+    }
+  }
+  free(x);
+  free(h);
+  free(hn);
+  free(a);
+  free(L);
+  free(Lp);
+}
+
+/* ---- verification inputs of a drafted tree ------------------------------------------ */
+
+/*
+ * The flattened tree of one sequence as the target model verifies it:
+ * entry 0 is the anchor, entry k + 1 is node k.  Node k is part of the tree
+ * when its token is >= 0 and its parent is the anchor (-1) or an earlier
+ * node (0 <= parent < k) that is itself part of the tree; other slots are
+ * padding.  For a tree node, its depth is 1 + its parent's (anchor 0).
+ *   out_tokens[i]    anchor token, node tokens; -1 for padding
+ *   out_positions[i] start + depth; -1 for padding
+ *   out_mask[i][j]   1 when entry j is entry i itself or one of its
+ *                    ancestors (the anchor is an ancestor of every tree
+ *                    node); a padding row holds only its own diagonal
+ * Arrays per sequence: parents, tokens [N]; out_mask [N+1][N+1] bytes,
+ * out_positions and out_tokens [N+1].
+ */
+void oracle_tree_verify_inputs(int32_t B, int32_t N, const int32_t *parents, const int32_t *tokens,
+                               const int32_t *first_tokens, const int32_t *start_positions, uint8_t *out_mask,
+                               int32_t *out_positions, int32_t *out_tokens) {
+  const int E = N + 1;
+  int32_t *depth = malloc(sizeof(int32_t) * (size_t)E);
+  int32_t *in_tree = malloc(sizeof(int32_t) * (size_t)E);
+  for (int b = 0; b < B; ++b) {
+    const int32_t *par = parents + (size_t)b * N, *tok = tokens + (size_t)b * N;
+    uint8_t *mask = out_mask + (size_t)b * E * E;
+    const int32_t start = start_positions ? start_positions[b] : 0;
+    in_tree[0] = 1;
+    depth[0] = 0;
+    for (int k = 0; k < N; ++k) {
+      const int32_t q = par[k];
+      const int ok = tok[k] >= 0 && q >= -1 && q < k && in_tree[q + 1];
+      in_tree[k + 1] = ok;
+      depth[k + 1] = ok ? depth[q + 1] + 1 : 0;
+    }
+    for (int i = 0; i < E; ++i) {
+      for (int j = 0; j < E; ++j) mask[(size_t)i * E + j] = 0;
+      mask[(size_t)i * E + i] = 1;
+      if (in_tree[i] && i > 0) {
+        /* walk up the parent links to the anchor */
+        int e = i;
+        while (e != 0) {
+          e = par[e - 1] + 1;
+          mask[(size_t)i * E + e] = 1;
+        }
+      }
+      out_positions[(size_t)b * E + i] = in_tree[i] ? start + depth[i] : -1;
+      out_tokens[(size_t)b * E + i] = i == 0 ? first_tokens[b] : (in_tree[i] ? tok[i - 1] : -1);
+    }
+  }
+  free(depth);
+  free(in_tree);
 }
