@@ -36,12 +36,14 @@ def _run(cmd):
     return res.returncode, err
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Builds the library (extra_flags / out: a differently configured copy, e.g. for tracing)."""
+    obj_dir = OBJ_DIR if out == LIB else OBJ_DIR + "_" + os.path.basename(out).replace(".", "_")
+    os.makedirs(obj_dir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include")]
     jobs = []
     for src in sources():
-        obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + ".o")
+        obj = os.path.join(obj_dir, os.path.basename(src)[:-4] + ".o")
         jobs.append((src, [HIPCC, *FLAGS, *extra_flags, *inc, "-c", src, "-o", obj], obj))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with ThreadPoolExecutor(max_workers=workers) as ex:
@@ -53,12 +55,12 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             raise RuntimeError(f"hipcc failed on {os.path.basename(src)} ({rc}):\n{err}")
         if err.strip() and verbose:
             print(err, flush=True)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     rc, err = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, _, o in jobs], "-o", tmp])
     if rc != 0:
         raise RuntimeError(f"link failed ({rc}):\n{err}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -90,7 +90,7 @@ void domino_set_timing_events(void* base_start, void* base_stop, void* chain_sta
 }
 
 int32_t domino_set_chain_mode(int32_t mode) {
-  if (mode < 0 || mode > 2) return -1;
+  if (mode < 0 || mode > 3) return -1;
   return g_chain_mode.exchange(mode);
 }
 

@@ -262,8 +262,10 @@ __device__ __forceinline__ void ll_put4(uint64_t* slot, int n, int b, int k, con
 
 // per-wave partial sums of W_hh h(p) over this wave's k chunks
 // kLL: the state comes as hand-off words of the persistent launch `ep`
+// seq0: first sequence of this work item's 16 NCB columns (three-launch schedule)
 template <class W, int NCB, bool kLds, bool kLL = false>
-__device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int item, const W* lds, f32x4 (&acc)[NCB], uint32_t ep = 0) {
+__device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int item, const W* lds, f32x4 (&acc)[NCB], uint32_t ep = 0,
+                                                int seq0 = 0) {
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (p == 0) return;  // h(0) = 0
@@ -277,7 +279,7 @@ __device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int i
   bool bok[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    const int b = cb * 16 + row;
+    const int b = seq0 + cb * 16 + row;
     bok[cb] = b < B;
     bb[cb] = bok[cb] ? b : 0;
   }
@@ -320,14 +322,14 @@ __device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int i
 
 template <class W, int NCB, bool kLL>
 __device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[NCB], float& h_own,
-                          uint32_t ep);
+                          uint32_t ep, int seq0 = 0);
 
 // input half on top of the hidden-half partials, then the gates: h(p+1)
 // tok: this step's previous tokens by sequence (raw argmax indices), or
 // null to read them from the argmax keys / first tokens
 template <class W, int NCB, bool kLds, bool kLL = false>
 __device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, float* red, const W* lds, const f32x4 (&acc_h)[NCB],
-                           const int32_t* tok = nullptr, float* h_own = nullptr, uint32_t ep = 0) {
+                           const int32_t* tok = nullptr, float* h_own = nullptr, uint32_t ep = 0, int seq0 = 0) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int d = a.d, B = a.B;
@@ -339,7 +341,7 @@ __device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, 
   bool bok[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    const int b = cb * 16 + row;
+    const int b = seq0 + cb * 16 + row;
     bok[cb] = b < B;
     const int t_ = bok[cb] ? (tok ? clamp_token(a, tok[b]) : prev_token(a, p, b)) : 0;
     xe[cb] = (const W*)a.embed + (size_t)t_ * d + kg * 8;
@@ -368,7 +370,7 @@ __device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, 
   }
 
   float h_dummy = 0.f;
-  gru_gates<W, NCB, kLL>(a, p, item, red, acc, h_own ? *h_own : h_dummy, ep);
+  gru_gates<W, NCB, kLL>(a, p, item, red, acc, h_own ? *h_own : h_dummy, ep, seq0);
 }
 
 // Sum the four waves' pre-activation partials and apply the gates: h(p+1).
@@ -378,7 +380,7 @@ __device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, 
 // hand-off words only.
 template <class W, int NCB, bool kLL>
 __device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[NCB], float& h_own,
-                          uint32_t ep) {
+                          uint32_t ep, int seq0) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int Hs = a.Hs, B = a.B, j0 = item * 4;
@@ -401,7 +403,7 @@ __device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, f
       pre[3] += v.w;
     }
     // result rows 4*kg + i are gate i of unit j0 + kg; column = sequence
-    const int b = cb * 16 + row, j = j0 + kg;
+    const int b = seq0 + cb * 16 + row, j = j0 + kg;
     float hn = 0.f;
     if (b < B) {
       const float rg = sigmoidf_(pre[0] + bias_at(a.b_ih, j) + bias_at(a.b_hh, j));
@@ -1287,6 +1289,9 @@ __global__ void chain_finalize(ChainArgs a) {
   }
 }
 
+// Three-launch schedule, phase G: work item = 4 units, all sequences.
+// (Splitting the sequences over workgroups, 16 per workgroup, measured
+// slower at 32 sequences: 16.4 against 14.9 us per step.)
 template <class W, int NCB>
 __global__ __launch_bounds__(256) void chain_gru_k(ChainArgs a, int p) {
   __shared__ __attribute__((aligned(16))) float red[4 * NCB * 64 * 4];
@@ -1598,7 +1603,7 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
   // sequences the three launches per step, each with all the waves a CU
   // holds for its phase, are faster.
   // fp32 weights (small models) always run the three launches per step
-  persistent = sizeof(W) == 2 && (mode == 2 || (mode == 0 && RG == 1)) && cus > 0 && a.Hs / 4 <= cus;
+  persistent = sizeof(W) == 2 && (mode >= 2 || (mode == 0 && RG == 1)) && cus > 0 && a.Hs / 4 <= cus;
   if constexpr (sizeof(W) == 2) {
     if (persistent) {
       const size_t g = gru_slice_elems(a.d, a.Hs) * sizeof(W);
@@ -1607,7 +1612,7 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
       // the grid is then one workgroup per CU
       if constexpr (NCB == 1 && resident_fits<W, KC>()) {
         constexpr int NTW = resident_tiles<KC>();
-        if (mode == 0) {
+        if (mode == 0 || mode == 3) {
           const size_t l2 = resident_lds(cus, a, NTW, KC, w);
           if (l2 > 0 && l2 <= kLdsBudget) return launch_persistent<W, RG, KC, 2, NTW>(a, l2, s);
         }

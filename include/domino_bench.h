@@ -35,9 +35,11 @@ void domino_set_timing_events(void *base_start, void *base_stop, void *chain_sta
  * runs all P steps and, for bf16 weights where every workgroup's share fits,
  * keeps W2 on chip (registers and LDS) for all of them; otherwise three
  * kernel launches per step.  1: three launches per step.  2: the persistent
- * launch with W2 read from memory every step.  All compute the same function
- * with the same summation order, so their outputs agree to the bit.  Returns
- * the previous mode; any other value is rejected with -1.
+ * launch with W2 read from memory every step.  3: the persistent launch,
+ * keeping W2 on chip wherever its share fits (else as 2), whatever the batch.
+ * All compute the same function with the same summation order, so their
+ * outputs agree to the bit.  Returns the previous mode; any other value is
+ * rejected with -1.
  */
 int32_t domino_set_chain_mode(int32_t mode);
 

@@ -177,7 +177,7 @@ def test_chain_mode_switch():
     prev = dh.set_chain_mode(1)
     assert dh.set_chain_mode(2) == 1
     assert dh.set_chain_mode(prev) == 2
-    for bad in (7, 3, -1):
+    for bad in (7, 4, -1):
         with pytest.raises(ValueError):
             dh.set_chain_mode(bad)
 
