@@ -25,8 +25,8 @@ STATUS_FINE, STATUS_BAD_FIRST_TOKEN, STATUS_TIMEOUT = 0, 1, 2
 
 # include/domino.h (the contract) and include/domino_bench.h (bench and test hooks)
 EXPORTS = ("domino_version", "domino_last_error", "domino_workspace_size", "domino_device_status",
-           "domino_release_cache", "domino_base_logits", "domino_draft_chain", "domino_tree_candidates",
-           "domino_tree_draft")
+           "domino_release_cache", "domino_base_logits", "domino_draft_chain", "domino_draft_chain_noalloc",
+           "domino_noalloc_device_status", "domino_tree_candidates", "domino_tree_draft")
 BENCH_EXPORTS = ("domino_set_timing_events", "domino_set_chain_mode", "domino_chain_stamp_offset")
 
 
@@ -71,6 +71,10 @@ def lib():
         L.domino_base_logits.argtypes = [P, P, P, i32, P, P]
         L.domino_draft_chain.restype = ctypes.c_int
         L.domino_draft_chain.argtypes = [P, P, P, P, P, i32, P, P, P, sz, P]
+        L.domino_draft_chain_noalloc.restype = ctypes.c_int
+        L.domino_draft_chain_noalloc.argtypes = [P, P, P, P, P, i32, P, P, P]
+        L.domino_noalloc_device_status.restype = ctypes.c_int
+        L.domino_noalloc_device_status.argtypes = [P]
         L.domino_tree_candidates.restype = ctypes.c_int
         L.domino_tree_candidates.argtypes = [P, P, i32, i32, P, P, P, sz, P]
         L.domino_tree_draft.restype = ctypes.c_int
@@ -161,6 +165,17 @@ def domino_draft_chain(dims: Dims, weights: Weights, H, base_logits, first_token
     _check(lib().domino_draft_chain(ctypes.byref(dims), ctypes.byref(weights), _ptr(H), _ptr(base_logits),
                                     _ptr(first_tokens), int(batch), _ptr(out_tokens), _ptr(out_logits),
                                     _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def domino_draft_chain_noalloc(dims: Dims, weights: Weights, H, base_logits, first_tokens, batch: int, out_tokens,
+                               out_logits, stream=None):
+    _check(lib().domino_draft_chain_noalloc(ctypes.byref(dims), ctypes.byref(weights), _ptr(H), _ptr(base_logits),
+                                            _ptr(first_tokens), int(batch), _ptr(out_tokens), _ptr(out_logits),
+                                            _stream(stream)))
+
+
+def domino_noalloc_device_status(stream=None):
+    _check(lib().domino_noalloc_device_status(_stream(stream)))
 
 
 def domino_tree_candidates(dims: Dims, base_logits, batch: int, topm: int, out_index, out_value, workspace,

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <string>
 
 #include "../../include/domino.h"
@@ -72,6 +73,141 @@ domino_status check_dims(const domino_dims* d) {
 }
 
 size_t elem_size(const domino_dims* d) { return d->dtype == DOMINO_BF16 ? 2 : 4; }
+
+// Largest workspace the allocation-free chain call serves from its static array.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+
+size_t chain_workspace_bytes(const domino_dims* dims, int32_t batch) {
+  const int bs = batch > 0 ? batch : 1;
+  const int group = bs < dh::kMaxChainGroup ? bs : dh::kMaxChainGroup;
+  return dh::chain_layout(dims->hidden, dims->gru_hidden, dims->rank, dims->block, group).total;
+}
+
+// Argument checks of the chain calls (everything but the workspace).
+domino_status check_chain_args(const domino_dims* dims, const domino_weights* w, const void* H,
+                               const float* base_logits, const int32_t* first_tokens, int32_t batch,
+                               const int32_t* out_tokens, const float* out_logits) {
+  domino_status st = check_dims(dims);
+  if (st != DOMINO_OK) return st;
+  if (!w) return fail(DOMINO_ERR_INVALID_ARGUMENT, "weights is NULL");
+  if (batch < 0) return fail(DOMINO_ERR_INVALID_ARGUMENT, "batch %d is negative", batch);
+  if (batch == 0) return DOMINO_OK;
+  REQUIRE_PTR(w->embed, "weights.embed");
+  REQUIRE_PTR(w->w_ih, "weights.w_ih");
+  REQUIRE_PTR(w->w_hh, "weights.w_hh");
+  REQUIRE_PTR(w->w1, "weights.w1");
+  REQUIRE_PTR(w->w2, "weights.w2");
+  OPTIONAL_PTR(w->b_ih, "weights.b_ih");
+  OPTIONAL_PTR(w->b_hh, "weights.b_hh");
+  OPTIONAL_PTR(w->b1, "weights.b1");
+  OPTIONAL_PTR(w->b2, "weights.b2");
+  REQUIRE_PTR(H, "H");
+  REQUIRE_PTR(base_logits, "base_logits");
+  REQUIRE_PTR(first_tokens, "first_tokens");
+  REQUIRE_PTR(out_tokens, "out_tokens");
+  OPTIONAL_PTR(out_logits, "out_logits");
+  return DOMINO_OK;
+}
+
+// The chain on a checked workspace `ws` of the size domino_workspace_size gives.
+domino_status run_draft_chain(const domino_dims* dims, const domino_weights* w, const void* H,
+                              const float* base_logits, const int32_t* first_tokens, int32_t batch,
+                              int32_t* out_tokens, float* out_logits, char* ws, hipStream_t s) {
+  const int d = dims->hidden, V = dims->vocab, Hs = dims->gru_hidden, r = dims->rank, P = dims->block;
+  const int group_max = batch < dh::kMaxChainGroup ? batch : dh::kMaxChainGroup;
+  const dh::ChainLayout L = dh::chain_layout(d, Hs, r, P, group_max);
+  const size_t es = elem_size(dims);
+  const int mode = g_chain_mode.load();
+  const hipEvent_t ev0 = g_chain_start.load(), ev1 = g_chain_stop.load();
+  for (int g0 = 0; g0 < batch; g0 += dh::kMaxChainGroup) {
+    const int Bg = batch - g0 < dh::kMaxChainGroup ? batch - g0 : dh::kMaxChainGroup;
+    const char* Hg = (const char*)H + (size_t)g0 * P * d * es;
+    dh::ChainArgs a;
+    a.d = d;
+    a.V = V;
+    a.Hs = Hs;
+    a.r = r;
+    a.P = P;
+    a.B = Bg;
+    a.embed = w->embed;
+    a.w_ih = w->w_ih;
+    a.w_hh = w->w_hh;
+    a.w1 = w->w1;
+    a.w2 = w->w2;
+    a.b_ih = w->b_ih;
+    a.b_hh = w->b_hh;
+    a.b1 = w->b1;
+    a.b2 = w->b2;
+    a.Lb = base_logits + (size_t)g0 * P * V;
+    a.out_logits = out_logits ? out_logits + (size_t)g0 * P * V : nullptr;
+    a.out_tokens = out_tokens + (size_t)g0 * P;
+    a.t0 = first_tokens + g0;
+    a.zh = (const float*)(ws + L.zh);
+    a.h = (float*)(ws + L.h);
+    a.hb = (uint16_t*)(ws + L.hb);
+    a.hb_step = L.hb_step;
+    a.act = ws + L.act;
+    a.keys = (uint64_t*)(ws + L.keys);
+    a.status = (int32_t*)(ws + L.status);
+    a.h_step = L.h_step;
+    a.ll_h = (uint64_t*)(ws + L.ll_h);
+    a.ll_act = (uint64_t*)(ws + L.ll_act);
+    a.ll_part = (uint64_t*)(ws + L.ll_part);
+    a.ll_tok = (uint64_t*)(ws + L.ll_tok);
+    a.epoch = (uint32_t*)(ws + L.status + 4);
+    a.marker = (uint64_t*)(ws + L.status + 8);
+    a.sig = (uint64_t*)(ws + L.status + 16);
+    a.ll_words = (L.trace - L.ll_h) / 8;
+    // the hand-off words are cleared again whenever the region they occupy changes
+    a.sig_value = ((uint64_t)L.ll_h << 32) ^ (uint64_t)a.ll_words ^ ((uint64_t)P << 56) ^ ((uint64_t)Bg << 48);
+    a.stamps = (uint64_t*)(ws + L.stamps);
+    a.act_step = L.act_step;
+#ifdef DH_TRACE_PHASES
+    a.trace = (uint64_t*)(ws + L.trace);
+#else
+    a.trace = nullptr;
+#endif
+    hipError_t e = dh::launch_chain(dims->dtype, a, Hg, mode, g0 == 0, s, ev0, ev1);
+    if (e != hipSuccess) return device_fail(e, "chain launch");
+  }
+  return ok();
+}
+
+}  // namespace
+
+// Workspace of domino_draft_chain_noalloc: a static array in every device's
+// copy of the code object, held until the process ends.  Host code never
+// uses this name as an address (on the host it is only a stand-in); it asks
+// the runtime for each device's address once and keeps that.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+struct NoAllocDevice {
+  std::mutex m;
+  void* ptr = nullptr;  // `scratch` on this device
+};
+NoAllocDevice g_noalloc[64];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on that device (with the device current) and kept.
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  NoAllocDevice& d = g_noalloc[dev];
+  std::lock_guard<std::mutex> lock(d.m);
+  if (!d.ptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    d.ptr = p;
+  }
+  *out = d.ptr;
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -168,91 +304,42 @@ domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* 
                                  const float* base_logits, const int32_t* first_tokens, int32_t batch,
                                  int32_t* out_tokens, float* out_logits, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  domino_status st = check_dims(dims);
+  domino_status st = check_chain_args(dims, w, H, base_logits, first_tokens, batch, out_tokens, out_logits);
   if (st != DOMINO_OK) return st;
-  if (!w) return fail(DOMINO_ERR_INVALID_ARGUMENT, "weights is NULL");
-  if (batch < 0) return fail(DOMINO_ERR_INVALID_ARGUMENT, "batch %d is negative", batch);
   if (batch == 0) return ok();
-  REQUIRE_PTR(w->embed, "weights.embed");
-  REQUIRE_PTR(w->w_ih, "weights.w_ih");
-  REQUIRE_PTR(w->w_hh, "weights.w_hh");
-  REQUIRE_PTR(w->w1, "weights.w1");
-  REQUIRE_PTR(w->w2, "weights.w2");
-  OPTIONAL_PTR(w->b_ih, "weights.b_ih");
-  OPTIONAL_PTR(w->b_hh, "weights.b_hh");
-  OPTIONAL_PTR(w->b1, "weights.b1");
-  OPTIONAL_PTR(w->b2, "weights.b2");
-  REQUIRE_PTR(H, "H");
-  REQUIRE_PTR(base_logits, "base_logits");
-  REQUIRE_PTR(first_tokens, "first_tokens");
-  REQUIRE_PTR(out_tokens, "out_tokens");
-  OPTIONAL_PTR(out_logits, "out_logits");
   REQUIRE_PTR(workspace, "workspace");
   const size_t need = domino_workspace_size(dims, batch, DOMINO_OP_CHAIN, 0, 0);
   if (workspace_bytes < need)
     return fail(DOMINO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes,
                 need);
+  return run_draft_chain(dims, w, H, base_logits, first_tokens, batch, out_tokens, out_logits, (char*)workspace,
+                         (hipStream_t)stream);
+}
 
-  const int d = dims->hidden, V = dims->vocab, Hs = dims->gru_hidden, r = dims->rank, P = dims->block;
-  const int group_max = batch < dh::kMaxChainGroup ? batch : dh::kMaxChainGroup;
-  const dh::ChainLayout L = dh::chain_layout(d, Hs, r, P, group_max);
-  char* ws = (char*)workspace;
-  const size_t es = elem_size(dims);
-  hipStream_t s = (hipStream_t)stream;
+domino_status domino_draft_chain_noalloc(const domino_dims* dims, const domino_weights* w, const void* H,
+                                         const float* base_logits, const int32_t* first_tokens, int32_t batch,
+                                         int32_t* out_tokens, float* out_logits, void* stream) {
+  domino_status st = check_chain_args(dims, w, H, base_logits, first_tokens, batch, out_tokens, out_logits);
+  if (st != DOMINO_OK) return st;
+  if (batch == 0) return ok();
+  const size_t need = chain_workspace_bytes(dims, batch);
+  if (need > kNoAllocScratchBytes)
+    return fail(DOMINO_ERR_UNSUPPORTED,
+                "this batch and these dims need %zu bytes of workspace; the allocation-free call holds %zu "
+                "(use domino_draft_chain with a workspace)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return device_fail(e, "locating the static workspace");
+  return run_draft_chain(dims, w, H, base_logits, first_tokens, batch, out_tokens, out_logits, (char*)ws,
+                         (hipStream_t)stream);
+}
 
-  for (int g0 = 0; g0 < batch; g0 += dh::kMaxChainGroup) {
-    const int Bg = batch - g0 < dh::kMaxChainGroup ? batch - g0 : dh::kMaxChainGroup;
-    const char* Hg = (const char*)H + (size_t)g0 * P * d * es;
-    dh::ChainArgs a;
-    a.d = d;
-    a.V = V;
-    a.Hs = Hs;
-    a.r = r;
-    a.P = P;
-    a.B = Bg;
-    a.embed = w->embed;
-    a.w_ih = w->w_ih;
-    a.w_hh = w->w_hh;
-    a.w1 = w->w1;
-    a.w2 = w->w2;
-    a.b_ih = w->b_ih;
-    a.b_hh = w->b_hh;
-    a.b1 = w->b1;
-    a.b2 = w->b2;
-    a.Lb = base_logits + (size_t)g0 * P * V;
-    a.out_logits = out_logits ? out_logits + (size_t)g0 * P * V : nullptr;
-    a.out_tokens = out_tokens + (size_t)g0 * P;
-    a.t0 = first_tokens + g0;
-    a.zh = (const float*)(ws + L.zh);
-    a.h = (float*)(ws + L.h);
-    a.hb = (uint16_t*)(ws + L.hb);
-    a.hb_step = L.hb_step;
-    a.act = ws + L.act;
-    a.keys = (uint64_t*)(ws + L.keys);
-    a.status = (int32_t*)(ws + L.status);
-    a.h_step = L.h_step;
-    a.ll_h = (uint64_t*)(ws + L.ll_h);
-    a.ll_act = (uint64_t*)(ws + L.ll_act);
-    a.ll_part = (uint64_t*)(ws + L.ll_part);
-    a.ll_tok = (uint64_t*)(ws + L.ll_tok);
-    a.epoch = (uint32_t*)(ws + L.status + 4);
-    a.marker = (uint64_t*)(ws + L.status + 8);
-    a.sig = (uint64_t*)(ws + L.status + 16);
-    a.ll_words = (L.trace - L.ll_h) / 8;
-    // the hand-off words are cleared again whenever the region they occupy changes
-    a.sig_value = ((uint64_t)L.ll_h << 32) ^ (uint64_t)a.ll_words ^ ((uint64_t)P << 56) ^ ((uint64_t)Bg << 48);
-    a.stamps = (uint64_t*)(ws + L.stamps);
-    a.act_step = L.act_step;
-#ifdef DH_TRACE_PHASES
-    a.trace = (uint64_t*)(ws + L.trace);
-#else
-    a.trace = nullptr;
-#endif
-    hipError_t e = dh::launch_chain(dims->dtype, a, Hg, g_chain_mode.load(), g0 == 0, s, g_chain_start.load(),
-                                     g_chain_stop.load());
-    if (e != hipSuccess) return device_fail(e, "chain launch");
-  }
-  return ok();
+domino_status domino_noalloc_device_status(void* stream) {
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return device_fail(e, "locating the static workspace");
+  return domino_device_status(ws, stream);
 }
 
 domino_status domino_tree_candidates(const domino_dims* dims, const float* base_logits, int32_t batch, int32_t topm,

@@ -179,6 +179,29 @@ domino_status domino_draft_chain(const domino_dims *dims, const domino_weights *
                                  void *stream);
 
 /*
+ * domino_draft_chain without a workspace argument and without allocating:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * workspace is a static 32 MiB array in the library's code object, one per
+ * device, held until the process ends; its address on each device is looked
+ * up on the first call on that device.  Every call on a device shares that
+ * device's array: calls that overlap on one device (on any streams) race and
+ * must not be issued.  Arguments, outputs and results are those of
+ * domino_draft_chain.  Returns DOMINO_ERR_UNSUPPORTED when the call needs
+ * more than 32 MiB of workspace (domino_workspace_size(dims, batch,
+ * DOMINO_OP_CHAIN, 0, 0) > 33554432; Qwen3-4B shapes at batch 32 and block
+ * 16 need about 20 MB).  The device status of the last call is read with
+ * domino_noalloc_device_status.
+ */
+domino_status domino_draft_chain_noalloc(const domino_dims *dims, const domino_weights *weights, const void *H,
+                                         const float *base_logits, const int32_t *first_tokens, int32_t batch,
+                                         int32_t *out_tokens, float *out_logits, void *stream);
+
+/* domino_device_status of the static workspace of domino_draft_chain_noalloc
+ * on the current device. */
+domino_status domino_noalloc_device_status(void *stream);
+
+/*
  * Top-M candidates of every base-logit row (the tree's candidate lists,
  * DominoTree summary, "Top-M" restriction): for each of batch*block rows of
  * base_logits [batch][block][vocab] (device, fp32), out_index/out_value
