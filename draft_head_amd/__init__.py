@@ -25,8 +25,10 @@ STATUS_FINE, STATUS_BAD_FIRST_TOKEN, STATUS_TIMEOUT = 0, 1, 2
 
 # include/domino.h (the contract) and include/domino_bench.h (bench and test hooks)
 EXPORTS = ("domino_version", "domino_last_error", "domino_workspace_size", "domino_device_status",
-           "domino_release_cache", "domino_base_logits", "domino_draft_chain", "domino_draft_chain_noalloc",
-           "domino_noalloc_device_status", "domino_tree_candidates", "domino_tree_draft")
+           "domino_release_cache", "domino_base_logits", "domino_draft_chain", "domino_draft_chain_sampled",
+           "domino_draft_chain_noalloc",
+           "domino_noalloc_device_status", "domino_tree_candidates", "domino_tree_draft",
+           "domino_tree_verify_inputs")
 BENCH_EXPORTS = ("domino_set_timing_events", "domino_set_chain_mode", "domino_chain_stamp_offset")
 
 
@@ -71,6 +73,8 @@ def lib():
         L.domino_base_logits.argtypes = [P, P, P, i32, P, P]
         L.domino_draft_chain.restype = ctypes.c_int
         L.domino_draft_chain.argtypes = [P, P, P, P, P, i32, P, P, P, sz, P]
+        L.domino_draft_chain_sampled.restype = ctypes.c_int
+        L.domino_draft_chain_sampled.argtypes = [P, P, P, P, P, i32, ctypes.c_float, ctypes.c_uint64, P, P, P, sz, P]
         L.domino_draft_chain_noalloc.restype = ctypes.c_int
         L.domino_draft_chain_noalloc.argtypes = [P, P, P, P, P, i32, P, P, P]
         L.domino_noalloc_device_status.restype = ctypes.c_int
@@ -79,6 +83,8 @@ def lib():
         L.domino_tree_candidates.argtypes = [P, P, i32, i32, P, P, P, sz, P]
         L.domino_tree_draft.restype = ctypes.c_int
         L.domino_tree_draft.argtypes = [P, P, P, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
+        L.domino_tree_verify_inputs.restype = ctypes.c_int
+        L.domino_tree_verify_inputs.argtypes = [P, P, P, P, i32, i32, P, P, P, P]
         L.domino_set_chain_mode.restype = i32
         L.domino_set_chain_mode.argtypes = [i32]
         L.domino_set_timing_events.restype = None
@@ -167,6 +173,15 @@ def domino_draft_chain(dims: Dims, weights: Weights, H, base_logits, first_token
                                     _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
+def domino_draft_chain_sampled(dims: Dims, weights: Weights, H, base_logits, first_tokens, batch: int,
+                               temperature: float, seed: int, out_tokens, out_logits, workspace, workspace_bytes: int,
+                               stream=None):
+    _check(lib().domino_draft_chain_sampled(ctypes.byref(dims), ctypes.byref(weights), _ptr(H), _ptr(base_logits),
+                                            _ptr(first_tokens), int(batch), float(temperature), int(seed),
+                                            _ptr(out_tokens), _ptr(out_logits), _ptr(workspace),
+                                            int(workspace_bytes), _stream(stream)))
+
+
 def domino_draft_chain_noalloc(dims: Dims, weights: Weights, H, base_logits, first_tokens, batch: int, out_tokens,
                                out_logits, stream=None):
     _check(lib().domino_draft_chain_noalloc(ctypes.byref(dims), ctypes.byref(weights), _ptr(H), _ptr(base_logits),
@@ -190,6 +205,25 @@ def domino_tree_draft(dims: Dims, weights: Weights, H, base_logits, first_tokens
                                    _ptr(first_tokens), int(batch), int(nodes), int(topm), _ptr(out_parents),
                                    _ptr(out_tokens), _ptr(out_depth), _ptr(out_scores), _ptr(workspace),
                                    int(workspace_bytes), _stream(stream)))
+
+
+def domino_tree_verify_inputs(parents, tokens, first_tokens, start_positions, batch: int, nodes: int, out_mask,
+                              out_positions, out_tokens, stream=None):
+    _check(lib().domino_tree_verify_inputs(_ptr(parents), _ptr(tokens), _ptr(first_tokens), _ptr(start_positions),
+                                           int(batch), int(nodes), _ptr(out_mask), _ptr(out_positions),
+                                           _ptr(out_tokens), _stream(stream)))
+
+
+def tree_verify_inputs(parents, tokens, first_tokens, start_positions=None, stream=None):
+    """Device tensors parents, tokens [B][N] -> (mask [B][N+1][N+1] uint8, positions, tokens [B][N+1])."""
+    import torch
+    B, N = parents.shape
+    dev = parents.device
+    mask = torch.empty((B, N + 1, N + 1), dtype=torch.uint8, device=dev)
+    pos = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+    tok = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+    domino_tree_verify_inputs(parents, tokens, first_tokens, start_positions, B, N, mask, pos, tok, stream)
+    return mask, pos, tok
 
 
 class DraftHead:
@@ -258,6 +292,21 @@ class DraftHead:
         if check:
             domino_device_status(workspace, stream)
         return out_tokens, (out_logits if want_logits else None), workspace
+
+    def draft_chain_sampled(self, H, base_logits, first_tokens, temperature, seed, want_logits=True,
+                            workspace=None, stream=None, check=True):
+        import torch
+        B = H.shape[0]
+        out_tokens = torch.empty((B, self.dims.block), dtype=torch.int32, device=self.device)
+        out_logits = (torch.empty((B, self.dims.block, self.dims.vocab), dtype=torch.float32, device=self.device)
+                      if want_logits else None)
+        if workspace is None:
+            workspace = self.workspace(B)
+        domino_draft_chain_sampled(self.dims, self.weights, H, base_logits, first_tokens, B, temperature, seed,
+                                   out_tokens, out_logits, workspace, workspace.numel(), stream)
+        if check:
+            domino_device_status(workspace, stream)
+        return out_tokens, out_logits, workspace
 
     def tree_draft(self, H, base_logits, first_tokens, nodes, topm, workspace=None, stream=None, check=True):
         """-> dict of device tensors parents, tokens, depth [B][N] int32 and scores [B][N] fp64, and the workspace."""

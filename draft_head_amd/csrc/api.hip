@@ -110,9 +110,11 @@ domino_status check_chain_args(const domino_dims* dims, const domino_weights* w,
 }
 
 // The chain on a checked workspace `ws` of the size domino_workspace_size gives.
+// temperature 0: greedy; > 0: Gumbel-max draws keyed by seed
 domino_status run_draft_chain(const domino_dims* dims, const domino_weights* w, const void* H,
                               const float* base_logits, const int32_t* first_tokens, int32_t batch,
-                              int32_t* out_tokens, float* out_logits, char* ws, hipStream_t s) {
+                              int32_t* out_tokens, float* out_logits, char* ws, hipStream_t s,
+                              float temperature = 0.f, uint64_t seed = 0) {
   const int d = dims->hidden, V = dims->vocab, Hs = dims->gru_hidden, r = dims->rank, P = dims->block;
   const int group_max = batch < dh::kMaxChainGroup ? batch : dh::kMaxChainGroup;
   const dh::ChainLayout L = dh::chain_layout(d, Hs, r, P, group_max);
@@ -162,6 +164,10 @@ domino_status run_draft_chain(const domino_dims* dims, const domino_weights* w, 
     a.sig_value = ((uint64_t)L.ll_h << 32) ^ (uint64_t)a.ll_words ^ ((uint64_t)P << 56) ^ ((uint64_t)Bg << 48);
     a.stamps = (uint64_t*)(ws + L.stamps);
     a.act_step = L.act_step;
+    a.temperature = temperature;
+    a.seed_lo = (uint32_t)seed;
+    a.seed_hi = (uint32_t)(seed >> 32);
+    a.seq_base = g0;
 #ifdef DH_TRACE_PHASES
     a.trace = (uint64_t*)(ws + L.trace);
 #else
@@ -316,6 +322,24 @@ domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* 
                          (hipStream_t)stream);
 }
 
+domino_status domino_draft_chain_sampled(const domino_dims* dims, const domino_weights* w, const void* H,
+                                         const float* base_logits, const int32_t* first_tokens, int32_t batch,
+                                         float temperature, uint64_t seed, int32_t* out_tokens, float* out_logits,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!(temperature >= 0.f) || temperature > 3.0e38f)
+    return fail(DOMINO_ERR_INVALID_ARGUMENT, "temperature must be finite and >= 0");
+  domino_status st = check_chain_args(dims, w, H, base_logits, first_tokens, batch, out_tokens, out_logits);
+  if (st != DOMINO_OK) return st;
+  if (batch == 0) return ok();
+  REQUIRE_PTR(workspace, "workspace");
+  const size_t need = domino_workspace_size(dims, batch, DOMINO_OP_CHAIN, 0, 0);
+  if (workspace_bytes < need)
+    return fail(DOMINO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required", workspace_bytes,
+                need);
+  return run_draft_chain(dims, w, H, base_logits, first_tokens, batch, out_tokens, out_logits, (char*)workspace,
+                         (hipStream_t)stream, temperature, seed);
+}
+
 domino_status domino_draft_chain_noalloc(const domino_dims* dims, const domino_weights* w, const void* H,
                                          const float* base_logits, const int32_t* first_tokens, int32_t batch,
                                          int32_t* out_tokens, float* out_logits, void* stream) {
@@ -445,6 +469,25 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   t.heap_cap = L.heap_cap;
   hipError_t e = dh::launch_tree(t, true, (hipStream_t)stream, g_chain_start.load(), g_chain_stop.load());
   if (e != hipSuccess) return device_fail(e, "tree launch");
+  return ok();
+}
+
+domino_status domino_tree_verify_inputs(const int32_t* parents, const int32_t* tokens, const int32_t* first_tokens,
+                                        const int32_t* start_positions, int32_t batch, int32_t nodes,
+                                        uint8_t* out_mask, int32_t* out_positions, int32_t* out_tokens, void* stream) {
+  if (batch < 0) return fail(DOMINO_ERR_INVALID_ARGUMENT, "batch %d is negative", batch);
+  if (nodes < 1 || nodes > 64) return fail(DOMINO_ERR_INVALID_ARGUMENT, "nodes %d must be in [1, 64]", nodes);
+  if (batch == 0) return ok();
+  REQUIRE_PTR(parents, "parents");
+  REQUIRE_PTR(tokens, "tokens");
+  REQUIRE_PTR(first_tokens, "first_tokens");
+  OPTIONAL_PTR(start_positions, "start_positions");
+  REQUIRE_PTR(out_mask, "out_mask");
+  REQUIRE_PTR(out_positions, "out_positions");
+  REQUIRE_PTR(out_tokens, "out_tokens");
+  const hipError_t e = dh::launch_tree_verify_inputs(parents, tokens, first_tokens, start_positions, batch, nodes,
+                                                     out_mask, out_positions, out_tokens, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "verification-input launch");
   return ok();
 }
 

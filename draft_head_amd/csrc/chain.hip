@@ -883,25 +883,66 @@ __device__ __forceinline__ void load_base_rows(const ChainArgs& a, int p, int v,
     }
 }
 
-// this lane's logits of a tile into its running argmaxes (and out, with kWrite)
-template <bool kWrite, int RG>
+// ---- sampling at temperature T (Gumbel-max) ------------------------------------------
+// A draw from softmax(L / T) is argmax_v (L_v + T g_v) with g_v standard
+// Gumbel noise.  The noise of (sequence b of the whole batch, position p,
+// entry v) is -log(-log u), u = (2 (x >> 9) + 1) / 2^24 (exact in fp32),
+// x = word (b & 1) of Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011)
+// at counter (v, p, b >> 1, 0) under key (seed lo, seed hi): one generator
+// call serves the pair of sequences a lane holds in a row group.
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1, uint32_t& x0, uint32_t& x1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  x0 = c0;
+  x1 = c1;
+}
+__device__ __forceinline__ float gumbel_of(uint32_t x) {
+  const float u = (float)(2u * (x >> 9) + 1u) * 0x1p-24f;  // exact
+  return -logf(-logf(u));
+}
+
+// this lane's logits of a tile into its running argmaxes (and out, with
+// kWrite); kSample: the argmax is taken over L + T g (the logits written are L)
+template <bool kWrite, int RG, bool kSample = false>
 __device__ __forceinline__ void rows_epilogue(const ChainArgs& a, int p, int v, int kg, const float (&lb)[RG][2],
                                               float b2, const f32x4 (&acc)[RG][2], LaneMax (&lm)[RG][2]) {
   if (v >= a.V) return;
 #pragma unroll
-  for (int g = 0; g < RG; ++g)
+  for (int g = 0; g < RG; ++g) {
+    uint32_t x[2] = {0u, 0u};
+    if constexpr (kSample) {  // the lane's sequences a.seq_base + 8g + 2kg + {0, 1}: one generator call
+      const uint32_t pair = (uint32_t)(a.seq_base + g * kSeqPerRowGroup + 2 * kg) >> 1;
+      philox4x32_10((uint32_t)v, (uint32_t)p, pair, 0u, a.seed_lo, a.seed_hi, x[0], x[1]);
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const float hi = acc[g][0][2 * j] + acc[g][1][2 * j];
       const float lo = acc[g][0][2 * j + 1] + acc[g][1][2 * j + 1];
       const float base = a.b2 ? lb[g][j] + b2 : lb[g][j];
       const float L = base + (hi + lo);
-      lane_max(lm[g][j], L, v);
+      if constexpr (kSample)
+        lane_max(lm[g][j], L + a.temperature * gumbel_of(x[j]), v);
+      else
+        lane_max(lm[g][j], L, v);
       if constexpr (kWrite) {
         const int b = g * kSeqPerRowGroup + 2 * kg + j;
         if (b < a.B) a.out_logits[((size_t)b * a.P + p) * a.V + v] = L;
       }
     }
+  }
 }
 
 // Fold the lanes' running argmaxes into one key per sequence for this
@@ -1040,7 +1081,7 @@ struct TileBuf {
 // rotated through register copies, each of which waits for its load.  The
 // first DH_O_EARLY tiles are issued before the activations exist (before
 // `ready` in the stepwise schedule).
-template <class W, int RG, int KC, bool kWrite, bool kLL, class Ready>
+template <class W, int RG, int KC, bool kWrite, bool kLL, class Ready, bool kSample = false>
 __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest,
                                               Ready ready, uint32_t ep, uint32_t* act_s) {
   static_assert(DH_O_EARLY >= 0 && DH_O_EARLY <= 2, "two tiles ahead");
@@ -1091,7 +1132,7 @@ __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_b
         else
           acc[g][c & 1] = mma(act_row_frag<W, KC>(act_s, a.B, g, row, c * 32 + kg * 8), tb.w[c], acc[g][c & 1]);
       }
-    rows_epilogue<kWrite, RG>(a, p, (t0 + 4 * i) * 16 + row, kg, tb.lb, tb.b2, acc, lm);
+    rows_epilogue<kWrite, RG, kSample>(a, p, (t0 + 4 * i) * 16 + row, kg, tb.lb, tb.b2, acc, lm);
   };
   int i = 0;
   for (; i + 3 <= n; i += 3) {
@@ -1122,7 +1163,7 @@ __device__ __forceinline__ int opaque_zero() {
 // clamped addresses so the waits stay exact), and re-reads the staged
 // activations from LDS per tile, so it needs few registers and the other
 // waves hide what latency is left.
-template <class W, int RG, int KC, int NWV, bool kWrite>
+template <class W, int RG, int KC, int NWV, bool kWrite, bool kSample = false>
 __device__ __forceinline__ void logits_wide_(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest,
                                              uint32_t* act_s) {
   const int lane = opaque_lane(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1151,7 +1192,7 @@ __device__ __forceinline__ void logits_wide_(const ChainArgs& a, int p, int t_be
 #pragma unroll
       for (int g = 0; g < RG; ++g)
         acc[g][c & 1] = mma(act_row_frag<W, KC>(as, a.B, g, row, c * 32 + kg * 8), tb.w[c], acc[g][c & 1]);
-    rows_epilogue<kWrite, RG>(a, p, (t0 + NWV * i) * 16 + row, kg, tb.lb, tb.b2, acc, lm);
+    rows_epilogue<kWrite, RG, kSample>(a, p, (t0 + NWV * i) * 16 + row, kg, tb.lb, tb.b2, acc, lm);
   };
   int i = 0;
   for (; i + 2 <= n; i += 2) {
@@ -1311,18 +1352,22 @@ __global__ __launch_bounds__(256) void chain_bottleneck_k(ChainArgs a, int p) {
     bottleneck_item<W, NCB, false>(a, p, it, red, nullptr, bottleneck_pre<NCB>(a, p, it, seq0), 0u, nullptr, seq0);
 }
 
-template <class W, int RG, int KC>
+template <class W, int RG, int KC, bool kSample>
 __global__ __launch_bounds__(256) void chain_logits_k(ChainArgs a, int p) {
   __shared__ uint64_t sbest[4 * kMaxChainGroup];
   __shared__ __attribute__((aligned(16))) uint32_t act_s[kMaxChainGroup * (256 + 8)];  // r <= 256
   const int T = (a.V + 15) / 16, G = gridDim.x, w = blockIdx.x;
+  const int t_begin = (int)((int64_t)T * w / G), t_end = (int)((int64_t)T * (w + 1) / G);
   act_clear_pads<W, KC>(act_s, a.B, a.r);  // made visible by the staging's barrier
-  logits_range<W, RG, KC, false>(a, p, (int)((int64_t)T * w / G), (int)((int64_t)T * (w + 1) / G), sbest,
-                                 [] { return true; }, 0u, act_s);
+  auto ready = [] { return true; };
+  if (a.out_logits)
+    logits_range_<W, RG, KC, true, false, decltype(ready), kSample>(a, p, t_begin, t_end, sbest, ready, 0u, act_s);
+  else
+    logits_range_<W, RG, KC, false, false, decltype(ready), kSample>(a, p, t_begin, t_end, sbest, ready, 0u, act_s);
 }
 
 // stepwise phase O with NWV waves per workgroup (one workgroup per CU)
-template <class W, int RG, int KC, int NWV>
+template <class W, int RG, int KC, int NWV, bool kSample>
 __global__ __launch_bounds__(64 * NWV) void chain_logits_wide_k(ChainArgs a, int p) {
   __shared__ uint64_t sbest[NWV * kMaxChainGroup];
   __shared__ __attribute__((aligned(16))) uint32_t act_s[kMaxChainGroup * (256 + 8)];  // r <= 256
@@ -1330,9 +1375,9 @@ __global__ __launch_bounds__(64 * NWV) void chain_logits_wide_k(ChainArgs a, int
   const int t_begin = (int)((int64_t)T * w / G), t_end = (int)((int64_t)T * (w + 1) / G);
   act_clear_pads<W, KC>(act_s, a.B, a.r);  // made visible by the staging's barrier
   if (a.out_logits)
-    logits_wide_<W, RG, KC, NWV, true>(a, p, t_begin, t_end, sbest, act_s);
+    logits_wide_<W, RG, KC, NWV, true, kSample>(a, p, t_begin, t_end, sbest, act_s);
   else
-    logits_wide_<W, RG, KC, NWV, false>(a, p, t_begin, t_end, sbest, act_s);
+    logits_wide_<W, RG, KC, NWV, false, kSample>(a, p, t_begin, t_end, sbest, act_s);
 }
 
 // All P steps in one launch (every workgroup resident); each owns one GRU work
@@ -1603,7 +1648,9 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
   // sequences the three launches per step, each with all the waves a CU
   // holds for its phase, are faster.
   // fp32 weights (small models) always run the three launches per step
-  persistent = sizeof(W) == 2 && (mode >= 2 || (mode == 0 && RG == 1)) && cus > 0 && a.Hs / 4 <= cus;
+  // sampling (temperature > 0) runs the three launches per step as well
+  const bool sample = a.temperature > 0.f;
+  persistent = !sample && sizeof(W) == 2 && (mode >= 2 || (mode == 0 && RG == 1)) && cus > 0 && a.Hs / 4 <= cus;
   if constexpr (sizeof(W) == 2) {
     if (persistent) {
       const size_t g = gru_slice_elems(a.d, a.Hs) * sizeof(W);
@@ -1630,10 +1677,17 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
     // one workgroup per 16 rows and 16 sequences: more CUs share the state reads
     hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 15) / 16), dim3(256), 0, s, a, p);
     constexpr int NWV = RG * KC >= 16 ? 8 : 16;  // waves per CU, as registers allow
-    if constexpr (sizeof(W) == 2)  // bf16: many light waves per CU
-      hipLaunchKernelGGL((chain_logits_wide_k<W, RG, KC, NWV>), dim3(nO), dim3(64 * NWV), 0, s, a, p);
-    else
-      hipLaunchKernelGGL((chain_logits_k<W, RG, KC>), dim3(nO), dim3(256), 0, s, a, p);
+    if constexpr (sizeof(W) == 2) {  // bf16: many light waves per CU
+      if (sample)
+        hipLaunchKernelGGL((chain_logits_wide_k<W, RG, KC, NWV, true>), dim3(nO), dim3(64 * NWV), 0, s, a, p);
+      else
+        hipLaunchKernelGGL((chain_logits_wide_k<W, RG, KC, NWV, false>), dim3(nO), dim3(64 * NWV), 0, s, a, p);
+    } else {
+      if (sample)
+        hipLaunchKernelGGL((chain_logits_k<W, RG, KC, true>), dim3(nO), dim3(256), 0, s, a, p);
+      else
+        hipLaunchKernelGGL((chain_logits_k<W, RG, KC, false>), dim3(nO), dim3(256), 0, s, a, p);
+    }
   }
   return hipGetLastError();
 }

@@ -67,6 +67,10 @@ struct ChainArgs {
   uint64_t sig_value;      // this launch's layout signature
   size_t ll_words;         // hand-off words from ll_h on (all four regions)
   uint64_t* stamps;        // [P+1] step start clocks of the persistent schedule (first workgroup)
+  // sampling: the token is argmax (L + temperature * Gumbel noise) when temperature > 0
+  float temperature;
+  uint32_t seed_lo, seed_hi;
+  int seq_base;            // index of this launch's first sequence in the whole batch (a multiple of 32)
 };
 
 // workspace carving for a chain launch of up to `group` sequences
@@ -129,5 +133,10 @@ size_t tree_gru_lds_total(int d, int Hs, int dtype);  // the GRU step's whole LD
 // scratch holds topm_scratch_bytes(rows, M)
 size_t topm_scratch_bytes(int rows, int M);
 hipError_t launch_topm(const float* Lb, int rows, int V, int M, void* scratch, int32_t* idx, float* val, hipStream_t s);
+
+// verification inputs of B flattened trees of N nodes (verify.hip)
+hipError_t launch_tree_verify_inputs(const int32_t* parents, const int32_t* tokens, const int32_t* first_tokens,
+                                     const int32_t* start_positions, int B, int N, uint8_t* mask, int32_t* positions,
+                                     int32_t* out_tokens, hipStream_t s);
 
 }  // namespace dh

@@ -179,6 +179,27 @@ domino_status domino_draft_chain(const domino_dims *dims, const domino_weights *
                                  void *stream);
 
 /*
+ * The correction chain with every token drawn at temperature T >= 0 instead
+ * of taken greedily (the pages report decoding at T = 1 next to greedy
+ * decoding: 163.com explainer, section 6; Korean review, section 5;
+ * DominoTree summary, experiments at T in {0, 0.5, 1}).  Everything is as in
+ * domino_draft_chain except the token of each position, which is the
+ * Gumbel-max draw from softmax(L / T):
+ *   out_tokens[b][p] = argmax_v (L[b][p][v] + T g(seed, b, p, v))
+ * (lowest index on exact ties), fed back to the GRU like the greedy token.
+ * g is standard Gumbel noise, -log(-log u), u = (2 (x >> 9) + 1) / 2^24,
+ * x = word (b & 1) of Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011)
+ * at counter (v, p, b >> 1, 0) under the key (seed & 0xffffffff, seed >> 32);
+ * b is the sequence's index in this call.  out_logits, if not NULL, are the
+ * unperturbed L.  T = 0 is the greedy chain.  The draws run the three-launch
+ * schedule.  temperature must be finite and >= 0.
+ */
+domino_status domino_draft_chain_sampled(const domino_dims *dims, const domino_weights *weights, const void *H,
+                                         const float *base_logits, const int32_t *first_tokens, int32_t batch,
+                                         float temperature, uint64_t seed, int32_t *out_tokens, float *out_logits,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * domino_draft_chain without a workspace argument and without allocating:
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation).  The
@@ -250,6 +271,29 @@ domino_status domino_tree_draft(const domino_dims *dims, const domino_weights *w
                                 const float *base_logits, const int32_t *first_tokens, int32_t batch, int32_t nodes,
                                 int32_t topm, int32_t *out_parents, int32_t *out_tokens, int32_t *out_depth,
                                 double *out_scores, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Verification inputs of drafted trees: the standard tree-attention input
+ * with an ancestor-only mask that DominoTree keeps for verification
+ * (DominoTree summary, "方法论 / 核心组件", verification), for `batch` trees
+ * of `nodes` slots as domino_tree_draft writes them.
+ * Inputs (device): parents, tokens [batch][nodes] int32 (pop order, -1 for
+ *   the anchor / unfilled); first_tokens [batch]; start_positions [batch]
+ *   (position id of each anchor) or NULL for 0.
+ * Outputs (device), over the flattened entries e = 0 (anchor) and e = k + 1
+ *   (node k), E = nodes + 1 per sequence:
+ *   out_mask [batch][E][E] uint8: 1 where entry j is entry i itself or one
+ *     of its ancestors (the anchor is an ancestor of every tree node);
+ *   out_positions [batch][E]: start + depth (anchor 0);
+ *   out_tokens [batch][E]: the anchor token, then the node tokens.
+ * Node k counts as part of the tree when its token is >= 0 and its parent is
+ * the anchor or an earlier node that is part of the tree; any other slot is
+ * padding: position -1, token -1, and a mask row with only its own entry.
+ * 1 <= nodes <= 64.  Integer work: the result is exact.
+ */
+domino_status domino_tree_verify_inputs(const int32_t *parents, const int32_t *tokens, const int32_t *first_tokens,
+                                        const int32_t *start_positions, int32_t batch, int32_t nodes,
+                                        uint8_t *out_mask, int32_t *out_positions, int32_t *out_tokens, void *stream);
 
 #ifdef __cplusplus
 }

@@ -217,3 +217,17 @@ def test_tree_arguments_rejected_before_launch():
     # which these sizes overflow (the bf16 step stages nothing)
     big = _dims(hidden=8192, gru_hidden=2048, dtype="f32")
     assert call(dims=ctypes.byref(big), wsb=1 << 40) == dh.ERR_UNSUPPORTED
+
+
+def test_verify_inputs_rejected_before_launch():
+    L = dh.lib()
+    a = [FAKE, FAKE, FAKE, None, 4, 16, FAKE, FAKE, FAKE, None]
+    for i, v, msg in ((5, 0, "nodes"), (5, 65, "nodes"), (4, -1, "batch"), (0, None, "parents"),
+                      (6, None, "out_mask"), (3, FAKE + 4, "start_positions")):
+        bad = list(a)
+        bad[i] = v
+        assert L.domino_tree_verify_inputs(*bad) == dh.ERR_INVALID_ARGUMENT, msg
+        assert msg in dh.last_error()
+    bad = list(a)
+    bad[4] = 0
+    assert L.domino_tree_verify_inputs(*bad) == dh.OK  # an empty batch launches nothing

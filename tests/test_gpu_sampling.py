@@ -1,0 +1,125 @@
+"""GPU parity of the sampled chain (temperature T > 0, Gumbel-max with
+Philox4x32-10 noise) against the oracle's sampled chain.
+
+Both sides draw the same noise from their own implementation of the
+generator, so the tokens must agree wherever the oracle's top-2 margin of the
+perturbed logits L + T g exceeds 1e-2 (the benchmark spec's margin rule, applied
+to the values the argmax is taken over); the logits (unperturbed) within
+1e-3 row-relative.  Past a tolerated divergence the oracle is re-run with
+the GPU's tokens fed back."""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import draft_head_amd as dh
+import oracle
+import synth
+from gpu_common import LOGIT_TOL, MARGIN_FIRM, say, weights_for
+from helpers import row_rel_err, small_config
+
+pytestmark = pytest.mark.gpu
+
+
+def compare_sampled(m, H, Lb, t0, T, seed, g_tokens, g_logits, label):
+    f_t, f_L, f_m = m.chain_sampled(H, Lb, t0, T, seed, forced=g_tokens, want_logits=g_logits is not None)
+    r_t, _, r_m = m.chain_sampled(H, Lb, t0, T, seed, want_logits=False)
+    firm = f_m > MARGIN_FIRM
+    bad = firm & (g_tokens != f_t)
+    assert not bad.any(), f"{label}: token mismatch at firm positions {np.argwhere(bad)[:5].tolist()}"
+    for b in range(g_tokens.shape[0]):
+        diff = np.nonzero(g_tokens[b] != r_t[b])[0]
+        if diff.size:
+            assert r_m[b, diff[0]] <= MARGIN_FIRM, f"{label}: seq {b} leaves the free oracle run at a firm position"
+    if g_logits is not None:
+        err = row_rel_err(g_logits, f_L)
+        assert err.max() <= LOGIT_TOL, f"{label}: logit error {err.max():.3e}"
+    return int((~firm).sum())
+
+
+@pytest.mark.parametrize("d,V,Hs,r,P,B,dtype", [
+    (16, 37, 8, 8, 5, 2, "f32"), (64, 1003, 40, 24, 7, 5, "bf16"), (96, 4099, 128, 256, 16, 32, "bf16"),
+    (48, 515, 16, 16, 3, 40, "bf16"), (64, 999, 32, 40, 16, 9, "f32")])
+@pytest.mark.parametrize("T", [0.5, 1.0])
+def test_sampled_chain_small(d, V, Hs, r, P, B, dtype, T):
+    cfg = small_config(d=d, V=V, Hs=Hs, r=r, P=P, B=B, dtype=dtype, biases=True)
+    say(f"case sampled chain T={T} d={d} V={V} Hs={Hs} r={r} P={P} B={B} {dtype}")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    H, t0 = head.upload(inp["H"]), head.upload(inp["t0"])
+    Lb = head.base_logits(H)
+    seed = 0x1234_5678_9ABC + B
+    toks, L, _ = head.draft_chain_sampled(H, Lb, t0, T, seed)
+    m = oracle.Model.from_config(cfg, w)
+    compare_sampled(m, inp["H"], Lb.cpu().numpy(), inp["t0"], T, seed, toks.cpu().numpy(), L.cpu().numpy(), "small")
+    # tokens only: the same draws
+    toks2, _, _ = head.draft_chain_sampled(H, Lb, t0, T, seed, want_logits=False)
+    assert torch.equal(toks, toks2)
+
+
+def test_zero_temperature_is_the_greedy_chain():
+    cfg = small_config(d=64, V=2003, Hs=32, r=32, P=8, B=6, dtype="bf16", biases=True)
+    say("case sampled chain T=0")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    H, t0 = head.upload(inp["H"]), head.upload(inp["t0"])
+    Lb = head.base_logits(H)
+    prev = dh.set_chain_mode(1)  # the sampled call runs the three launches per step
+    try:
+        g_t, g_L, _ = head.draft_chain(H, Lb, t0)
+    finally:
+        dh.set_chain_mode(prev)
+    s_t, s_L, _ = head.draft_chain_sampled(H, Lb, t0, 0.0, seed=5)
+    assert torch.equal(g_t, s_t) and torch.equal(g_L, s_L)
+
+
+def test_draws_follow_softmax():
+    """W2 = 0: every position's logits are the given row, so each sequence's token is one
+    draw from softmax(L / T); 2000 sequences, chi-square against the closed form."""
+    say("case sampled chain frequencies")
+    cfg = small_config(d=8, V=6, Hs=8, r=8, P=2, B=2000, dtype="f32", biases=False)
+    w = synth.make_weights(cfg)
+    w["w2"] = np.zeros_like(w["w2"])
+    T = 0.8
+    L = np.array([1.0, 0.5, 0.0, -0.5, 2.0, 1.2], np.float32)
+    B = cfg.batch
+    head = dh.DraftHead.from_config(cfg, w)
+    H = head.upload(np.zeros((B, 2, 8), np.float32))
+    Lb = head.upload(np.broadcast_to(L, (B, 2, 6)).copy())
+    t0 = head.upload(np.zeros(B, np.int32))
+    toks, _, _ = head.draft_chain_sampled(H, Lb, t0, T, seed=77, want_logits=False)
+    g = toks.cpu().numpy()
+    p = np.exp(L / T - (L / T).max())
+    p /= p.sum()
+    for pos in range(2):
+        chi = stats.chisquare(np.bincount(g[:, pos], minlength=6), p * B)
+        assert chi.pvalue > 1e-3
+    o_t, _, _ = oracle.Model.from_config(cfg, w).chain_sampled(np.zeros((B, 2, 8), np.float32),
+                                                               np.broadcast_to(L, (B, 2, 6)).copy(),
+                                                               np.zeros(B, np.int32), T, 77, want_logits=False)
+    assert np.array_equal(g, o_t)
+
+
+@pytest.mark.parametrize("key,sample", [("qwen3_4b_b1", [0]), ("qwen3_4b_b32", [0, 17, 31])])
+def test_sampled_chain_full_size(key, sample):
+    cfg = synth.CONFIGS[key]
+    say(f"case sampled chain full {key} T=1")
+    head = dh.DraftHead.from_config(cfg, weights_for(key))
+    inp = synth.make_inputs(cfg)
+    H, t0 = head.upload(inp["H"]), head.upload(inp["t0"])
+    Lb = head.base_logits(H)
+    toks, _, _ = head.draft_chain_sampled(H, Lb, t0, 1.0, seed=2026, want_logits=False)
+    m = oracle.Model.from_config(cfg, weights_for(key))
+    g = toks.cpu().numpy()
+    # the oracle draws for sequence b with its index in the batch: run it on the batch's
+    # leading sequences up to the last sampled one would cost too much, so each sampled
+    # sequence is checked on its own with the noise stream of its index
+    for b in sample:
+        Hb = np.ascontiguousarray(inp["H"][b:b + 1])
+        Lbb = Lb[b:b + 1].cpu().numpy()
+        f_t, _, f_m = m.chain_sampled(Hb, Lbb, inp["t0"][b:b + 1], 1.0, 2026, seq0=b, forced=g[b:b + 1],
+                                      want_logits=False)
+        firm = f_m > MARGIN_FIRM
+        assert not (firm & (f_t != g[b:b + 1])).any(), (key, b)
