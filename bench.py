@@ -43,8 +43,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_F32_PEAK_TFLOPS = 157.3
 METRIC = "draft blocks/sec (16-pos Domino chain, Qwen3-4B shape) + % of HBM/MFMA peak"
 MARGIN_FIRM = 1e-2              # tokens must agree where the oracle's top-2 margin exceeds this
-EXTRA = ("qwen3_4b_b32", "qwen3_8b_b16", "qwen3_4b_tree")
-PARITY_SAMPLE = {"qwen3_4b_b1": [0], "qwen3_4b_b32": [0, 31], "qwen3_8b_b16": [0, 15], "qwen3_4b_tree": [0, 7]}
+EXTRA = ("qwen3_4b_b32", "qwen3_8b_b16", "qwen3_4b_tree", "qwen3_4b_b1_sampled")
+PARITY_SAMPLE = {"qwen3_4b_b1": [0], "qwen3_4b_b32": [0, 31], "qwen3_8b_b16": [0, 15], "qwen3_4b_tree": [0, 7],
+                 "qwen3_4b_b1_sampled": [0]}
+# workloads that are a base config run another way: (base config, temperature, seed)
+SAMPLED = {"qwen3_4b_b1_sampled": ("qwen3_4b_b1", 1.0, 20260)}
 
 
 def log(*a):
@@ -163,7 +166,7 @@ def host_info():
 class Workload:
     """Device buffers of one workload and its step()."""
 
-    def __init__(self, cfg, weights, inputs, chain_mode, write_logits):
+    def __init__(self, cfg, weights, inputs, chain_mode, write_logits, temperature=0.0, seed=0):
         import torch
 
         import draft_head_amd as dh
@@ -184,6 +187,7 @@ class Workload:
         else:
             self.ws = self.head.workspace(B)
         self.chain_mode = chain_mode
+        self.temperature, self.seed = temperature, seed
         self.stream = torch.cuda.current_stream()
 
     def base(self):
@@ -195,6 +199,10 @@ class Workload:
             dh.domino_tree_draft(self.head.dims, self.head.weights, self.H, self.Lb, self.t0, self.B, c.nodes, c.topm,
                                  self.tree["parents"], self.tree["tokens"], self.tree["depth"], self.scores, self.ws,
                                  self.ws.numel(), self.stream)
+        elif self.temperature > 0:
+            dh.domino_draft_chain_sampled(self.head.dims, self.head.weights, self.H, self.Lb, self.t0, self.B,
+                                          self.temperature, self.seed, self.toks, self.logits, self.ws,
+                                          self.ws.numel(), self.stream)
         else:
             dh.domino_draft_chain(self.head.dims, self.head.weights, self.H, self.Lb, self.t0, self.B, self.toks,
                                   self.logits, self.ws, self.ws.numel(), self.stream)
@@ -399,6 +407,28 @@ def parity_chain(cfg, w, inp, g_tokens, sample, oracle_runs=None):
                     "oracle top-2 margin <= 1e-2, then equal wherever the forced-prefix oracle's margin > 1e-2"}
 
 
+def parity_sampled(cfg, w, inp, Lb_gpu, g_tokens, sample, T, seed):
+    """The sampled chain: tokens against the oracle's draws on the same fp32 base logits, under
+    the margin rule on the perturbed logits L + T g (forced-prefix past a tolerated divergence)."""
+    import numpy as np
+
+    import oracle
+    m = oracle.Model.from_config(cfg, w)
+    checked, mism, near = 0, 0, 0
+    for b in sample:
+        H = np.ascontiguousarray(inp["H"][b:b + 1])
+        f_t, _, f_m = m.chain_sampled(H, np.ascontiguousarray(Lb_gpu[b:b + 1]), inp["t0"][b:b + 1], T, seed, seq0=b,
+                                      forced=g_tokens[b:b + 1], want_logits=False)
+        firm = f_m > MARGIN_FIRM
+        checked += int(firm.sum())
+        near += int((~firm).sum())
+        mism += int((firm & (f_t != g_tokens[b:b + 1])).sum())
+    return {"sequences": list(sample), "positions_checked": checked, "mismatches": mism, "near_ties": near,
+            "ok": mism == 0, "temperature": T, "seed": seed,
+            "rule": "timed draws vs the oracle's Gumbel-max draws on the same base logits and noise: equal wherever "
+                    "the oracle's top-2 margin of L + T g exceeds 1e-2 (forced prefix)"}
+
+
 def parity_tree(cfg, w, inp, Lb_gpu, g_tree, g_scores, sample):
     import numpy as np
 
@@ -476,17 +506,43 @@ def tiny_1t():
 
 
 # ---- one workload end to end ---------------------------------------------------------------------
-def run_workload(cfg, args, steps, warmup, weights, parity_lbs=None):
+def verify_inputs_record(wl, reps=50):
+    """The tree's verification inputs (ancestor-only mask, positions, tokens) from the timed
+    trees: launch time by events around the call, bytes = what it reads and writes."""
+    import numpy as np
+    torch, dh = wl.torch, wl.dh
+    B, N = wl.B, wl.cfg.nodes
+    E = N + 1
+    mask = torch.empty((B, E, E), dtype=torch.uint8, device=wl.head.device)
+    pos = torch.empty((B, E), dtype=torch.int32, device=wl.head.device)
+    tok = torch.empty((B, E), dtype=torch.int32, device=wl.head.device)
+    run = lambda: dh.domino_tree_verify_inputs(wl.tree["parents"], wl.tree["tokens"], wl.t0, None, B, N, mask, pos,
+                                               tok, wl.stream)
+    run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(wl.stream)
+    for _ in range(reps):
+        run()
+    ev[1].record(wl.stream)
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+    byts = B * (2 * N * 4 + 4) + B * (E * E + 2 * E * 4)
+    return {"us": us, "bytes": byts, "bound": "latency (one 64-lane workgroup per tree)",
+            "achieved_gbs": byts / us * 1e-3}, (mask.cpu().numpy(), pos.cpu().numpy(), tok.cpu().numpy())
+
+
+def run_workload(cfg, args, steps, warmup, weights, parity_lbs=None, label=None, temperature=0.0, seed=0):
     import numpy as np
     import synth
     inp = synth.make_inputs(cfg)
-    wl = Workload(cfg, weights, inp, args.chain_mode, args.logits)
-    log(f"{cfg.name}: timing {steps} steps")
+    wl = Workload(cfg, weights, inp, args.chain_mode, args.logits, temperature, seed)
+    name = label or cfg.name
+    log(f"{name}: timing {steps} steps")
     t = time_steps(wl, steps, warmup)
     g_tokens = wl.toks.cpu().numpy()
     g_tree = {k: v.cpu().numpy() for k, v in wl.tree.items()} if cfg.tree else None
     g_scores = wl.scores.cpu().numpy() if cfg.tree else None
-    Lb_gpu = wl.Lb.cpu().numpy() if cfg.tree else None
+    Lb_gpu = wl.Lb.cpu().numpy() if (cfg.tree or temperature > 0) else None
     t_base, t_chain, tb_med, tc_med = time_launches(wl, steps)
     roof, kernels = roofline_record(cfg, cfg.batch, t_base, t_chain, args.logits, args.chain_mode)
     kernels["base"]["us_median"], kernels["chain"]["us_median"] = tb_med * 1e6, tc_med * 1e6
@@ -494,24 +550,34 @@ def run_workload(cfg, args, steps, warmup, weights, parity_lbs=None):
     rec = {"value": cfg.batch / (t["ms_per_step"] * 1e-3), "unit": "draft blocks/s",
            "ms_per_step": t["ms_per_step"], "step_ms": t["step_ms"], "steps": steps, "warmup": warmup,
            "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
-           "config": {"workload": cfg.name, "batch": cfg.batch, "block": cfg.block, "hidden": cfg.hidden,
+           "config": {"workload": name, "batch": cfg.batch, "block": cfg.block, "hidden": cfg.hidden,
                       "vocab": cfg.vocab, "gru_hidden": cfg.gru_hidden, "rank": cfg.rank,
                       "chain_mode": args.chain_mode, "write_logits": bool(args.logits), "schedule": sched,
+                      **({"temperature": temperature, "seed": seed} if temperature > 0 else {}),
                       **({"tree_nodes": cfg.nodes, "tree_topm": cfg.topm} if cfg.tree else {})},
            "roofline": roof, "kernels": kernels, "wall_s_timed": t["wall_s_timed"]}
     if step_us:
         rec["chain_step_us"] = [round(x, 2) for x in step_us]
-    if cfg.name == "qwen3_4b_b32" and not args.no_cache_probe:
+    if cfg.name == "qwen3_4b_b32" and not args.no_cache_probe and temperature == 0:
         log(f"{cfg.name}: cache probe")
         rec["infinity_cache"] = cache_probe(wl)
+    verify = None
+    if cfg.tree:
+        rec["verify_inputs"], verify = verify_inputs_record(wl)
     del wl
     import torch
     torch.cuda.empty_cache()
     if not args.no_parity:
         log(f"{cfg.name}: oracle parity")
-        sample = [b for b in PARITY_SAMPLE.get(cfg.name, [0]) if b < cfg.batch]
+        sample = [b for b in PARITY_SAMPLE.get(name, [0]) if b < cfg.batch]
         if cfg.tree:
             rec["parity"] = parity_tree(cfg, weights, inp, Lb_gpu, g_tree, g_scores, sample)
+            import oracle
+            o = oracle.tree_verify_inputs(g_tree["parents"], g_tree["tokens"], inp["t0"])
+            rec["verify_inputs"]["parity"] = {"ok": all(np.array_equal(x, y) for x, y in zip(verify, o)),
+                                              "rule": "mask, positions and tokens bit-exact against the oracle"}
+        elif temperature > 0:
+            rec["parity"] = parity_sampled(cfg, weights, inp, Lb_gpu, g_tokens, sample, temperature, seed)
         else:
             rec["parity"] = parity_chain(cfg, weights, inp, g_tokens, sample, parity_lbs)
     return rec, inp, g_tokens
@@ -537,7 +603,8 @@ def main():
             __graft_entry__.build()
             break
 
-    cfg = synth.CONFIGS[args.config]
+    base, T, seed = SAMPLED.get(args.config, (args.config, 0.0, 0))
+    cfg = synth.CONFIGS[base]
     cache = {}
 
     def weights_of(c):
@@ -549,31 +616,35 @@ def main():
         return cache[key]
 
     w = weights_of(cfg)
-    head, inp, g_tokens = run_workload(cfg, dataclass_args(args, parity=False), args.steps, args.warmup, w)
+    head, inp, g_tokens = run_workload(cfg, dataclass_args(args, parity=(T > 0 or cfg.tree) and not args.no_parity), args.steps,
+                                       args.warmup, w, label=args.config, temperature=T, seed=seed)
     out = {"metric": METRIC, "value": head["value"], "unit": "draft blocks/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",
            "config": {**head["config"], "parallelism": "none (one GPU)"},
            "step_ms": head["step_ms"], "roofline": head["roofline"], "kernels": head["kernels"],
            "wall_s_timed": head["wall_s_timed"]}
-    if "chain_step_us" in head:
-        out["chain_step_us"] = head["chain_step_us"]
+    for k in ("chain_step_us", "parity", "verify_inputs"):
+        if k in head:
+            out[k] = head[k]
     if not args.no_cpu_baseline:
         log("oracle baseline")
         out["cpu_baseline"], lbs = cpu_baseline(cfg, w, inp, args.cpu_seconds)
         out["cpu_baseline"]["host"] = host_info()
         out["cpu_baseline"]["tiny_f32_single_thread"] = tiny_1t()
-        if not args.no_parity and not cfg.tree:
+        if not args.no_parity and not cfg.tree and T == 0:
             out["parity"] = parity_chain(cfg, w, inp, g_tokens, sorted(lbs)[:4], lbs)
-    elif not args.no_parity and not cfg.tree:
+    elif not args.no_parity and not cfg.tree and T == 0:
         out["parity"] = parity_chain(cfg, w, inp, g_tokens, PARITY_SAMPLE.get(cfg.name, [0]))
     extra = [] if args.extra in ("", "none") else [e for e in args.extra.split(",") if e != cfg.name]
     if extra:
         out["configs"] = {}
     for name in extra:
-        c = synth.CONFIGS[name]
+        base, T, seed = SAMPLED.get(name, (name, 0.0, 0))
+        c = synth.CONFIGS[base]
         try:
-            rec, _, _ = run_workload(c, args, args.extra_steps, min(args.warmup, 10), weights_of(c))
+            rec, _, _ = run_workload(c, args, args.extra_steps, min(args.warmup, 10), weights_of(c), label=name,
+                                     temperature=T, seed=seed)
         except Exception as e:  # a failing extra workload is reported, never hides the headline
             rec = {"error": f"{type(e).__name__}: {e}"}
         out["configs"][name] = rec

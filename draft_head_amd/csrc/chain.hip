@@ -57,6 +57,14 @@ __device__ __forceinline__ int opaque_lane() {
   return l;
 }
 
+// an int the compiler cannot see through (keeps a loop-invariant LDS read
+// inside the loop, where it costs a few registers instead of many)
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
 __device__ __forceinline__ float bias_at(const float* b, int i) { return b ? b[i] : 0.f; }
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
 
@@ -685,8 +693,8 @@ struct LaneMax {
   float v;
   int32_t i;
 };
-__device__ __forceinline__ void lane_max(LaneMax& m, float L, int32_t idx) {
-  const bool take = L > m.v || m.i < 0;
+__device__ __forceinline__ void lane_max(LaneMax& m, float L, int32_t idx, bool valid = true) {
+  const bool take = valid & ((L > m.v) | (m.i < 0));  // no short circuit: selects, not branches
   m.v = take ? L : m.v;
   m.i = take ? idx : m.i;
 }
@@ -868,8 +876,9 @@ template <int RG, bool kSkipEmpty>
 __device__ __forceinline__ void load_base_rows(const ChainArgs& a, int p, int v, int kg, float (&lb)[RG][2],
                                                float& b2) {
   const int vc = min(v, a.V - 1);
-  const float bias = (a.b2 ? a.b2 : a.Lb)[vc];  // always loaded (a uniform select of the address)
-  b2 = a.b2 ? bias : 0.f;
+  // always loaded (a uniform select of the address); the value is only used
+  // when b2 exists (rows_epilogue), so no select here waits for the load
+  b2 = (a.b2 ? a.b2 : a.Lb)[vc];
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
@@ -916,10 +925,12 @@ __device__ __forceinline__ float gumbel_of(uint32_t x) {
 
 // this lane's logits of a tile into its running argmaxes (and out, with
 // kWrite); kSample: the argmax is taken over L + T g (the logits written are L)
+// (entries past V take part in no argmax and are not written; a select, not a
+// branch, so no load is waited for inside a masked region)
 template <bool kWrite, int RG, bool kSample = false>
 __device__ __forceinline__ void rows_epilogue(const ChainArgs& a, int p, int v, int kg, const float (&lb)[RG][2],
                                               float b2, const f32x4 (&acc)[RG][2], LaneMax (&lm)[RG][2]) {
-  if (v >= a.V) return;
+  const bool valid = v < a.V;
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     uint32_t x[2] = {0u, 0u};
@@ -934,12 +945,12 @@ __device__ __forceinline__ void rows_epilogue(const ChainArgs& a, int p, int v, 
       const float base = a.b2 ? lb[g][j] + b2 : lb[g][j];
       const float L = base + (hi + lo);
       if constexpr (kSample)
-        lane_max(lm[g][j], L + a.temperature * gumbel_of(x[j]), v);
+        lane_max(lm[g][j], L + a.temperature * gumbel_of(x[j]), v, valid);
       else
-        lane_max(lm[g][j], L, v);
+        lane_max(lm[g][j], L, v, valid);
       if constexpr (kWrite) {
         const int b = g * kSeqPerRowGroup + 2 * kg + j;
-        if (b < a.B) a.out_logits[((size_t)b * a.P + p) * a.V + v] = L;
+        if (valid && b < a.B) a.out_logits[((size_t)b * a.P + p) * a.V + v] = L;
       }
     }
   }
@@ -1147,14 +1158,6 @@ __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_b
   if (i + 1 < n) consume(i + 1, s1);
   publish_rows<RG, kLL>(a, p, lm, sbest, ep);
   return true;
-}
-
-// an int the compiler cannot see through (keeps a loop-invariant LDS read
-// inside the loop, where it costs a few registers instead of many)
-__device__ __forceinline__ int opaque_zero() {
-  int z;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-  return z;
 }
 
 // phase O of the stepwise schedule with many waves: each of NWV waves takes
