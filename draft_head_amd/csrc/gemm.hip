@@ -168,6 +168,161 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_rows16(const uint16_t* __rest
   }
 }
 
+// At most 16 rows of A, B read in whole-row pieces.  Streaming B in the MFMA
+// fragment pattern (each load instruction: 16 rows x 64 B) reaches about 4.3
+// TB/s on this part; 512-byte runs of single rows reach about 6 TB/s.  So each
+// wave loads a "slab" of a 16-row tile, 256 k wide (two rows per instruction,
+// eight instructions), two slabs ahead, writes the slab it is about to use to
+// its own 8 KB of LDS and reads the B fragments back from there.  Row r's
+// 16-byte unit u sits at unit position r * 32 + (u ^ r): both the writes and
+// the fragment reads fall in distinct banks.  A is staged once in LDS in
+// fragment order.  The workgroup's (tile, slab) pairs are split evenly over
+// its waves; a tile cut between waves w and w + 1 is finished by wave w as
+// its lower slabs plus wave w + 1's higher slabs, a fixed order.
+//
+// Output: scattered 64-byte stores issued while B streams cost about 13% of
+// the kernel's time (stores share the load counter, and the partial-line
+// writes land all over C's rows).  With STAGE, a wave keeps its finished
+// tiles in registers (at most kR16Keep; the launch guarantees it), and at
+// the end the workgroup assembles its whole column block in LDS and writes it
+// row by row in 256-byte runs.  Loads use a wave-uniform base plus 32-bit lane
+// offsets fixed for the whole kernel.
+constexpr int kR16SlabK = 256;  // k per slab: 8 chunks of 32
+constexpr int kR16Keep = 8;     // finished tiles a wave holds for the block store
+template <int WAVES, bool STAGE>
+__global__ __launch_bounds__(64 * WAVES) void gemm_rows16_slab(const uint16_t* __restrict__ A, int lda,
+                                                               const uint16_t* __restrict__ B, int ldb,
+                                                               float* __restrict__ C, int ldc, int M, int N, int K) {
+  // [k chunks][64 lanes] of A, then WAVES slabs of 8 KB; after the main loop, the output block [16][cols]
+  extern __shared__ __attribute__((aligned(16))) uint4 sA[];
+  __shared__ __attribute__((aligned(16))) float4 part[WAVES][64];
+  const int nck = K / 32, NS = K / kR16SlabK;
+  for (int q = threadIdx.x; q < nck * 64; q += blockDim.x) {
+    const int c = q >> 6, l = q & 63, r = l & 15, k = c * 32 + (l >> 4) * 8;
+    sA[q] = r < M ? *reinterpret_cast<const uint4*>(A + (size_t)r * lda + k) : make_uint4(0, 0, 0, 0);
+  }
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane & 15, kg = lane >> 4, dr = lane >> 5, unit = lane & 31;
+  unsigned char* slab = reinterpret_cast<unsigned char*>(sA + nck * 64) + (size_t)wv * 8192;
+  const int T = (N + 15) / 16, G = gridDim.x, g = blockIdx.x;
+  const int tb = (int)((int64_t)T * g / G), te = (int)((int64_t)T * (g + 1) / G);
+  const int64_t total = (int64_t)(te - tb) * NS;
+  const int64_t lo = total * wv / WAVES, hi = total * (wv + 1) / WAVES;
+  const int t_lo = tb + (int)(lo / NS);
+  const bool lo_cut = lo % NS != 0;  // the range starts inside tile t_lo
+  uint32_t voff[8];                  // byte offsets of the lane's loads from a slab's start: row 2q + dr, unit
+#pragma unroll
+  for (int q = 0; q < 8; ++q) voff[q] = (uint32_t)((2 * q + dr) * ldb + unit * 8) * 2u;
+  __syncthreads();
+
+  // the loads of unit u (tile tb + u / NS, slab u % NS); past hi they repeat the last unit (never used)
+  auto issue = [&](int64_t u, bf16x8 (&v)[8]) {
+    const int64_t uu = u < hi ? u : hi - 1;
+    const int t = tb + (int)(uu / NS), s = (int)(uu % NS);
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(B + (size_t)t * 16 * ldb + s * kR16SlabK);
+    const int rmax = N - 1 - t * 16;
+    if (rmax >= 15) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = load8(reinterpret_cast<const uint16_t*>(base + voff[q]));
+    } else {  // the last tile of a ragged B: rows past its end read its last row
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        v[q] = load8(reinterpret_cast<const uint16_t*>(base) + (size_t)min(2 * q + dr, rmax) * ldb + unit * 8);
+    }
+  };
+  auto store_tile = [&](int t, const f32x4& v) {
+    const int n = t * 16 + row;
+    if (n >= N) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (kg * 4 + i < M) C[(size_t)(kg * 4 + i) * ldc + n] = v[i];
+  };
+  f32x4 kept[kR16Keep];
+  int nkept = 0, tfirst = 0;  // kept[j] is tile tfirst + j: a wave's finished tiles are consecutive
+  auto finish = [&](int t, const f32x4& v) {
+    if (!STAGE) {
+      store_tile(t, v);
+      return;
+    }
+    if (nkept == 0) tfirst = t;
+#pragma unroll
+    for (int j = 0; j < kR16Keep; ++j)
+      if (j == nkept) kept[j] = v;
+    ++nkept;
+  };
+  f32x4 head = {0.f, 0.f, 0.f, 0.f};  // lower slabs of the tile cut at the end of this wave's range
+  int cut_tile = -1;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 b0[8], b1[8], b2[8];
+  if (lo < hi) {
+    issue(lo, b0);
+    issue(lo + 1, b1);
+  }
+  auto consume = [&](int64_t u, const bf16x8 (&v)[8]) {
+    const int t = tb + (int)(u / NS), s = (int)(u % NS);
+    if (s == 0 || u == lo) acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int r = 2 * q + dr;
+      *reinterpret_cast<bf16x8*>(slab + (size_t)(r * 32 + (unit ^ r)) * 16) = v[q];
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {  // the wave's own LDS writes above complete before these reads
+      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(slab + (size_t)(row * 32 + ((c * 4 + kg) ^ row)) * 16);
+      const bf16x8 af = __builtin_bit_cast(bf16x8, sA[(s * 8 + c) * 64 + lane]);
+      acc = mma(af, bf, acc);
+    }
+    const bool higher = t == t_lo && lo_cut;  // this wave holds only the higher slabs of tile t
+    const bool last = s == NS - 1 || u == hi - 1;
+    if (last) {
+      if (higher) {
+        part[wv][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      } else if (s == NS - 1) {
+        finish(t, acc);
+      } else {  // the range ends inside tile t
+        head = acc;
+        cut_tile = t;
+      }
+    }
+  };
+  int64_t u = lo;
+  for (; u + 3 <= hi; u += 3) {
+    issue(u + 2, b2);
+    consume(u, b0);
+    issue(u + 3, b0);
+    consume(u + 1, b1);
+    issue(u + 4, b1);
+    consume(u + 2, b2);
+  }
+  if (u < hi) consume(u, b0);
+  if (u + 1 < hi) consume(u + 1, b1);
+  __syncthreads();  // part[] written; A and the slabs no longer read
+  f32x4 joined = head;
+  if (cut_tile >= 0) {
+    const float4 q = part[wv + 1][lane];
+    joined = f32x4{head[0] + q.x, head[1] + q.y, head[2] + q.z, head[3] + q.w};
+    if (!STAGE) store_tile(cut_tile, joined);
+  }
+  if (STAGE) {
+    float* blk = reinterpret_cast<float*>(sA);
+    const int cols = (te - tb) * 16;
+    auto put = [&](int t, const f32x4& v) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) blk[(kg * 4 + i) * cols + (t - tb) * 16 + row] = v[i];
+    };
+#pragma unroll
+    for (int j = 0; j < kR16Keep; ++j)
+      if (j < nkept) put(tfirst + j, kept[j]);
+    if (cut_tile >= 0) put(cut_tile, joined);
+    __syncthreads();
+    const int c0 = tb * 16, cn = min(cols, N - c0);
+    for (int q = threadIdx.x; q < M * cols; q += blockDim.x) {
+      const int m = q / cols, c = q - m * cols;
+      if (c < cn) C[(size_t)m * ldc + c0 + c] = blk[q];
+    }
+  }
+}
+
 #ifndef DH_WIDE_BK
 #define DH_WIDE_BK 64   // k depth of a stage of gemm_wide
 #endif
@@ -505,8 +660,36 @@ hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int 
   if (dtype == kF32)
     return launch_stream((const float*)A, lda, (const float*)B, ldb, C, ldc, M, N, K, s);
   if (M <= 16) {
-    constexpr int WV = DH_R16_WAVES;
     const int cus = device_cus();
+    // whole 256-wide slabs; A, eight 8 KB slabs and the partial sums within the LDS; at least one
+    // tile per wave, so that no tile is cut twice.  The block store needs every wave's finished
+    // tiles (at most ceil(tiles per workgroup / waves) of them) to fit its registers, and the
+    // block ([16][tiles * 16] fp32) to fit the A and slab space.
+    constexpr int SW = 8;
+    const size_t slds = (size_t)(K / 32) * 64 * 16 + (size_t)SW * 8192;
+    if (cus > 0 && K % kR16SlabK == 0 && lda % 8 == 0 && ldb % 8 == 0 && ldb < (1 << 26) &&
+        slds + SW * 64 * 16 <= 160 * 1024 && (N + 15) / 16 >= SW * cus) {
+      const int per_wg = ((N + 15) / 16 + cus - 1) / cus;
+      const bool stage = (per_wg + SW - 1) / SW <= kR16Keep && (size_t)per_wg * 1024 <= slds;
+      const void* fn = stage ? (const void*)gemm_rows16_slab<SW, true> : (const void*)gemm_rows16_slab<SW, false>;
+      static thread_local int slab_attr_device[2] = {-1, -1};
+      int dev = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) return e;
+      if (slab_attr_device[stage] != dev) {
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - SW * 64 * 16));
+        if (e != hipSuccess) return e;
+        slab_attr_device[stage] = dev;
+      }
+      if (stage)
+        hipLaunchKernelGGL((gemm_rows16_slab<SW, true>), dim3(cus), dim3(64 * SW), slds, s, (const uint16_t*)A, lda,
+                           (const uint16_t*)B, ldb, C, ldc, M, N, K);
+      else
+        hipLaunchKernelGGL((gemm_rows16_slab<SW, false>), dim3(cus), dim3(64 * SW), slds, s, (const uint16_t*)A,
+                           lda, (const uint16_t*)B, ldb, C, ldc, M, N, K);
+      return hipGetLastError();
+    }
+    constexpr int WV = DH_R16_WAVES;
     const size_t lds = (size_t)((K + 31) / 32) * 64 * 16;
     if (cus > 0 && (N + 15) / 16 >= WV * cus && lds <= 128 * 1024) {
       static thread_local int attr_device = -1;

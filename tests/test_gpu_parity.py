@@ -94,9 +94,15 @@ def test_base_logits_ragged(dtype, d, V, B, P):
     _check_base_rel(g, oracle.Model.from_config(cfg, w).base_logits(inp["H"]), "ragged")
 
 
-# one sequence, many columns: the persistent balanced kernel (at least eight
-# 16-column tiles per CU), with ragged rows, columns and k tails
-@pytest.mark.parametrize("d,V,P", [(264, 33013, 5), (2568, 40009, 16), (40, 70001, 3), (1032, 36871, 1)])
+# one sequence, many columns: the persistent balanced kernels (at least eight
+# 16-column tiles per CU), with ragged rows, columns and k tails; k a multiple
+# of 256 takes the slab-streaming kernel (the widest k whose A and slabs fit
+# the LDS, the fewest tiles it takes, one row; up to 64 tiles per workgroup
+# its output goes out as one block per workgroup, beyond that tile by tile),
+# any other k the fragment one
+@pytest.mark.parametrize("d,V,P", [(264, 33013, 5), (2568, 40009, 16), (40, 70001, 3), (1032, 36871, 1),
+                                   (256, 32769, 5), (1024, 40009, 16), (2816, 36001, 7), (2560, 65537, 1),
+                                   (256, 270001, 2)])
 def test_base_logits_one_sequence_wide(d, V, P):
     cfg = small_config(d=d, V=V, B=1, P=P, dtype="bf16")
     say(f"case base logits one sequence wide d={d} V={V} P={P}")
