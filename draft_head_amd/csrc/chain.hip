@@ -38,7 +38,7 @@
 namespace dh {
 
 // Opt-in phase timestamps (constant 100 MHz clock) for tuning builds only.
-[[maybe_unused]] constexpr int kTraceSlots = 12;
+[[maybe_unused]] constexpr int kTraceSlots = 16;
 #ifdef DH_TRACE_PHASES
 #define DH_STAMP(p, slot) \
   do { if (a.trace && threadIdx.x == 0) a.trace[((size_t)(p) * gridDim.x + blockIdx.x) * kTraceSlots + (slot)] = wall_clock64(); } while (0)
@@ -268,14 +268,24 @@ __device__ __forceinline__ void ll_put4(uint64_t* slot, int n, int b, int k, con
   }
 }
 
-// per-wave partial sums of W_hh h(p) over this wave's k chunks
+// The GRU pre-activations are sums over k chunks of 32 in sixteen chains:
+// chain v = w + 4j takes, in increasing order, the chunks c with c % 4 == w
+// and (c / 4) % 4 == j, the hidden-half chunks first, then the input-half
+// ones; the total is sum over w of (sum over j of chain (w, j)), both left to
+// right.  A kernel with four waves keeps chains (w, 0..3) in wave w; one with
+// sixteen keeps chain v in wave v; they produce the same bits.
+constexpr int kGruChains = 16;
+
+// per-wave partial sums of W_hh h(p) over this wave's k chunks, chains (wv, 0..3)
 // kLL: the state comes as hand-off words of the persistent launch `ep`
 // seq0: first sequence of this work item's 16 NCB columns (three-launch schedule)
 template <class W, int NCB, bool kLds, bool kLL = false>
-__device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int item, const W* lds, f32x4 (&acc)[NCB], uint32_t ep = 0,
+__device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int item, const W* lds, f32x4 (&acc)[4][NCB], uint32_t ep = 0,
                                                 int seq0 = 0) {
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[j][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (p == 0) return;  // h(0) = 0
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
@@ -291,7 +301,7 @@ __device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int i
     bok[cb] = b < B;
     bb[cb] = bok[cb] ? b : 0;
   }
-  constexpr int U = NCB == 1 ? 8 : 4;
+  constexpr int U = NCB == 1 ? 8 : 4;  // a multiple of 4: chunk c0 + 4q is in chain (wv, q % 4)
   const int nch = (Hs + 31) / 32;
   for (int c0 = wv; c0 < nch; c0 += 4 * U) {  // this wave's chunks wv, wv + 4, ... in order
     frag_t<W> A[U];
@@ -324,19 +334,19 @@ __device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int i
 #pragma unroll
     for (int q = 0; q < U; ++q)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(A[q], S[q][cb], acc[cb]);
+      for (int cb = 0; cb < NCB; ++cb) acc[q & 3][cb] = mma(A[q], S[q][cb], acc[q & 3][cb]);
   }
 }
 
 template <class W, int NCB, bool kLL>
-__device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[NCB], float& h_own,
+__device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[4][NCB], float& h_own,
                           uint32_t ep, int seq0 = 0);
 
 // input half on top of the hidden-half partials, then the gates: h(p+1)
 // tok: this step's previous tokens by sequence (raw argmax indices), or
 // null to read them from the argmax keys / first tokens
 template <class W, int NCB, bool kLds, bool kLL = false>
-__device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, float* red, const W* lds, const f32x4 (&acc_h)[NCB],
+__device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, float* red, const W* lds, const f32x4 (&acc_h)[4][NCB],
                            const int32_t* tok = nullptr, float* h_own = nullptr, uint32_t ep = 0, int seq0 = 0) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
@@ -354,11 +364,13 @@ __device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, 
     const int t_ = bok[cb] ? (tok ? clamp_token(a, tok[b]) : prev_token(a, p, b)) : 0;
     xe[cb] = (const W*)a.embed + (size_t)t_ * d + kg * 8;
   }
-  f32x4 acc[NCB];
+  f32x4 acc[4][NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = acc_h[cb];
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[j][cb] = acc_h[j][cb];
 
-  // E[prev] is stored exactly in W: one MFMA per chunk
+  // E[prev] is stored exactly in W: one MFMA per chunk (U a multiple of 4, as above)
   constexpr int U = NCB == 1 ? 16 : 8;
   const int ncx = (d + 31) / 32;
   for (int c0 = wv; c0 < ncx; c0 += 4 * U) {  // this wave's chunks wv, wv + 4, ... in order
@@ -374,7 +386,7 @@ __device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, 
 #pragma unroll
     for (int q = 0; q < U; ++q)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(A[q], X[q][cb], acc[cb]);
+      for (int cb = 0; cb < NCB; ++cb) acc[q & 3][cb] = mma(A[q], X[q][cb], acc[q & 3][cb]);
   }
 
   float h_dummy = 0.f;
@@ -386,25 +398,50 @@ __device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, 
 // once here rather than by every reader.  kLL (persistent): the lane keeps
 // its own unit's fp32 state in h_own across steps, and the state goes out as
 // hand-off words only.
+template <class W, int NCB, bool kLL, int NWG = 4>
+__device__ __forceinline__ void gru_apply(const ChainArgs& a, int p, int item, float* red, float& h_own, uint32_t ep,
+                                          int seq0);
+
+// four waves: each folds its own chains (wv, 0..3), then the waves' sums are added in order
 template <class W, int NCB, bool kLL>
-__device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[NCB], float& h_own,
+__device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[4][NCB], float& h_own,
                           uint32_t ep, int seq0) {
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const f32x4 s = ((acc[0][cb] + acc[1][cb]) + acc[2][cb]) + acc[3][cb];
+    *reinterpret_cast<float4*>(&red[((wv * NCB + cb) * 64 + lane) * 4]) = make_float4(s[0], s[1], s[2], s[3]);
+  }
+  gru_apply<W, NCB, kLL, 4>(a, p, item, red, h_own, ep, seq0);
+}
+
+// red holds, per wave w of NWG and column block cb, the float4 of every lane:
+// NWG 4, wave w's sum of its chains; NWG 16, chain w alone.  Totals them in
+// the canonical order, applies the gates and hands out h(p+1).
+template <class W, int NCB, bool kLL, int NWG>
+__device__ __forceinline__ void gru_apply(const ChainArgs& a, int p, int item, float* red, float& h_own, uint32_t ep,
+                                          int seq0) {
+  static_assert(NWG == 4 || NWG == 16, "four waves with four chains each, or one chain per wave");
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int Hs = a.Hs, B = a.B, j0 = item * 4;
   const float* h_in = a.h + (size_t)p * a.h_step;
   float* h_out = a.h + (size_t)(p + 1) * a.h_step;
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-    *reinterpret_cast<float4*>(&red[((wv * NCB + cb) * 64 + lane) * 4]) =
-        make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
   __syncthreads();
   if (wv < NCB) {
     const int cb = wv;
+    auto part = [&](int w) { return *reinterpret_cast<const float4*>(&red[((w * NCB + cb) * 64 + lane) * 4]); };
     float pre[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float4 v = *reinterpret_cast<const float4*>(&red[((w * NCB + cb) * 64 + lane) * 4]);
+      float4 v = part(w);
+      if constexpr (NWG == 16) {
+#pragma unroll
+        for (int j = 1; j < 4; ++j) {
+          const float4 u = part(w + 4 * j);
+          v = make_float4(v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w);
+        }
+      }
       pre[0] += v.x;
       pre[1] += v.y;
       pre[2] += v.z;
@@ -458,7 +495,9 @@ __device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, f
 // so they are fetched while the workgroup still waits for it; each workgroup
 // reads the same rows every step, so they stay in its XCD's L2.
 constexpr int kXPre = 12;  // chunks per wave fetched ahead (the register budget allows no more)
+static_assert(kXPre % 4 == 0, "chunk wv + 4j is in chain (wv, j % 4)");
 constexpr int kXTail = 20;  // chunks per batch after them (d <= 5120 in one more round)
+static_assert(kXTail % 4 == 0, "chunk c0 + 4q is in chain (wv, q % 4)");
 template <class W>
 __device__ __forceinline__ void gru_x_prefetch(const ChainArgs& a, int item, frag_t<W> (&xw)[kXPre]) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, kg = lane >> 4;
@@ -475,7 +514,7 @@ __device__ __forceinline__ void gru_x_prefetch(const ChainArgs& a, int item, fra
 
 template <class W, int NCB>
 __device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int item, float* red, const frag_t<W> (&xw)[kXPre],
-                                               const f32x4 (&acc_h)[NCB], const int32_t* tok, float& h_own,
+                                               const f32x4 (&acc_h)[4][NCB], const int32_t* tok, float& h_own,
                                                uint32_t ep) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
@@ -492,9 +531,11 @@ __device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int it
     const int t_ = bok[cb] ? (tok ? clamp_token(a, tok[b]) : prev_token(a, p, b)) : 0;
     xe[cb] = (const W*)a.embed + (size_t)t_ * d + kg * 8;
   }
-  f32x4 acc[NCB];
+  f32x4 acc[4][NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = acc_h[cb];
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[j][cb] = acc_h[j][cb];
   const int ncx = (d + 31) / 32;
   {
     frag_t<W> X[kXPre][NCB];
@@ -508,8 +549,9 @@ __device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int it
 #pragma unroll
     for (int j = 0; j < kXPre; ++j)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(xw[j], X[j][cb], acc[cb]);
+      for (int cb = 0; cb < NCB; ++cb) acc[j & 3][cb] = mma(xw[j], X[j][cb], acc[j & 3][cb]);
   }
+  DH_STAMP(p, 12);
   // chunks beyond the prefetched ones (d > 4 * 32 * kXPre), same order
   for (int c0 = wv + 4 * kXPre; c0 < ncx; c0 += 4 * kXTail) {
     frag_t<W> A[kXTail], X[kXTail][NCB];
@@ -524,7 +566,7 @@ __device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int it
 #pragma unroll
     for (int q = 0; q < kXTail; ++q)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(A[q], X[q][cb], acc[cb]);
+      for (int cb = 0; cb < NCB; ++cb) acc[q & 3][cb] = mma(A[q], X[q][cb], acc[q & 3][cb]);
   }
   DH_STAMP(p, 8);
   gru_gates<W, NCB, true>(a, p, item, red, acc, h_own, ep);
@@ -595,6 +637,7 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
   constexpr int U = NCB == 1 ? 8 : 4;
   const int nch = (Hs + 31) / 32;
   if (kLL && h_s) stage_words_ll(a.status, a.ll_h + (size_t)(p + 1) * B * Hs, B * Hs, ll_tag(ep, p), h_s);
+  DH_STAMP(p, 10);
   for (int c0 = wv; c0 < nch; c0 += 4 * U) {  // this wave's chunks wv, wv + 4, ... in order
     frag_t<W> A[U];
     typename act<W>::type S[U][NCB];
@@ -1251,6 +1294,7 @@ __device__ __forceinline__ void ll_tokens_reduce(const ChainArgs& a, int p, uint
     }
     return good;
   });
+  DH_STAMP(p, 14);
   key = wave_max_u64(key);
   if ((tid & 63) == 0) sred[wv] = key;
   __syncthreads();
@@ -1340,10 +1384,103 @@ template <class W, int NCB>
 __global__ __launch_bounds__(256) void chain_gru_k(ChainArgs a, int p) {
   __shared__ __attribute__((aligned(16))) float red[4 * NCB * 64 * 4];
   for (int it = blockIdx.x; it < a.Hs / 4; it += gridDim.x) {
-    f32x4 acc_h[NCB];
+    f32x4 acc_h[4][NCB];
     gru_hidden_part<W, NCB, false>(a, p, it, nullptr, acc_h);
     gru_finish<W, NCB, false>(a, p, it, red, nullptr, acc_h);
   }
+}
+
+// Three-launch schedule, phase G with sixteen waves: one work item per
+// workgroup, wave v computes GRU chain v (chunks v, v + 16, ... of the hidden
+// half, then of the input half), the first batches of both halves loaded
+// together; the same sums as the four-wave form.  (Staging the work item's
+// weight rows in LDS with whole-row loads first measured slower at 32
+// sequences, 17.3 against 14.1 us: the time goes to the sequences' state and
+// embedding fragments, which every workgroup reads.)
+constexpr int kGru16UH = 2;  // hidden-half chunks per wave per batch (Hs <= 1024 in one batch)
+template <class W, int NCB>
+__global__ __launch_bounds__(1024) void chain_gru16_k(ChainArgs a, int p) {
+  static_assert(sizeof(W) == 2, "bf16 weights (fp32 fragments need twice the registers)");
+  // input-half chunks per wave per batch: d <= 2560 in one batch for 16 sequences, two batches for 32
+  constexpr int kGru16UX = NCB == 1 ? 5 : 4;
+  __shared__ __attribute__((aligned(16))) float red[kGruChains * NCB * 64 * 4];
+  const int item = blockIdx.x;
+  const int lane = opaque_lane(), v = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int d = a.d, Hs = a.Hs, B = a.B;
+  const W *rx, *rh;
+  bool has_x, has_h;
+  gru_rows<W, false>(a, item, nullptr, rx, rh, has_x, has_h);
+  int bb[NCB];
+  bool bok[NCB];
+  const W* xe[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int b = cb * 16 + row;
+    bok[cb] = b < B;
+    bb[cb] = bok[cb] ? b : 0;
+    xe[cb] = (const W*)a.embed + (size_t)(bok[cb] ? prev_token(a, p, b) : 0) * d + kg * 8;
+  }
+  const int nch = (Hs + 31) / 32, ncx = (d + 31) / 32;
+  const bool hid = p > 0;  // h(0) = 0: no hidden half at the first step
+  f32x4 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  frag_t<W> AH[kGru16UH], AX[kGru16UX];
+  typename act<W>::type SH[kGru16UH][NCB];
+  frag_t<W> XX[kGru16UX][NCB];
+  auto load_h = [&](int c0) {
+#pragma unroll
+    for (int q = 0; q < kGru16UH; ++q) {
+      const int c = c0 + 16 * q, k = c * 32;
+      const bool kok = hid && c < nch && k + kg * 8 < Hs;
+      AH[q] = load8_or_zero(rh + k, kok && has_h);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) SH[q][cb] = state_frag<W>(a, p, bb[cb], k + kg * 8, kok && bok[cb]);
+    }
+  };
+  auto load_x = [&](int c0) {
+#pragma unroll
+    for (int q = 0; q < kGru16UX; ++q) {
+      const int c = c0 + 16 * q, k = c * 32;
+      const bool kok = c < ncx && k + kg * 8 < d;
+      AX[q] = load8_or_zero(rx + k, kok && has_x);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) XX[q][cb] = load8_or_zero(xe[cb] + k, kok && bok[cb]);
+    }
+  };
+  // chunks past the end load zeros and add exact zeros, as in the four-wave form
+  auto mma_h = [&]() {
+#pragma unroll
+    for (int q = 0; q < kGru16UH; ++q)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(AH[q], SH[q][cb], acc[cb]);
+  };
+  auto mma_x = [&]() {
+#pragma unroll
+    for (int q = 0; q < kGru16UX; ++q)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(AX[q], XX[q][cb], acc[cb]);
+  };
+  if (hid) load_h(v);
+  load_x(v);
+  if (hid) {
+    mma_h();
+    for (int c0 = v + 16 * kGru16UH; c0 < nch; c0 += 16 * kGru16UH) {
+      load_h(c0);
+      mma_h();
+    }
+  }
+  mma_x();
+  for (int c0 = v + 16 * kGru16UX; c0 < ncx; c0 += 16 * kGru16UX) {
+    load_x(c0);
+    mma_x();
+  }
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+    *reinterpret_cast<float4*>(&red[((v * NCB + cb) * 64 + lane) * 4]) = make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
+  float h_dummy = 0.f;
+  gru_apply<W, NCB, false, 16>(a, p, item, red, h_dummy, 0u, 0);
 }
 
 template <class W, int NCB>
@@ -1421,9 +1558,11 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
   uint32_t* h_s = NTW > 0 && wg < nW && stage_state(a.B, a.Hs)
                       ? reinterpret_cast<uint32_t*>(w2l + (size_t)max(0, t_end - t_begin - 4 * NTW) * w2_lds_tile_bytes(KC))
                       : nullptr;
-  f32x4 acc_h[NCB];  // hidden half of this workgroup's next GRU step
+  f32x4 acc_h[4][NCB];  // hidden half of this workgroup's next GRU step, chains (wv, 0..3)
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc_h[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc_h[j][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   __shared__ int32_t tok_s[kMaxChainGroup];
   __shared__ uint64_t sred_t[4 * kMaxChainGroup];
   const uint32_t ep = *a.epoch;  // advanced by the prologue launch
@@ -1484,6 +1623,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
     DH_STAMP(p, 5);
 #ifndef DH_HIDDEN_LATE
     if (hidden && wg < nW) gru_hidden_part<W, NCB, kGruLds, true>(a, p + 1, wg, gl, acc_h, ep);
+    DH_STAMP(p, 15);
 #else
     if (hidden) gru_hidden_part<W, NCB, kGruLds, true>(a, p + 1, wg, gl, acc_h, ep);
 #endif
@@ -1639,6 +1779,9 @@ static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStr
   return hipEventRecord(g.last, s);
 }
 
+#ifndef DH_GRU16
+#define DH_GRU16 1
+#endif
 constexpr size_t kLdsBudget = 144 * 1024;  // dynamic LDS the persistent kernel may use (160 KB per CU)
 
 template <class W, int RG, int KC>
@@ -1675,8 +1818,17 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
   }
   const int nG = a.Hs / 4, nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
   const int nO = T < cus ? T : (cus > 0 ? cus : 256);
+  // phase G, bf16 weights: sixteen waves per work item
+  const bool gru16 = DH_GRU16 && sizeof(W) == 2;
   for (int p = 0; p < a.P; ++p) {
-    hipLaunchKernelGGL((chain_gru_k<W, NCB>), dim3(nG), dim3(256), 0, s, a, p);
+    if constexpr (sizeof(W) == 2) {
+      if (gru16)
+        hipLaunchKernelGGL((chain_gru16_k<W, NCB>), dim3(nG), dim3(1024), 0, s, a, p);
+      else
+        hipLaunchKernelGGL((chain_gru_k<W, NCB>), dim3(nG), dim3(256), 0, s, a, p);
+    } else {
+      hipLaunchKernelGGL((chain_gru_k<W, NCB>), dim3(nG), dim3(256), 0, s, a, p);
+    }
     // one workgroup per 16 rows and 16 sequences: more CUs share the state reads
     hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 15) / 16), dim3(256), 0, s, a, p);
     constexpr int NWV = RG * KC >= 16 ? 8 : 16;  // waves per CU, as registers allow

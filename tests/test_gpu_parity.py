@@ -175,6 +175,8 @@ CHAIN_SHAPES = [
     (48, 515, 16, 16, 3, 40, "bf16"),   # two launches of <= 32 sequences
     (64, 999, 32, 40, 16, 9, "f32"),
     (32, 64, 8, 8, 1, 1, "bf16"),
+    (64, 2053, 32, 256, 5, 24, "bf16"),  # rank 256: whole-row phase O, ragged vocabulary and row groups
+    (32, 1037, 16, 256, 3, 40, "bf16"),
 ]
 
 
