@@ -93,19 +93,56 @@ __device__ __forceinline__ void copy8(W* dst, const W* src) {
 
 __host__ __device__ inline size_t gru_slice_elems(int d, int Hs) { return (size_t)12 * (d + 8) + (size_t)12 * (Hs + 8); }
 
+__device__ __forceinline__ void store8(uint16_t* p, const bf16x8& v) {
+  *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, v);
+}
+__device__ __forceinline__ void store8(float* p, const f32x8& v) {
+  reinterpret_cast<float4*>(p)[0] = v.lo;
+  reinterpret_cast<float4*>(p)[1] = v.hi;
+}
+
+// n pieces of 8 elements, piece q from src(q) to dst(q) (LDS), with NB pieces
+// per thread loaded before any of them is stored: a loop of single
+// load-then-store pairs waits one memory round trip per piece.
+template <class W, int NB, class Src, class Dst>
+__device__ __forceinline__ void copy8_batched(int n, Src src, Dst dst) {
+  if (n <= 0) return;
+  for (int q0 = 0; q0 < n; q0 += NB * (int)blockDim.x) {
+    typename frag<W>::type v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) v[u] = load8(src(min(q0 + u * (int)blockDim.x + (int)threadIdx.x, n - 1)));
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int q = q0 + u * (int)blockDim.x + (int)threadIdx.x;
+      if (q < n) store8(dst(q), v[u]);
+    }
+  }
+}
+
 template <class W>
 __device__ __forceinline__ void stage_gru_slice(const ChainArgs& a, int item, W* lds) {
   const int d = a.d, Hs = a.Hs, j0 = item * 4;
   const int nx = d / 8, nh = Hs / 8;
-  for (int i = threadIdx.x; i < 12 * nx; i += blockDim.x) {
-    const int row = i / nx, c = i - row * nx, g = row >> 2, u = row & 3;
-    copy8(lds + (size_t)row * (d + 8) + c * 8, (const W*)a.w_ih + ((size_t)g * Hs + j0 + u) * d + c * 8);
-  }
   W* lh = lds + (size_t)12 * (d + 8);
-  for (int i = threadIdx.x; i < 12 * nh; i += blockDim.x) {
-    const int row = i / nh, c = i - row * nh, g = row >> 2, u = row & 3;
-    copy8(lh + (size_t)row * (Hs + 8) + c * 8, (const W*)a.w_hh + ((size_t)g * Hs + j0 + u) * Hs + c * 8);
-  }
+  // W_ih rows then W_hh rows, as one list of pieces
+  copy8_batched<W, 11>(
+      12 * (nx + nh),
+      [&](int i) -> const W* {
+        if (i < 12 * nx) {
+          const int row = i / nx, c = i - row * nx;
+          return (const W*)a.w_ih + ((size_t)(row >> 2) * Hs + j0 + (row & 3)) * d + c * 8;
+        }
+        const int ih = i - 12 * nx, row = ih / nh, c = ih - row * nh;
+        return (const W*)a.w_hh + ((size_t)(row >> 2) * Hs + j0 + (row & 3)) * Hs + c * 8;
+      },
+      [&](int i) -> W* {
+        if (i < 12 * nx) {
+          const int row = i / nx, c = i - row * nx;
+          return lds + (size_t)row * (d + 8) + c * 8;
+        }
+        const int ih = i - 12 * nx, row = ih / nh, c = ih - row * nh;
+        return lh + (size_t)row * (Hs + 8) + c * 8;
+      });
   __syncthreads();
 }
 
@@ -577,11 +614,16 @@ __device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int it
 template <class W>
 __device__ __forceinline__ void stage_w1_slice(const ChainArgs& a, int item, W* lds) {
   const int Hs = a.Hs, nh = Hs / 8, k0 = item * 16;
-  for (int i = threadIdx.x; i < 16 * nh; i += blockDim.x) {
-    const int row = i / nh, c = i - row * nh;
-    copy8(lds + (size_t)row * (Hs + 8) + c * 8,
-          (const W*)a.w1 + (size_t)min(k0 + row, a.r - 1) * (a.d + Hs) + a.d + c * 8);
-  }
+  copy8_batched<W, 8>(
+      16 * nh,
+      [&](int i) -> const W* {
+        const int row = i / nh, c = i - row * nh;
+        return (const W*)a.w1 + (size_t)min(k0 + row, a.r - 1) * (a.d + Hs) + a.d + c * 8;
+      },
+      [&](int i) -> W* {
+        const int row = i / nh, c = i - row * nh;
+        return lds + (size_t)row * (Hs + 8) + c * 8;
+      });
   __syncthreads();
 }
 
@@ -841,6 +883,32 @@ __device__ __forceinline__ void agpr_load8(bf16x8* o, const void* const (&p)[8])
       : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
       : "memory");
 }
+// The same for sixteen loads (two tiles): fewer waits at the start of the launch.
+__device__ __forceinline__ void agpr_load16(bf16x8* o, const void* const (&p)[16]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %16, off\n\t"
+      "global_load_dwordx4 %1, %17, off\n\t"
+      "global_load_dwordx4 %2, %18, off\n\t"
+      "global_load_dwordx4 %3, %19, off\n\t"
+      "global_load_dwordx4 %4, %20, off\n\t"
+      "global_load_dwordx4 %5, %21, off\n\t"
+      "global_load_dwordx4 %6, %22, off\n\t"
+      "global_load_dwordx4 %7, %23, off\n\t"
+      "global_load_dwordx4 %8, %24, off\n\t"
+      "global_load_dwordx4 %9, %25, off\n\t"
+      "global_load_dwordx4 %10, %26, off\n\t"
+      "global_load_dwordx4 %11, %27, off\n\t"
+      "global_load_dwordx4 %12, %28, off\n\t"
+      "global_load_dwordx4 %13, %29, off\n\t"
+      "global_load_dwordx4 %14, %30, off\n\t"
+      "global_load_dwordx4 %15, %31, off\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&a"(o[0]), "=&a"(o[1]), "=&a"(o[2]), "=&a"(o[3]), "=&a"(o[4]), "=&a"(o[5]), "=&a"(o[6]), "=&a"(o[7]),
+        "=&a"(o[8]), "=&a"(o[9]), "=&a"(o[10]), "=&a"(o[11]), "=&a"(o[12]), "=&a"(o[13]), "=&a"(o[14]), "=&a"(o[15])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]),
+        "v"(p[8]), "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15])
+      : "memory");
+}
 __device__ __forceinline__ void agpr_load1(bf16x8& o, const void* p) {
   asm volatile("global_load_dwordx4 %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=&a"(o) : "v"(p) : "memory");
 }
@@ -857,7 +925,15 @@ __device__ __forceinline__ void load_resident_w2(const ChainArgs& a, int t_begin
   };
   frag_t<W>* flat = &w2r[0][0];
 #pragma unroll
-  for (int f0 = 0; f0 + 8 <= N; f0 += 8) {
+  for (int f0 = 0; f0 + 16 <= N; f0 += 16) {
+    const void* const p[16] = {ptr_of(f0),      ptr_of(f0 + 1),  ptr_of(f0 + 2),  ptr_of(f0 + 3),
+                               ptr_of(f0 + 4),  ptr_of(f0 + 5),  ptr_of(f0 + 6),  ptr_of(f0 + 7),
+                               ptr_of(f0 + 8),  ptr_of(f0 + 9),  ptr_of(f0 + 10), ptr_of(f0 + 11),
+                               ptr_of(f0 + 12), ptr_of(f0 + 13), ptr_of(f0 + 14), ptr_of(f0 + 15)};
+    agpr_load16(flat + f0, p);
+  }
+#pragma unroll
+  for (int f0 = N - N % 16; f0 + 8 <= N; f0 += 8) {
     const void* const p[8] = {ptr_of(f0), ptr_of(f0 + 1), ptr_of(f0 + 2), ptr_of(f0 + 3),
                               ptr_of(f0 + 4), ptr_of(f0 + 5), ptr_of(f0 + 6), ptr_of(f0 + 7)};
     agpr_load8(flat + f0, p);
@@ -869,11 +945,14 @@ __device__ __forceinline__ void load_resident_w2(const ChainArgs& a, int t_begin
 // the LDS tier: tiles t_begin + 4*NTW + j, j < n_lds
 template <class W, int KC>
 __device__ __forceinline__ void stage_w2_lds(const ChainArgs& a, int t_first, int n_lds, unsigned char* lds) {
-  for (int q = threadIdx.x; q < n_lds * KC * 64; q += blockDim.x) {
-    const int l = q & 63, c = (q >> 6) % KC, j = q / (KC * 64);
-    *reinterpret_cast<uint4*>(lds + (size_t)q * 16) =
-        *reinterpret_cast<const uint4*>(w2_frag_ptr<W>(a, t_first + j, l & 15, l >> 4, c));
-  }
+  static_assert(sizeof(W) == 2, "resident W2 is bf16");
+  copy8_batched<W, 13>(
+      n_lds * KC * 64,
+      [&](int q) {
+        const int l = q & 63, c = (q >> 6) % KC, j = q / (KC * 64);
+        return w2_frag_ptr<W>(a, t_first + j, l & 15, l >> 4, c);
+      },
+      [&](int q) { return reinterpret_cast<W*>(lds + (size_t)q * 16); });
   __syncthreads();
 }
 
@@ -1332,12 +1411,14 @@ constexpr uint32_t kEpochLimit = 1u << 25;
 // Before the steps: the H half of the bottleneck for every position,
 // zh[b][p][k] = sum_i H[b][p][i] W1[k][i] (one 16x16 tile per workgroup, k
 // split over the waves), and the zeroed keys and initial state.
+// Sixteen waves per tile, so that d <= 2560 takes one batch of loads per wave.
+constexpr int kPrologueWaves = 16;
 template <class W>
-__global__ __launch_bounds__(256) void chain_prologue(ChainArgs a, const void* H, int reset_status) {
-  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 4];
+__global__ __launch_bounds__(64 * kPrologueWaves) void chain_prologue(ChainArgs a, const void* H, int reset_status) {
+  __shared__ __attribute__((aligned(16))) float red[kPrologueWaves * 64 * 4];
   const int M = a.B * a.P;
-  splitk_tile<W>((const W*)H, a.d, (const W*)a.w1, a.d + a.Hs, (float*)a.zh, a.r, M, a.r, a.d, blockIdx.x, blockIdx.y,
-                 red);
+  splitk_tile_n<W, kPrologueWaves, sizeof(W) == 2 ? 5 : 3>((const W*)H, a.d, (const W*)a.w1, a.d + a.Hs, (float*)a.zh,
+                                                          a.r, M, a.r, a.d, blockIdx.x, blockIdx.y, red);
   const int nblk = gridDim.x * gridDim.y, blk = blockIdx.y * gridDim.x + blockIdx.x;
   const int tid = blk * blockDim.x + threadIdx.x, stride = nblk * blockDim.x;
   if (blk == 0) {
@@ -1861,9 +1942,9 @@ hipError_t launch_chain(int dtype, const ChainArgs& a, const void* H, int mode, 
   if (a.B <= 0) return hipSuccess;
   const dim3 pro((a.r + 15) / 16, (a.B * a.P + 15) / 16);
   if (dtype == kBF16)
-    hipLaunchKernelGGL(chain_prologue<uint16_t>, pro, dim3(256), 0, s, a, H, reset_status ? 1 : 0);
+    hipLaunchKernelGGL(chain_prologue<uint16_t>, pro, dim3(64 * kPrologueWaves), 0, s, a, H, reset_status ? 1 : 0);
   else
-    hipLaunchKernelGGL(chain_prologue<float>, pro, dim3(256), 0, s, a, H, reset_status ? 1 : 0);
+    hipLaunchKernelGGL(chain_prologue<float>, pro, dim3(64 * kPrologueWaves), 0, s, a, H, reset_status ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // row groups of 8 sequences in phase O

@@ -147,13 +147,15 @@ __device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, c, 0, 0, 0);
 }
 
-// ---- one 16x16 tile of C = A B^T with k split over the 4 waves -------------------
+// ---- one 16x16 tile of C = A B^T with k split over the waves ---------------------
 // For narrow products: each wave sums its share of the k chunks, the partials
-// meet in LDS (red: 4 * 64 * 4 floats) and wave 0 writes the tile.
-template <class W>
-__device__ void splitk_tile(const W* __restrict__ A, int lda, const W* __restrict__ B, int ldb, float* __restrict__ C,
-                            int ldc, int M, int N, int K, int n_tile, int m_tile, float* red) {
-  constexpr int U = sizeof(W) == 2 ? 8 : 4;
+// meet in LDS and wave 0 writes the tile.
+// One 16x16 output tile of C = A B^T with k split over the NWV waves of the
+// workgroup: wave w takes chunks of 32 from w * U on, U at a time, NWV * U
+// apart; the waves' partial tiles (red: NWV x 64 float4) are added in wave order.
+template <class W, int NWV, int U>
+__device__ void splitk_tile_n(const W* __restrict__ A, int lda, const W* __restrict__ B, int ldb, float* __restrict__ C,
+                              int ldc, int M, int N, int K, int n_tile, int m_tile, float* red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int n0 = n_tile * 16, m0 = m_tile * 16;
@@ -161,7 +163,7 @@ __device__ void splitk_tile(const W* __restrict__ A, int lda, const W* __restric
   const W* arow = A + (size_t)min(m0 + row, M - 1) * lda + kg * 8;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int nck = (K + 31) / 32;
-  for (int c0 = wv * U; c0 < nck; c0 += 4 * U) {
+  for (int c0 = wv * U; c0 < nck; c0 += NWV * U) {
     frag_t<W> af[U], bf[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -178,7 +180,7 @@ __device__ void splitk_tile(const W* __restrict__ A, int lda, const W* __restric
   if (wv == 0) {
     float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NWV; ++w) {
       const float4 q = *reinterpret_cast<const float4*>(&red[(w * 64 + lane) * 4]);
       v[0] += q.x;
       v[1] += q.y;
@@ -195,6 +197,13 @@ __device__ void splitk_tile(const W* __restrict__ A, int lda, const W* __restric
     }
   }
   __syncthreads();
+}
+
+// the same with four waves, 8 chunks per batch (bf16) or 4 (fp32)
+template <class W>
+__device__ void splitk_tile(const W* __restrict__ A, int lda, const W* __restrict__ B, int ldb, float* __restrict__ C,
+                            int ldc, int M, int N, int K, int n_tile, int m_tile, float* red) {
+  splitk_tile_n<W, 4, sizeof(W) == 2 ? 8 : 4>(A, lda, B, ldb, C, ldc, M, N, K, n_tile, m_tile, red);
 }
 
 // ---- greedy argmax as one 64-bit max ------------------------------------------
