@@ -103,7 +103,9 @@ __device__ __forceinline__ void store8(float* p, const f32x8& v) {
 
 // n pieces of 8 elements, piece q from src(q) to dst(q) (LDS), with NB pieces
 // per thread loaded before any of them is stored: a loop of single
-// load-then-store pairs waits one memory round trip per piece.
+// load-then-store pairs waits one memory round trip per piece.  Indices past
+// the end repeat piece n - 1 (the same bytes to the same place), so no store
+// sits in a branch the compiler could sink its load into.
 template <class W, int NB, class Src, class Dst>
 __device__ __forceinline__ void copy8_batched(int n, Src src, Dst dst) {
   if (n <= 0) return;
@@ -112,10 +114,7 @@ __device__ __forceinline__ void copy8_batched(int n, Src src, Dst dst) {
 #pragma unroll
     for (int u = 0; u < NB; ++u) v[u] = load8(src(min(q0 + u * (int)blockDim.x + (int)threadIdx.x, n - 1)));
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int q = q0 + u * (int)blockDim.x + (int)threadIdx.x;
-      if (q < n) store8(dst(q), v[u]);
-    }
+    for (int u = 0; u < NB; ++u) store8(dst(min(q0 + u * (int)blockDim.x + (int)threadIdx.x, n - 1)), v[u]);
   }
 }
 
@@ -1121,19 +1120,37 @@ __device__ __forceinline__ void stage_act_ll(const ChainArgs& a, int p, uint32_t
                  [r](int q) { return act_stage_index<W, KC>(q % r, q / r, r); });
 }
 // the same staging from the stepwise schedule's activation buffer (bf16: hi
-// [B][r] then lo [B][r]; fp32: [B][r])
+// [B][r] then lo [B][r]; fp32: [B][r]), four words per load and every
+// thread's loads in flight before its stores (a loop of single
+// load-then-store pairs waits one memory round trip per word); indices past
+// the end repeat the last piece, as in copy8_batched
 template <class W, int KC>
 __device__ __forceinline__ void stage_act_global(const ChainArgs& a, int p, uint32_t* act_s) {
-  const int B = a.B, r = a.r, n = B * r;
-  const uint32_t* slot = reinterpret_cast<const uint32_t*>((const char*)a.act + (size_t)p * a.act_step);
-  for (int q = threadIdx.x; q < n; q += blockDim.x) {
-    const int b = q / r, w = q - b * r;
+  constexpr int NB = 4;  // (the asm below names four)
+  const int B = a.B, r = a.r, n4 = B * r / 4;  // r is a multiple of 8
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* slot = reinterpret_cast<const u32x4*>((const char*)a.act + (size_t)p * a.act_step);
+  auto dst = [&](int q) {
+    const int wq = 4 * q;
     if constexpr (sizeof(W) == 2) {
-      act_s[act_stage_index<W, KC>(w, b, r)] =
-          w < r / 2 ? slot[(size_t)b * (r / 2) + w] : slot[(size_t)B * (r / 2) + (size_t)b * (r / 2) + w - r / 2];
+      const int half = B * (r / 2), lo = wq >= half, rem = wq - (lo ? half : 0);
+      const int b = rem / (r / 2), w = rem - b * (r / 2);
+      return act_s + act_stage_index<W, KC>(lo ? w + r / 2 : w, b, r);
     } else {
-      act_s[act_stage_index<W, KC>(w, b, r)] = slot[q];
+      const int b = wq / r;
+      return act_s + act_stage_index<W, KC>(wq - b * r, b, r);
     }
+  };
+  for (int q0 = 0; q0 < n4; q0 += NB * (int)blockDim.x) {
+    u32x4 v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) v[u] = slot[min(q0 + u * (int)blockDim.x + (int)threadIdx.x, n4 - 1)];
+    // all four loads issued before the first store (left alone, the scheduler
+    // pairs each load with its store, one round trip each)
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      *reinterpret_cast<u32x4*>(dst(min(q0 + u * (int)blockDim.x + (int)threadIdx.x, n4 - 1))) = v[u];
   }
   __syncthreads();
 }
