@@ -193,7 +193,10 @@ __device__ __forceinline__ uint32_t ll_tag(uint32_t ep, int p) { return ep * 128
 
 // The same right operand from a hand-off slot with n elements per row
 // (bf16 weights: words [0, n/2) hold hi pairs, [n/2, n) lo pairs; fp32: one
-// value per word).  Returns whether every word read carries `tag`.
+// value per word).  Returns whether every word read carries `tag`.  (Its
+// callers poll off the critical path or for many sequences; the words are
+// checked as they come, which needs fewer registers than loading them all
+// first.)
 template <class W>
 __device__ __forceinline__ bool ll_frag(const uint64_t* slot, int n, int b, int k, uint32_t tag, bool ok,
                                         typename act<W>::type& out) {
@@ -208,7 +211,7 @@ __device__ __forceinline__ bool ll_frag(const uint64_t* slot, int n, int b, int 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint64_t wh = ld_agent64(row + k / 2 + i), wl = ld_agent64(row + n / 2 + k / 2 + i);
-      good = good && ll_ok(wh, tag) && ll_ok(wl, tag);
+      good = good & ll_ok(wh, tag) & ll_ok(wl, tag);
       h[i] = ll_data(wh);
       l[i] = ll_data(wl);
     }
@@ -219,7 +222,7 @@ __device__ __forceinline__ bool ll_frag(const uint64_t* slot, int n, int b, int 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint64_t w = ld_agent64(row + k + i);
-      good = good && ll_ok(w, tag);
+      good = good & ll_ok(w, tag);
       v[i] = __uint_as_float(ll_data(w));
     }
     out.lo = make_float4(v[0], v[1], v[2], v[3]);
@@ -258,25 +261,31 @@ struct IdentityIndex {
 template <class Index = IdentityIndex>
 __device__ __forceinline__ void stage_words_ll(int32_t* status, const uint64_t* slot, int n, uint32_t tag,
                                                uint32_t* dst, Index index = Index()) {
-  for (int base = 0; base < n; base += kStageWordsPerThread * (int)blockDim.x) {
+  const int bd = blockDim.x, tid = threadIdx.x;
+  for (int base = 0; base < n; base += kStageWordsPerThread * bd) {
+    const int ni = min(kStageWordsPerThread, (n - base + bd - 1) / bd);  // the same in every thread
     uint32_t v[kStageWordsPerThread];
     ll_wait(status, [&] {
+      // every load before any tag check (a check between two loads, or a
+      // load under a lane-dependent branch, waits a round trip per word);
+      // lanes past the end re-read word n - 1
+      uint64_t w[kStageWordsPerThread];
+#pragma unroll
+      for (int i = 0; i < kStageWordsPerThread; ++i)
+        if (i < ni) w[i] = ld_agent64(slot + min(base + tid + i * bd, n - 1));
       bool good = true;
 #pragma unroll
-      for (int i = 0; i < kStageWordsPerThread; ++i) {
-        const int q = base + threadIdx.x + i * (int)blockDim.x;
-        if (q < n) {
-          const uint64_t w = ld_agent64(slot + q);
-          good = good && ll_ok(w, tag);
-          v[i] = ll_data(w);
+      for (int i = 0; i < kStageWordsPerThread; ++i)
+        if (i < ni) {
+          good = good & ll_ok(w[i], tag);
+          v[i] = ll_data(w[i]);
         }
-      }
       return good;
     });
 #pragma unroll
     for (int i = 0; i < kStageWordsPerThread; ++i) {
-      const int q = base + threadIdx.x + i * (int)blockDim.x;
-      if (q < n) dst[index(q)] = v[i];
+      const int q = base + tid + i * bd;
+      if (i < ni && q < n) dst[index(q)] = v[i];
     }
   }
   __syncthreads();
@@ -362,7 +371,7 @@ __device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int i
           const bool kok = c < nch && k + kg * 8 < Hs;
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
-            good = ll_frag<W>(slot, Hs, bb[cb], k + kg * 8, ll_tag(ep, p - 1), kok && bok[cb], S[q][cb]) && good;
+            good = ll_frag<W>(slot, Hs, bb[cb], k + kg * 8, ll_tag(ep, p - 1), kok && bok[cb], S[q][cb]) & good;
         }
         return good;
       });
@@ -705,7 +714,7 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
           const bool kok = c < nch && k + kg * 8 < Hs;
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
-            good = ll_frag<W>(slot, Hs, bb[cb], k + kg * 8, ll_tag(ep, p), kok && bok[cb], S[q][cb]) && good;
+            good = ll_frag<W>(slot, Hs, bb[cb], k + kg * 8, ll_tag(ep, p), kok && bok[cb], S[q][cb]) & good;
         }
         return good;
       });
@@ -1385,7 +1394,7 @@ __device__ __forceinline__ void ll_tokens_reduce(const ChainArgs& a, int p, uint
     key = 0;
     for (int w = tid; w < (int)gridDim.x; w += blockDim.x) {
       const uint64_t hi = ld_agent64(part + ((size_t)w * B + b) * 2), lo = ld_agent64(part + ((size_t)w * B + b) * 2 + 1);
-      good = good && ll_ok(hi, tag) && ll_ok(lo, tag);
+      good = good & ll_ok(hi, tag) & ll_ok(lo, tag);
       key = umax64(key, pair_key(hi, lo));
     }
     return good;
