@@ -1437,43 +1437,49 @@ constexpr uint32_t kEpochLimit = 1u << 25;
 // Before the steps: the H half of the bottleneck for every position,
 // zh[b][p][k] = sum_i H[b][p][i] W1[k][i] (one 16x16 tile per workgroup, k
 // split over the waves), and the zeroed keys and initial state.
-// Sixteen waves per tile, so that d <= 2560 takes one batch of loads per wave.
-constexpr int kPrologueWaves = 16;
 template <class W>
-__global__ __launch_bounds__(64 * kPrologueWaves) void chain_prologue(ChainArgs a, const void* H, int reset_status) {
-  __shared__ __attribute__((aligned(16))) float red[kPrologueWaves * 64 * 4];
+__global__ __launch_bounds__(256) void chain_prologue(ChainArgs a, const void* H, int reset_status) {
+  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 4];
   const int M = a.B * a.P;
-  splitk_tile_n<W, kPrologueWaves, sizeof(W) == 2 ? 5 : 3>((const W*)H, a.d, (const W*)a.w1, a.d + a.Hs, (float*)a.zh,
-                                                          a.r, M, a.r, a.d, blockIdx.x, blockIdx.y, red);
   const int nblk = gridDim.x * gridDim.y, blk = blockIdx.y * gridDim.x + blockIdx.x;
   const int tid = blk * blockDim.x + threadIdx.x, stride = nblk * blockDim.x;
   if (blk == 0) {
-    // First launch on this workspace, or on a different layout of it, or the
-    // launch counter about to overflow the tags: clear the hand-off words, so
-    // that no leftover bits can carry a current tag; between clears the launch
-    // counter alone keeps earlier launches' words from passing.
-    __shared__ int fresh;
-    if (threadIdx.x == 0) fresh = *a.marker != kLLMarker || *a.sig != a.sig_value || *a.epoch + 1 >= kEpochLimit;
-    __syncthreads();
+    // The launch's bookkeeping, every read in flight at once (a chain of
+    // dependent reads costs a memory round trip each).  First launch on this
+    // workspace, or on a different layout of it, or the launch counter about
+    // to overflow the tags: clear the hand-off words, so that no leftover bits
+    // can carry a current tag; between clears the launch counter alone keeps
+    // earlier launches' words from passing.  Out-of-range first tokens set
+    // status 1 unless a status is already set.
+    __shared__ int fresh, status_in;
+    __shared__ uint32_t epoch_in;
+    if (threadIdx.x == 0) {
+      const uint64_t mk = *a.marker, sg = *a.sig;
+      const uint32_t ep = *a.epoch;
+      const int32_t st = *a.status;
+      fresh = mk != kLLMarker || sg != a.sig_value || ep + 1 >= kEpochLimit;
+      epoch_in = ep;
+      status_in = reset_status ? 0 : st;
+    }
+    const int b = threadIdx.x;  // B <= kMaxChainGroup <= blockDim
+    const int bad = __syncthreads_or(b < a.B && (a.t0[b] < 0 || a.t0[b] >= a.V));
     if (fresh) {
       uint4* w = reinterpret_cast<uint4*>(a.ll_h);
       for (size_t i = threadIdx.x; i < a.ll_words / 2; i += blockDim.x) w[i] = make_uint4(0, 0, 0, 0);
       if (threadIdx.x == 0) {
-        *a.epoch = 0;
         *a.marker = kLLMarker;
         *a.sig = a.sig_value;
       }
     }
+    if (threadIdx.x == 0) {
+      *a.epoch = (fresh ? 0u : epoch_in) + 1u;  // tags of this launch's hand-off words
+      *a.status = status_in == 0 && bad ? 1 : status_in;
+    }
   }
+  splitk_tile<W>((const W*)H, a.d, (const W*)a.w1, a.d + a.Hs, (float*)a.zh, a.r, M, a.r, a.d, blockIdx.x, blockIdx.y,
+                 red);
   for (int i = tid; i < a.P * a.B; i += stride) a.keys[i] = 0;
   for (int i = tid; i < a.B * a.Hs; i += stride) a.h[i] = 0.f;  // state slot 0
-  if (tid == 0) {
-    *a.epoch += 1;  // tags of this launch's hand-off words
-    int32_t s = reset_status ? 0 : *a.status;
-    for (int b = 0; b < a.B; ++b)
-      if ((a.t0[b] < 0 || a.t0[b] >= a.V) && s == 0) s = 1;
-    *a.status = s;
-  }
 }
 
 __global__ void chain_finalize(ChainArgs a) {
@@ -1968,9 +1974,9 @@ hipError_t launch_chain(int dtype, const ChainArgs& a, const void* H, int mode, 
   if (a.B <= 0) return hipSuccess;
   const dim3 pro((a.r + 15) / 16, (a.B * a.P + 15) / 16);
   if (dtype == kBF16)
-    hipLaunchKernelGGL(chain_prologue<uint16_t>, pro, dim3(64 * kPrologueWaves), 0, s, a, H, reset_status ? 1 : 0);
+    hipLaunchKernelGGL(chain_prologue<uint16_t>, pro, dim3(256), 0, s, a, H, reset_status ? 1 : 0);
   else
-    hipLaunchKernelGGL(chain_prologue<float>, pro, dim3(64 * kPrologueWaves), 0, s, a, H, reset_status ? 1 : 0);
+    hipLaunchKernelGGL(chain_prologue<float>, pro, dim3(256), 0, s, a, H, reset_status ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // row groups of 8 sequences in phase O
