@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-cache-probe", action="store_true")
+    ap.add_argument("--no-input-table", action="store_true",
+                    help="chain calls compute W_ih x from the embedding instead of reading the per-token table")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 256 MiB once on the device (counter calibration under rocprofv3 --pmc)")
     ap.add_argument("--oracle-tiny-1t", action="store_true", help=argparse.SUPPRESS)
@@ -85,13 +87,15 @@ def copy_probe():
 
 
 # ---- algorithmic bytes and flops ---------------------------------------------------------
-def algorithmic_traffic(cfg, B, write_logits):
+def algorithmic_traffic(cfg, B, write_logits, table=False):
     """Bytes each launch must move and flops it must do, from the method's definition.
 
     base:  the LM-head GEMM, L^base = H W_lm^T (W_lm once, H, L^base out).
     chain: the P sequential steps; every step reads W2, the GRU weights, the
            state half of W1, one base-logit row and the fed-back embedding
-           rows, whatever the kernel keeps on chip between steps.
+           rows, whatever the kernel keeps on chip between steps.  With the
+           per-token input table (table=True) a step reads one table row
+           (3 Hs fp32) per sequence instead of W_ih and an embedding row.
     chain_compulsory: the same work with every weight counted once.
     """
     es = 2 if cfg.dtype == "bf16" else 4
@@ -99,12 +103,19 @@ def algorithmic_traffic(cfg, B, write_logits):
     M = B * P
     base_bytes = V * d * es + M * d * es + M * V * 4
     base_flops = 2.0 * M * V * d
-    weights = V * r * es + 3 * Hs * (d + Hs) * es + r * Hs * es   # W2, W_ih + W_hh, W1 state half
-    per_seq = V * 4 + d * es + (V * 4 if write_logits else 0)    # base row, embedding row, logits
+    logits = V * 4 if write_logits else 0
+    if table:
+        weights = V * r * es + 3 * Hs * Hs * es + r * Hs * es     # W2, W_hh, W1 state half
+        per_seq = V * 4 + 3 * Hs * 4 + logits                     # base row, table row, logits
+        gru_flops = 3 * Hs * Hs
+    else:
+        weights = V * r * es + 3 * Hs * (d + Hs) * es + r * Hs * es   # W2, W_ih + W_hh, W1 state half
+        per_seq = V * 4 + d * es + logits                            # base row, embedding row, logits
+        gru_flops = 3 * Hs * (d + Hs)
     step = weights + B * per_seq
     tail = M * r * 4 + M * 4                                      # H half of the bottleneck in, tokens out
     chain_bytes = P * step + tail
-    chain_flops = 2.0 * P * B * (3 * Hs * (d + Hs) + r * Hs + V * r)
+    chain_flops = 2.0 * P * B * (gru_flops + r * Hs + V * r)
     compulsory = weights + P * B * per_seq + tail
     return {"base": (base_bytes, base_flops), "chain": (chain_bytes, chain_flops), "chain_step_bytes": step,
             "chain_compulsory": compulsory}
@@ -166,12 +177,23 @@ def host_info():
 class Workload:
     """Device buffers of one workload and its step()."""
 
-    def __init__(self, cfg, weights, inputs, chain_mode, write_logits, temperature=0.0, seed=0):
+    def __init__(self, cfg, weights, inputs, chain_mode, write_logits, temperature=0.0, seed=0, table=True):
         import torch
 
         import draft_head_amd as dh
         self.dh, self.torch, self.cfg = dh, torch, cfg
         self.head = dh.DraftHead.from_config(cfg, weights, "cuda:0")
+        # the per-token GRU input table: built once per set of weights, before any timed step
+        self.table = None
+        if table and not cfg.tree:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            t = self.head.prepare_input_table()
+            e1.record()
+            torch.cuda.synchronize()
+            self.table = {"prepare_ms": e0.elapsed_time(e1), "bytes": t.numel() * 4,
+                          "note": "domino_prepare_input_table, once per set of weights; not part of a step"}
         self.H = self.head.upload(inputs["H"])
         self.t0 = self.head.upload(inputs["t0"])
         dev, B, P, V = self.head.device, cfg.batch, cfg.block, cfg.vocab
@@ -271,8 +293,8 @@ def time_launches(wl, K):
     return float(tb.mean()), float(tc.mean()), float(np.median(tb)), float(np.median(tc))
 
 
-def roofline_record(cfg, B, t_base, t_chain, write_logits, chain_mode):
-    tr = algorithmic_traffic(cfg, B, write_logits)
+def roofline_record(cfg, B, t_base, t_chain, write_logits, chain_mode, table=False):
+    tr = algorithmic_traffic(cfg, B, write_logits, table)
     if cfg.tree:
         byts, flops, comp = tree_traffic(cfg, B)
         tr["chain"], tr["chain_compulsory"] = (byts, flops), comp
@@ -535,7 +557,7 @@ def run_workload(cfg, args, steps, warmup, weights, parity_lbs=None, label=None,
     import numpy as np
     import synth
     inp = synth.make_inputs(cfg)
-    wl = Workload(cfg, weights, inp, args.chain_mode, args.logits, temperature, seed)
+    wl = Workload(cfg, weights, inp, args.chain_mode, args.logits, temperature, seed, table=not args.no_input_table)
     name = label or cfg.name
     log(f"{name}: timing {steps} steps")
     t = time_steps(wl, steps, warmup)
@@ -544,7 +566,7 @@ def run_workload(cfg, args, steps, warmup, weights, parity_lbs=None, label=None,
     g_scores = wl.scores.cpu().numpy() if cfg.tree else None
     Lb_gpu = wl.Lb.cpu().numpy() if (cfg.tree or temperature > 0) else None
     t_base, t_chain, tb_med, tc_med = time_launches(wl, steps)
-    roof, kernels = roofline_record(cfg, cfg.batch, t_base, t_chain, args.logits, args.chain_mode)
+    roof, kernels = roofline_record(cfg, cfg.batch, t_base, t_chain, args.logits, args.chain_mode, wl.table is not None)
     kernels["base"]["us_median"], kernels["chain"]["us_median"] = tb_med * 1e6, tc_med * 1e6
     sched, step_us = chain_schedule(wl)
     rec = {"value": cfg.batch / (t["ms_per_step"] * 1e-3), "unit": "draft blocks/s",
@@ -553,11 +575,14 @@ def run_workload(cfg, args, steps, warmup, weights, parity_lbs=None, label=None,
            "config": {"workload": name, "batch": cfg.batch, "block": cfg.block, "hidden": cfg.hidden,
                       "vocab": cfg.vocab, "gru_hidden": cfg.gru_hidden, "rank": cfg.rank,
                       "chain_mode": args.chain_mode, "write_logits": bool(args.logits), "schedule": sched,
+                      "input_table": wl.table is not None,
                       **({"temperature": temperature, "seed": seed} if temperature > 0 else {}),
                       **({"tree_nodes": cfg.nodes, "tree_topm": cfg.topm} if cfg.tree else {})},
            "roofline": roof, "kernels": kernels, "wall_s_timed": t["wall_s_timed"]}
     if step_us:
         rec["chain_step_us"] = [round(x, 2) for x in step_us]
+    if wl.table is not None:
+        rec["input_table"] = wl.table
     if cfg.name == "qwen3_4b_b32" and not args.no_cache_probe and temperature == 0:
         log(f"{cfg.name}: cache probe")
         rec["infinity_cache"] = cache_probe(wl)
@@ -624,7 +649,7 @@ def main():
            "config": {**head["config"], "parallelism": "none (one GPU)"},
            "step_ms": head["step_ms"], "roofline": head["roofline"], "kernels": head["kernels"],
            "wall_s_timed": head["wall_s_timed"]}
-    for k in ("chain_step_us", "parity", "verify_inputs"):
+    for k in ("chain_step_us", "parity", "verify_inputs", "input_table"):
         if k in head:
             out[k] = head[k]
     if not args.no_cpu_baseline:

@@ -25,7 +25,8 @@ STATUS_FINE, STATUS_BAD_FIRST_TOKEN, STATUS_TIMEOUT = 0, 1, 2
 
 # include/domino.h (the contract) and include/domino_bench.h (bench and test hooks)
 EXPORTS = ("domino_version", "domino_last_error", "domino_workspace_size", "domino_device_status",
-           "domino_release_cache", "domino_base_logits", "domino_draft_chain", "domino_draft_chain_sampled",
+           "domino_release_cache", "domino_base_logits", "domino_prepare_input_table", "domino_draft_chain",
+           "domino_draft_chain_sampled",
            "domino_draft_chain_noalloc",
            "domino_noalloc_device_status", "domino_tree_candidates", "domino_tree_draft",
            "domino_tree_verify_inputs")
@@ -44,7 +45,7 @@ class Dims(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("lm_head", "embed", "w_ih", "w_hh", "b_ih", "b_hh", "w1", "b1", "w2", "b2")]
+                ("lm_head", "embed", "w_ih", "w_hh", "b_ih", "b_hh", "w1", "b1", "w2", "b2", "input_table")]
 
 
 _lib = None
@@ -71,6 +72,8 @@ def lib():
         L.domino_release_cache.argtypes = []
         L.domino_base_logits.restype = ctypes.c_int
         L.domino_base_logits.argtypes = [P, P, P, i32, P, P]
+        L.domino_prepare_input_table.restype = ctypes.c_int
+        L.domino_prepare_input_table.argtypes = [P, P, P, P]
         L.domino_draft_chain.restype = ctypes.c_int
         L.domino_draft_chain.argtypes = [P, P, P, P, P, i32, P, P, P, sz, P]
         L.domino_draft_chain_sampled.restype = ctypes.c_int
@@ -164,6 +167,10 @@ def domino_chain_stamp_offset(dims: Dims, batch: int) -> int:
 def domino_base_logits(dims: Dims, weights: Weights, H, batch: int, base_logits, stream=None):
     _check(lib().domino_base_logits(ctypes.byref(dims), ctypes.byref(weights), _ptr(H), int(batch),
                                     _ptr(base_logits), _stream(stream)))
+
+
+def domino_prepare_input_table(dims: Dims, weights: Weights, table, stream=None):
+    _check(lib().domino_prepare_input_table(ctypes.byref(dims), ctypes.byref(weights), _ptr(table), _stream(stream)))
 
 
 def domino_draft_chain(dims: Dims, weights: Weights, H, base_logits, first_tokens, batch: int, out_tokens,
@@ -269,6 +276,22 @@ class DraftHead:
             out = torch.empty((B, self.dims.block, self.dims.vocab), dtype=torch.float32, device=self.device)
         domino_base_logits(self.dims, self.weights, H, B, out, stream)
         return out
+
+    def prepare_input_table(self, stream=None):
+        """Builds the per-token GRU input table (domino_prepare_input_table) into a new device
+        tensor [V][3 Hs] fp32 and passes it to the chain calls from now on; returns it."""
+        import torch
+        d = self.dims
+        table = torch.empty((d.vocab, 3 * d.gru_hidden), dtype=torch.float32, device=self.device)
+        domino_prepare_input_table(d, self.weights, table, stream)
+        self.tensors["input_table"] = table
+        self.weights = make_weights(self.tensors)
+        return table
+
+    def drop_input_table(self):
+        """The chain calls compute W_ih x from the embedding again."""
+        self.tensors.pop("input_table", None)
+        self.weights = make_weights(self.tensors)
 
     def workspace(self, batch, op=OP_CHAIN, nodes=0, topm=0):
         import torch

@@ -101,6 +101,7 @@ domino_status check_chain_args(const domino_dims* dims, const domino_weights* w,
   OPTIONAL_PTR(w->b_hh, "weights.b_hh");
   OPTIONAL_PTR(w->b1, "weights.b1");
   OPTIONAL_PTR(w->b2, "weights.b2");
+  OPTIONAL_PTR(w->input_table, "weights.input_table");
   REQUIRE_PTR(H, "H");
   REQUIRE_PTR(base_logits, "base_logits");
   REQUIRE_PTR(first_tokens, "first_tokens");
@@ -140,6 +141,7 @@ domino_status run_draft_chain(const domino_dims* dims, const domino_weights* w, 
     a.b_hh = w->b_hh;
     a.b1 = w->b1;
     a.b2 = w->b2;
+    a.xt = w->input_table;
     a.Lb = base_logits + (size_t)g0 * P * V;
     a.out_logits = out_logits ? out_logits + (size_t)g0 * P * V : nullptr;
     a.out_tokens = out_tokens + (size_t)g0 * P;
@@ -303,6 +305,23 @@ domino_status domino_base_logits(const domino_dims* dims, const domino_weights* 
                          dims->vocab, dims->hidden, true, (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "base-logit GEMM launch");
   if (ev1 && (e = hipEventRecord(ev1, (hipStream_t)stream)) != hipSuccess) return device_fail(e, "timing event");
+  return ok();
+}
+
+domino_status domino_prepare_input_table(const domino_dims* dims, const domino_weights* w, float* table,
+                                        void* stream) {
+  domino_status st = check_dims(dims);
+  if (st != DOMINO_OK) return st;
+  if (!w) return fail(DOMINO_ERR_INVALID_ARGUMENT, "weights is NULL");
+  REQUIRE_PTR(w->embed, "weights.embed");
+  REQUIRE_PTR(w->w_ih, "weights.w_ih");
+  REQUIRE_PTR(table, "table");
+  if ((int64_t)3 * dims->gru_hidden > INT32_MAX / 2) return fail(DOMINO_ERR_UNSUPPORTED, "gru_hidden too large");
+  // table[v][g] = sum_k embed[v][k] w_ih[g][k]: the vocabulary as the rows of the product
+  const hipError_t e = dh::launch_gemm_nt(dims->dtype, w->embed, dims->hidden, w->w_ih, dims->hidden, table,
+                                          3 * dims->gru_hidden, dims->vocab, 3 * dims->gru_hidden, dims->hidden, true,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "input-table GEMM launch");
   return ok();
 }
 

@@ -383,14 +383,33 @@ __device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int i
   }
 }
 
-template <class W, int NCB, bool kLL>
+// The input half W_ih E[prev] of this lane's unit (r, z, n gates) read from
+// the per-token table (kernels instantiated with kTab), for the lanes that
+// apply the gates (wave cb < NCB: sequence seq0 + 16 cb + row, unit
+// 4 item + kg); zeros elsewhere.  tok: the previous tokens by sequence, or
+// null to read them from the argmax keys / first tokens.
+template <int NCB>
+__device__ __forceinline__ float4 gru_table_in(const ChainArgs& a, int p, int item, const int32_t* tok, int seq0 = 0) {
+  const int lane = opaque_lane(), wv = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int b = seq0 + wv * 16 + row;
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (wv < NCB && b < a.B) {
+    const int t = tok ? clamp_token(a, tok[b]) : prev_token(a, p, b);
+    const float* q = a.xt + (size_t)t * 3 * a.Hs + item * 4 + kg;
+    x = make_float4(q[0], q[a.Hs], q[2 * a.Hs], 0.f);
+  }
+  return x;
+}
+
+template <class W, int NCB, bool kLL, bool kTab = false>
 __device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[4][NCB], float& h_own,
-                          uint32_t ep, int seq0 = 0);
+                          uint32_t ep, int seq0 = 0, float4 xin = float4{0.f, 0.f, 0.f, 0.f});
 
 // input half on top of the hidden-half partials, then the gates: h(p+1)
 // tok: this step's previous tokens by sequence (raw argmax indices), or
 // null to read them from the argmax keys / first tokens
-template <class W, int NCB, bool kLds, bool kLL = false>
+template <class W, int NCB, bool kLds, bool kLL = false, bool kTab = false>
 __device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, float* red, const W* lds, const f32x4 (&acc_h)[4][NCB],
                            const int32_t* tok = nullptr, float* h_own = nullptr, uint32_t ep = 0, int seq0 = 0) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
@@ -415,9 +434,11 @@ __device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, 
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[j][cb] = acc_h[j][cb];
 
-  // E[prev] is stored exactly in W: one MFMA per chunk (U a multiple of 4, as above)
+  // E[prev] is stored exactly in W: one MFMA per chunk (U a multiple of 4,
+  // as above).  With the per-token table the input half is read instead.
   constexpr int U = NCB == 1 ? 16 : 8;
-  const int ncx = (d + 31) / 32;
+  const int ncx = kTab ? 0 : (d + 31) / 32;
+  const float4 xin = kTab ? gru_table_in<NCB>(a, p, item, tok, seq0) : float4{0.f, 0.f, 0.f, 0.f};
   for (int c0 = wv; c0 < ncx; c0 += 4 * U) {  // this wave's chunks wv, wv + 4, ... in order
     frag_t<W> A[U], X[U][NCB];
 #pragma unroll
@@ -435,7 +456,7 @@ __device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, 
   }
 
   float h_dummy = 0.f;
-  gru_gates<W, NCB, kLL>(a, p, item, red, acc, h_own ? *h_own : h_dummy, ep, seq0);
+  gru_gates<W, NCB, kLL, kTab>(a, p, item, red, acc, h_own ? *h_own : h_dummy, ep, seq0, xin);
 }
 
 // Sum the four waves' pre-activation partials and apply the gates: h(p+1).
@@ -443,29 +464,29 @@ __device__ __forceinline__ void gru_finish(const ChainArgs& a, int p, int item, 
 // once here rather than by every reader.  kLL (persistent): the lane keeps
 // its own unit's fp32 state in h_own across steps, and the state goes out as
 // hand-off words only.
-template <class W, int NCB, bool kLL, int NWG = 4>
+template <class W, int NCB, bool kLL, int NWG = 4, bool kTab = false>
 __device__ __forceinline__ void gru_apply(const ChainArgs& a, int p, int item, float* red, float& h_own, uint32_t ep,
-                                          int seq0);
+                                          int seq0, float4 xin);
 
 // four waves: each folds its own chains (wv, 0..3), then the waves' sums are added in order
-template <class W, int NCB, bool kLL>
+template <class W, int NCB, bool kLL, bool kTab>
 __device__ __forceinline__ void gru_gates(const ChainArgs& a, int p, int item, float* red, const f32x4 (&acc)[4][NCB], float& h_own,
-                          uint32_t ep, int seq0) {
+                          uint32_t ep, int seq0, float4 xin) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const f32x4 s = ((acc[0][cb] + acc[1][cb]) + acc[2][cb]) + acc[3][cb];
     *reinterpret_cast<float4*>(&red[((wv * NCB + cb) * 64 + lane) * 4]) = make_float4(s[0], s[1], s[2], s[3]);
   }
-  gru_apply<W, NCB, kLL, 4>(a, p, item, red, h_own, ep, seq0);
+  gru_apply<W, NCB, kLL, 4, kTab>(a, p, item, red, h_own, ep, seq0, xin);
 }
 
 // red holds, per wave w of NWG and column block cb, the float4 of every lane:
 // NWG 4, wave w's sum of its chains; NWG 16, chain w alone.  Totals them in
 // the canonical order, applies the gates and hands out h(p+1).
-template <class W, int NCB, bool kLL, int NWG>
+template <class W, int NCB, bool kLL, int NWG, bool kTab>
 __device__ __forceinline__ void gru_apply(const ChainArgs& a, int p, int item, float* red, float& h_own, uint32_t ep,
-                                          int seq0) {
+                                          int seq0, float4 xin) {
   static_assert(NWG == 4 || NWG == 16, "four waves with four chains each, or one chain per wave");
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
@@ -491,6 +512,11 @@ __device__ __forceinline__ void gru_apply(const ChainArgs& a, int p, int item, f
       pre[1] += v.y;
       pre[2] += v.z;
       pre[3] += v.w;
+    }
+    if constexpr (kTab) {  // the input half from the per-token table, after the hidden half's chains
+      pre[0] += xin.x;
+      pre[1] += xin.y;
+      pre[2] += xin.z;
     }
     // result rows 4*kg + i are gate i of unit j0 + kg; column = sequence
     const int b = seq0 + cb * 16 + row, j = j0 + kg;
@@ -557,7 +583,7 @@ __device__ __forceinline__ void gru_x_prefetch(const ChainArgs& a, int item, fra
   }
 }
 
-template <class W, int NCB>
+template <class W, int NCB, bool kTab = false>
 __device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int item, float* red, const frag_t<W> (&xw)[kXPre],
                                                const f32x4 (&acc_h)[4][NCB], const int32_t* tok, float& h_own,
                                                uint32_t ep) {
@@ -581,6 +607,10 @@ __device__ __forceinline__ void gru_finish_pre(const ChainArgs& a, int p, int it
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[j][cb] = acc_h[j][cb];
+  if constexpr (kTab) {  // the input half from the per-token table (xw was not fetched)
+    gru_gates<W, NCB, true, true>(a, p, item, red, acc, h_own, ep, 0, gru_table_in<NCB>(a, p, item, tok));
+    return;
+  }
   const int ncx = (d + 31) / 32;
   {
     frag_t<W> X[kXPre][NCB];
@@ -1493,13 +1523,13 @@ __global__ void chain_finalize(ChainArgs a) {
 // Three-launch schedule, phase G: work item = 4 units, all sequences.
 // (Splitting the sequences over workgroups, 16 per workgroup, measured
 // slower at 32 sequences: 16.4 against 14.9 us per step.)
-template <class W, int NCB>
+template <class W, int NCB, bool kTab>
 __global__ __launch_bounds__(256) void chain_gru_k(ChainArgs a, int p) {
   __shared__ __attribute__((aligned(16))) float red[4 * NCB * 64 * 4];
   for (int it = blockIdx.x; it < a.Hs / 4; it += gridDim.x) {
     f32x4 acc_h[4][NCB];
     gru_hidden_part<W, NCB, false>(a, p, it, nullptr, acc_h);
-    gru_finish<W, NCB, false>(a, p, it, red, nullptr, acc_h);
+    gru_finish<W, NCB, false, false, kTab>(a, p, it, red, nullptr, acc_h);
   }
 }
 
@@ -1511,7 +1541,7 @@ __global__ __launch_bounds__(256) void chain_gru_k(ChainArgs a, int p) {
 // sequences, 17.3 against 14.1 us: the time goes to the sequences' state and
 // embedding fragments, which every workgroup reads.)
 constexpr int kGru16UH = 2;  // hidden-half chunks per wave per batch (Hs <= 1024 in one batch)
-template <class W, int NCB>
+template <class W, int NCB, bool kTab>
 __global__ __launch_bounds__(1024) void chain_gru16_k(ChainArgs a, int p) {
   static_assert(sizeof(W) == 2, "bf16 weights (fp32 fragments need twice the registers)");
   // input-half chunks per wave per batch: d <= 2560 in one batch for 16 sequences, two batches for 32
@@ -1575,8 +1605,10 @@ __global__ __launch_bounds__(1024) void chain_gru16_k(ChainArgs a, int p) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(AX[q], XX[q][cb], acc[cb]);
   };
+  // kTab: the input half from the per-token table
+  const float4 xin = kTab ? gru_table_in<NCB>(a, p, item, nullptr) : float4{0.f, 0.f, 0.f, 0.f};
   if (hid) load_h(v);
-  load_x(v);
+  if (!kTab) load_x(v);
   if (hid) {
     mma_h();
     for (int c0 = v + 16 * kGru16UH; c0 < nch; c0 += 16 * kGru16UH) {
@@ -1584,16 +1616,18 @@ __global__ __launch_bounds__(1024) void chain_gru16_k(ChainArgs a, int p) {
       mma_h();
     }
   }
-  mma_x();
-  for (int c0 = v + 16 * kGru16UX; c0 < ncx; c0 += 16 * kGru16UX) {
-    load_x(c0);
+  if (!kTab) {
     mma_x();
+    for (int c0 = v + 16 * kGru16UX; c0 < ncx; c0 += 16 * kGru16UX) {
+      load_x(c0);
+      mma_x();
+    }
   }
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
     *reinterpret_cast<float4*>(&red[((v * NCB + cb) * 64 + lane) * 4]) = make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
   float h_dummy = 0.f;
-  gru_apply<W, NCB, false, 16>(a, p, item, red, h_dummy, 0u, 0);
+  gru_apply<W, NCB, false, 16, kTab>(a, p, item, red, h_dummy, 0u, 0, xin);
 }
 
 template <class W, int NCB>
@@ -1639,7 +1673,7 @@ __global__ __launch_bounds__(64 * NWV) void chain_logits_wide_k(ChainArgs a, int
 // W1 in LDS.  NTW > 0 (W2 resident on chip): the GRU weights come from
 // memory, W_ih fetched ahead of the token; kLds 2 puts the W1 slice in LDS;
 // the LDS tier of W2 follows it.
-template <class W, int RG, int KC, int kLds, int NTW>
+template <class W, int RG, int KC, int kLds, int NTW, bool kTab>
 __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
   constexpr int NCB = RG <= 2 ? 1 : 2;  // 16-sequence column blocks of phases G and W
   constexpr bool kGruLds = kLds >= 1 && NTW == 0;
@@ -1697,11 +1731,11 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
         }
         if (wg < nW) pre = bottleneck_pre<NCB>(a, p, wg);
         frag_t<W> xw[kXPre];
-        gru_x_prefetch<W>(a, wg, xw);
+        if constexpr (!kTab) gru_x_prefetch<W>(a, wg, xw);
         DH_STAMP(p, 0);
         if (wg == 0 && p > 0)
           for (int b = threadIdx.x; b < a.B; b += blockDim.x) a.out_tokens[(size_t)b * a.P + p - 1] = tok_s[b];
-        gru_finish_pre<W, NCB>(a, p, wg, red, xw, acc_h, tk, h_own, ep);
+        gru_finish_pre<W, NCB, kTab>(a, p, wg, red, xw, acc_h, tk, h_own, ep);
       } else {
         if (p > 0) {
           ll_tokens_read(a, p - 1, ep, tok_s);
@@ -1711,7 +1745,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
         DH_STAMP(p, 0);
         if (wg == 0 && p > 0)
           for (int b = threadIdx.x; b < a.B; b += blockDim.x) a.out_tokens[(size_t)b * a.P + p - 1] = tok_s[b];
-        gru_finish<W, NCB, kGruLds, true>(a, p, wg, red, gl, acc_h, tk, &h_own, ep);
+        gru_finish<W, NCB, kGruLds, true, kTab>(a, p, wg, red, gl, acc_h, tk, &h_own, ep);
       }
     }
     DH_STAMP(p, 1);
@@ -1850,10 +1884,10 @@ void release_chain_cache() {
   if (have_cur) (void)hipSetDevice(cur);
 }
 
-template <class W, int RG, int KC, int kLds, int NTW>
-static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStream_t s) {
+template <class W, int RG, int KC, int kLds, int NTW, bool kTab>
+static hipError_t launch_persistent_(const ChainArgs& a, size_t lds_bytes, hipStream_t s) {
   static thread_local CoopGrid cache;
-  const void* fn = (const void*)chain_persistent<W, RG, KC, kLds, NTW>;
+  const void* fn = (const void*)chain_persistent<W, RG, KC, kLds, NTW, kTab>;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -1886,10 +1920,16 @@ static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStr
     e = hipEventCreateWithFlags(&g.last, hipEventDisableTiming);
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chain_persistent<W, RG, KC, kLds, NTW>), dim3(cache.blocks), dim3(256), lds_bytes, s, a);
+  hipLaunchKernelGGL((chain_persistent<W, RG, KC, kLds, NTW, kTab>), dim3(cache.blocks), dim3(256), lds_bytes, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return hipEventRecord(g.last, s);
+}
+// with or without the per-token input table
+template <class W, int RG, int KC, int kLds, int NTW>
+static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStream_t s) {
+  return a.xt ? launch_persistent_<W, RG, KC, kLds, NTW, true>(a, lds_bytes, s)
+              : launch_persistent_<W, RG, KC, kLds, NTW, false>(a, lds_bytes, s);
 }
 
 #ifndef DH_GRU16
@@ -1933,14 +1973,23 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
   const int nO = T < cus ? T : (cus > 0 ? cus : 256);
   // phase G, bf16 weights: sixteen waves per work item
   const bool gru16 = DH_GRU16 && sizeof(W) == 2;
+  const bool tab = a.xt != nullptr;
   for (int p = 0; p < a.P; ++p) {
     if constexpr (sizeof(W) == 2) {
-      if (gru16)
-        hipLaunchKernelGGL((chain_gru16_k<W, NCB>), dim3(nG), dim3(1024), 0, s, a, p);
-      else
-        hipLaunchKernelGGL((chain_gru_k<W, NCB>), dim3(nG), dim3(256), 0, s, a, p);
+      if (gru16) {
+        if (tab)
+          hipLaunchKernelGGL((chain_gru16_k<W, NCB, true>), dim3(nG), dim3(1024), 0, s, a, p);
+        else
+          hipLaunchKernelGGL((chain_gru16_k<W, NCB, false>), dim3(nG), dim3(1024), 0, s, a, p);
+      } else if (tab) {
+        hipLaunchKernelGGL((chain_gru_k<W, NCB, true>), dim3(nG), dim3(256), 0, s, a, p);
+      } else {
+        hipLaunchKernelGGL((chain_gru_k<W, NCB, false>), dim3(nG), dim3(256), 0, s, a, p);
+      }
+    } else if (tab) {
+      hipLaunchKernelGGL((chain_gru_k<W, NCB, true>), dim3(nG), dim3(256), 0, s, a, p);
     } else {
-      hipLaunchKernelGGL((chain_gru_k<W, NCB>), dim3(nG), dim3(256), 0, s, a, p);
+      hipLaunchKernelGGL((chain_gru_k<W, NCB, false>), dim3(nG), dim3(256), 0, s, a, p);
     }
     // one workgroup per 16 rows and 16 sequences: more CUs share the state reads
     hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 15) / 16), dim3(256), 0, s, a, p);

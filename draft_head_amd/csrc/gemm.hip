@@ -647,7 +647,7 @@ static hipError_t launch_wide(const uint16_t* A, int lda, const uint16_t* B, int
 hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int ldb, float* C, int ldc, int M, int N,
                           int K, bool prefer_tiles, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (N <= 4096) {  // few columns: split k inside each workgroup
+  if (N <= 4096 && M <= 4096) {  // few columns and rows: split k inside each workgroup
     dim3 grid((N + 15) / 16, (M + 15) / 16);
     if (dtype == kF32)
       hipLaunchKernelGGL(gemm_splitk<float>, grid, dim3(256), 0, s, (const float*)A, lda, (const float*)B, ldb, C, ldc,

@@ -41,6 +41,7 @@ struct ChainArgs {
   const float* b_hh;
   const float* b1;
   const float* b2;
+  const float* xt;         // [V][3 Hs] W_ih E[v] per token (input half of the GRU), or null: computed from embed and w_ih
   const float* Lb;         // [B][P][V]
   float* out_logits;       // [B][P][V] or null
   int32_t* out_tokens;     // [B][P]

@@ -109,6 +109,8 @@ typedef struct {
   const float *b1;     /* [r] or NULL                                       */
   const void *w2;      /* [V][r]                                            */
   const float *b2;     /* [V] or NULL                                       */
+  const float *input_table; /* [V][3Hs] fp32 from domino_prepare_input_table,
+                        * or NULL; used by the chain calls only          */
 } domino_weights;
 
 /* Library version string (static storage). */
@@ -155,9 +157,28 @@ domino_status domino_base_logits(const domino_dims *dims, const domino_weights *
                                  int32_t batch, float *base_logits, void *stream);
 
 /*
+ * The GRU's input half for every token, once per set of weights (the GRU
+ * reads the embedding of the previous drafted token: 163.com explainer,
+ * section 4, causal encoder; Dutch Domino summary, "Methodologie", part 2):
+ *   table[v][g] = sum_k embed[v][k] * w_ih[g][k]   for v < vocab, g < 3 gru_hidden
+ * with fp32 accumulation, stored fp32 (row v holds the r, z and n blocks of
+ * W_ih embed[v]).  table is caller-owned device memory of
+ * vocab * 3 * gru_hidden floats (1.87 GB at V = 151936, gru_hidden = 1024).
+ * Passed as weights.input_table to the chain calls, it replaces their
+ * W_ih x product: each step then reads one table row per sequence instead of
+ * an embedding row and all of w_ih.  embed and w_ih are read here only; the
+ * table must be rebuilt when either changes.  Uses weights.embed and
+ * weights.w_ih; the other weight pointers are not read.  Runs on the MFMA
+ * matrix cores (about 2.4 TFLOP at the Qwen3-4B shapes).
+ */
+domino_status domino_prepare_input_table(const domino_dims *dims, const domino_weights *weights, float *table,
+                                        void *stream);
+
+/*
  * The sequential correction chain over one draft block for `batch`
  * independent sequences.  For position p = 0..P-1 and each sequence:
  *   h    = GRU(embed[prev], h)       prev = first_tokens[b] at p = 0, else the token drafted at p-1
+ *          (with weights.input_table: its row prev as W_ih embed[prev])
  *   a    = SiLU(W1 [H[b][p] ; h] + b1)
  *   L    = base_logits[b][p] + W2 a + b2
  *   out_tokens[b][p] = argmax_v L   (lowest index among equal maxima; -0 == +0)

@@ -231,3 +231,27 @@ def test_verify_inputs_rejected_before_launch():
     bad = list(a)
     bad[4] = 0
     assert L.domino_tree_verify_inputs(*bad) == dh.OK  # an empty batch launches nothing
+
+
+def test_input_table_arguments_rejected():
+    L = dh.lib()
+    d = _dims()
+    # the table call: every bad argument is caught before a launch
+    assert L.domino_prepare_input_table(ctypes.byref(d), ctypes.byref(_weights()), None, None) == \
+        dh.ERR_INVALID_ARGUMENT
+    assert "table is NULL" in dh.last_error()
+    assert L.domino_prepare_input_table(ctypes.byref(d), ctypes.byref(_weights()), FAKE + 4, None) == \
+        dh.ERR_INVALID_ARGUMENT
+    assert "aligned" in dh.last_error()
+    for wname in ("embed", "w_ih"):
+        assert L.domino_prepare_input_table(ctypes.byref(d), ctypes.byref(_weights(**{wname: None})), FAKE,
+                                            None) == dh.ERR_INVALID_ARGUMENT
+        assert wname in dh.last_error()
+    assert L.domino_prepare_input_table(ctypes.byref(_dims(hidden=12)), ctypes.byref(_weights()), FAKE, None) == \
+        dh.ERR_INVALID_ARGUMENT
+    # a misaligned table passed to the chain is rejected too
+    ws = dh.domino_workspace_size(d, 4, dh.OP_CHAIN)
+    st = L.domino_draft_chain(ctypes.byref(d), ctypes.byref(_weights(input_table=FAKE + 8)), FAKE, FAKE, FAKE, 4,
+                              FAKE, None, FAKE, ws, None)
+    assert st == dh.ERR_INVALID_ARGUMENT
+    assert "input_table" in dh.last_error()
