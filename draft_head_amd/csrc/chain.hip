@@ -687,13 +687,26 @@ __device__ __forceinline__ BottleneckPre bottleneck_pre(const ChainArgs& a, int 
   return q;
 }
 
+// The bottleneck's pre-activations are sums over k chunks of 32 in the same
+// sixteen chains as the GRU's: chain v takes the chunks c with c % 16 == v in
+// increasing order, and the total is ((zh + b1) + F0) + F1 + F2 + F3 (left to
+// right) with Fw = ((chain w + chain w+4) + chain w+8) + chain w+12.  With
+// NWV = 4 waves, wave w keeps chains w, w+4, w+8, w+12 and folds them itself;
+// with 8 (16), wave w keeps chains w and w+8 (chain w) and the fold reads
+// every chain from LDS (red: 16 NCB float4 per lane); the sums are the same
+// bits.
 // kLL: state in and activations out as hand-off words of the persistent launch
 // `ep`; with h_s (LDS, B * Hs words) the whole workgroup polls the state
-// words once and the waves read their fragments from there.
-template <class W, int NCB, bool kLdsW, bool kLL = false>
+// words once and the waves read their fragments from there.  kOutLL (stepwise
+// schedule with phase W inside the phase-O launch): the state from the
+// stepwise buffer, the activations out as hand-off words of launch `ep`.
+template <class W, int NCB, bool kLdsW, bool kLL = false, int NWV = 4, bool kOutLL = kLL>
 __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int item, float* red, const W* w1_lds,
                                 const BottleneckPre& pre_terms, uint32_t ep = 0, uint32_t* h_s = nullptr,
                                 int seq0 = 0) {
+  static_assert(NWV == 4 || NWV == 8 || NWV == 16, "four, eight or sixteen waves");
+  static_assert(!kLL || kOutLL, "hand-off words in, hand-off words out");
+  constexpr int NC = 16 / NWV;  // chains per wave: wv, wv + NWV, ...
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int Hs = a.Hs, B = a.B, r = a.r;
@@ -711,19 +724,22 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
     bok[cb] = b < B;
     bb[cb] = bok[cb] ? b : 0;
   }
-  f32x4 acc[NCB];
+  f32x4 acc[NC][NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = NCB == 1 ? 8 : 4;
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[j][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // chunks per batch, a multiple of NC: chunk c0 + NWV q is in this wave's chain q % NC
+  constexpr int U = NWV == 16 ? 2 : (NWV == 8 ? 4 : (NCB == 1 ? 8 : 4));
   const int nch = (Hs + 31) / 32;
   if (kLL && h_s) stage_words_ll(a.status, a.ll_h + (size_t)(p + 1) * B * Hs, B * Hs, ll_tag(ep, p), h_s);
   DH_STAMP(p, 10);
-  for (int c0 = wv; c0 < nch; c0 += 4 * U) {  // this wave's chunks wv, wv + 4, ... in order
+  for (int c0 = wv; c0 < nch; c0 += NWV * U) {  // this wave's chunks wv, wv + NWV, ... in order
     frag_t<W> A[U];
     typename act<W>::type S[U][NCB];
 #pragma unroll
     for (int q = 0; q < U; ++q) {
-      const int c = c0 + 4 * q, k = c * 32;
+      const int c = c0 + NWV * q, k = c * 32;
       const bool kok = c < nch && k + kg * 8 < Hs;
       A[q] = load8_or_zero(rw + k, kok);
       if (kLL && h_s) {
@@ -740,7 +756,7 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
         bool good = true;
 #pragma unroll
         for (int q = 0; q < U; ++q) {
-          const int c = c0 + 4 * q, k = c * 32;
+          const int c = c0 + NWV * q, k = c * 32;
           const bool kok = c < nch && k + kg * 8 < Hs;
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
@@ -753,13 +769,20 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
 #pragma unroll
     for (int q = 0; q < U; ++q)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma(A[q], S[q][cb], acc[cb]);
+      for (int cb = 0; cb < NCB; ++cb) acc[q % NC][cb] = mma(A[q], S[q][cb], acc[q % NC][cb]);
   }
   DH_STAMP(p, 9);
+  auto red4 = [&](int e, int cb) -> float4& { return *reinterpret_cast<float4*>(&red[((e * NCB + cb) * 64 + lane) * 4]); };
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-    *reinterpret_cast<float4*>(&red[((wv * NCB + cb) * 64 + lane) * 4]) =
-        make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
+  for (int cb = 0; cb < NCB; ++cb) {
+    if constexpr (NWV == 4) {  // this wave's fold F_wv
+      const f32x4 f = ((acc[0][cb] + acc[1][cb]) + acc[2][cb]) + acc[3][cb];
+      red4(wv, cb) = make_float4(f[0], f[1], f[2], f[3]);
+    } else {  // chains wv, wv + NWV, ...
+#pragma unroll
+      for (int j = 0; j < NC; ++j) red4(wv + NWV * j, cb) = make_float4(acc[j][cb][0], acc[j][cb][1], acc[j][cb][2], acc[j][cb][3]);
+    }
+  }
   __syncthreads();
   if (wv < NCB) {
     const int cb = wv;
@@ -767,7 +790,14 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
                     pre_terms.zh.z + pre_terms.b1.z, pre_terms.zh.w + pre_terms.b1.w};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float4 v = *reinterpret_cast<const float4*>(&red[((w * NCB + cb) * 64 + lane) * 4]);
+      float4 v = red4(w, cb);
+      if constexpr (NWV != 4) {
+#pragma unroll
+        for (int j = 1; j < 4; ++j) {
+          const float4 u = red4(w + 4 * j, cb);
+          v = make_float4(v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w);
+        }
+      }
       pre[0] += v.x;
       pre[1] += v.y;
       pre[2] += v.z;
@@ -779,7 +809,7 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = pre[i] / (1.f + expf(-pre[i]));
       char* slot = (char*)a.act + (size_t)p * a.act_step;
-      if constexpr (kLL) {
+      if constexpr (kOutLL) {
         ll_put4<W>(a.ll_act + (size_t)p * B * r, r, b, k, s, ll_tag(ep, p));
       } else if constexpr (sizeof(W) == 2) {
         uint16_t hi[4], lo[4];
@@ -1344,9 +1374,11 @@ __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_b
 // clamped addresses so the waits stay exact), and re-reads the staged
 // activations from LDS per tile, so it needs few registers and the other
 // waves hide what latency is left.
-template <class W, int RG, int KC, int NWV, bool kWrite, bool kSample = false>
+// (kLL: the activations come as hand-off words of launch ep, else from the
+// stepwise activation buffer)
+template <class W, int RG, int KC, int NWV, bool kWrite, bool kSample = false, bool kLL = false>
 __device__ __forceinline__ void logits_wide_(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest,
-                                             uint32_t* act_s) {
+                                             uint32_t* act_s, uint32_t ep = 0) {
   const int lane = opaque_lane(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15, kg = lane >> 4;
   const int t0 = t_begin + wv, n = t_end > t0 ? (t_end - t0 + NWV - 1) / NWV : 0;
@@ -1359,7 +1391,10 @@ __device__ __forceinline__ void logits_wide_(const ChainArgs& a, int p, int t_be
   };
   TileBuf<W, RG, KC> s0, s1;
   issue(0, s0);
-  stage_act_global<W, KC>(a, p, act_s);
+  if constexpr (kLL)
+    stage_act_ll<W, KC>(a, p, ep, act_s);
+  else
+    stage_act_global<W, KC>(a, p, act_s);
   LaneMax lm[RG][2];
 #pragma unroll
   for (int g = 0; g < RG; ++g) lm[g][0] = lm[g][1] = LaneMax{0.f, -1};
@@ -1665,6 +1700,37 @@ __global__ __launch_bounds__(64 * NWV) void chain_logits_wide_k(ChainArgs a, int
     logits_wide_<W, RG, KC, NWV, true, kSample>(a, p, t_begin, t_end, sbest, act_s);
   else
     logits_wide_<W, RG, KC, NWV, false, kSample>(a, p, t_begin, t_end, sbest, act_s);
+}
+
+// Stepwise schedule with phases W and O in one launch (bf16 weights): the
+// first nW * ceil(B / 16) workgroups first compute one bottleneck item each
+// (16 units of 16 sequences, NWV waves) and hand the activations out as
+// tagged words of this call (tag: the call's epoch and p); then every
+// workgroup stages those words and runs its vocabulary tiles, the item
+// workgroups a smaller share of them.  The item workgroups have the lowest
+// indices, so they are dispatched first and wait for no one: the launch
+// needs no co-residency.  Waits are bounded (device status 2).
+template <class W, int RG, int KC, int NWV, bool kSample>
+__global__ __launch_bounds__(64 * NWV) void chain_wo_k(ChainArgs a, int p) {
+  static_assert(sizeof(W) == 2, "bf16 weights");
+  __shared__ uint64_t sbest[NWV * kMaxChainGroup];
+  __shared__ __attribute__((aligned(16))) uint32_t act_s[kMaxChainGroup * (256 + 8)];  // r <= 256
+  __shared__ __attribute__((aligned(16))) float red[16 * 64 * 4];                      // bottleneck chains
+  const uint32_t ep = *a.epoch;  // advanced by the prologue launch of this call
+  const int nW = (a.r + 15) / 16, nI = nW * ((a.B + 15) / 16);
+  const int T = (a.V + 15) / 16, G = gridDim.x, w = blockIdx.x;
+  if (w < nI) {
+    const int item = w % nW, seq0 = (w / nW) * 16;
+    bottleneck_item<W, 1, false, false, NWV, true>(a, p, item, red, nullptr, bottleneck_pre<1>(a, p, item, seq0), ep,
+                                                   nullptr, seq0);
+  }
+  int t_begin, t_end;
+  o_tile_range(w, G, min(nI, G), T, t_begin, t_end);
+  act_clear_pads<W, KC>(act_s, a.B, a.r);  // made visible by the staging's barrier
+  if (a.out_logits)
+    logits_wide_<W, RG, KC, NWV, true, kSample, true>(a, p, t_begin, t_end, sbest, act_s, ep);
+  else
+    logits_wide_<W, RG, KC, NWV, false, kSample, true>(a, p, t_begin, t_end, sbest, act_s, ep);
 }
 
 // All P steps in one launch (every workgroup resident); each owns one GRU work
@@ -1991,15 +2057,26 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
     } else {
       hipLaunchKernelGGL((chain_gru_k<W, NCB, false>), dim3(nG), dim3(256), 0, s, a, p);
     }
-    // one workgroup per 16 rows and 16 sequences: more CUs share the state reads
-    hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 15) / 16), dim3(256), 0, s, a, p);
     constexpr int NWV = RG * KC >= 16 ? 8 : 16;  // waves per CU, as registers allow
-    if constexpr (sizeof(W) == 2) {  // bf16: many light waves per CU
+    if constexpr (sizeof(W) == 2 && RG <= 2) {
+      // bf16, up to 16 sequences: phase W inside the phase-O launch (measured
+      // 453 -> 386 us per block at one sequence; at 32 sequences the 32 item
+      // workgroups take as long as the separate launch, which stays)
+      const int nI = nW * ((a.B + 15) / 16), nWO = nO > nI ? nO : nI;
+      if (sample)
+        hipLaunchKernelGGL((chain_wo_k<W, RG, KC, NWV, true>), dim3(nWO), dim3(64 * NWV), 0, s, a, p);
+      else
+        hipLaunchKernelGGL((chain_wo_k<W, RG, KC, NWV, false>), dim3(nWO), dim3(64 * NWV), 0, s, a, p);
+    } else if constexpr (sizeof(W) == 2) {  // bf16: many light waves per CU
+      // one workgroup per 16 rows and 16 sequences: more CUs share the state reads
+      hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 15) / 16), dim3(256), 0, s, a, p);
       if (sample)
         hipLaunchKernelGGL((chain_logits_wide_k<W, RG, KC, NWV, true>), dim3(nO), dim3(64 * NWV), 0, s, a, p);
       else
         hipLaunchKernelGGL((chain_logits_wide_k<W, RG, KC, NWV, false>), dim3(nO), dim3(64 * NWV), 0, s, a, p);
     } else {
+      // one workgroup per 16 rows and 16 sequences: more CUs share the state reads
+      hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 15) / 16), dim3(256), 0, s, a, p);
       if (sample)
         hipLaunchKernelGGL((chain_logits_k<W, RG, KC, true>), dim3(nO), dim3(256), 0, s, a, p);
       else
