@@ -1226,7 +1226,7 @@ __device__ __forceinline__ void stage_act_global(const ChainArgs& a, int p, uint
 
 // phase O with resident W2 (persistent schedule): the base logits of every
 // owned tile are fetched before the activations exist
-template <class W, int RG, int KC, int NTW, bool kWrite>
+template <class W, int RG, int KC, int NTW, bool kWrite, bool kSample>
 __device__ __forceinline__ void logits_resident_(const ChainArgs& a, int p, int t_begin, int t_end,
                                                  const frag_t<W> (&w2r)[NTW][KC], const unsigned char* w2_lds,
                                                  uint32_t* act_s, uint64_t* sbest, uint32_t ep) {
@@ -1267,21 +1267,21 @@ __device__ __forceinline__ void logits_resident_(const ChainArgs& a, int p, int 
         for (int g = 0; g < RG; ++g) acc[g][c & 1] = mma(af[g][c], w, acc[g][c & 1]);
       }
     }
-    rows_epilogue<kWrite, RG>(a, p, tile_of(i) * 16 + row, kg, lb[i], b2[i], acc, lm);
+    rows_epilogue<kWrite, RG, kSample>(a, p, tile_of(i) * 16 + row, kg, lb[i], b2[i], acc, lm);
   }
   DH_STAMP(p, 6);
   publish_rows<RG, true>(a, p, lm, sbest, ep);
   DH_STAMP(p, 7);
 }
 
-template <class W, int RG, int KC, int NTW>
+template <class W, int RG, int KC, int NTW, bool kSample>
 __device__ __forceinline__ void logits_resident(const ChainArgs& a, int p, int t_begin, int t_end,
                                                 const frag_t<W> (&w2r)[NTW][KC], const unsigned char* w2_lds,
                                                 uint32_t* act_s, uint64_t* sbest, uint32_t ep) {
   if (a.out_logits)
-    logits_resident_<W, RG, KC, NTW, true>(a, p, t_begin, t_end, w2r, w2_lds, act_s, sbest, ep);
+    logits_resident_<W, RG, KC, NTW, true, kSample>(a, p, t_begin, t_end, w2r, w2_lds, act_s, sbest, ep);
   else
-    logits_resident_<W, RG, KC, NTW, false>(a, p, t_begin, t_end, w2r, w2_lds, act_s, sbest, ep);
+    logits_resident_<W, RG, KC, NTW, false, kSample>(a, p, t_begin, t_end, w2r, w2_lds, act_s, sbest, ep);
 }
 
 template <class W, int RG, int KC>
@@ -1739,8 +1739,9 @@ __global__ __launch_bounds__(64 * NWV) void chain_wo_k(ChainArgs a, int p) {
 // W1 in LDS.  NTW > 0 (W2 resident on chip): the GRU weights come from
 // memory, W_ih fetched ahead of the token; kLds 2 puts the W1 slice in LDS;
 // the LDS tier of W2 follows it.
-template <class W, int RG, int KC, int kLds, int NTW, bool kTab>
+template <class W, int RG, int KC, int kLds, int NTW, bool kTab, bool kSample>
 __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
+  static_assert(!kSample || NTW > 0, "sampling with W2 on chip only");
   constexpr int NCB = RG <= 2 ? 1 : 2;  // 16-sequence column blocks of phases G and W
   constexpr bool kGruLds = kLds >= 1 && NTW == 0;
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
@@ -1830,7 +1831,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
 #endif
     // O: this workgroup's vocabulary tiles, then its argmax pairs
     if constexpr (NTW > 0)
-      logits_resident<W, RG, KC, NTW>(a, p, t_begin, t_end, w2r, w2l, act_s, sbest, ep);
+      logits_resident<W, RG, KC, NTW, kSample>(a, p, t_begin, t_end, w2r, w2l, act_s, sbest, ep);
     else
       logits_range<W, RG, KC, true>(a, p, t_begin, t_end, sbest, [] { return true; }, ep, act_s);
     DH_STAMP(p, 5);
@@ -1950,10 +1951,10 @@ void release_chain_cache() {
   if (have_cur) (void)hipSetDevice(cur);
 }
 
-template <class W, int RG, int KC, int kLds, int NTW, bool kTab>
+template <class W, int RG, int KC, int kLds, int NTW, bool kTab, bool kSample>
 static hipError_t launch_persistent_(const ChainArgs& a, size_t lds_bytes, hipStream_t s) {
   static thread_local CoopGrid cache;
-  const void* fn = (const void*)chain_persistent<W, RG, KC, kLds, NTW, kTab>;
+  const void* fn = (const void*)chain_persistent<W, RG, KC, kLds, NTW, kTab, kSample>;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -1986,16 +1987,17 @@ static hipError_t launch_persistent_(const ChainArgs& a, size_t lds_bytes, hipSt
     e = hipEventCreateWithFlags(&g.last, hipEventDisableTiming);
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chain_persistent<W, RG, KC, kLds, NTW, kTab>), dim3(cache.blocks), dim3(256), lds_bytes, s, a);
+  hipLaunchKernelGGL((chain_persistent<W, RG, KC, kLds, NTW, kTab, kSample>), dim3(cache.blocks), dim3(256), lds_bytes, s,
+                     a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return hipEventRecord(g.last, s);
 }
-// with or without the per-token input table
-template <class W, int RG, int KC, int kLds, int NTW>
+// with or without the per-token input table; sampled tokens (W2 on chip only)
+template <class W, int RG, int KC, int kLds, int NTW, bool kSample = false>
 static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStream_t s) {
-  return a.xt ? launch_persistent_<W, RG, KC, kLds, NTW, true>(a, lds_bytes, s)
-              : launch_persistent_<W, RG, KC, kLds, NTW, false>(a, lds_bytes, s);
+  return a.xt ? launch_persistent_<W, RG, KC, kLds, NTW, true, kSample>(a, lds_bytes, s)
+              : launch_persistent_<W, RG, KC, kLds, NTW, false, kSample>(a, lds_bytes, s);
 }
 
 #ifndef DH_GRU16
@@ -2012,13 +2014,12 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
   // hand-offs between its phases are what bounds a step; with more
   // sequences the three launches per step, each with all the waves a CU
   // holds for its phase, are faster.
-  // fp32 weights (small models) always run the three launches per step
-  // sampling (temperature > 0) runs the three launches per step as well
+  // fp32 weights (small models) always run the three launches per step;
+  // sampling (temperature > 0) runs in one launch only with W2 on chip
   const bool sample = a.temperature > 0.f;
-  persistent = !sample && sizeof(W) == 2 && (mode >= 2 || (mode == 0 && RG == 1)) && cus > 0 && a.Hs / 4 <= cus;
+  persistent = sizeof(W) == 2 && (mode >= 2 || (mode == 0 && RG == 1)) && cus > 0 && a.Hs / 4 <= cus;
   if constexpr (sizeof(W) == 2) {
     if (persistent) {
-      const size_t g = gru_slice_elems(a.d, a.Hs) * sizeof(W);
       const size_t w = (size_t)16 * (a.Hs + 8) * sizeof(W);
       // W2 stays on chip (registers + LDS) when every workgroup's share fits;
       // the grid is then one workgroup per CU
@@ -2026,9 +2027,16 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
         constexpr int NTW = resident_tiles<KC>();
         if (mode == 0 || mode == 3) {
           const size_t l2 = resident_lds(cus, a, NTW, KC, w);
-          if (l2 > 0 && l2 <= kLdsBudget) return launch_persistent<W, RG, KC, 2, NTW>(a, l2, s);
+          if (l2 > 0 && l2 <= kLdsBudget)
+            return sample ? launch_persistent<W, RG, KC, 2, NTW, true>(a, l2, s)
+                          : launch_persistent<W, RG, KC, 2, NTW, false>(a, l2, s);
         }
       }
+    }
+    if (persistent && sample) persistent = false;  // three launches per step
+    if (persistent) {
+      const size_t g = gru_slice_elems(a.d, a.Hs) * sizeof(W);
+      const size_t w = (size_t)16 * (a.Hs + 8) * sizeof(W);
       const size_t act = act_stage_bytes(a.B, KC, sizeof(W));
       if (act + g + w <= kLdsBudget) return launch_persistent<W, RG, KC, 2, 0>(a, act + g + w, s);
       if (act + g <= kLdsBudget) return launch_persistent<W, RG, KC, 1, 0>(a, act + g, s);

@@ -212,8 +212,10 @@ domino_status domino_draft_chain(const domino_dims *dims, const domino_weights *
  * x = word (b & 1) of Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011)
  * at counter (v, p, b >> 1, 0) under the key (seed & 0xffffffff, seed >> 32);
  * b is the sequence's index in this call.  out_logits, if not NULL, are the
- * unperturbed L.  T = 0 is the greedy chain.  The draws run the three-launch
- * schedule.  temperature must be finite and >= 0.
+ * unperturbed L.  T = 0 is the greedy chain.  The draws run in the chain's
+ * one-launch schedule where W2 stays on chip (bf16, up to 8 sequences), else
+ * in three launches per step; both draw the same tokens.  temperature must be
+ * finite and >= 0.
  */
 domino_status domino_draft_chain_sampled(const domino_dims *dims, const domino_weights *weights, const void *H,
                                          const float *base_logits, const int32_t *first_tokens, int32_t batch,

@@ -123,3 +123,31 @@ def test_sampled_chain_full_size(key, sample):
                                       want_logits=False)
         firm = f_m > MARGIN_FIRM
         assert not (firm & (f_t != g[b:b + 1])).any(), (key, b)
+
+
+@pytest.mark.parametrize("B,table", [(1, False), (5, True), (8, False)])
+def test_sampled_chain_schedules_agree_bitwise(B, table):
+    """Up to 8 sequences the draws run in the one-launch schedule with W2 on chip;
+    the three-launch schedule must draw the same tokens and logits."""
+    cfg = small_config(d=96, V=1501, Hs=48, r=64, P=12, B=B, dtype="bf16", biases=True)
+    say(f"case sampled chain schedules agree B={B} table={table}")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    if table:
+        head.prepare_input_table()
+    H, t0 = head.upload(inp["H"]), head.upload(inp["t0"])
+    Lb = head.base_logits(H)
+    out = []
+    prev = dh.set_chain_mode(0)
+    try:
+        for mode in (0, 1):
+            dh.set_chain_mode(mode)
+            out.append(head.draft_chain_sampled(H, Lb, t0, 1.0, seed=77 + B))
+    finally:
+        dh.set_chain_mode(prev)
+    (t_a, L_a, _), (t_b, L_b, _) = out
+    assert torch.equal(t_a, t_b) and torch.equal(L_a, L_b)
+    m = oracle.Model.from_config(cfg, w)
+    compare_sampled(m, inp["H"], Lb.cpu().numpy(), inp["t0"], 1.0, 77 + B, t_a.cpu().numpy(), L_a.cpu().numpy(),
+                    "one launch")
