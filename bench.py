@@ -121,18 +121,22 @@ def algorithmic_traffic(cfg, B, write_logits, table=False):
             "chain_compulsory": compulsory}
 
 
-def tree_traffic(cfg, B):
+def tree_traffic(cfg, B, table=False):
     """Bytes and flops of one tree call: the top-M pass over every base-logit row, then
     N rounds that each read the GRU weights, the state half of W1 and, per sequence,
-    M rows of W2, M base-logit entries, one embedding row and two fp64 states."""
+    M rows of W2, M base-logit entries, one embedding row and two fp64 states.  With the
+    fp64 input table a round reads W_hh and one table row (3 Hs fp64) per sequence
+    instead of W_ih and an embedding row."""
     es = 2 if cfg.dtype == "bf16" else 4
     d, V, Hs, r, P, N, M = cfg.hidden, cfg.vocab, cfg.gru_hidden, cfg.rank, cfg.block, cfg.nodes, cfg.topm
     topm_bytes = B * P * V * 4
-    rnd = 3 * Hs * (d + Hs) * es + r * Hs * es + B * (M * r * es + M * 4 + d * es + 2 * Hs * 8)
+    gru_w = 3 * Hs * (Hs if table else d + Hs) * es
+    x_row = 3 * Hs * 8 if table else d * es
+    rnd = gru_w + r * Hs * es + B * (M * r * es + M * 4 + x_row + 2 * Hs * 8)
     byts = topm_bytes + B * P * d * es + r * d * es + N * rnd
-    flops = 2.0 * B * N * (3 * Hs * (d + Hs) + r * Hs + M * r) + 2.0 * B * P * r * d
-    compulsory = topm_bytes + B * P * d * es + r * d * es + 3 * Hs * (d + Hs) * es + r * Hs * es + \
-        N * B * (M * r * es + M * 4 + d * es + 2 * Hs * 8)
+    flops = 2.0 * B * N * (3 * Hs * (Hs if table else d + Hs) + r * Hs + M * r) + 2.0 * B * P * r * d
+    compulsory = topm_bytes + B * P * d * es + r * d * es + gru_w + r * Hs * es + \
+        N * B * (M * r * es + M * 4 + x_row + 2 * Hs * 8)
     return byts, flops, compulsory
 
 
@@ -185,15 +189,16 @@ class Workload:
         self.head = dh.DraftHead.from_config(cfg, weights, "cuda:0")
         # the per-token GRU input table: built once per set of weights, before any timed step
         self.table = None
-        if table and not cfg.tree:
+        if table:  # fp32 for the chain, fp64 for the tree
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record()
-            t = self.head.prepare_input_table()
+            t = self.head.prepare_input_table_f64() if cfg.tree else self.head.prepare_input_table()
             e1.record()
             torch.cuda.synchronize()
-            self.table = {"prepare_ms": e0.elapsed_time(e1), "bytes": t.numel() * 4,
-                          "note": "domino_prepare_input_table, once per set of weights; not part of a step"}
+            call = "domino_prepare_input_table_f64" if cfg.tree else "domino_prepare_input_table"
+            self.table = {"prepare_ms": e0.elapsed_time(e1), "bytes": t.numel() * t.element_size(),
+                          "note": f"{call}, once per set of weights; not part of a step"}
         self.H = self.head.upload(inputs["H"])
         self.t0 = self.head.upload(inputs["t0"])
         dev, B, P, V = self.head.device, cfg.batch, cfg.block, cfg.vocab
@@ -296,7 +301,7 @@ def time_launches(wl, K):
 def roofline_record(cfg, B, t_base, t_chain, write_logits, chain_mode, table=False):
     tr = algorithmic_traffic(cfg, B, write_logits, table)
     if cfg.tree:
-        byts, flops, comp = tree_traffic(cfg, B)
+        byts, flops, comp = tree_traffic(cfg, B, table)
         tr["chain"], tr["chain_compulsory"] = (byts, flops), comp
     peak_mfma = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     kernel_key = {"base": "base_gemm", "chain": "chain_steps"}

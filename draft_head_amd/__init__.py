@@ -25,7 +25,8 @@ STATUS_FINE, STATUS_BAD_FIRST_TOKEN, STATUS_TIMEOUT = 0, 1, 2
 
 # include/domino.h (the contract) and include/domino_bench.h (bench and test hooks)
 EXPORTS = ("domino_version", "domino_last_error", "domino_workspace_size", "domino_device_status",
-           "domino_release_cache", "domino_base_logits", "domino_prepare_input_table", "domino_draft_chain",
+           "domino_release_cache", "domino_base_logits", "domino_prepare_input_table",
+           "domino_prepare_input_table_f64", "domino_draft_chain",
            "domino_draft_chain_sampled",
            "domino_draft_chain_noalloc",
            "domino_noalloc_device_status", "domino_tree_candidates", "domino_tree_draft",
@@ -45,7 +46,8 @@ class Dims(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("lm_head", "embed", "w_ih", "w_hh", "b_ih", "b_hh", "w1", "b1", "w2", "b2", "input_table")]
+                ("lm_head", "embed", "w_ih", "w_hh", "b_ih", "b_hh", "w1", "b1", "w2", "b2", "input_table",
+                 "input_table_f64")]
 
 
 _lib = None
@@ -74,6 +76,8 @@ def lib():
         L.domino_base_logits.argtypes = [P, P, P, i32, P, P]
         L.domino_prepare_input_table.restype = ctypes.c_int
         L.domino_prepare_input_table.argtypes = [P, P, P, P]
+        L.domino_prepare_input_table_f64.restype = ctypes.c_int
+        L.domino_prepare_input_table_f64.argtypes = [P, P, P, P]
         L.domino_draft_chain.restype = ctypes.c_int
         L.domino_draft_chain.argtypes = [P, P, P, P, P, i32, P, P, P, sz, P]
         L.domino_draft_chain_sampled.restype = ctypes.c_int
@@ -171,6 +175,11 @@ def domino_base_logits(dims: Dims, weights: Weights, H, batch: int, base_logits,
 
 def domino_prepare_input_table(dims: Dims, weights: Weights, table, stream=None):
     _check(lib().domino_prepare_input_table(ctypes.byref(dims), ctypes.byref(weights), _ptr(table), _stream(stream)))
+
+
+def domino_prepare_input_table_f64(dims: Dims, weights: Weights, table, stream=None):
+    _check(lib().domino_prepare_input_table_f64(ctypes.byref(dims), ctypes.byref(weights), _ptr(table),
+                                                _stream(stream)))
 
 
 def domino_draft_chain(dims: Dims, weights: Weights, H, base_logits, first_tokens, batch: int, out_tokens,
@@ -288,9 +297,21 @@ class DraftHead:
         self.weights = make_weights(self.tensors)
         return table
 
+    def prepare_input_table_f64(self, stream=None):
+        """The fp64 table for the tree (domino_prepare_input_table_f64), passed to
+        domino_tree_draft from now on; returns it."""
+        import torch
+        d = self.dims
+        table = torch.empty((d.vocab, 3 * d.gru_hidden), dtype=torch.float64, device=self.device)
+        domino_prepare_input_table_f64(d, self.weights, table, stream)
+        self.tensors["input_table_f64"] = table
+        self.weights = make_weights(self.tensors)
+        return table
+
     def drop_input_table(self):
-        """The chain calls compute W_ih x from the embedding again."""
+        """The chain and tree calls compute W_ih x from the embedding again."""
         self.tensors.pop("input_table", None)
+        self.tensors.pop("input_table_f64", None)
         self.weights = make_weights(self.tensors)
 
     def workspace(self, batch, op=OP_CHAIN, nodes=0, topm=0):

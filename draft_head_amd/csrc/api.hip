@@ -325,6 +325,20 @@ domino_status domino_prepare_input_table(const domino_dims* dims, const domino_w
   return ok();
 }
 
+domino_status domino_prepare_input_table_f64(const domino_dims* dims, const domino_weights* w, double* table,
+                                            void* stream) {
+  domino_status st = check_dims(dims);
+  if (st != DOMINO_OK) return st;
+  if (!w) return fail(DOMINO_ERR_INVALID_ARGUMENT, "weights is NULL");
+  REQUIRE_PTR(w->embed, "weights.embed");
+  REQUIRE_PTR(w->w_ih, "weights.w_ih");
+  REQUIRE_PTR(table, "table");
+  const hipError_t e = dh::launch_input_table_f64(dims->dtype, w->embed, w->w_ih, dims->vocab, dims->gru_hidden,
+                                                  dims->hidden, table, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "fp64 input-table launch");
+  return ok();
+}
+
 domino_status domino_draft_chain(const domino_dims* dims, const domino_weights* w, const void* H,
                                  const float* base_logits, const int32_t* first_tokens, int32_t batch,
                                  int32_t* out_tokens, float* out_logits, void* workspace, size_t workspace_bytes,
@@ -433,6 +447,7 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   OPTIONAL_PTR(w->b_hh, "weights.b_hh");
   OPTIONAL_PTR(w->b1, "weights.b1");
   OPTIONAL_PTR(w->b2, "weights.b2");
+  OPTIONAL_PTR(w->input_table_f64, "weights.input_table_f64");
   REQUIRE_PTR(H, "H");
   REQUIRE_PTR(base_logits, "base_logits");
   REQUIRE_PTR(first_tokens, "first_tokens");
@@ -468,6 +483,7 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   t.b_hh = w->b_hh;
   t.b1 = w->b1;
   t.b2 = w->b2;
+  t.xt = w->input_table_f64;
   t.Lb = base_logits;
   t.t0 = first_tokens;
   t.out_parents = out_parents;

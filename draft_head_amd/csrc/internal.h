@@ -100,6 +100,7 @@ struct TreeArgs {
   const float* b_hh;
   const float* b1;
   const float* b2;
+  const double* xt;         // [V][3 Hs] W_ih E[v] per token in fp64 (input half of the GRU), or null
   const float* Lb;          // [B][P][V]
   const int32_t* t0;        // [B]
   int32_t* out_parents;     // [B][N]
@@ -127,6 +128,9 @@ struct TreeLayout {
 TreeLayout tree_layout(int d, int Hs, int r, int P, int group, int N, int M);
 
 hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
+// table[v][g] = sum_k E[v][k] Wih[g][k] in fp64 for v < V, g < 3 Hs
+hipError_t launch_input_table_f64(int dtype, const void* E, const void* Wih, int V, int Hs, int d, double* table,
+                                  hipStream_t s);
 // dynamic LDS of the tree's GRU kernel (must stay within the CU's 160 KB)
 size_t tree_gru_lds(int d, int Hs, int dtype);
 size_t tree_gru_lds_total(int d, int Hs, int dtype);  // the GRU step's whole LDS (160 KB per CU)

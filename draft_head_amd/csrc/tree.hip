@@ -460,9 +460,10 @@ __global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0) {
   for (int s = 0; s < kSeqPerWave; ++s)
 #pragma unroll
     for (int g = 0; g < 6; ++g) acc[s][g] = 0.0;
-  // input half, R 8-wide runs of every gate row in flight at a time
+  // input half, R 8-wide runs of every gate row in flight at a time (read
+  // from the per-token table instead when there is one)
   constexpr int R = 1;
-  for (int k0 = lane * 8; k0 < d; k0 += 512 * R) {
+  for (int k0 = lane * 8; k0 < (t.xt ? 0 : d); k0 += 512 * R) {
     double w[R][3][8];
 #pragma unroll
     for (int u = 0; u < R; ++u)
@@ -522,6 +523,12 @@ __global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0) {
   const int sq = s0 + lane;  // the sequence this lane finishes
   if (lane < kSeqPerWave && sq < nb && mine) {
     const TreeCur c = sc[sq];
+    if (t.xt) {
+      const double* q = t.xt + (size_t)min(max(c.token, 0), t.V - 1) * 3 * Hs + j;
+      a6[0] = q[0];
+      a6[1] = q[Hs];
+      a6[2] = q[2 * Hs];
+    }
     auto bi = [&](int row) { return t.b_ih ? (double)t.b_ih[row] : 0.0; };
     auto bh = [&](int row) { return t.b_hh ? (double)t.b_hh[row] : 0.0; };
     const double r = 1.0 / (1.0 + exp(-(a6[0] + bi(j) + a6[3] + bh(j))));
@@ -530,6 +537,82 @@ __global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0) {
     const double hprev = hl[(size_t)sq * Hs + j];
     t.states[((size_t)(b0 + sq) * (t.N + 1) + c.slot) * Hs + j] = (1.0 - z) * nn + z * hprev;
   }
+}
+
+// ---- per-token input half in fp64: table[v][g] = sum_k embed[v][k] w_ih[g][k] ----------------
+// Workgroup = a 64 x 64 block of the table (64 tokens, 64 gate rows), four
+// waves in 2 x 2, each four 16 x 16 fp64 MFMA tiles (rows: tokens, columns:
+// gate rows).  k runs in 32-wide blocks; in a block lane l holds 8 consecutive
+// k values, 8 (l / 16) + 0..7, of its token row and of its gate row, and MFMA
+// i takes value i of every lane (the products are exact in fp64).  Loads go
+// straight from memory into registers; rows past the end repeat the last
+// row and are not stored, k past d contributes zeros.
+template <class W>
+__global__ __launch_bounds__(256) void input_table_f64_k(const W* __restrict__ E, const W* __restrict__ Wih, int V,
+                                                         int G3, int d, double* __restrict__ table) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int rr = lane & 15, kq = lane >> 4;
+  const int t0 = blockIdx.x * 64 + (wv >> 1) * 32, g0 = blockIdx.y * 64 + (wv & 1) * 32;
+  const W* er[2];
+  const W* wr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    er[i] = E + (size_t)min(t0 + 16 * i + rr, V - 1) * d;
+    wr[i] = Wih + (size_t)min(g0 + 16 * i + rr, G3 - 1) * d;
+  }
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int k0 = 0; k0 < d; k0 += 32) {
+    const int k = k0 + 8 * kq;
+    const bool ok = k < d;  // d is a multiple of 8: a lane's run is all in or all out
+    const int kc = ok ? k : 0;
+    Run8<W> ra[2], rb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      ra[i].load(er[i] + kc);
+      rb[i].load(wr[i] + kc);
+    }
+    double a8[2][8], b8[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      ra[i].get(a8[i]);
+      rb[i].get(b8[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a8[i][e] = ok ? a8[i][e] : 0.0;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a8[i][e], b8[j][e], acc[i][j], 0, 0, 0);
+  }
+  // register q of lane l holds row 4 q + l / 16 (token) of column l % 16 (gate row)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + 16 * i + 4 * q + kq, g = g0 + 16 * j + rr;
+        if (t < V && g < G3) table[(size_t)t * G3 + g] = acc[i][j][q];
+      }
+}
+
+hipError_t launch_input_table_f64(int dtype, const void* E, const void* Wih, int V, int Hs, int d, double* table,
+                                  hipStream_t s) {
+  const int G3 = 3 * Hs;
+  const dim3 grid((V + 63) / 64, (G3 + 63) / 64);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(input_table_f64_k<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)E, (const uint16_t*)Wih, V,
+                       G3, d, table);
+  else
+    hipLaunchKernelGGL(input_table_f64_k<float>, grid, dim3(256), 0, s, (const float*)E, (const float*)Wih, V, G3, d,
+                       table);
+  return hipGetLastError();
 }
 
 // ---- the same GRU step on the fp64 matrix cores (bf16 weights) ----------------------------
@@ -554,6 +637,8 @@ constexpr int kGruWaves = 8;  // waves of tree_gru_mfma, splitting the k blocks
 constexpr int kGruPreI = 10;  // input-half blocks per wave whose loads are all issued up front
 constexpr int kGruPreH = 4;   // hidden-half blocks per wave whose loads are all issued up front
 
+// kTab: the input half comes from the per-token fp64 table (t.xt) instead.
+template <bool kTab>
 __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int b0) {
   __shared__ double red[kGruWaves][2][12][kTreeSeqs];  // [wave][input, hidden][gate row][sequence]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -568,9 +653,11 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int 
   const TreeCur* curs = reinterpret_cast<const TreeCur*>(t.cur) + b0;
   // the weights do not depend on the tree: their loads go out first
   uint4 wpi[kGruPreI], wph[kGruPreH];
+  if constexpr (!kTab) {
 #pragma unroll
-  for (int q = 0; q < kGruPreI; ++q)
-    wpi[q] = *reinterpret_cast<const uint4*>(wi + min((wv + kGruWaves * q) * 32 + 8 * kq, d - 8));
+    for (int q = 0; q < kGruPreI; ++q)
+      wpi[q] = *reinterpret_cast<const uint4*>(wi + min((wv + kGruWaves * q) * 32 + 8 * kq, d - 8));
+  }
 #pragma unroll
   for (int q = 0; q < kGruPreH; ++q)
     wph[q] = *reinterpret_cast<const uint4*>(wh + min((wv + kGruWaves * q) * 32 + 8 * kq, Hs - 8));
@@ -586,9 +673,20 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int 
   const int f_slot = __shfl(c.slot, fs), f_ps = __shfl(c.parent_slot, fs);
   const int f_exp = __shfl(c.expand, fs);
   uint4 xp[kGruPreI];
+  double gx[3] = {0.0, 0.0, 0.0};  // kTab: the finishing lane's input half from the table
+  if constexpr (kTab) {
+    const int f_tok = __shfl(c.token, fs);
+    if (threadIdx.x < 4 * kTreeSeqs) {
+      const double* q = t.xt + (size_t)min(max(f_tok, 0), t.V - 1) * 3 * Hs + min(j0 + fu, Hs - 1);
+      gx[0] = q[0];
+      gx[1] = q[Hs];
+      gx[2] = q[2 * Hs];
+    }
+  } else {
 #pragma unroll
-  for (int q = 0; q < kGruPreI; ++q)
-    xp[q] = *reinterpret_cast<const uint4*>(xr + min((wv + kGruWaves * q) * 32 + 8 * kq, d - 8));
+    for (int q = 0; q < kGruPreI; ++q)
+      xp[q] = *reinterpret_cast<const uint4*>(xr + min((wv + kGruWaves * q) * 32 + 8 * kq, d - 8));
+  }
   F64x8 hp[kGruPreH];
 #pragma unroll
   for (int q = 0; q < kGruPreH; ++q) hp[q] = load_f64x8(hr + min((wv + kGruWaves * q) * 32 + 8 * kq, Hs - 8));
@@ -602,7 +700,7 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int 
   f64x4 acc_i[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
   f64x4 acc_h[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
 #pragma unroll
-  for (int q = 0; q < kGruPreI; ++q) {
+  for (int q = 0; q < (kTab ? 0 : kGruPreI); ++q) {
     const bool ok = (wv + kGruWaves * q) * 32 + 8 * kq < d;
     double w8[8], x8[8];
     bf16x8_to_f64(wpi[q], w8);
@@ -622,7 +720,7 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int 
   }
   // blocks past those (wider hidden sizes), four in flight at a time
   constexpr int NB = 4;
-  const int nbi = (d + 31) / 32, nbh = (Hs + 31) / 32;
+  const int nbi = kTab ? 0 : (d + 31) / 32, nbh = (Hs + 31) / 32;
   for (int bk = wv + kGruWaves * kGruPreI; bk < nbi; bk += kGruWaves * NB) {
     uint4 wr[NB], xv[NB];
 #pragma unroll
@@ -683,6 +781,7 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int 
           gi[q] += red[w][0][4 * q + fu][fs];
           gh[q] += red[w][1][4 * q + fu][fs];
         }
+        if constexpr (kTab) gi[q] = gx[q];
       }
       auto bi = [&](int row) { return t.b_ih ? (double)t.b_ih[row] : 0.0; };
       auto bh = [&](int row) { return t.b_hh ? (double)t.b_hh[row] : 0.0; };
@@ -1070,8 +1169,10 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
   }
   for (int k = 0; k < t.N; ++k) {
     for (int b0 = 0; b0 < t.B; b0 += kTreeSeqs) {
-      if (mfma)
-        hipLaunchKernelGGL(tree_gru_mfma, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), 0, s, t, b0);
+      if (mfma && t.xt)
+        hipLaunchKernelGGL(tree_gru_mfma<true>, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), 0, s, t, b0);
+      else if (mfma)
+        hipLaunchKernelGGL(tree_gru_mfma<false>, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), 0, s, t, b0);
       else
         hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(64 * 4 * (kTreeSeqs / kSeqPerWave)), lds, s, t, b0);
     }

@@ -111,6 +111,9 @@ typedef struct {
   const float *b2;     /* [V] or NULL                                       */
   const float *input_table; /* [V][3Hs] fp32 from domino_prepare_input_table,
                         * or NULL; used by the chain calls only          */
+  const double *input_table_f64; /* [V][3Hs] fp64 from
+                        * domino_prepare_input_table_f64, or NULL; used by
+                        * domino_tree_draft only                         */
 } domino_weights;
 
 /* Library version string (static storage). */
@@ -173,6 +176,19 @@ domino_status domino_base_logits(const domino_dims *dims, const domino_weights *
  */
 domino_status domino_prepare_input_table(const domino_dims *dims, const domino_weights *weights, float *table,
                                         void *stream);
+
+/*
+ * The same table in fp64 for the tree, whose GRU and scores run in fp64:
+ *   table[v][g] = sum_k embed[v][k] * w_ih[g][k]   (products exact, fp64 sums)
+ * for v < vocab, g < 3 gru_hidden; table is caller-owned device memory of
+ * vocab * 3 * gru_hidden doubles (3.73 GB at V = 151936, gru_hidden = 1024).
+ * Passed as weights.input_table_f64 to domino_tree_draft, it replaces the
+ * tree GRU's W_ih x product (one table row per expanded node instead of an
+ * embedding row and all of w_ih).  Uses weights.embed and weights.w_ih only;
+ * runs on the fp64 matrix cores (about 2.4 TFLOP at the Qwen3-4B shapes).
+ */
+domino_status domino_prepare_input_table_f64(const domino_dims *dims, const domino_weights *weights, double *table,
+                                            void *stream);
 
 /*
  * The sequential correction chain over one draft block for `batch`

@@ -180,3 +180,63 @@ def test_candidates_match_oracle_topm(kind):
             oi, ov = oracle.topm(row, M)
             assert np.array_equal(gi[b, p], oi), (kind, b, p)
             assert np.array_equal(gv[b, p], ov)
+
+
+# ---- the tree with the per-token fp64 input table ------------------------------------
+@pytest.mark.parametrize("d,V,Hs,dtype", [(64, 1003, 40, "bf16"), (96, 2051, 64, "bf16"), (16, 37, 8, "f32"),
+                                          (3080, 1000, 1288, "bf16"), (32, 300, 8, "f32")])
+def test_input_table_f64_exact(d, V, Hs, dtype):
+    """E W_ih^T in fp64: the products are exact, so the table equals the exact sum up
+    to fp64 rounding (a K-term bound), and the oracle's own fp64 product within it."""
+    cfg = small_config(d=d, V=V, Hs=Hs, r=16, P=3, B=2, dtype=dtype)
+    say(f"case input table fp64 d={d} V={V} Hs={Hs} {dtype}")
+    w = synth.make_weights(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    T = head.prepare_input_table_f64().cpu().numpy()
+    from helpers import widen
+    E, Wd = widen(w["embed"], dtype), widen(w["w_ih"], dtype)
+    exact = E @ Wd.T
+    bound = 4.0 * d * 2.0 ** -53 * (np.abs(E) @ np.abs(Wd).T) + 1e-300  # both sides round
+    assert np.all(np.abs(T - exact) <= bound)
+
+
+@pytest.mark.parametrize("d,V,Hs,r,P,B,N,M,dtype", [
+    (16, 37, 8, 8, 4, 2, 16, 3, "f32"),
+    (96, 2051, 64, 64, 16, 5, 16, 64, "bf16"),
+    (48, 515, 16, 16, 5, 9, 40, 5, "bf16"),
+    (3080, 1000, 1288, 64, 2, 3, 8, 16, "bf16"),
+    (64, 777, 24, 16, 3, 17, 12, 6, "bf16"),
+])
+def test_tree_with_table_matches_oracle(d, V, Hs, r, P, B, N, M, dtype):
+    cfg = small_config(d=d, V=V, Hs=Hs, r=r, P=P, B=B, dtype=dtype, biases=True)
+    say(f"case tree with table d={d} V={V} Hs={Hs} r={r} P={P} B={B} N={N} M={M} {dtype}")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    m = oracle.Model.from_config(cfg, w)
+    Lb = m.base_logits(inp["H"])
+    head = dh.DraftHead.from_config(cfg, w)
+    head.prepare_input_table_f64()
+    out, ws = head.tree_draft(head.upload(inp["H"]), head.upload(Lb), head.upload(inp["t0"]), N, M, check=False)
+    torch.cuda.synchronize()
+    assert dh.DraftHead.device_status(ws) == 0
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    _compare(g, m.tree(inp["H"], Lb, inp["t0"], N, M), "tree with table")
+
+
+def test_tree_with_table_full_size_after_gpu_base_logits():
+    key = "qwen3_4b_tree"
+    cfg = synth.CONFIGS[key]
+    say(f"case tree with table full {key}")
+    w = weights_for("qwen3_4b_b1")
+    inp = synth.make_inputs(cfg)
+    head = dh.DraftHead.from_config(cfg, w)
+    head.prepare_input_table_f64()
+    H = head.upload(inp["H"])
+    Lb = head.base_logits(H)
+    out, _ = head.tree_draft(H, Lb, head.upload(inp["t0"]), cfg.nodes, cfg.topm)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    o = oracle.Model.from_config(cfg, w).tree(inp["H"], Lb.cpu().numpy(), inp["t0"], cfg.nodes, cfg.topm)
+    _compare(g, o, key + " (table)")
+    del head
+    torch.cuda.empty_cache()
