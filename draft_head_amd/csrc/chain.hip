@@ -1576,12 +1576,26 @@ __global__ __launch_bounds__(256) void chain_gru_k(ChainArgs a, int p) {
 // sequences, 17.3 against 14.1 us: the time goes to the sequences' state and
 // embedding fragments, which every workgroup reads.)
 constexpr int kGru16UH = 2;  // hidden-half chunks per wave per batch (Hs <= 1024 in one batch)
-template <class W, int NCB, bool kTab>
+// kStage (with the per-token table, when the state fits): the workgroup first
+// copies the split state of every sequence (hi and lo rows of Hs bf16 each)
+// into LDS with whole-row loads, rows padded by 8 elements, and the waves read
+// their fragments from there: every workgroup reads the same state, and
+// fragment-shaped reads of it from L2 are several times slower.  The chains'
+// partial sums then reuse the same LDS.
+__host__ __device__ inline size_t gru16_stage_bytes(int B, int Hs, int NCB) {
+  const size_t st = (size_t)2 * B * (Hs + 8) * 2, red = (size_t)kGruChains * NCB * 64 * 16;
+  return st > red ? st : red;
+}
+template <class W, int NCB, bool kTab, bool kStage = false>
 __global__ __launch_bounds__(1024) void chain_gru16_k(ChainArgs a, int p) {
   static_assert(sizeof(W) == 2, "bf16 weights (fp32 fragments need twice the registers)");
+  static_assert(!kStage || kTab, "the staged state with the per-token table only");
   // input-half chunks per wave per batch: d <= 2560 in one batch for 16 sequences, two batches for 32
   constexpr int kGru16UX = NCB == 1 ? 5 : 4;
-  __shared__ __attribute__((aligned(16))) float red[kGruChains * NCB * 64 * 4];
+  __shared__ __attribute__((aligned(16))) float red_st[kStage ? 4 : kGruChains * NCB * 64 * 4];
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];  // kStage: the state, then the sums
+  float* red = kStage ? reinterpret_cast<float*>(dyn_lds) : red_st;
+  const W* hs = reinterpret_cast<const W*>(dyn_lds);
   const int item = blockIdx.x;
   const int lane = opaque_lane(), v = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
@@ -1601,6 +1615,19 @@ __global__ __launch_bounds__(1024) void chain_gru16_k(ChainArgs a, int p) {
   }
   const int nch = (Hs + 31) / 32, ncx = (d + 31) / 32;
   const bool hid = p > 0;  // h(0) = 0: no hidden half at the first step
+  const int SR = Hs + 8;   // staged row stride
+  if constexpr (kStage) {
+    if (hid) {
+      const int per = Hs / 8;
+      const uint16_t* src = a.hb + (size_t)p * a.hb_step;  // hi rows [B][Hs], then lo rows
+      copy8_batched<W, 8>(2 * B * per, [&](int q) { return (const W*)src + (size_t)q * 8; },
+                          [&](int q) {
+                            const int r = q / per;
+                            return (W*)dyn_lds + (size_t)r * SR + (size_t)(q - r * per) * 8;
+                          });
+      __syncthreads();
+    }
+  }
   f32x4 acc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1614,7 +1641,14 @@ __global__ __launch_bounds__(1024) void chain_gru16_k(ChainArgs a, int p) {
       const bool kok = hid && c < nch && k + kg * 8 < Hs;
       AH[q] = load8_or_zero(rh + k, kok && has_h);
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) SH[q][cb] = state_frag<W>(a, p, bb[cb], k + kg * 8, kok && bok[cb]);
+      for (int cb = 0; cb < NCB; ++cb) {
+        if constexpr (kStage) {
+          SH[q][cb].hi = load8_or_zero(hs + (size_t)bb[cb] * SR + k + kg * 8, kok && bok[cb]);
+          SH[q][cb].lo = load8_or_zero(hs + (size_t)(B + bb[cb]) * SR + k + kg * 8, kok && bok[cb]);
+        } else {
+          SH[q][cb] = state_frag<W>(a, p, bb[cb], k + kg * 8, kok && bok[cb]);
+        }
+      }
     }
   };
   auto load_x = [&](int c0) {
@@ -1658,6 +1692,7 @@ __global__ __launch_bounds__(1024) void chain_gru16_k(ChainArgs a, int p) {
       mma_x();
     }
   }
+  if constexpr (kStage) __syncthreads();  // the sums take the staged state's place
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
     *reinterpret_cast<float4*>(&red[((v * NCB + cb) * 64 + lane) * 4]) = make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
@@ -2048,10 +2083,32 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
   // phase G, bf16 weights: sixteen waves per work item
   const bool gru16 = DH_GRU16 && sizeof(W) == 2;
   const bool tab = a.xt != nullptr;
+  // the sixteen-wave GRU with the state staged in LDS (per-token table, more than 16
+  // sequences, state within the LDS): 620 -> 605 us per block at 32 sequences, while
+  // at 16 it measured slower (496 -> 505 us)
+  const size_t lds16 = gru16_stage_bytes(a.B, a.Hs, NCB);
+  bool stage16 = false;
+  if constexpr (sizeof(W) == 2 && NCB == 2) {
+    if (gru16 && tab && lds16 <= 144 * 1024) {
+      stage16 = true;
+      static thread_local int attr_dev = -1;
+      int dev = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) return e;
+      if (attr_dev != dev) {
+        e = hipFuncSetAttribute((const void*)chain_gru16_k<W, NCB, true, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                144 * 1024);
+        if (e != hipSuccess) return e;
+        attr_dev = dev;
+      }
+    }
+  }
   for (int p = 0; p < a.P; ++p) {
     if constexpr (sizeof(W) == 2) {
       if (gru16) {
-        if (tab)
+        if (tab && stage16)
+          hipLaunchKernelGGL((chain_gru16_k<W, NCB, true, true>), dim3(nG), dim3(1024), lds16, s, a, p);
+        else if (tab)
           hipLaunchKernelGGL((chain_gru16_k<W, NCB, true>), dim3(nG), dim3(1024), 0, s, a, p);
         else
           hipLaunchKernelGGL((chain_gru16_k<W, NCB, false>), dim3(nG), dim3(1024), 0, s, a, p);

@@ -255,3 +255,21 @@ def test_input_table_arguments_rejected():
                               FAKE, None, FAKE, ws, None)
     assert st == dh.ERR_INVALID_ARGUMENT
     assert "input_table" in dh.last_error()
+
+
+def test_input_table_f64_arguments_rejected():
+    L = dh.lib()
+    d = _dims()
+    assert L.domino_prepare_input_table_f64(ctypes.byref(d), ctypes.byref(_weights()), None, None) == \
+        dh.ERR_INVALID_ARGUMENT
+    assert "table is NULL" in dh.last_error()
+    for wname in ("embed", "w_ih"):
+        assert L.domino_prepare_input_table_f64(ctypes.byref(d), ctypes.byref(_weights(**{wname: None})), FAKE,
+                                                None) == dh.ERR_INVALID_ARGUMENT
+        assert wname in dh.last_error()
+    # a misaligned fp64 table passed to the tree is rejected
+    ws = dh.domino_workspace_size(d, 2, dh.OP_TREE, 16, 64)
+    st = L.domino_tree_draft(ctypes.byref(d), ctypes.byref(_weights(input_table_f64=FAKE + 8)), FAKE, FAKE, FAKE, 2,
+                             16, 64, FAKE, FAKE, None, None, FAKE, ws, None)
+    assert st == dh.ERR_INVALID_ARGUMENT
+    assert "input_table_f64" in dh.last_error()
