@@ -350,7 +350,9 @@ def chain_schedule(wl):
     st = wl.ws[off:off + 8 * n].view(torch.int64).cpu().numpy().astype(np.int64)
     if np.all(st > 0):
         return "one persistent launch for all steps", (np.diff(st) * 10e-3).tolist()  # 100 MHz ticks -> us
-    return "three launches per step", None
+    if wl.cfg.dtype == "bf16" and min(wl.B, 32) <= 16:
+        return "two launches per step (GRU; bottleneck and W2 in one launch)", None
+    return "three launches per step (GRU; bottleneck; W2)", None
 
 
 def cache_probe(wl, reps=10):

@@ -230,7 +230,8 @@ domino_status domino_draft_chain(const domino_dims *dims, const domino_weights *
  * b is the sequence's index in this call.  out_logits, if not NULL, are the
  * unperturbed L.  T = 0 is the greedy chain.  The draws run in the chain's
  * one-launch schedule where W2 stays on chip (bf16, up to 8 sequences), else
- * in three launches per step; both draw the same tokens.  temperature must be
+ * in the stepwise schedule (two or three launches per step); both draw the
+ * same tokens.  temperature must be
  * finite and >= 0.
  */
 domino_status domino_draft_chain_sampled(const domino_dims *dims, const domino_weights *weights, const void *H,

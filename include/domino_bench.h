@@ -33,8 +33,10 @@ void domino_set_timing_events(void *base_start, void *base_stop, void *chain_sta
 /*
  * Chain scheduling.  0 (default): the library picks; one persistent launch
  * runs all P steps and, for bf16 weights where every workgroup's share fits,
- * keeps W2 on chip (registers and LDS) for all of them; otherwise three
- * kernel launches per step.  1: three launches per step.  2: the persistent
+ * keeps W2 on chip (registers and LDS) for all of them; otherwise the
+ * stepwise schedule: per step a GRU launch, then the bottleneck and the W2
+ * pass, in one launch for bf16 weights up to 16 sequences and in two
+ * otherwise.  1: the stepwise schedule.  2: the persistent
  * launch with W2 read from memory every step.  3: the persistent launch,
  * keeping W2 on chip wherever its share fits (else as 2), whatever the batch.
  * All compute the same function with the same summation order, so their
