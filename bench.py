@@ -298,7 +298,7 @@ def time_launches(wl, K):
     return float(tb.mean()), float(tc.mean()), float(np.median(tb)), float(np.median(tc))
 
 
-def roofline_record(cfg, B, t_base, t_chain, write_logits, chain_mode, table=False):
+def roofline_record(cfg, B, t_base, t_chain, write_logits, chain_mode, table=False, workload=None):
     tr = algorithmic_traffic(cfg, B, write_logits, table)
     if cfg.tree:
         byts, flops, comp = tree_traffic(cfg, B, table)
@@ -314,7 +314,7 @@ def roofline_record(cfg, B, t_base, t_chain, write_logits, chain_mode, table=Fal
         else:
             k = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": peak_mfma, "unit": "TFLOP/s"}
         k["frac"] = k["achieved"] / k["peak"]
-        k["traffic"] = measured_traffic(cfg.name, kernel_key[name])
+        k["traffic"] = measured_traffic(workload or cfg.name, kernel_key[name])
         k["us"] = t * 1e6
         k["algorithmic_bytes"] = byts
         k["flops"] = flops
@@ -573,7 +573,8 @@ def run_workload(cfg, args, steps, warmup, weights, parity_lbs=None, label=None,
     g_scores = wl.scores.cpu().numpy() if cfg.tree else None
     Lb_gpu = wl.Lb.cpu().numpy() if (cfg.tree or temperature > 0) else None
     t_base, t_chain, tb_med, tc_med = time_launches(wl, steps)
-    roof, kernels = roofline_record(cfg, cfg.batch, t_base, t_chain, args.logits, args.chain_mode, wl.table is not None)
+    roof, kernels = roofline_record(cfg, cfg.batch, t_base, t_chain, args.logits, args.chain_mode, wl.table is not None,
+                                    workload=name)
     kernels["base"]["us_median"], kernels["chain"]["us_median"] = tb_med * 1e6, tc_med * 1e6
     sched, step_us = chain_schedule(wl)
     rec = {"value": cfg.batch / (t["ms_per_step"] * 1e-3), "unit": "draft blocks/s",
