@@ -1373,7 +1373,11 @@ __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_b
 // flight while it multiplies one (two named buffers, loads always issued from
 // clamped addresses so the waits stay exact), and re-reads the staged
 // activations from LDS per tile, so it needs few registers and the other
-// waves hide what latency is left.
+// waves hide what latency is left.  With two row groups (9 to 16 sequences)
+// the registers hold a third buffer and each wave runs two tiles ahead
+// (495 -> 476 us per block at 16 sequences); with one row group the sixteen
+// waves of a workgroup, and with four the tile's row groups, leave no room
+// for it (at four the third buffer spilled and cost 603 -> 616 us).
 // (kLL: the activations come as hand-off words of launch ep, else from the
 // stepwise activation buffer)
 template <class W, int RG, int KC, int NWV, bool kWrite, bool kSample = false, bool kLL = false>
@@ -1389,8 +1393,10 @@ __device__ __forceinline__ void logits_wide_(const ChainArgs& a, int p, int t_be
     for (int c = 0; c < KC; ++c) tb.w[c] = load8(w2_frag_ptr<W>(a, t, row, kg, c));
     load_base_rows<RG, false>(a, p, t * 16 + row, kg, tb.lb, tb.b2);
   };
-  TileBuf<W, RG, KC> s0, s1;
+  constexpr bool kAhead2 = RG == 2;
+  TileBuf<W, RG, KC> s0, s1, s2;
   issue(0, s0);
+  if constexpr (kAhead2) issue(1, s1);
   if constexpr (kLL)
     stage_act_ll<W, KC>(a, p, ep, act_s);
   else
@@ -1411,13 +1417,26 @@ __device__ __forceinline__ void logits_wide_(const ChainArgs& a, int p, int t_be
     rows_epilogue<kWrite, RG, kSample>(a, p, (t0 + NWV * i) * 16 + row, kg, tb.lb, tb.b2, acc, lm);
   };
   int i = 0;
-  for (; i + 2 <= n; i += 2) {
-    issue(i + 1, s1);
-    consume(i, s0);
-    issue(i + 2, s0);
-    consume(i + 1, s1);
+  if constexpr (kAhead2) {
+    for (; i + 3 <= n; i += 3) {
+      issue(i + 2, s2);
+      consume(i, s0);
+      issue(i + 3, s0);
+      consume(i + 1, s1);
+      issue(i + 4, s1);
+      consume(i + 2, s2);
+    }
+    if (i < n) consume(i, s0);
+    if (i + 1 < n) consume(i + 1, s1);
+  } else {
+    for (; i + 2 <= n; i += 2) {
+      issue(i + 1, s1);
+      consume(i, s0);
+      issue(i + 2, s0);
+      consume(i + 1, s1);
+    }
+    if (i < n) consume(i, s0);
   }
-  if (i < n) consume(i, s0);
   publish_rows<RG, false, NWV>(a, p, lm, sbest, 0u);
 }
 
