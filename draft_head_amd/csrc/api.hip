@@ -147,6 +147,9 @@ domino_status run_draft_chain(const domino_dims* dims, const domino_weights* w, 
     a.out_tokens = out_tokens + (size_t)g0 * P;
     a.t0 = first_tokens + g0;
     a.zh = (const float*)(ws + L.zh);
+    a.zh_splits = dh::zh_splits(d, r, P, Bg);
+    a.zh_stride = Bg * P * r;
+    a.zh_sum = (float*)(ws + L.zh_sum);
     a.h = (float*)(ws + L.h);
     a.hb = (uint16_t*)(ws + L.hb);
     a.hb_step = L.hb_step;

@@ -671,8 +671,43 @@ __device__ __forceinline__ void stage_w1_slice(const ChainArgs& a, int item, W* 
 struct BottleneckPre {
   float4 zh, b1;
 };
+// The H half summed over its k splits, in split order.  A lane reads only
+// rows of its own work item, so the persistent schedule's bottleneck
+// workgroups add the splits of their rows once per launch (zh_sum_rows) and
+// read the sums (kSummed); the stepwise kernels add them where they read them.
+template <class F>
+__device__ __forceinline__ float4 zh_splits_sum(const ChainArgs& a, const float* z, F&& ld) {
+  const int ns = a.zh_splits;
+  float4 v = ld(z);
+  float4 t[kMaxZhSplits - 1];
+#pragma unroll
+  for (int s = 1; s < kMaxZhSplits; ++s) t[s - 1] = ld(z + (size_t)min(s, ns - 1) * a.zh_stride);  // all loads first
+#pragma unroll
+  for (int s = 1; s < kMaxZhSplits; ++s)
+    if (s < ns) {
+      v.x += t[s - 1].x;
+      v.y += t[s - 1].y;
+      v.z += t[s - 1].z;
+      v.w += t[s - 1].w;
+    }
+  return v;
+}
+// the sums for work item `item` (rows 16 item .. 16 item + 15) at every
+// sequence and position, by the whole workgroup, into zh_sum
+__device__ __forceinline__ void zh_sum_rows(const ChainArgs& a, int item) {
+  const int n = a.B * a.P * 4;  // (sequence, position, group of four rows)
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int bp = i >> 2, k = item * 16 + (i & 3) * 4;
+    if (k < a.r) {
+      const size_t o = (size_t)bp * a.r + k;
+      const float4 v = zh_splits_sum(a, a.zh + o, [](const float* q) { return *reinterpret_cast<const float4*>(q); });
+      *reinterpret_cast<float4*>(a.zh_sum + o) = v;
+    }
+  }
+  __syncthreads();
+}
 // (sequences seq0 .. seq0 + 16 NCB - 1)
-template <int NCB>
+template <int NCB, bool kSummed = false>
 __device__ __forceinline__ BottleneckPre bottleneck_pre(const ChainArgs& a, int p, int item, int seq0 = 0) {
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
@@ -681,7 +716,13 @@ __device__ __forceinline__ BottleneckPre bottleneck_pre(const ChainArgs& a, int 
   q.b1 = q.zh;
   const int b = seq0 + wv * 16 + row, k = item * 16 + kg * 4;
   if (wv < NCB && b < a.B && k < a.r) {  // r is a multiple of 8: k..k+3 are valid together
-    q.zh = *reinterpret_cast<const float4*>(&a.zh[((size_t)b * a.P + p) * a.r + k]);
+    const size_t o = ((size_t)b * a.P + p) * a.r + k;
+    if (a.zh_splits == 1)
+      q.zh = *reinterpret_cast<const float4*>(&a.zh[o]);
+    else if (kSummed)
+      q.zh = *reinterpret_cast<const float4*>(&a.zh_sum[o]);
+    else
+      q.zh = zh_splits_sum(a, a.zh + o, [](const float* z) { return *reinterpret_cast<const float4*>(z); });
     if (a.b1) q.b1 = *reinterpret_cast<const float4*>(&a.b1[k]);
   }
   return q;
@@ -1519,13 +1560,16 @@ constexpr uint64_t kLLMarker = 0x6c6c2d646f6d696eull;
 // tags are epoch * 128 + step + 1 in 32 bits (steps < 64)
 constexpr uint32_t kEpochLimit = 1u << 25;
 // Before the steps: the H half of the bottleneck for every position,
-// zh[b][p][k] = sum_i H[b][p][i] W1[k][i] (one 16x16 tile per workgroup, k
-// split over the waves), and the zeroed keys and initial state.
+// zh[b][p][k] = sum_i H[b][p][i] W1[k][i], and the zeroed keys and initial
+// state.  One 16x16 tile per workgroup and k split (blockIdx.z) over the
+// waves; split s writes its partial sum to zh + s * zh_stride (with few
+// tiles the splits spread one tile's k range over many CUs, whose fetch
+// rate bounds this kernel).
 template <class W>
 __global__ __launch_bounds__(256) void chain_prologue(ChainArgs a, const void* H, int reset_status) {
   __shared__ __attribute__((aligned(16))) float red[4 * 64 * 4];
   const int M = a.B * a.P;
-  const int nblk = gridDim.x * gridDim.y, blk = blockIdx.y * gridDim.x + blockIdx.x;
+  const int nblk = gridDim.x * gridDim.y * gridDim.z, blk = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
   const int tid = blk * blockDim.x + threadIdx.x, stride = nblk * blockDim.x;
   if (blk == 0) {
     // The launch's bookkeeping, every read in flight at once (a chain of
@@ -1560,8 +1604,15 @@ __global__ __launch_bounds__(256) void chain_prologue(ChainArgs a, const void* H
       *a.status = status_in == 0 && bad ? 1 : status_in;
     }
   }
-  splitk_tile<W>((const W*)H, a.d, (const W*)a.w1, a.d + a.Hs, (float*)a.zh, a.r, M, a.r, a.d, blockIdx.x, blockIdx.y,
-                 red);
+  if (a.zh_splits == 1) {
+    splitk_tile<W>((const W*)H, a.d, (const W*)a.w1, a.d + a.Hs, (float*)a.zh, a.r, M, a.r, a.d, blockIdx.x, blockIdx.y,
+                   red);
+  } else {
+    const int nck = (a.d + 31) / 32, per = (nck + a.zh_splits - 1) / a.zh_splits, s = blockIdx.z;
+    const int cb = min(s * per, nck), ce = min(cb + per, nck);
+    splitk_tile_n<W, 4, 4>((const W*)H, a.d, (const W*)a.w1, a.d + a.Hs, (float*)a.zh + (size_t)s * a.zh_stride, a.r,
+                           M, a.r, a.d, blockIdx.x, blockIdx.y, red, cb, ce);
+  }
   for (int i = tid; i < a.P * a.B; i += stride) a.keys[i] = 0;
   for (int i = tid; i < a.B * a.Hs; i += stride) a.h[i] = 0.f;  // state slot 0
 }
@@ -1820,6 +1871,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
   if (kGruLds && wg < nG) stage_gru_slice<W>(a, wg, gl);
   if (kLds >= 2 && wg < nW) stage_w1_slice<W>(a, wg, wl);
   if constexpr (NTW > 0) stage_w2_lds<W, KC>(a, t_begin + 4 * NTW, max(0, t_end - t_begin - 4 * NTW), w2l);
+  if (wg < nW && a.zh_splits > 1) zh_sum_rows(a, wg);
   // resident W2: the bottleneck workgroups stage the state words after their
   // LDS tiles when one poll round covers them (more rounds cost a memory
   // round trip each, more than per-lane polling)
@@ -1850,7 +1902,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
           ll_tokens_read(a, p - 1, ep, tok_s);
           tk = tok_s;
         }
-        if (wg < nW) pre = bottleneck_pre<NCB>(a, p, wg);
+        if (wg < nW) pre = bottleneck_pre<NCB, true>(a, p, wg);
         frag_t<W> xw[kXPre];
         if constexpr (!kTab) gru_x_prefetch<W>(a, wg, xw);
         DH_STAMP(p, 0);
@@ -1862,7 +1914,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
           ll_tokens_read(a, p - 1, ep, tok_s);
           tk = tok_s;
         }
-        if (wg < nW) pre = bottleneck_pre<NCB>(a, p, wg);
+        if (wg < nW) pre = bottleneck_pre<NCB, true>(a, p, wg);
         DH_STAMP(p, 0);
         if (wg == 0 && p > 0)
           for (int b = threadIdx.x; b < a.B; b += blockDim.x) a.out_tokens[(size_t)b * a.P + p - 1] = tok_s[b];
@@ -1872,7 +1924,7 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
     DH_STAMP(p, 1);
     // W: the bottleneck of this step from h(p+1)
     if (wg < nW) {
-      if (wg >= nG) pre = bottleneck_pre<NCB>(a, p, wg);
+      if (wg >= nG) pre = bottleneck_pre<NCB, true>(a, p, wg);
       DH_STAMP(p, 2);
       bottleneck_item<W, NCB, (kLds >= 2), true>(a, p, wg, red, wl, pre, ep, h_s);
     }
@@ -1907,8 +1959,18 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
 // ---- host side ------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Splits of the H half's k range: enough workgroups in the prologue to
+// spread its reads over about 256 CUs, at most kMaxZhSplits, at least four
+// chunks of 32 per split.
+int zh_splits(int d, int r, int P, int B) {
+  const int tiles = ((r + 15) / 16) * ((B * P + 15) / 16), nck = (d + 31) / 32;
+  int s = (256 + tiles - 1) / tiles;
+  s = s < kMaxZhSplits ? s : kMaxZhSplits;
+  s = s < nck / 4 ? s : nck / 4;
+  return s > 1 ? s : 1;
+}
+
 ChainLayout chain_layout(int d, int Hs, int r, int P, int group) {
-  (void)d;
   ChainLayout L;
   size_t off = 0;
   L.status = off;
@@ -1918,6 +1980,13 @@ ChainLayout chain_layout(int d, int Hs, int r, int P, int group) {
   L.keys = off;
   off += align256((size_t)P * group * 8);
   L.zh = off;
+  size_t zh_floats = 0;  // the partials of any launch of up to `group` sequences
+  for (int b = 1; b <= group; ++b) {
+    const size_t f = (size_t)zh_splits(d, r, P, b) * b * P * r;
+    zh_floats = f > zh_floats ? f : zh_floats;
+  }
+  off += align256(zh_floats * 4);
+  L.zh_sum = off;
   off += align256((size_t)group * P * r * 4);
   // one slot per step for every value handed between workgroups, so no slot
   // is read before it is written within a launch
@@ -2182,7 +2251,7 @@ static hipError_t run_chain_kc(const ChainArgs& a, int mode, hipStream_t s, bool
 hipError_t launch_chain(int dtype, const ChainArgs& a, const void* H, int mode, bool reset_status, hipStream_t s,
                         hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (a.B <= 0) return hipSuccess;
-  const dim3 pro((a.r + 15) / 16, (a.B * a.P + 15) / 16);
+  const dim3 pro((a.r + 15) / 16, (a.B * a.P + 15) / 16, a.zh_splits);
   if (dtype == kBF16)
     hipLaunchKernelGGL(chain_prologue<uint16_t>, pro, dim3(256), 0, s, a, H, reset_status ? 1 : 0);
   else

@@ -150,20 +150,22 @@ __device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 c) {
 // ---- one 16x16 tile of C = A B^T with k split over the waves ---------------------
 // For narrow products: each wave sums its share of the k chunks, the partials
 // meet in LDS and wave 0 writes the tile.
-// One 16x16 output tile of C = A B^T with k split over the NWV waves of the
-// workgroup: wave w takes chunks of 32 from w * U on, U at a time, NWV * U
-// apart; the waves' partial tiles (red: NWV x 64 float4) are added in wave order.
+// One 16x16 output tile of C = A B^T over the k chunks of 32 in [c_begin,
+// c_end) (all of k by default), split over the NWV waves of the workgroup:
+// wave w takes chunks from c_begin + w * U on, U at a time, NWV * U apart; the
+// waves' partial tiles (red: NWV x 64 float4) are added in wave order.
 template <class W, int NWV, int U>
 __device__ void splitk_tile_n(const W* __restrict__ A, int lda, const W* __restrict__ B, int ldb, float* __restrict__ C,
-                              int ldc, int M, int N, int K, int n_tile, int m_tile, float* red) {
+                              int ldc, int M, int N, int K, int n_tile, int m_tile, float* red, int c_begin = 0,
+                              int c_end = -1) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int n0 = n_tile * 16, m0 = m_tile * 16;
   const W* brow = B + (size_t)min(n0 + row, N - 1) * ldb + kg * 8;
   const W* arow = A + (size_t)min(m0 + row, M - 1) * lda + kg * 8;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int nck = (K + 31) / 32;
-  for (int c0 = wv * U; c0 < nck; c0 += NWV * U) {
+  const int nck = c_end < 0 ? (K + 31) / 32 : c_end;
+  for (int c0 = c_begin + wv * U; c0 < nck; c0 += NWV * U) {
     frag_t<W> af[U], bf[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {

@@ -11,6 +11,7 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kMaxChainGroup = 32;  // sequences per chain launch (two 16-column MFMA blocks)
 constexpr int kMaxChainGrid = 1024; // workgroups of a persistent chain launch at most
+constexpr int kMaxZhSplits = 8;     // k splits of the H half of the bottleneck at most
 // device-side status word at offset 0 of a workspace
 constexpr int kDeviceStatusFirstToken = 1;  // a first token outside [0, V) was replaced by 0
 constexpr int kDeviceStatusTimeout = 2;     // a wait between workgroups gave up
@@ -46,7 +47,10 @@ struct ChainArgs {
   float* out_logits;       // [B][P][V] or null
   int32_t* out_tokens;     // [B][P]
   const int32_t* t0;       // [B]
-  const float* zh;         // [B][P][r]  W1[:, :d] H
+  const float* zh;         // [zh_splits][B][P][r]  W1[:, :d] H, as partial sums over k splits
+  int zh_splits;           // partial sums in zh (added in split order by the bottleneck)
+  int zh_stride;           // floats between consecutive partials
+  float* zh_sum;           // [B][P][r] the partials added, written by the persistent launch's bottleneck workgroups
   float* h;                // [P+1][h_step] GRU state after each step (slot 0 = zeros)
   uint16_t* hb;            // [P+1][hb_step] the same states split for bf16 MFMA: hi [B][Hs], lo [B][Hs]
   void* act;               // [P][act_step bytes] bottleneck activations of each step:
@@ -76,10 +80,12 @@ struct ChainArgs {
 
 // workspace carving for a chain launch of up to `group` sequences
 struct ChainLayout {
-  size_t status, stamps, keys, zh, h, hb, act, ll_h, ll_act, ll_part, ll_tok, trace, total;
+  size_t status, stamps, keys, zh, zh_sum, h, hb, act, ll_h, ll_act, ll_part, ll_tok, trace, total;
   int h_step, hb_step, act_step;
 };
 ChainLayout chain_layout(int d, int Hs, int r, int P, int group);
+// k splits of the H half for a launch of B sequences
+int zh_splits(int d, int r, int P, int B);
 // frees the per-device events that order persistent launches
 void release_chain_cache();
 
