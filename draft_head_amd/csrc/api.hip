@@ -505,6 +505,15 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   t.cur = ws + L.cur;
   t.status = (int32_t*)(ws + L.status);
   t.heap_cap = L.heap_cap;
+  t.ll_act = (uint64_t*)(ws + L.ll_act);
+  t.ll_cur = (uint64_t*)(ws + L.ll_cur);
+  t.epoch = (uint32_t*)(ws + L.status + 4);
+  t.marker = (uint64_t*)(ws + L.status + 8);
+  t.sig = (uint64_t*)(ws + L.status + 16);
+  t.ll_words = (L.total - L.ll_act) / 8;
+  // the hand-off words are cleared again whenever the region they occupy changes
+  t.sig_value = ((uint64_t)L.ll_act << 32) ^ (uint64_t)t.ll_words ^ ((uint64_t)nodes << 56) ^ ((uint64_t)batch << 40) ^
+                0x7472656500000000ull;
   hipError_t e = dh::launch_tree(t, true, (hipStream_t)stream, g_chain_start.load(), g_chain_stop.load());
   if (e != hipSuccess) return device_fail(e, "tree launch");
   return ok();

@@ -188,9 +188,6 @@ __device__ __forceinline__ typename act<W>::type state_frag(const ChainArgs& a, 
 #define DH_HIDDEN_SLEEP 16
 #endif
 
-// Tag of the hand-off words a persistent launch writes at step p (P <= 64).
-__device__ __forceinline__ uint32_t ll_tag(uint32_t ep, int p) { return ep * 128u + (uint32_t)p + 1u; }
-
 // The same right operand from a hand-off slot with n elements per row
 // (bf16 weights: words [0, n/2) hold hi pairs, [n/2, n) lo pairs; fp32: one
 // value per word).  Returns whether every word read carries `tag`.  (Its
@@ -211,7 +208,7 @@ __device__ __forceinline__ bool ll_frag(const uint64_t* slot, int n, int b, int 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint64_t wh = ld_agent64(row + k / 2 + i), wl = ld_agent64(row + n / 2 + k / 2 + i);
-      good = good & ll_ok(wh, tag) & ll_ok(wl, tag);
+      good = good & (int)ll_ok(wh, tag) & (int)ll_ok(wl, tag);
       h[i] = ll_data(wh);
       l[i] = ll_data(wl);
     }
@@ -1519,7 +1516,7 @@ __device__ __forceinline__ void ll_tokens_reduce(const ChainArgs& a, int p, uint
     key = 0;
     for (int w = tid; w < (int)gridDim.x; w += blockDim.x) {
       const uint64_t hi = ld_agent64(part + ((size_t)w * B + b) * 2), lo = ld_agent64(part + ((size_t)w * B + b) * 2 + 1);
-      good = good & ll_ok(hi, tag) & ll_ok(lo, tag);
+      good = good & (int)ll_ok(hi, tag) & (int)ll_ok(lo, tag);
       key = umax64(key, pair_key(hi, lo));
     }
     return good;
@@ -1556,9 +1553,6 @@ __device__ __forceinline__ void ll_tokens_read(const ChainArgs& a, int p, uint32
 }
 
 // ---- kernels ------------------------------------------------------------------------
-constexpr uint64_t kLLMarker = 0x6c6c2d646f6d696eull;
-// tags are epoch * 128 + step + 1 in 32 bits (steps < 64)
-constexpr uint32_t kEpochLimit = 1u << 25;
 // Before the steps: the H half of the bottleneck for every position,
 // zh[b][p][k] = sum_i H[b][p][i] W1[k][i], and the zeroed keys and initial
 // state.  One 16x16 tile per workgroup and k split (blockIdx.z) over the

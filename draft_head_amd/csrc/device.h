@@ -247,6 +247,14 @@ __device__ __forceinline__ void ll_put(uint64_t* w, uint32_t data, uint32_t tag)
   __hip_atomic_store(w, ((uint64_t)tag << 32) | data, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ bool ll_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+// a workspace's hand-off words are cleared once (marker and layout signature
+// written after); tags are epoch * 128 + step + 1 in 32 bits (steps < 64),
+// with the epoch advanced once per call
+constexpr uint64_t kLLMarker = 0x6c6c2d646f6d696eull;
+constexpr uint32_t kEpochLimit = 1u << 25;
+__host__ __device__ __forceinline__ uint32_t ll_tag(uint32_t epoch, int step) {
+  return epoch * 128u + (uint32_t)step + 1u;
+}
 __device__ __forceinline__ uint32_t ll_data(uint64_t w) { return (uint32_t)w; }
 
 // Repeat `attempt` (it issues the loads and tells, per lane, whether every

@@ -125,10 +125,19 @@ struct TreeArgs {
   void* cur;                // [B] node being expanded this round
   int32_t* status;
   int heap_cap;
+  // tagged hand-off words of the one-launch-per-round schedule (bf16 weights)
+  uint64_t* ll_act;         // [N][B][r][2] the bottleneck of each round, fp64 as two 32-bit halves
+  uint64_t* ll_cur;         // [N][B][2] each round's popped node: token; parent slot + 1 | expand << 16
+  uint32_t* epoch;          // call counter, advanced by tree_init
+  uint64_t* marker;         // kLLMarker once the hand-off words have been cleared
+  uint64_t* sig;            // layout signature the hand-off words were cleared for
+  uint64_t sig_value;       // this call's layout signature
+  size_t ll_words;          // hand-off words from ll_act on (both regions)
 };
 
 struct TreeLayout {
-  size_t status, seg_keys, cand_idx, cand_val, zh, act, states, heap_score, heap_meta, heap_count, cur, total;
+  size_t status, seg_keys, cand_idx, cand_val, zh, act, states, heap_score, heap_meta, heap_count, cur, ll_act, ll_cur,
+      total;
   int heap_cap;
 };
 TreeLayout tree_layout(int d, int Hs, int r, int P, int group, int N, int M);

@@ -225,6 +225,12 @@ struct TreeCur {
   double score;         // its cumulative score
 };
 
+// Two cursor slots: round k reads slot k & 1 and its pop writes the other,
+// so nothing that reads round k's cursor can see round k + 1's.
+__device__ __forceinline__ TreeCur* tree_cur(const TreeArgs& t, int k) {
+  return reinterpret_cast<TreeCur*>(t.cur) + (size_t)(k & 1) * t.B;
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
@@ -364,8 +370,31 @@ __global__ __launch_bounds__(64 * kZhWaves) void tree_zh(TreeArgs t) {
   }
 }
 
-// empty heaps; the anchor as each sequence's first node to expand
+// empty heaps; the anchor as each sequence's first node to expand.  Block 0
+// also advances the call counter that tags the hand-off words of the
+// one-launch-per-round schedule, after clearing those words on the first use
+// of this workspace layout (or before the counter would overflow the tags).
 __global__ void tree_init(TreeArgs t) {
+  if (blockIdx.x == 0) {
+    __shared__ int fresh;
+    __shared__ uint32_t epoch_in;
+    if (threadIdx.x == 0) {
+      const uint64_t mk = *t.marker, sg = *t.sig;
+      const uint32_t ep = *t.epoch;
+      fresh = mk != kLLMarker || sg != t.sig_value || ep + 1 >= kEpochLimit;
+      epoch_in = ep;
+    }
+    __syncthreads();
+    if (fresh) {
+      uint4* w = reinterpret_cast<uint4*>(t.ll_act);
+      for (size_t i = threadIdx.x; i < t.ll_words / 2; i += blockDim.x) w[i] = make_uint4(0, 0, 0, 0);
+      if (threadIdx.x == 0) {
+        *t.marker = kLLMarker;
+        *t.sig = t.sig_value;
+      }
+    }
+    if (threadIdx.x == 0) *t.epoch = (fresh ? 0u : epoch_in) + 1u;
+  }
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= t.B) return;
   t.heap_count[b] = 0;
@@ -382,7 +411,7 @@ __global__ void tree_init(TreeArgs t) {
   c.expand = t.P > 0 ? 1 : 0;
   c.node = -1;
   c.score = 0.0;
-  reinterpret_cast<TreeCur*>(t.cur)[b] = c;
+  tree_cur(t, 0)[b] = c;
 }
 
 // ---- fp64 GRU step of each sequence's current node -----------------------------------------
@@ -396,7 +425,7 @@ __global__ void tree_init(TreeArgs t) {
 constexpr int kTreeSeqs = 8;
 constexpr int kSeqPerWave = 2;  // four waves per GRU unit, each with a quarter of the sequences
 
-__global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0) {
+__global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0, int k) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ TreeCur sc[kTreeSeqs];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -405,7 +434,7 @@ __global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0) {
   const int nb = min(kTreeSeqs, t.B - b0);
   double* hl = reinterpret_cast<double*>(lds);                      // [kTreeSeqs][Hs]
   unsigned char* xl = lds + (size_t)kTreeSeqs * Hs * sizeof(double);  // [kTreeSeqs][d] stored type
-  if (threadIdx.x < nb) sc[threadIdx.x] = reinterpret_cast<const TreeCur*>(t.cur)[b0 + threadIdx.x];
+  if (threadIdx.x < nb) sc[threadIdx.x] = tree_cur(t, k)[b0 + threadIdx.x];
   __syncthreads();
   // stage every sequence's parent state and embedding row: batches of kStage
   // 16-byte pieces per thread are loaded before any is stored, so their
@@ -638,19 +667,22 @@ constexpr int kGruPreI = 10;  // input-half blocks per wave whose loads are all 
 constexpr int kGruPreH = 4;   // hidden-half blocks per wave whose loads are all issued up front
 
 // kTab: the input half comes from the per-token fp64 table (t.xt) instead.
-template <bool kTab>
-__global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int b0) {
+// kLL (one launch per round): the node of round kr arrives as the hand-off
+// words of round kr - 1's pop (tag), polled by wave 0 while the weight loads
+// are in flight; otherwise it is read from round kr's cursor.
+template <bool kTab, bool kLL>
+__device__ __forceinline__ void gru_mfma_step(const TreeArgs& t, int b0, int item, int kr, uint32_t tag) {
   __shared__ double red[kGruWaves][2][12][kTreeSeqs];  // [wave][input, hidden][gate row][sequence]
+  __shared__ int cur_s[kTreeSeqs][3];                   // kLL: token, parent slot, expand
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int d = t.d, Hs = t.Hs;
   const int nb = min(kTreeSeqs, t.B - b0);
-  const int j0 = blockIdx.x * 4;
+  const int j0 = item * 4;
   const int rr = lane & 15, kq = lane >> 4;  // A row and B column; k group
   const int g = rr < 12 ? rr >> 2 : 2, u = rr < 12 ? rr & 3 : 3;
   const size_t wrow = (size_t)g * Hs + min(j0 + u, Hs - 1);
   const uint16_t* wi = (const uint16_t*)t.w_ih + wrow * d;
   const uint16_t* wh = (const uint16_t*)t.w_hh + wrow * Hs;
-  const TreeCur* curs = reinterpret_cast<const TreeCur*>(t.cur) + b0;
   // the weights do not depend on the tree: their loads go out first
   uint4 wpi[kGruPreI], wph[kGruPreH];
   if constexpr (!kTab) {
@@ -663,7 +695,34 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int 
     wph[q] = *reinterpret_cast<const uint4*>(wh + min((wv + kGruWaves * q) * 32 + 8 * kq, Hs - 8));
   // this lane's column: sequence sq's token row and parent state (zeros without a parent)
   const int sq = min(rr, nb - 1);
-  const TreeCur c = curs[sq];
+  TreeCur c;
+  if constexpr (kLL) {
+    if (wv == 0) {
+      const uint64_t* src = t.ll_cur + ((size_t)(kr - 1) * t.B + b0 + min(lane, nb - 1)) * 2;
+      uint64_t w0 = 0, w1 = 0;
+      ll_wait(t.status, [&] {
+        w0 = ld_agent64(src);
+        w1 = ld_agent64(src + 1);
+        return (int)ll_ok(w0, tag) & (int)ll_ok(w1, tag);
+      });
+      if (lane < nb) {  // (clamped, so that words left by a timed-out wait stay in bounds)
+        const uint32_t v = ll_data(w1);
+        cur_s[lane][0] = (int)ll_data(w0);
+        cur_s[lane][1] = (int)min(v & 0xFFFFu, (uint32_t)kr) - 1;
+        cur_s[lane][2] = (int)((v >> 16) & 1u);
+      }
+    }
+    __syncthreads();
+    c.slot = kr;
+    c.token = cur_s[sq][0];
+    c.parent_slot = cur_s[sq][1];
+    c.expand = cur_s[sq][2];
+    c.depth = 0;
+    c.node = kr - 1;
+    c.score = 0.0;
+  } else {
+    c = tree_cur(t, kr)[b0 + sq];
+  }
   const bool has_h = c.expand && c.parent_slot >= 0;
   const uint16_t* xr = (const uint16_t*)t.embed + (size_t)min(max(c.token, 0), t.V - 1) * d;
   const double* hr = t.states + ((size_t)(b0 + sq) * (t.N + 1) + max(c.parent_slot, 0)) * Hs;
@@ -794,14 +853,20 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int 
   }
 }
 
+template <bool kTab>
+__global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int b0, int k) {
+  gru_mfma_step<kTab, false>(t, b0, blockIdx.x, k, 0u);
+}
+
 
 // ---- fp64 bottleneck of each sequence's current node: a = SiLU(W1 [H_delta ; S] + b1) -------
-// Workgroup = 16 bottleneck units of one sequence; wave w takes 4, lanes split Hs.
-template <class W>
-__global__ __launch_bounds__(256) void tree_bottleneck(TreeArgs t) {
+// Rows k0 .. k0 + 3 of sequence b's bottleneck in round kr, by one wave whose
+// lanes split the state.
+// kLL: the results go out as hand-off words of round kr (tag), else to t.act.
+template <class W, bool kLL>
+__device__ __forceinline__ void bottleneck_rows(const TreeArgs& t, int b, int k0, int kr, uint32_t tag) {
   constexpr int U = 2;  // runs of 8 per lane and row whose reads go out first (state width <= 1024)
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int b = blockIdx.y, k0 = blockIdx.x * 16 + wv * 4;
+  const int lane = threadIdx.x & 63;
   const int Hs = t.Hs, r = t.r;
   const size_t ld = (size_t)t.d + Hs;
   const W* w1s = reinterpret_cast<const W*>(t.w1) + t.d;  // state half of W1
@@ -811,7 +876,7 @@ __global__ __launch_bounds__(256) void tree_bottleneck(TreeArgs t) {
   for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int q = 0; q < 4; ++q) wr[u][q].load(w1s + (size_t)min(k0 + q, r - 1) * ld + min(lane * 8 + 512 * u, Hs - 8));
-  const TreeCur c = reinterpret_cast<const TreeCur*>(t.cur)[b];
+  const TreeCur c = tree_cur(t, kr)[b];
   if (!c.expand) return;
   const double* st = t.states + ((size_t)b * (t.N + 1) + c.slot) * Hs;
   F64x8 sv[U];
@@ -852,8 +917,22 @@ __global__ __launch_bounds__(256) void tree_bottleneck(TreeArgs t) {
   const int k = k0 + lane;
   if (lane < 4 && k < r) {
     const double z = (lane == 0 ? v[0] : lane == 1 ? v[1] : lane == 2 ? v[2] : v[3]) + zq + bq;
-    t.act[(size_t)b * r + k] = z / (1.0 + exp(-z));
+    const double a = z / (1.0 + exp(-z));
+    if constexpr (kLL) {
+      const uint64_t bits = (uint64_t)__double_as_longlong(a);
+      uint64_t* w = t.ll_act + (((size_t)kr * t.B + b) * r + k) * 2;
+      ll_put(w, (uint32_t)bits, tag);
+      ll_put(w + 1, (uint32_t)(bits >> 32), tag);
+    } else {
+      t.act[(size_t)b * r + k] = a;
+    }
   }
+}
+
+// Workgroup = 16 bottleneck rows of one sequence, four per wave.
+template <class W>
+__global__ __launch_bounds__(256) void tree_bottleneck(TreeArgs t, int k) {
+  bottleneck_rows<W, false>(t, blockIdx.y, blockIdx.x * 16 + (threadIdx.x >> 6) * 4, k, 0u);
 }
 
 // ---- score the current node's children, push them, pop the best entry ----------------------
@@ -888,9 +967,6 @@ __device__ __forceinline__ void best_offer(BestEntry& e, int slot, double s, int
   e.m.w = take ? m.w : e.m.w;
 }
 
-// One workgroup per sequence.  Wave w scores candidates w, w+4, ...: lanes
-// split the bottleneck in runs of 4 and the partial dot products are reduced
-// across the wave.
 __device__ __forceinline__ void best_offer_lane(BestEntry& e, int src_lane_xor) {
   BestEntry o;
   o.slot = __shfl_xor(e.slot, src_lane_xor);
@@ -902,20 +978,29 @@ __device__ __forceinline__ void best_offer_lane(BestEntry& e, int src_lane_xor) 
   best_offer(e, o.slot, o.s, o.m);
 }
 
-__global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
-  __shared__ double a[256];    // bottleneck (r <= 256)
-  __shared__ double l[256];    // corrected candidate logits (M <= 256)
-  __shared__ int lid[256];     // their token ids
+// Round k of sequence b: score the current node's M children, push them, pop
+// the best entry; one workgroup of NWV waves.  Wave w scores candidates w,
+// w + NWV, ...: lanes split the bottleneck in runs of 4 and the partial dot
+// products are reduced across the wave.  kLL (one launch per round): the
+// bottleneck arrives as round k's hand-off words, and the popped node also
+// goes out as hand-off words (tag) for the GRU step of round k + 1 in the same
+// launch; the first batch of candidate rows is read before the bottleneck.
+template <int NWV, bool kLL>
+__device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint32_t tag) {
+  constexpr int CB = 64 / NWV;  // candidate rows per wave and batch (a batch covers 64 candidates)
+  __shared__ double a[256];     // bottleneck (r <= 256)
+  __shared__ double l[256];     // corrected candidate logits (M <= 256)
+  __shared__ int lid[256];      // their token ids
   __shared__ double lse_s;
-  __shared__ BestEntry wbest[4];
-  __shared__ double last_s;    // the last entry pushed
+  __shared__ BestEntry wbest[NWV];
+  __shared__ double last_s;     // the last entry pushed
   __shared__ int4 last_m;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = t.r, M = t.M, P = t.P;
   // the bottleneck does not depend on the cursor: its read goes out first
-  const double av = t.act[(size_t)b * r + min(tid, r - 1)];
-  TreeCur* curp = reinterpret_cast<TreeCur*>(t.cur) + b;
-  const TreeCur c = *curp;
+  double av = 0.0;
+  if constexpr (!kLL) av = t.act[(size_t)b * r + min(tid, r - 1)];
+  const TreeCur c = tree_cur(t, k)[b];
   double* hs = t.heap_score + (size_t)b * t.heap_cap;
   int4* hm = t.heap_meta + (size_t)b * t.heap_cap;
   int count = t.heap_count[b];
@@ -948,65 +1033,88 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
 
   if (c.expand) {
     const int delta = c.depth;
-    if (tid < r) a[tid] = av;
-    __syncthreads();
     const int32_t* cidx = t.cand_idx + ((size_t)b * P + delta) * M;
     const float* cval = t.cand_val + ((size_t)b * P + delta) * M;
     const int kk = min(lane * 4, r - 4);
     const bool kin = lane * 4 < r;
-    // wave w scores candidates w, w+4, ...; 16 W2 rows per batch in flight
-    constexpr int CB = 16;
-    for (int j0 = wv; j0 < M; j0 += 4 * CB) {
+    // one batch: CB candidate rows of W2 per wave, all reads in flight; the
+    // storage-type and bias tests sit outside the row loops, so that the row
+    // reads go out back to back
+    struct Batch {
       double w[CB][4];
       int vv[CB];
       float cv[CB];
+      double bv[CB];
+    };
+    auto load_batch = [&](int j0, Batch& bt) {
 #pragma unroll
       for (int q = 0; q < CB; ++q) {
-        const int j = min(j0 + 4 * q, M - 1);
-        vv[q] = cidx[j];
-        cv[q] = cval[j];
+        const int j = min(j0 + NWV * q, M - 1);
+        bt.vv[q] = cidx[j];
+        bt.cv[q] = cval[j];
       }
-      // the storage-type and bias tests sit outside the row loops, so that the
-      // CB row reads go out back to back
-      double bv[CB];
       float bf[CB];
       if (t.b2) {
 #pragma unroll
-        for (int q = 0; q < CB; ++q) bf[q] = t.b2[vv[q]];
+        for (int q = 0; q < CB; ++q) bf[q] = t.b2[bt.vv[q]];
       }
       if (t.dtype == kBF16) {
         uint2 u[CB];
 #pragma unroll
-        for (int q = 0; q < CB; ++q) u[q] = *reinterpret_cast<const uint2*>((const uint16_t*)t.w2 + (size_t)vv[q] * r + kk);
+        for (int q = 0; q < CB; ++q)
+          u[q] = *reinterpret_cast<const uint2*>((const uint16_t*)t.w2 + (size_t)bt.vv[q] * r + kk);
 #pragma unroll
         for (int q = 0; q < CB; ++q) {
-          w[q][0] = (double)__uint_as_float(u[q].x << 16);
-          w[q][1] = (double)__uint_as_float(u[q].x & 0xFFFF0000u);
-          w[q][2] = (double)__uint_as_float(u[q].y << 16);
-          w[q][3] = (double)__uint_as_float(u[q].y & 0xFFFF0000u);
+          bt.w[q][0] = (double)__uint_as_float(u[q].x << 16);
+          bt.w[q][1] = (double)__uint_as_float(u[q].x & 0xFFFF0000u);
+          bt.w[q][2] = (double)__uint_as_float(u[q].y << 16);
+          bt.w[q][3] = (double)__uint_as_float(u[q].y & 0xFFFF0000u);
         }
       } else {
         float4 u[CB];
 #pragma unroll
-        for (int q = 0; q < CB; ++q) u[q] = *reinterpret_cast<const float4*>((const float*)t.w2 + (size_t)vv[q] * r + kk);
+        for (int q = 0; q < CB; ++q)
+          u[q] = *reinterpret_cast<const float4*>((const float*)t.w2 + (size_t)bt.vv[q] * r + kk);
 #pragma unroll
-        for (int q = 0; q < CB; ++q) w[q][0] = u[q].x, w[q][1] = u[q].y, w[q][2] = u[q].z, w[q][3] = u[q].w;
+        for (int q = 0; q < CB; ++q) bt.w[q][0] = u[q].x, bt.w[q][1] = u[q].y, bt.w[q][2] = u[q].z, bt.w[q][3] = u[q].w;
       }
 #pragma unroll
-      for (int q = 0; q < CB; ++q) bv[q] = t.b2 ? (double)bf[q] : 0.0;
+      for (int q = 0; q < CB; ++q) bt.bv[q] = t.b2 ? (double)bf[q] : 0.0;
+    };
+    auto score_batch = [&](int j0, const Batch& bt) {
 #pragma unroll
       for (int q = 0; q < CB; ++q) {
-        const int j = j0 + 4 * q;
+        const int j = j0 + NWV * q;
         double sdot = 0.0;
         if (kin)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sdot += w[q][e] * a[kk + e];
+          for (int e = 0; e < 4; ++e) sdot += bt.w[q][e] * a[kk + e];
         sdot = wave_sum(sdot);
         if (lane == 0 && j < M) {
-          l[j] = (double)cv[q] + bv[q] + sdot;
-          lid[j] = vv[q];
+          l[j] = (double)bt.cv[q] + bt.bv[q] + sdot;
+          lid[j] = bt.vv[q];
         }
       }
+    };
+    Batch bt;
+    load_batch(wv, bt);
+    if constexpr (kLL) {
+      // the bottleneck of round k, one fp64 value (two words) per thread
+      const uint64_t* src = t.ll_act + (((size_t)k * t.B + b) * r + min(tid, r - 1)) * 2;
+      uint64_t w0 = 0, w1 = 0;
+      ll_wait(t.status, [&] {
+        w0 = ld_agent64(src);
+        w1 = ld_agent64(src + 1);
+        return (int)ll_ok(w0, tag) & (int)ll_ok(w1, tag);
+      });
+      av = __longlong_as_double((long long)(((uint64_t)ll_data(w1) << 32) | ll_data(w0)));
+    }
+    if (tid < r) a[tid] = av;
+    __syncthreads();
+    score_batch(wv, bt);
+    for (int j0 = wv + NWV * CB; j0 < M; j0 += NWV * CB) {
+      load_batch(j0, bt);
+      score_batch(j0, bt);
     }
     __syncthreads();
     // log-sum-exp over the M candidates (one wave)
@@ -1037,7 +1145,7 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
   }
 
   // pop: best entry under (score desc, parent asc, rank asc): within each
-  // wave by shuffles, then over the four waves
+  // wave by shuffles, then over the waves
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) best_offer_lane(best, m);
   if (lane == 0) wbest[wv] = best;
@@ -1045,7 +1153,7 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
   if (tid == 0) {
     BestEntry e = wbest[0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) best_offer(e, wbest[w].slot, wbest[w].s, wbest[w].m);
+    for (int w = 1; w < NWV; ++w) best_offer(e, wbest[w].slot, wbest[w].s, wbest[w].m);
     const size_t o = (size_t)b * t.N + k;
     const int bi = e.slot;
     TreeCur n;
@@ -1084,7 +1192,41 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
       n.score = s;
     }
     t.heap_count[b] = count;
-    *curp = n;
+    tree_cur(t, k + 1)[b] = n;
+    if constexpr (kLL) {
+      if (k + 1 < t.N) {
+        uint64_t* w = t.ll_cur + ((size_t)k * t.B + b) * 2;
+        ll_put(w, (uint32_t)n.token, tag);
+        ll_put(w + 1, (uint32_t)(n.parent_slot + 1) | ((uint32_t)n.expand << 16), tag);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) { score_pop<4, false>(t, blockIdx.x, k, 0u); }
+
+// ---- one launch per round (bf16 weights) ------------------------------------------------------
+// Launch k runs round k's bottleneck, its score and pop, and the GRU step of
+// round k + 1, in workgroups of 8 waves numbered in that order: ceil(r / 32)
+// per sequence for the bottleneck (four rows per wave), one per sequence for
+// the score and pop, ceil(Hs / 4) per group of kTreeSeqs sequences for the
+// GRU.  The bottleneck and the popped node pass between them as tagged
+// hand-off words; everything else a round reads was written by an earlier
+// launch.  A workgroup waits only for lower-numbered ones (score on
+// bottleneck, GRU on score), and each XCD starts its workgroups in order, so
+// the waits end whether or not all workgroups fit on the device at once.
+template <bool kTab>
+__global__ __launch_bounds__(64 * kGruWaves) void tree_round(TreeArgs t, int k) {
+  const uint32_t tag = ll_tag(*t.epoch, k);
+  const int nr = (t.r + 31) / 32, nbt = nr * t.B, wg = blockIdx.x;
+  if (wg < nbt) {
+    const int b = wg / nr;
+    bottleneck_rows<uint16_t, true>(t, b, (wg - b * nr) * 32 + (threadIdx.x >> 6) * 4, k, tag);
+  } else if (wg < nbt + t.B) {
+    score_pop<kGruWaves, true>(t, wg - nbt, k, tag);
+  } else {
+    const int g = wg - nbt - t.B, nu = (t.Hs + 3) / 4;
+    gru_mfma_step<kTab, true>(t, (g / nu) * kTreeSeqs, g - (g / nu) * nu, k + 1, tag);
   }
 }
 
@@ -1119,7 +1261,11 @@ TreeLayout tree_layout(int d, int Hs, int r, int P, int group, int N, int M) {
   L.heap_count = off;
   off += al256((size_t)group * 4);
   L.cur = off;
-  off += al256((size_t)group * 32);
+  off += al256((size_t)2 * group * sizeof(TreeCur));  // two slots (round parity)
+  L.ll_act = off;
+  off += al256((size_t)N * group * r * 16);
+  L.ll_cur = off;
+  off += al256((size_t)N * group * 16);
   L.total = off;
   return L;
 }
@@ -1167,20 +1313,30 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
     if (e != hipSuccess) return e;
     attr_lds = lds;
   }
-  for (int k = 0; k < t.N; ++k) {
+  if (mfma) {
+    // bf16 weights: round 0's GRU step, then one launch per round (round k's
+    // bottleneck, score and pop, and round k + 1's GRU step)
     for (int b0 = 0; b0 < t.B; b0 += kTreeSeqs) {
-      if (mfma && t.xt)
-        hipLaunchKernelGGL(tree_gru_mfma<true>, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), 0, s, t, b0);
-      else if (mfma)
-        hipLaunchKernelGGL(tree_gru_mfma<false>, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), 0, s, t, b0);
+      if (t.xt)
+        hipLaunchKernelGGL(tree_gru_mfma<true>, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), 0, s, t, b0, 0);
       else
-        hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(64 * 4 * (kTreeSeqs / kSeqPerWave)), lds, s, t, b0);
+        hipLaunchKernelGGL(tree_gru_mfma<false>, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), 0, s, t, b0, 0);
     }
-    if (t.dtype == kBF16)
-      hipLaunchKernelGGL(tree_bottleneck<uint16_t>, dim3((t.r + 15) / 16, t.B), dim3(256), 0, s, t);
-    else
-      hipLaunchKernelGGL(tree_bottleneck<float>, dim3((t.r + 15) / 16, t.B), dim3(256), 0, s, t);
-    hipLaunchKernelGGL(tree_score_pop, dim3(t.B), dim3(256), 0, s, t, k);
+    const int nbt = (t.r + 31) / 32 * t.B, ngr = (t.Hs + 3) / 4 * ((t.B + kTreeSeqs - 1) / kTreeSeqs);
+    for (int k = 0; k < t.N; ++k) {
+      const int grid = nbt + t.B + (k + 1 < t.N ? ngr : 0);
+      if (t.xt)
+        hipLaunchKernelGGL(tree_round<true>, dim3(grid), dim3(64 * kGruWaves), 0, s, t, k);
+      else
+        hipLaunchKernelGGL(tree_round<false>, dim3(grid), dim3(64 * kGruWaves), 0, s, t, k);
+    }
+  } else {
+    for (int k = 0; k < t.N; ++k) {
+      for (int b0 = 0; b0 < t.B; b0 += kTreeSeqs)
+        hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(64 * 4 * (kTreeSeqs / kSeqPerWave)), lds, s, t, b0, k);
+      hipLaunchKernelGGL(tree_bottleneck<float>, dim3((t.r + 15) / 16, t.B), dim3(256), 0, s, t, k);
+      hipLaunchKernelGGL(tree_score_pop, dim3(t.B), dim3(256), 0, s, t, k);
+    }
   }
   e = hipGetLastError();
   if (e == hipSuccess && ev_start && ev_stop) e = hipEventRecord(ev_stop, s);
