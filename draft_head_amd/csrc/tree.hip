@@ -987,10 +987,10 @@ __device__ __forceinline__ void best_offer_lane(BestEntry& e, int src_lane_xor) 
 // launch; the first batch of candidate rows is read before the bottleneck.
 template <int NWV, bool kLL>
 __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint32_t tag) {
-  constexpr int CB = 64 / NWV;  // candidate rows per wave and batch (a batch covers 64 candidates)
   __shared__ double a[256];     // bottleneck (r <= 256)
   __shared__ double l[256];     // corrected candidate logits (M <= 256)
   __shared__ int lid[256];      // their token ids
+  __shared__ double part[NWV][64];  // the waves' partial dot products of 64 candidates
   __shared__ double lse_s;
   __shared__ BestEntry wbest[NWV];
   __shared__ double last_s;     // the last entry pushed
@@ -1035,69 +1035,68 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
     const int delta = c.depth;
     const int32_t* cidx = t.cand_idx + ((size_t)b * P + delta) * M;
     const float* cval = t.cand_val + ((size_t)b * P + delta) * M;
-    const int kk = min(lane * 4, r - 4);
-    const bool kin = lane * 4 < r;
-    // one batch: CB candidate rows of W2 per wave, all reads in flight; the
-    // storage-type and bias tests sit outside the row loops, so that the row
-    // reads go out back to back
+    // Candidates go 64 at a time, one per lane; wave w takes the k range
+    // [w kc, w kc + kc) of every candidate's W2 row (its reads go out before
+    // the bottleneck is needed) and the waves' partial dot products meet in
+    // LDS, added in wave order: no cross-lane reduction per candidate.
+    constexpr int KQ = 256 / NWV / 8;  // runs of 8 k values per lane and wave (r <= 256)
+    const int kc = ((r + NWV - 1) / NWV + 7) & ~7;
+    const int kb = min(wv * kc, r), ke = min(kb + kc, r);
     struct Batch {
-      double w[CB][4];
-      int vv[CB];
-      float cv[CB];
-      double bv[CB];
+      uint4 w[2 * KQ];  // bf16: w[0..KQ) hold 8 values each; fp32: two per run
+      int v;
+      float cv, bf;
     };
     auto load_batch = [&](int j0, Batch& bt) {
-#pragma unroll
-      for (int q = 0; q < CB; ++q) {
-        const int j = min(j0 + NWV * q, M - 1);
-        bt.vv[q] = cidx[j];
-        bt.cv[q] = cval[j];
-      }
-      float bf[CB];
-      if (t.b2) {
-#pragma unroll
-        for (int q = 0; q < CB; ++q) bf[q] = t.b2[bt.vv[q]];
-      }
+      const int j = min(j0 + lane, M - 1);
+      bt.v = cidx[j];
+      bt.cv = cval[j];
+      bt.bf = t.b2 ? t.b2[bt.v] : 0.f;
       if (t.dtype == kBF16) {
-        uint2 u[CB];
+        const uint16_t* row = (const uint16_t*)t.w2 + (size_t)bt.v * r;
 #pragma unroll
-        for (int q = 0; q < CB; ++q)
-          u[q] = *reinterpret_cast<const uint2*>((const uint16_t*)t.w2 + (size_t)bt.vv[q] * r + kk);
-#pragma unroll
-        for (int q = 0; q < CB; ++q) {
-          bt.w[q][0] = (double)__uint_as_float(u[q].x << 16);
-          bt.w[q][1] = (double)__uint_as_float(u[q].x & 0xFFFF0000u);
-          bt.w[q][2] = (double)__uint_as_float(u[q].y << 16);
-          bt.w[q][3] = (double)__uint_as_float(u[q].y & 0xFFFF0000u);
-        }
+        for (int q = 0; q < KQ; ++q) bt.w[q] = *reinterpret_cast<const uint4*>(row + min(kb + 8 * q, r - 8));
       } else {
-        float4 u[CB];
+        const float* row = (const float*)t.w2 + (size_t)bt.v * r;
 #pragma unroll
-        for (int q = 0; q < CB; ++q)
-          u[q] = *reinterpret_cast<const float4*>((const float*)t.w2 + (size_t)bt.vv[q] * r + kk);
-#pragma unroll
-        for (int q = 0; q < CB; ++q) bt.w[q][0] = u[q].x, bt.w[q][1] = u[q].y, bt.w[q][2] = u[q].z, bt.w[q][3] = u[q].w;
+        for (int q = 0; q < KQ; ++q) {
+          bt.w[2 * q] = *reinterpret_cast<const uint4*>(row + min(kb + 8 * q, r - 8));
+          bt.w[2 * q + 1] = *reinterpret_cast<const uint4*>(row + min(kb + 8 * q, r - 8) + 4);
+        }
       }
-#pragma unroll
-      for (int q = 0; q < CB; ++q) bt.bv[q] = t.b2 ? (double)bf[q] : 0.0;
     };
     auto score_batch = [&](int j0, const Batch& bt) {
+      double sdot = 0.0;
 #pragma unroll
-      for (int q = 0; q < CB; ++q) {
-        const int j = j0 + NWV * q;
-        double sdot = 0.0;
-        if (kin)
+      for (int q = 0; q < KQ; ++q) {
+        if (kb + 8 * q < ke) {
+          double w[8];
+          if (t.dtype == kBF16) {
+            bf16x8_to_f64(bt.w[q], w);
+          } else {
+            const uint4 u0 = bt.w[2 * q], u1 = bt.w[2 * q + 1];
+            w[0] = __uint_as_float(u0.x), w[1] = __uint_as_float(u0.y), w[2] = __uint_as_float(u0.z);
+            w[3] = __uint_as_float(u0.w), w[4] = __uint_as_float(u1.x), w[5] = __uint_as_float(u1.y);
+            w[6] = __uint_as_float(u1.z), w[7] = __uint_as_float(u1.w);
+          }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sdot += bt.w[q][e] * a[kk + e];
-        sdot = wave_sum(sdot);
-        if (lane == 0 && j < M) {
-          l[j] = (double)bt.cv[q] + bt.bv[q] + sdot;
-          lid[j] = bt.vv[q];
+          for (int e = 0; e < 8; ++e) sdot += w[e] * a[kb + 8 * q + e];
         }
       }
+      part[wv][lane] = sdot;
+      __syncthreads();
+      const int j = j0 + lane;
+      if (wv == 0 && j < M) {
+        double tot = part[0][lane];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) tot += part[w][lane];
+        l[j] = (double)bt.cv + (double)bt.bf + tot;
+        lid[j] = bt.v;
+      }
+      __syncthreads();  // part is reused by the next group
     };
     Batch bt;
-    load_batch(wv, bt);
+    load_batch(0, bt);
     if constexpr (kLL) {
       // the bottleneck of round k, one fp64 value (two words) per thread
       const uint64_t* src = t.ll_act + (((size_t)k * t.B + b) * r + min(tid, r - 1)) * 2;
@@ -1111,12 +1110,11 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
     }
     if (tid < r) a[tid] = av;
     __syncthreads();
-    score_batch(wv, bt);
-    for (int j0 = wv + NWV * CB; j0 < M; j0 += NWV * CB) {
+    score_batch(0, bt);
+    for (int j0 = 64; j0 < M; j0 += 64) {
       load_batch(j0, bt);
       score_batch(j0, bt);
     }
-    __syncthreads();
     // log-sum-exp over the M candidates (one wave)
     if (wv == 0) {
       double mx = -INFINITY;
