@@ -499,6 +499,7 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   t.cand_val = (float*)(ws + L.cand_val);
   t.zh = (double*)(ws + L.zh);
   t.states = (double*)(ws + L.states);
+  t.gh = (double*)(ws + L.gh);
   t.heap_score = (double*)(ws + L.heap_score);
   t.heap_meta = (int4*)(ws + L.heap_meta);
   t.heap_count = (int32_t*)(ws + L.heap_count);

@@ -119,6 +119,7 @@ struct TreeArgs {
   double* zh;               // [B][P][r] W1[:, :d] H in fp64
   double* act;              // [B][r] bottleneck of the node being expanded, fp64
   double* states;           // [B][N+1][Hs] fp64 GRU state per node (slot 0 = anchor)
+  double* gh;               // [B][N+1][3][Hs] W_hh h of each node's state (one launch per round with the table)
   double* heap_score;       // [B][heap_cap]
   int4* heap_meta;          // [B][heap_cap] (parent, rank, token, depth)
   int32_t* heap_count;      // [B]
@@ -136,8 +137,8 @@ struct TreeArgs {
 };
 
 struct TreeLayout {
-  size_t status, seg_keys, cand_idx, cand_val, zh, act, states, heap_score, heap_meta, heap_count, cur, ll_act, ll_cur,
-      total;
+  size_t status, seg_keys, cand_idx, cand_val, zh, act, states, gh, heap_score, heap_meta, heap_count, cur, ll_act,
+      ll_cur, total;
   int heap_cap;
 };
 TreeLayout tree_layout(int d, int Hs, int r, int P, int group, int N, int M);

@@ -853,6 +853,122 @@ __device__ __forceinline__ void gru_mfma_step(const TreeArgs& t, int b0, int ite
   }
 }
 
+// The GRU step of round kr in the one-launch-per-round schedule with the
+// per-token table.  The hidden half does not depend on which node is popped:
+// before the node arrives, the workgroup multiplies its units' W_hh rows by
+// the state of slot kr - 1 (written by the previous launch) for every
+// sequence of the group, the same MFMA blocks and wave order as
+// gru_mfma_step, and keeps the sums in t.gh, where every later round finds the
+// hidden half of any parent.  Once the node arrives, its finishing lanes read
+// the parent's hidden half, the table row of its token and the parent's own
+// units of the state, and apply the gates: the result has the bits of
+// gru_mfma_step's.
+__device__ __forceinline__ void gru_tab_ll_step(const TreeArgs& t, int b0, int item, int kr, uint32_t tag) {
+  __shared__ double red[kGruWaves][12][kTreeSeqs];  // [wave][gate row][sequence], hidden half
+  __shared__ int cur_s[kTreeSeqs][3];               // token, parent slot, expand
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int Hs = t.Hs;
+  const int nb = min(kTreeSeqs, t.B - b0);
+  const int j0 = item * 4;
+  const int rr = lane & 15, kq = lane >> 4;
+  const int g = rr < 12 ? rr >> 2 : 2, u = rr < 12 ? rr & 3 : 3;
+  const uint16_t* wh = (const uint16_t*)t.w_hh + ((size_t)g * Hs + min(j0 + u, Hs - 1)) * Hs;
+  const int sq = min(rr, nb - 1);
+  const int ps = kr - 1;  // the slot whose hidden half this launch adds to t.gh
+  const double* hr = t.states + ((size_t)(b0 + sq) * (t.N + 1) + ps) * Hs;
+  uint4 wph[kGruPreH];
+  F64x8 hp[kGruPreH];
+#pragma unroll
+  for (int q = 0; q < kGruPreH; ++q) {
+    const int k = min((wv + kGruWaves * q) * 32 + 8 * kq, Hs - 8);
+    wph[q] = *reinterpret_cast<const uint4*>(wh + k);
+    hp[q] = load_f64x8(hr + k);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f64x4 acc_h[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+#pragma unroll
+  for (int q = 0; q < kGruPreH; ++q) {
+    const bool ok = (wv + kGruWaves * q) * 32 + 8 * kq < Hs;
+    double w8[8];
+    bf16x8_to_f64(wph[q], w8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc_h[q & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w8[i], ok ? hp[q].v[i] : 0.0, acc_h[q & 1], 0, 0, 0);
+  }
+  constexpr int NB = 4;
+  const int nbh = (Hs + 31) / 32;
+  for (int bk = wv + kGruWaves * kGruPreH; bk < nbh; bk += kGruWaves * NB) {  // wider states
+    uint4 wr[NB];
+    F64x8 hv[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int k = min((bk + kGruWaves * q) * 32 + 8 * kq, Hs - 8);
+      wr[q] = *reinterpret_cast<const uint4*>(wh + k);
+      hv[q] = load_f64x8(hr + k);
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const bool ok = (bk + kGruWaves * q) * 32 + 8 * kq < Hs;
+      double w8[8];
+      bf16x8_to_f64(wr[q], w8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc_h[q & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(w8[i], ok ? hv[q].v[i] : 0.0, acc_h[q & 1], 0, 0, 0);
+    }
+  }
+  if (rr < kTreeSeqs) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) red[wv][4 * i + kq][rr] = acc_h[0][i] + acc_h[1][i];
+  }
+  __syncthreads();
+  const int fs = lane & 7, fu = (lane >> 3) & 3, j = j0 + fu;
+  const bool fin = threadIdx.x < 4 * kTreeSeqs && fs < nb && j < Hs;
+  double* ghp = t.gh + (size_t)(b0 + fs) * (t.N + 1) * 3 * Hs + j;
+  if (fin) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      double v = red[0][4 * q + fu][fs];
+#pragma unroll
+      for (int w = 1; w < kGruWaves; ++w) v += red[w][4 * q + fu][fs];
+      ghp[((size_t)ps * 3 + q) * Hs] = v;
+    }
+  }
+  // the node of round kr: the hand-off words of round kr - 1's pop
+  if (wv == 0) {
+    const uint64_t* src = t.ll_cur + ((size_t)(kr - 1) * t.B + b0 + min(lane, nb - 1)) * 2;
+    uint64_t w0 = 0, w1 = 0;
+    ll_wait(t.status, [&] {
+      w0 = ld_agent64(src);
+      w1 = ld_agent64(src + 1);
+      return (int)ll_ok(w0, tag) & (int)ll_ok(w1, tag);
+    });
+    if (lane < nb) {  // (clamped, so that words left by a timed-out wait stay in bounds)
+      const uint32_t v = ll_data(w1);
+      cur_s[lane][0] = (int)ll_data(w0);
+      cur_s[lane][1] = (int)min(v & 0xFFFFu, (uint32_t)kr) - 1;
+      cur_s[lane][2] = (int)((v >> 16) & 1u);
+    }
+  }
+  __syncthreads();
+  if (fin && cur_s[fs][2]) {
+    const int tok = min(max(cur_s[fs][0], 0), t.V - 1), par = cur_s[fs][1];
+    const double* q = t.xt + (size_t)tok * 3 * Hs + j;
+    double gi[3] = {q[0], q[Hs], q[2 * Hs]}, gh[3] = {0.0, 0.0, 0.0};
+    double hprev = 0.0;
+    if (par >= 0) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) gh[i] = ghp[((size_t)par * 3 + i) * Hs];
+      hprev = t.states[((size_t)(b0 + fs) * (t.N + 1) + par) * Hs + j];
+    }
+    auto bi = [&](int row) { return t.b_ih ? (double)t.b_ih[row] : 0.0; };
+    auto bh = [&](int row) { return t.b_hh ? (double)t.b_hh[row] : 0.0; };
+    const double r = 1.0 / (1.0 + exp(-(gi[0] + bi(j) + gh[0] + bh(j))));
+    const double z = 1.0 / (1.0 + exp(-(gi[1] + bi(Hs + j) + gh[1] + bh(Hs + j))));
+    const double nn = tanh(gi[2] + bi(2 * Hs + j) + r * (gh[2] + bh(2 * Hs + j)));
+    t.states[((size_t)(b0 + fs) * (t.N + 1) + kr) * Hs + j] = (1.0 - z) * nn + z * hprev;
+  }
+}
+
 template <bool kTab>
 __global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int b0, int k) {
   gru_mfma_step<kTab, false>(t, b0, blockIdx.x, k, 0u);
@@ -1224,7 +1340,10 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_round(TreeArgs t, int k) 
     score_pop<kGruWaves, true>(t, wg - nbt, k, tag);
   } else {
     const int g = wg - nbt - t.B, nu = (t.Hs + 3) / 4;
-    gru_mfma_step<kTab, true>(t, (g / nu) * kTreeSeqs, g - (g / nu) * nu, k + 1, tag);
+    if constexpr (kTab)
+      gru_tab_ll_step(t, (g / nu) * kTreeSeqs, g - (g / nu) * nu, k + 1, tag);
+    else
+      gru_mfma_step<false, true>(t, (g / nu) * kTreeSeqs, g - (g / nu) * nu, k + 1, tag);
   }
 }
 
@@ -1251,6 +1370,8 @@ TreeLayout tree_layout(int d, int Hs, int r, int P, int group, int N, int M) {
   off += al256((size_t)group * r * 8);
   L.states = off;
   off += al256((size_t)group * (N + 1) * Hs * 8);
+  L.gh = off;
+  off += al256((size_t)group * (N + 1) * 3 * Hs * 8);
   L.heap_cap = N * M;
   L.heap_score = off;
   off += al256((size_t)group * L.heap_cap * 8);
