@@ -231,10 +231,41 @@ __device__ __forceinline__ TreeCur* tree_cur(const TreeArgs& t, int k) {
   return reinterpret_cast<TreeCur*>(t.cur) + (size_t)(k & 1) * t.B;
 }
 
+// ---- reductions across the 64 lanes of a wave, without LDS ---------------------------------
+// The lanes of each row of 16 combine through DPP moves (swaps within quads,
+// then the mirrored halves of the row, then the mirrored row); the four row
+// results are read as uniform values and combined as (row 0 . row 1) .
+// (row 2 . row 3).  The operation is commutative and each step pairs lanes
+// symmetrically, so every lane ends with the same bits.
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_mov_dpp(v, kCtrl, 0xF, 0xF, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp_i32<kCtrl>((int)b), hi = dpp_i32<kCtrl>((int)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, l), hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
+template <class Op>
+__device__ __forceinline__ double wave_reduce(double v, Op op) {
+  v = op(v, dpp_f64<kDppQuadXor1>(v));
+  v = op(v, dpp_f64<kDppQuadXor2>(v));
+  v = op(v, dpp_f64<kDppRowHalfMirror>(v));
+  v = op(v, dpp_f64<kDppRowMirror>(v));
+  return op(op(readlane_f64(v, 0), readlane_f64(v, 16)), op(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  return wave_reduce(v, [](double x, double y) { return x + y; });
+}
+__device__ __forceinline__ double wave_max(double v) {
+  return wave_reduce(v, [](double x, double y) { return fmax(x, y); });
 }
 
 // 8 consecutive stored elements widened to fp64
@@ -1083,15 +1114,31 @@ __device__ __forceinline__ void best_offer(BestEntry& e, int slot, double s, int
   e.m.w = take ? m.w : e.m.w;
 }
 
-__device__ __forceinline__ void best_offer_lane(BestEntry& e, int src_lane_xor) {
+// the best entry of the wave, in every lane (the same pairing as wave_reduce;
+// the order is total over distinct entries, so the result is symmetric)
+template <int kCtrl>
+__device__ __forceinline__ void best_offer_dpp(BestEntry& e) {
+  best_offer(e, dpp_i32<kCtrl>(e.slot), dpp_f64<kCtrl>(e.s),
+             make_int4(dpp_i32<kCtrl>(e.m.x), dpp_i32<kCtrl>(e.m.y), dpp_i32<kCtrl>(e.m.z), dpp_i32<kCtrl>(e.m.w)));
+}
+__device__ __forceinline__ BestEntry best_readlane(const BestEntry& e, int l) {
   BestEntry o;
-  o.slot = __shfl_xor(e.slot, src_lane_xor);
-  o.s = __shfl_xor(e.s, src_lane_xor);
-  o.m.x = __shfl_xor(e.m.x, src_lane_xor);
-  o.m.y = __shfl_xor(e.m.y, src_lane_xor);
-  o.m.z = __shfl_xor(e.m.z, src_lane_xor);
-  o.m.w = __shfl_xor(e.m.w, src_lane_xor);
-  best_offer(e, o.slot, o.s, o.m);
+  o.slot = __builtin_amdgcn_readlane(e.slot, l);
+  o.s = readlane_f64(e.s, l);
+  o.m = make_int4(__builtin_amdgcn_readlane(e.m.x, l), __builtin_amdgcn_readlane(e.m.y, l),
+                  __builtin_amdgcn_readlane(e.m.z, l), __builtin_amdgcn_readlane(e.m.w, l));
+  return o;
+}
+__device__ __forceinline__ BestEntry wave_best(BestEntry e) {
+  best_offer_dpp<kDppQuadXor1>(e);
+  best_offer_dpp<kDppQuadXor2>(e);
+  best_offer_dpp<kDppRowHalfMirror>(e);
+  best_offer_dpp<kDppRowMirror>(e);
+  BestEntry a = best_readlane(e, 0), b = best_readlane(e, 16), c = best_readlane(e, 32), d = best_readlane(e, 48);
+  best_offer(a, b.slot, b.s, b.m);
+  best_offer(c, d.slot, d.s, d.m);
+  best_offer(a, c.slot, c.s, c.m);
+  return a;
 }
 
 // Round k of sequence b: score the current node's M children, push them, pop
@@ -1181,23 +1228,24 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
         }
       }
     };
+    // runs past the wave's range take zero weights (selects, no branches, so
+    // that every LDS read can go out at once); a[] is zero past r
     auto score_batch = [&](int j0, const Batch& bt) {
       double sdot = 0.0;
 #pragma unroll
       for (int q = 0; q < KQ; ++q) {
-        if (kb + 8 * q < ke) {
-          double w[8];
-          if (t.dtype == kBF16) {
-            bf16x8_to_f64(bt.w[q], w);
-          } else {
-            const uint4 u0 = bt.w[2 * q], u1 = bt.w[2 * q + 1];
-            w[0] = __uint_as_float(u0.x), w[1] = __uint_as_float(u0.y), w[2] = __uint_as_float(u0.z);
-            w[3] = __uint_as_float(u0.w), w[4] = __uint_as_float(u1.x), w[5] = __uint_as_float(u1.y);
-            w[6] = __uint_as_float(u1.z), w[7] = __uint_as_float(u1.w);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sdot += w[e] * a[kb + 8 * q + e];
+        const bool in = kb + 8 * q < ke;
+        double w[8];
+        if (t.dtype == kBF16) {
+          bf16x8_to_f64(bt.w[q], w);
+        } else {
+          const uint4 u0 = bt.w[2 * q], u1 = bt.w[2 * q + 1];
+          w[0] = __uint_as_float(u0.x), w[1] = __uint_as_float(u0.y), w[2] = __uint_as_float(u0.z);
+          w[3] = __uint_as_float(u0.w), w[4] = __uint_as_float(u1.x), w[5] = __uint_as_float(u1.y);
+          w[6] = __uint_as_float(u1.z), w[7] = __uint_as_float(u1.w);
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sdot += (in ? w[e] : 0.0) * a[min(kb + 8 * q + e, 255)];
       }
       part[wv][lane] = sdot;
       __syncthreads();
@@ -1224,7 +1272,7 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
       });
       av = __longlong_as_double((long long)(((uint64_t)ll_data(w1) << 32) | ll_data(w0)));
     }
-    if (tid < r) a[tid] = av;
+    if (tid < 256) a[tid] = tid < r ? av : 0.0;
     __syncthreads();
     score_batch(0, bt);
     for (int j0 = 64; j0 < M; j0 += 64) {
@@ -1235,8 +1283,7 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
     if (wv == 0) {
       double mx = -INFINITY;
       for (int j = lane; j < M; j += 64) mx = fmax(mx, l[j]);
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m));
+      mx = wave_max(mx);
       double se = 0.0;
       for (int j = lane; j < M; j += 64) se += exp(l[j] - mx);
       se = wave_sum(se);
@@ -1260,8 +1307,7 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
 
   // pop: best entry under (score desc, parent asc, rank asc): within each
   // wave by shuffles, then over the waves
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) best_offer_lane(best, m);
+  best = wave_best(best);
   if (lane == 0) wbest[wv] = best;
   __syncthreads();
   if (tid == 0) {
