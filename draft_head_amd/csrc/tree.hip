@@ -1141,6 +1141,69 @@ __device__ __forceinline__ BestEntry wave_best(BestEntry e) {
   return a;
 }
 
+// 64 candidates, one per lane: the W2 run [kb, kb + 8 KQ) of this lane's
+// candidate row, as stored, with its id, base value and bias.  score() adds the
+// wave's partial dot products over [kb, ke) (runs past ke take zero weights:
+// selects, no branches, so every LDS read can go out at once; a[] is zero
+// past r) and lets wave 0 sum the waves' partials in wave order.
+template <class W, int KQ>
+struct ScoreBatch {
+  uint4 w[KQ * sizeof(W) / 2];  // 8 bf16 per uint4, or 4 floats
+  int v;
+  float cv, bf;
+  __device__ __forceinline__ void load(const TreeArgs& t, const int32_t* cidx, const float* cval, int j0, int M,
+                                       int kb) {
+    const int lane = threadIdx.x & 63, r = t.r;
+    const int j = min(j0 + lane, M - 1);
+    v = cidx[j];
+    cv = cval[j];
+    const W* row = reinterpret_cast<const W*>(t.w2) + (size_t)v * r;
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      const W* p = row + min(kb + 8 * q, r - 8);
+      if constexpr (sizeof(W) == 2) {
+        w[q] = *reinterpret_cast<const uint4*>(p);
+      } else {
+        w[2 * q] = *reinterpret_cast<const uint4*>(p);
+        w[2 * q + 1] = *reinterpret_cast<const uint4*>(p + 4);
+      }
+    }
+    bf = t.b2 ? t.b2[v] : 0.f;
+  }
+  template <int NWV>
+  __device__ __forceinline__ void score(const double* a, double (*part)[64], double* l, int* lid, int j0, int M,
+                                        int kb, int ke) const {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    double sdot = 0.0;
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      const bool in = kb + 8 * q < ke;
+      double x[8];
+      if constexpr (sizeof(W) == 2) {
+        bf16x8_to_f64(w[q], x);
+      } else {
+        const uint4 u0 = w[2 * q], u1 = w[2 * q + 1];
+        x[0] = __uint_as_float(u0.x), x[1] = __uint_as_float(u0.y), x[2] = __uint_as_float(u0.z);
+        x[3] = __uint_as_float(u0.w), x[4] = __uint_as_float(u1.x), x[5] = __uint_as_float(u1.y);
+        x[6] = __uint_as_float(u1.z), x[7] = __uint_as_float(u1.w);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sdot += (in ? x[e] : 0.0) * a[min(kb + 8 * q + e, 255)];
+    }
+    part[wv][lane] = sdot;
+    __syncthreads();
+    const int j = j0 + lane;
+    if (wv == 0 && j < M) {
+      double tot = part[0][lane];
+#pragma unroll
+      for (int u = 1; u < NWV; ++u) tot += part[u][lane];
+      l[j] = (double)cv + (double)bf + tot;
+      lid[j] = v;
+    }
+    __syncthreads();  // part is reused by the next group
+  }
+};
+
 // Round k of sequence b: score the current node's M children, push them, pop
 // the best entry; one workgroup of NWV waves.  Wave w scores candidates w,
 // w + NWV, ...: lanes split the bottleneck in runs of 4 and the partial dot
@@ -1148,7 +1211,7 @@ __device__ __forceinline__ BestEntry wave_best(BestEntry e) {
 // bottleneck arrives as round k's hand-off words, and the popped node also
 // goes out as hand-off words (tag) for the GRU step of round k + 1 in the same
 // launch; the first batch of candidate rows is read before the bottleneck.
-template <int NWV, bool kLL>
+template <class W, int NWV, bool kLL>
 __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint32_t tag) {
   __shared__ double a[256];     // bottleneck (r <= 256)
   __shared__ double l[256];     // corrected candidate logits (M <= 256)
@@ -1205,62 +1268,8 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
     constexpr int KQ = 256 / NWV / 8;  // runs of 8 k values per lane and wave (r <= 256)
     const int kc = ((r + NWV - 1) / NWV + 7) & ~7;
     const int kb = min(wv * kc, r), ke = min(kb + kc, r);
-    struct Batch {
-      uint4 w[2 * KQ];  // bf16: w[0..KQ) hold 8 values each; fp32: two per run
-      int v;
-      float cv, bf;
-    };
-    auto load_batch = [&](int j0, Batch& bt) {
-      const int j = min(j0 + lane, M - 1);
-      bt.v = cidx[j];
-      bt.cv = cval[j];
-      bt.bf = t.b2 ? t.b2[bt.v] : 0.f;
-      if (t.dtype == kBF16) {
-        const uint16_t* row = (const uint16_t*)t.w2 + (size_t)bt.v * r;
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) bt.w[q] = *reinterpret_cast<const uint4*>(row + min(kb + 8 * q, r - 8));
-      } else {
-        const float* row = (const float*)t.w2 + (size_t)bt.v * r;
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-          bt.w[2 * q] = *reinterpret_cast<const uint4*>(row + min(kb + 8 * q, r - 8));
-          bt.w[2 * q + 1] = *reinterpret_cast<const uint4*>(row + min(kb + 8 * q, r - 8) + 4);
-        }
-      }
-    };
-    // runs past the wave's range take zero weights (selects, no branches, so
-    // that every LDS read can go out at once); a[] is zero past r
-    auto score_batch = [&](int j0, const Batch& bt) {
-      double sdot = 0.0;
-#pragma unroll
-      for (int q = 0; q < KQ; ++q) {
-        const bool in = kb + 8 * q < ke;
-        double w[8];
-        if (t.dtype == kBF16) {
-          bf16x8_to_f64(bt.w[q], w);
-        } else {
-          const uint4 u0 = bt.w[2 * q], u1 = bt.w[2 * q + 1];
-          w[0] = __uint_as_float(u0.x), w[1] = __uint_as_float(u0.y), w[2] = __uint_as_float(u0.z);
-          w[3] = __uint_as_float(u0.w), w[4] = __uint_as_float(u1.x), w[5] = __uint_as_float(u1.y);
-          w[6] = __uint_as_float(u1.z), w[7] = __uint_as_float(u1.w);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sdot += (in ? w[e] : 0.0) * a[min(kb + 8 * q + e, 255)];
-      }
-      part[wv][lane] = sdot;
-      __syncthreads();
-      const int j = j0 + lane;
-      if (wv == 0 && j < M) {
-        double tot = part[0][lane];
-#pragma unroll
-        for (int w = 1; w < NWV; ++w) tot += part[w][lane];
-        l[j] = (double)bt.cv + (double)bt.bf + tot;
-        lid[j] = bt.v;
-      }
-      __syncthreads();  // part is reused by the next group
-    };
-    Batch bt;
-    load_batch(0, bt);
+    ScoreBatch<W, KQ> bt;
+    bt.load(t, cidx, cval, 0, M, kb);
     if constexpr (kLL) {
       // the bottleneck of round k, one fp64 value (two words) per thread
       const uint64_t* src = t.ll_act + (((size_t)k * t.B + b) * r + min(tid, r - 1)) * 2;
@@ -1274,10 +1283,10 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
     }
     if (tid < 256) a[tid] = tid < r ? av : 0.0;
     __syncthreads();
-    score_batch(0, bt);
+    bt.template score<NWV>(a, part, l, lid, 0, M, kb, ke);
     for (int j0 = 64; j0 < M; j0 += 64) {
-      load_batch(j0, bt);
-      score_batch(j0, bt);
+      bt.load(t, cidx, cval, j0, M, kb);
+      bt.template score<NWV>(a, part, l, lid, j0, M, kb, ke);
     }
     // log-sum-exp over the M candidates (one wave)
     if (wv == 0) {
@@ -1363,7 +1372,10 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
   }
 }
 
-__global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) { score_pop<4, false>(t, blockIdx.x, k, 0u); }
+template <class W>
+__global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
+  score_pop<W, 4, false>(t, blockIdx.x, k, 0u);
+}
 
 // ---- one launch per round (bf16 weights) ------------------------------------------------------
 // Launch k runs round k's bottleneck, its score and pop, and the GRU step of
@@ -1383,7 +1395,7 @@ __global__ __launch_bounds__(64 * kGruWaves) void tree_round(TreeArgs t, int k) 
     const int b = wg / nr;
     bottleneck_rows<uint16_t, true>(t, b, (wg - b * nr) * 32 + (threadIdx.x >> 6) * 4, k, tag);
   } else if (wg < nbt + t.B) {
-    score_pop<kGruWaves, true>(t, wg - nbt, k, tag);
+    score_pop<uint16_t, kGruWaves, true>(t, wg - nbt, k, tag);
   } else {
     const int g = wg - nbt - t.B, nu = (t.Hs + 3) / 4;
     if constexpr (kTab)
@@ -1500,7 +1512,7 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
       for (int b0 = 0; b0 < t.B; b0 += kTreeSeqs)
         hipLaunchKernelGGL(tree_gru, dim3((t.Hs + 3) / 4), dim3(64 * 4 * (kTreeSeqs / kSeqPerWave)), lds, s, t, b0, k);
       hipLaunchKernelGGL(tree_bottleneck<float>, dim3((t.r + 15) / 16, t.B), dim3(256), 0, s, t, k);
-      hipLaunchKernelGGL(tree_score_pop, dim3(t.B), dim3(256), 0, s, t, k);
+      hipLaunchKernelGGL(tree_score_pop<float>, dim3(t.B), dim3(256), 0, s, t, k);
     }
   }
   e = hipGetLastError();
