@@ -1143,9 +1143,10 @@ __device__ __forceinline__ BestEntry wave_best(BestEntry e) {
 
 // 64 candidates, one per lane: the W2 run [kb, kb + 8 KQ) of this lane's
 // candidate row, as stored, with its id, base value and bias.  score() adds the
-// wave's partial dot products over [kb, ke) (runs past ke take zero weights:
-// selects, no branches, so every LDS read can go out at once; a[] is zero
-// past r) and lets wave 0 sum the waves' partials in wave order.
+// wave's partial dot products over [kb, ke), taking bottleneck value kb + i
+// from lane i of the wave (av; read as a uniform value, so no LDS is
+// involved; runs past ke take zero weights through selects), and lets wave 0
+// sum the waves' partials in wave order.
 template <class W, int KQ>
 struct ScoreBatch {
   uint4 w[KQ * sizeof(W) / 2];  // 8 bf16 per uint4, or 4 floats
@@ -1171,8 +1172,8 @@ struct ScoreBatch {
     bf = t.b2 ? t.b2[v] : 0.f;
   }
   template <int NWV>
-  __device__ __forceinline__ void score(const double* a, double (*part)[64], double* l, int* lid, int j0, int M,
-                                        int kb, int ke) const {
+  __device__ __forceinline__ void score(double av, double (*part)[64], double* l, int* lid, int j0, int M, int kb,
+                                        int ke) const {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     double sdot = 0.0;
 #pragma unroll
@@ -1188,7 +1189,7 @@ struct ScoreBatch {
         x[6] = __uint_as_float(u1.z), x[7] = __uint_as_float(u1.w);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sdot += (in ? x[e] : 0.0) * a[min(kb + 8 * q + e, 255)];
+      for (int e = 0; e < 8; ++e) sdot += (in ? x[e] : 0.0) * readlane_f64(av, 8 * q + e);
     }
     part[wv][lane] = sdot;
     __syncthreads();
@@ -1213,7 +1214,6 @@ struct ScoreBatch {
 // launch; the first batch of candidate rows is read before the bottleneck.
 template <class W, int NWV, bool kLL>
 __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint32_t tag) {
-  __shared__ double a[256];     // bottleneck (r <= 256)
   __shared__ double l[256];     // corrected candidate logits (M <= 256)
   __shared__ int lid[256];      // their token ids
   __shared__ double part[NWV][64];  // the waves' partial dot products of 64 candidates
@@ -1223,9 +1223,19 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
   __shared__ int4 last_m;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = t.r, M = t.M, P = t.P;
-  // the bottleneck does not depend on the cursor: its read goes out first
+  // the bottleneck does not depend on the cursor: its read goes out first.
+  // Candidates go 64 at a time, one per lane; wave w takes the k range
+  // [w kc, w kc + kc) of every candidate's W2 row (its reads go out before
+  // the bottleneck is needed) and the waves' partial dot products meet in
+  // LDS, added in wave order: no cross-lane reduction per candidate.  Lane i
+  // of wave w holds bottleneck value w kc + i (mod the KW lanes a range can
+  // span).
+  constexpr int KQ = 256 / NWV / 8, KW = 8 * KQ;  // runs of 8 k values per lane and wave (r <= 256)
+  const int kc = ((r + NWV - 1) / NWV + 7) & ~7;
+  const int kb = min(wv * kc, r), ke = min(kb + kc, r);
+  const int arow = min(kb + (lane & (KW - 1)), r - 1);
   double av = 0.0;
-  if constexpr (!kLL) av = t.act[(size_t)b * r + min(tid, r - 1)];
+  if constexpr (!kLL) av = t.act[(size_t)b * r + arow];
   const TreeCur c = tree_cur(t, k)[b];
   double* hs = t.heap_score + (size_t)b * t.heap_cap;
   int4* hm = t.heap_meta + (size_t)b * t.heap_cap;
@@ -1261,18 +1271,11 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
     const int delta = c.depth;
     const int32_t* cidx = t.cand_idx + ((size_t)b * P + delta) * M;
     const float* cval = t.cand_val + ((size_t)b * P + delta) * M;
-    // Candidates go 64 at a time, one per lane; wave w takes the k range
-    // [w kc, w kc + kc) of every candidate's W2 row (its reads go out before
-    // the bottleneck is needed) and the waves' partial dot products meet in
-    // LDS, added in wave order: no cross-lane reduction per candidate.
-    constexpr int KQ = 256 / NWV / 8;  // runs of 8 k values per lane and wave (r <= 256)
-    const int kc = ((r + NWV - 1) / NWV + 7) & ~7;
-    const int kb = min(wv * kc, r), ke = min(kb + kc, r);
     ScoreBatch<W, KQ> bt;
     bt.load(t, cidx, cval, 0, M, kb);
     if constexpr (kLL) {
       // the bottleneck of round k, one fp64 value (two words) per thread
-      const uint64_t* src = t.ll_act + (((size_t)k * t.B + b) * r + min(tid, r - 1)) * 2;
+      const uint64_t* src = t.ll_act + (((size_t)k * t.B + b) * r + arow) * 2;
       uint64_t w0 = 0, w1 = 0;
       ll_wait(t.status, [&] {
         w0 = ld_agent64(src);
@@ -1281,12 +1284,10 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
       });
       av = __longlong_as_double((long long)(((uint64_t)ll_data(w1) << 32) | ll_data(w0)));
     }
-    if (tid < 256) a[tid] = tid < r ? av : 0.0;
-    __syncthreads();
-    bt.template score<NWV>(a, part, l, lid, 0, M, kb, ke);
+    bt.template score<NWV>(av, part, l, lid, 0, M, kb, ke);
     for (int j0 = 64; j0 < M; j0 += 64) {
       bt.load(t, cidx, cval, j0, M, kb);
-      bt.template score<NWV>(a, part, l, lid, j0, M, kb, ke);
+      bt.template score<NWV>(av, part, l, lid, j0, M, kb, ke);
     }
     // log-sum-exp over the M candidates (one wave)
     if (wv == 0) {
