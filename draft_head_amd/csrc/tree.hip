@@ -906,6 +906,17 @@ __device__ __forceinline__ void gru_tab_ll_step(const TreeArgs& t, int b0, int i
   const uint16_t* wh = (const uint16_t*)t.w_hh + ((size_t)g * Hs + min(j0 + u, Hs - 1)) * Hs;
   const int sq = min(rr, nb - 1);
   const int ps = kr - 1;  // the slot whose hidden half this launch adds to t.gh
+  // Start once the bottleneck of the group's first sequence is out (when that
+  // node is expanded): the state reads below would otherwise share the memory
+  // system with the bottleneck's hand-off, which is on the round's critical
+  // path, while this work has until the popped node arrives (286 against
+  // 298 us per tree at batch 8).  A matter of timing only: nothing read here
+  // depends on it.
+  if (threadIdx.x == 0 && tree_cur(t, kr - 1)[b0].expand) {
+    const uint64_t* w = t.ll_act + (((size_t)(kr - 1) * t.B + b0) * t.r + t.r - 1) * 2;
+    ll_wait<4>(t.status, [&] { return (int)ll_ok(ld_agent64(w), tag); });
+  }
+  __syncthreads();
   const double* hr = t.states + ((size_t)(b0 + sq) * (t.N + 1) + ps) * Hs;
   uint4 wph[kGruPreH];
   F64x8 hp[kGruPreH];
