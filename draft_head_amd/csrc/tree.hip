@@ -1337,22 +1337,30 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
     for (int w = 1; w < NWV; ++w) best_offer(e, wbest[w].slot, wbest[w].s, wbest[w].m);
     const size_t o = (size_t)b * t.N + k;
     const int bi = e.slot;
+    const double s = e.s;
+    const int4 m = e.m;
     TreeCur n;
-    n.expand = 0;
     n.slot = k + 1;
-    n.parent_slot = -1;
-    n.token = 0;
-    n.depth = 0;
     n.node = k;
-    n.score = 0.0;
+    n.expand = bi >= 0 && m.w < P && k + 1 < t.N ? 1 : 0;
+    n.parent_slot = bi >= 0 ? m.x + 1 : -1;  // node index -> state slot; the anchor's slot is 0
+    n.token = bi >= 0 ? m.z : 0;
+    n.depth = bi >= 0 ? m.w : 0;
+    n.score = bi >= 0 ? s : 0.0;
+    // the next round's GRU step waits for the popped node: it goes out first
+    if constexpr (kLL) {
+      if (k + 1 < t.N) {
+        uint64_t* w = t.ll_cur + ((size_t)k * t.B + b) * 2;
+        ll_put(w, (uint32_t)n.token, tag);
+        ll_put(w + 1, (uint32_t)(n.parent_slot + 1) | ((uint32_t)n.expand << 16), tag);
+      }
+    }
     if (bi < 0) {
       t.out_parents[o] = -1;
       t.out_tokens[o] = -1;
       if (t.out_depth) t.out_depth[o] = 0;
       if (t.out_scores) t.out_scores[o] = -INFINITY;
     } else {
-      const double s = e.s;
-      const int4 m = e.m;
       t.out_parents[o] = m.x;
       t.out_tokens[o] = m.z;
       if (t.out_depth) t.out_depth[o] = m.w;
@@ -1366,21 +1374,9 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
         hm[bi] = tail_m;
       }
       count -= 1;
-      n.expand = (m.w < P && k + 1 < t.N) ? 1 : 0;
-      n.parent_slot = m.x + 1;  // node index -> state slot; the anchor's slot is 0
-      n.token = m.z;
-      n.depth = m.w;
-      n.score = s;
     }
     t.heap_count[b] = count;
     tree_cur(t, k + 1)[b] = n;
-    if constexpr (kLL) {
-      if (k + 1 < t.N) {
-        uint64_t* w = t.ll_cur + ((size_t)k * t.B + b) * 2;
-        ll_put(w, (uint32_t)n.token, tag);
-        ll_put(w + 1, (uint32_t)(n.parent_slot + 1) | ((uint32_t)n.expand << 16), tag);
-      }
-    }
   }
 }
 
