@@ -498,6 +498,7 @@ domino_status domino_tree_draft(const domino_dims* dims, const domino_weights* w
   t.cand_idx = (int32_t*)(ws + L.cand_idx);
   t.cand_val = (float*)(ws + L.cand_val);
   t.zh = (double*)(ws + L.zh);
+  t.zh_cur = (double*)(ws + L.zh_cur);
   t.states = (double*)(ws + L.states);
   t.gh = (double*)(ws + L.gh);
   t.heap_score = (double*)(ws + L.heap_score);

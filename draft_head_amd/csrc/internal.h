@@ -117,6 +117,7 @@ struct TreeArgs {
   int32_t* cand_idx;        // [B][P][M] top-M candidates per row
   float* cand_val;          // [B][P][M]
   double* zh;               // [B][P][r] W1[:, :d] H in fp64
+  double* zh_cur;           // [B][r] the row of zh at the depth of the node each sequence expands next
   double* act;              // [B][r] bottleneck of the node being expanded, fp64
   double* states;           // [B][N+1][Hs] fp64 GRU state per node (slot 0 = anchor)
   double* gh;               // [B][N+1][3][Hs] W_hh h of each node's state (one launch per round with the table)
@@ -137,7 +138,7 @@ struct TreeArgs {
 };
 
 struct TreeLayout {
-  size_t status, seg_keys, cand_idx, cand_val, zh, act, states, gh, heap_score, heap_meta, heap_count, cur, ll_act,
+  size_t status, seg_keys, cand_idx, cand_val, zh, zh_cur, act, states, gh, heap_score, heap_meta, heap_count, cur, ll_act,
       ll_cur, total;
   int heap_cap;
 };

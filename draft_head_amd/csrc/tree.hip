@@ -426,7 +426,9 @@ __global__ void tree_init(TreeArgs t) {
     }
     if (threadIdx.x == 0) *t.epoch = (fresh ? 0u : epoch_in) + 1u;
   }
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < t.B * t.r) t.zh_cur[i] = t.zh[((size_t)(i / t.r) * t.P) * t.r + i % t.r];  // depth 0: the anchor
+  const int b = i;
   if (b >= t.B) return;
   t.heap_count[b] = 0;
   int32_t t0 = t.t0[b];
@@ -1028,21 +1030,22 @@ __device__ __forceinline__ void bottleneck_rows(const TreeArgs& t, int b, int k0
   const int Hs = t.Hs, r = t.r;
   const size_t ld = (size_t)t.d + Hs;
   const W* w1s = reinterpret_cast<const W*>(t.w1) + t.d;  // state half of W1
-  // the weights do not depend on the tree: their reads go out before the cursor's
+  // Nothing here reads the cursor: the node expanded in round kr has state
+  // slot kr, and the previous pop (or tree_init) left the H half of its depth
+  // in zh_cur.  A sequence whose node is not expanded gets values that no
+  // one reads.
   Run8<W> wr[U][4];
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int q = 0; q < 4; ++q) wr[u][q].load(w1s + (size_t)min(k0 + q, r - 1) * ld + min(lane * 8 + 512 * u, Hs - 8));
-  const TreeCur c = tree_cur(t, kr)[b];
-  if (!c.expand) return;
-  const double* st = t.states + ((size_t)b * (t.N + 1) + c.slot) * Hs;
+  const double* st = t.states + ((size_t)b * (t.N + 1) + kr) * Hs;
   F64x8 sv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) sv[u] = load_f64x8(st + min(lane * 8 + 512 * u, Hs - 8));
   // lane q < 4 finishes row k0 + q: its W1_H half and bias
   const int kq = min(k0 + (lane & 3), r - 1);
-  const double zq = t.zh[((size_t)b * t.P + c.depth) * r + kq];
+  const double zq = t.zh_cur[(size_t)b * r + kq];
   const double bq = t.b1 ? (double)t.b1[kq] : 0.0;
   __builtin_amdgcn_sched_barrier(0);
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
@@ -1232,6 +1235,7 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
   __shared__ BestEntry wbest[NWV];
   __shared__ double last_s;     // the last entry pushed
   __shared__ int4 last_m;
+  __shared__ int next_depth;    // depth of the node the next round expands, or -1
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = t.r, M = t.M, P = t.P;
   // the bottleneck does not depend on the cursor: its read goes out first.
@@ -1377,7 +1381,13 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
     }
     t.heap_count[b] = count;
     tree_cur(t, k + 1)[b] = n;
+    next_depth = n.expand ? n.depth : -1;
   }
+  // the H half at the depth of the node the next round expands, for its bottleneck
+  __syncthreads();
+  const int nd = next_depth;
+  if (nd >= 0)
+    for (int i = tid; i < r; i += blockDim.x) t.zh_cur[(size_t)b * r + i] = t.zh[((size_t)b * P + nd) * r + i];
 }
 
 template <class W>
@@ -1432,6 +1442,8 @@ TreeLayout tree_layout(int d, int Hs, int r, int P, int group, int N, int M) {
   off += al256((size_t)group * P * M * 4);
   L.zh = off;
   off += al256((size_t)group * P * r * 8);
+  L.zh_cur = off;
+  off += al256((size_t)group * r * 8);
   L.act = off;
   off += al256((size_t)group * r * 8);
   L.states = off;
@@ -1488,7 +1500,7 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
     hipLaunchKernelGGL(tree_zh<uint16_t>, zh_grid, dim3(64 * kZhWaves), 0, s, t);
   else
     hipLaunchKernelGGL(tree_zh<float>, zh_grid, dim3(64 * kZhWaves), 0, s, t);
-  hipLaunchKernelGGL(tree_init, dim3((t.B + 255) / 256), dim3(256), 0, s, t);
+  hipLaunchKernelGGL(tree_init, dim3((t.B * t.r + 255) / 256), dim3(256), 0, s, t);
   // bf16 weights: the GRU step on the fp64 matrix cores (static LDS only)
   const bool mfma = t.dtype == kBF16;
   const size_t lds = mfma ? 0 : tree_gru_lds(t.d, t.Hs, t.dtype);
