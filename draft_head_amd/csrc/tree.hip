@@ -1185,9 +1185,8 @@ struct ScoreBatch {
     }
     bf = t.b2 ? t.b2[v] : 0.f;
   }
-  template <int NWV>
-  __device__ __forceinline__ void score(double av, double (*part)[64], double* l, int* lid, int j0, int M, int kb,
-                                        int ke) const {
+  // this wave's partial dot product of the lane's candidate, into part[wv][lane]
+  __device__ __forceinline__ void partial(double av, double (*part)[64], int kb, int ke) const {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     double sdot = 0.0;
 #pragma unroll
@@ -1206,16 +1205,15 @@ struct ScoreBatch {
       for (int e = 0; e < 8; ++e) sdot += (in ? x[e] : 0.0) * readlane_f64(av, 8 * q + e);
     }
     part[wv][lane] = sdot;
-    __syncthreads();
-    const int j = j0 + lane;
-    if (wv == 0 && j < M) {
-      double tot = part[0][lane];
+  }
+  // after a barrier: the corrected logit of the lane's candidate (wave 0)
+  template <int NWV>
+  __device__ __forceinline__ double logit(const double (*part)[64]) const {
+    const int lane = threadIdx.x & 63;
+    double tot = part[0][lane];
 #pragma unroll
-      for (int u = 1; u < NWV; ++u) tot += part[u][lane];
-      l[j] = (double)cv + (double)bf + tot;
-      lid[j] = v;
-    }
-    __syncthreads();  // part is reused by the next group
+    for (int u = 1; u < NWV; ++u) tot += part[u][lane];
+    return (double)cv + (double)bf + tot;
   }
 };
 
@@ -1299,32 +1297,64 @@ __device__ __forceinline__ void score_pop(const TreeArgs& t, int b, int k, uint3
       });
       av = __longlong_as_double((long long)(((uint64_t)ll_data(w1) << 32) | ll_data(w0)));
     }
-    bt.template score<NWV>(av, part, l, lid, 0, M, kb, ke);
-    for (int j0 = 64; j0 < M; j0 += 64) {
-      bt.load(t, cidx, cval, j0, M, kb);
-      bt.template score<NWV>(av, part, l, lid, j0, M, kb, ke);
-    }
-    // log-sum-exp over the M candidates (one wave)
-    if (wv == 0) {
-      double mx = -INFINITY;
-      for (int j = lane; j < M; j += 64) mx = fmax(mx, l[j]);
-      mx = wave_max(mx);
-      double se = 0.0;
-      for (int j = lane; j < M; j += 64) se += exp(l[j] - mx);
-      se = wave_sum(se);
-      if (lane == 0) lse_s = mx + log(se);
-    }
+    bt.partial(av, part, kb, ke);
     __syncthreads();
-    const double lse = lse_s;
-    for (int j = tid; j < M; j += blockDim.x) {
-      const double sj = c.score + (l[j] - lse);
-      const int4 mj = make_int4(c.node, j, lid[j], delta + 1);
-      hs[count + j] = sj;
-      hm[count + j] = mj;
-      best_offer(best, count + j, sj, mj);
-      if (j == M - 1) {
-        last_s = sj;
-        last_m = mj;
+    if (M <= 64) {
+      // one group: wave 0 finishes in registers (log-sum-exp over the M
+      // candidates, the children's scores, their push) while the other waves
+      // go on to the pop with their heap entries
+      if (wv == 0) {
+        const bool valid = lane < M;
+        const double lj = bt.template logit<NWV>(part);
+        const double mx = wave_max(valid ? lj : -INFINITY);
+        const double se = wave_sum(valid ? exp(lj - mx) : 0.0);
+        const double sj = c.score + (lj - (mx + log(se)));
+        const int4 mj = make_int4(c.node, lane, bt.v, delta + 1);
+        if (valid) {
+          hs[count + lane] = sj;
+          hm[count + lane] = mj;
+          best_offer(best, count + lane, sj, mj);
+        }
+        if (lane == M - 1) {
+          last_s = sj;
+          last_m = mj;
+        }
+      }
+    } else {
+      for (int j0 = 0;;) {
+        if (wv == 0 && j0 + lane < M) {
+          l[j0 + lane] = bt.template logit<NWV>(part);
+          lid[j0 + lane] = bt.v;
+        }
+        __syncthreads();  // part is reused by the next group
+        j0 += 64;
+        if (j0 >= M) break;
+        bt.load(t, cidx, cval, j0, M, kb);
+        bt.partial(av, part, kb, ke);
+        __syncthreads();
+      }
+      // log-sum-exp over the M candidates (one wave)
+      if (wv == 0) {
+        double mx = -INFINITY;
+        for (int j = lane; j < M; j += 64) mx = fmax(mx, l[j]);
+        mx = wave_max(mx);
+        double se = 0.0;
+        for (int j = lane; j < M; j += 64) se += exp(l[j] - mx);
+        se = wave_sum(se);
+        if (lane == 0) lse_s = mx + log(se);
+      }
+      __syncthreads();
+      const double lse = lse_s;
+      for (int j = tid; j < M; j += blockDim.x) {
+        const double sj = c.score + (l[j] - lse);
+        const int4 mj = make_int4(c.node, j, lid[j], delta + 1);
+        hs[count + j] = sj;
+        hm[count + j] = mj;
+        best_offer(best, count + j, sj, mj);
+        if (j == M - 1) {
+          last_s = sj;
+          last_m = mj;
+        }
       }
     }
     count += M;
