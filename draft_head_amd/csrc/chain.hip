@@ -741,13 +741,14 @@ __device__ __forceinline__ BottleneckPre bottleneck_pre(const ChainArgs& a, int 
 template <class W, int NCB, bool kLdsW, bool kLL = false, int NWV = 4, bool kOutLL = kLL>
 __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int item, float* red, const W* w1_lds,
                                 const BottleneckPre& pre_terms, uint32_t ep = 0, uint32_t* h_s = nullptr,
-                                int seq0 = 0) {
+                                int seq0 = 0, int seq_end = kMaxChainGroup) {
   static_assert(NWV == 4 || NWV == 8 || NWV == 16, "four, eight or sixteen waves");
   static_assert(!kLL || kOutLL, "hand-off words in, hand-off words out");
   constexpr int NC = 16 / NWV;  // chains per wave: wv, wv + NWV, ...
   const int lane = opaque_lane(), wv = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int Hs = a.Hs, B = a.B, r = a.r;
+  const int bend = min(B, seq_end);  // columns from seq_end on are left out
   const int k0 = item * 16;
   const W* rw;
   if constexpr (kLdsW)
@@ -759,7 +760,7 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int b = seq0 + cb * 16 + row;
-    bok[cb] = b < B;
+    bok[cb] = b < bend;
     bb[cb] = bok[cb] ? b : 0;
   }
   f32x4 acc[NC][NCB];
@@ -842,7 +843,7 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
       pre[3] += v.w;
     }
     const int b = seq0 + cb * 16 + row, k = k0 + kg * 4;
-    if (b < B && k < r) {  // r is a multiple of 8, so k..k+3 are all valid
+    if (b < bend && k < r) {  // r is a multiple of 8, so k..k+3 are all valid
       float s[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = pre[i] / (1.f + expf(-pre[i]));
@@ -1766,11 +1767,12 @@ __global__ __launch_bounds__(1024) void chain_gru16_k(ChainArgs a, int p) {
 
 template <class W, int NCB>
 // (blockIdx.y: the block of 16 NCB sequences)
-__global__ __launch_bounds__(256) void chain_bottleneck_k(ChainArgs a, int p) {
+__global__ __launch_bounds__(256) void chain_bottleneck_k(ChainArgs a, int p, int seqs) {
   __shared__ __attribute__((aligned(16))) float red[4 * NCB * 64 * 4];
-  const int seq0 = blockIdx.y * 16 * NCB;
+  const int seq0 = blockIdx.y * seqs;
   for (int it = blockIdx.x; it < (a.r + 15) / 16; it += gridDim.x)
-    bottleneck_item<W, NCB, false>(a, p, it, red, nullptr, bottleneck_pre<NCB>(a, p, it, seq0), 0u, nullptr, seq0);
+    bottleneck_item<W, NCB, false>(a, p, it, red, nullptr, bottleneck_pre<NCB>(a, p, it, seq0), 0u, nullptr, seq0,
+                                   seq0 + seqs);
 }
 
 template <class W, int RG, int KC, bool kSample>
@@ -2215,15 +2217,16 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
       else
         hipLaunchKernelGGL((chain_wo_k<W, RG, KC, NWV, false>), dim3(nWO), dim3(64 * NWV), 0, s, a, p);
     } else if constexpr (sizeof(W) == 2) {  // bf16: many light waves per CU
-      // one workgroup per 16 rows and 16 sequences: more CUs share the state reads
-      hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 15) / 16), dim3(256), 0, s, a, p);
+      // one workgroup per 16 rows and 8 sequences (half of each MFMA's columns
+      // left out): twice the CUs share the state reads, which bound this launch
+      hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 7) / 8), dim3(256), 0, s, a, p, 8);
       if (sample)
         hipLaunchKernelGGL((chain_logits_wide_k<W, RG, KC, NWV, true>), dim3(nO), dim3(64 * NWV), 0, s, a, p);
       else
         hipLaunchKernelGGL((chain_logits_wide_k<W, RG, KC, NWV, false>), dim3(nO), dim3(64 * NWV), 0, s, a, p);
     } else {
       // one workgroup per 16 rows and 16 sequences: more CUs share the state reads
-      hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 15) / 16), dim3(256), 0, s, a, p);
+      hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 15) / 16), dim3(256), 0, s, a, p, 16);
       if (sample)
         hipLaunchKernelGGL((chain_logits_k<W, RG, KC, true>), dim3(nO), dim3(256), 0, s, a, p);
       else
