@@ -2217,9 +2217,11 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
       else
         hipLaunchKernelGGL((chain_wo_k<W, RG, KC, NWV, false>), dim3(nWO), dim3(64 * NWV), 0, s, a, p);
     } else if constexpr (sizeof(W) == 2) {  // bf16: many light waves per CU
-      // one workgroup per 16 rows and 8 sequences (half of each MFMA's columns
-      // left out): twice the CUs share the state reads, which bound this launch
-      hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 7) / 8), dim3(256), 0, s, a, p, 8);
+      // one workgroup per 16 rows and 4 sequences (most of each MFMA's columns
+      // left out): more CUs share the state reads, which bound this launch
+      // (batch 32: 604 us per block with 16 sequences a workgroup, 593 with
+      // 8, 587 with 4)
+      hipLaunchKernelGGL((chain_bottleneck_k<W, 1>), dim3(nW, (a.B + 3) / 4), dim3(256), 0, s, a, p, 4);
       if (sample)
         hipLaunchKernelGGL((chain_logits_wide_k<W, RG, KC, NWV, true>), dim3(nO), dim3(64 * NWV), 0, s, a, p);
       else
