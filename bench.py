@@ -340,7 +340,9 @@ def chain_schedule(wl):
     """Which schedule the library ran: the persistent one writes its step clocks."""
     import numpy as np
     if wl.cfg.tree:
-        return "tree: three launches per node", None
+        if wl.cfg.dtype == "bf16":
+            return "tree: one launch per round (bottleneck, score and pop, next GRU step)", None
+        return "tree: three launches per round", None
     dh, torch = wl.dh, wl.torch
     off = dh.domino_chain_stamp_offset(wl.head.dims, wl.B)
     n = wl.cfg.block + 1
