@@ -177,6 +177,11 @@ CHAIN_SHAPES = [
     (32, 64, 8, 8, 1, 1, "bf16"),
     (64, 2053, 32, 256, 5, 24, "bf16"),  # rank 256: whole-row phase O, ragged vocabulary and row groups
     (32, 1037, 16, 256, 3, 40, "bf16"),
+    # W1[:, :d] H split over k across workgroups (few tiles): 4 splits of 4
+    # chunks; 6 splits, the last of 2 chunks and a ragged k tail; fp32, 4 splits
+    (512, 1531, 64, 64, 4, 2, "bf16"),
+    (1000, 2003, 32, 256, 16, 3, "bf16"),
+    (520, 777, 16, 32, 2, 1, "f32"),
 ]
 
 
@@ -242,6 +247,31 @@ def test_chain_modes_agree_bitwise(B, r):
     assert s0 == s1 == s2 == 0
     assert np.array_equal(t0_, t1_) and np.array_equal(L0, L1)
     assert np.array_equal(t0_, t2_) and np.array_equal(L0, L2)
+
+
+# the H half split over k (B 1: 8 splits, B 3: 6, B 8: 2): the persistent
+# schedule adds the splits once per launch, the stepwise one where it reads
+# them, in the same order
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_chain_h_half_splits_agree_bitwise(B):
+    cfg = small_config(d=1000, V=1501, Hs=48, r=256, P=16, B=B, dtype="bf16", biases=True)
+    say(f"case chain H-half splits agree B={B}")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    prev = dh.set_chain_mode(0)
+    try:
+        head, _, t0_, L0, s0 = _run(cfg, w, inp)
+        dh.set_chain_mode(1)
+        _, _, t1_, L1, s1 = _run(cfg, w, inp, head=head)
+        dh.set_chain_mode(2)
+        _, _, t2_, L2, s2 = _run(cfg, w, inp, head=head)
+    finally:
+        dh.set_chain_mode(prev)
+    assert s0 == s1 == s2 == 0
+    assert np.array_equal(t0_, t1_) and np.array_equal(L0, L1)
+    assert np.array_equal(t0_, t2_) and np.array_equal(L0, L2)
+    m = oracle.Model.from_config(cfg, w)
+    say("  ", compare_chain(m, inp["H"], m.base_logits(inp["H"]), inp["t0"], t0_, L0, "H-half splits"))
 
 
 def test_chain_bad_first_token_flagged(chain_mode):
