@@ -53,6 +53,9 @@ def _compare(g, o, label):
     (3080, 1000, 1288, 64, 2, 3, 8, 16, "bf16"),  # GRU k blocks past the preloaded ones, ragged last block
     (64, 777, 24, 16, 3, 17, 12, 6, "bf16"),      # three GRU passes (sequences 16..)
     (128, 1500, 32, 256, 4, 3, 12, 16, "bf16"),   # the largest rank: full bottleneck vector in the pop
+    (32, 300, 8, 32, 3, 2, 64, 256, "bf16"),     # bf16 (one launch per round): four groups of 64 candidates
+    (64, 700, 16, 48, 4, 3, 20, 65, "bf16"),     # one candidate past a group of 64
+    (64, 500, 16, 16, 4, 2, 1, 8, "bf16"),       # a single round: no GRU step in the round's launch
 ])
 def test_tree_matches_oracle(d, V, Hs, r, P, B, N, M, dtype):
     cfg = small_config(d=d, V=V, Hs=Hs, r=r, P=P, B=B, dtype=dtype, biases=True)
@@ -65,6 +68,32 @@ def test_tree_matches_oracle(d, V, Hs, r, P, B, N, M, dtype):
     assert st == 0
     o = m.tree(inp["H"], Lb, inp["t0"], N, M)
     _compare(g, o, "small")
+
+
+def test_tree_workspace_reuse_and_layout_change():
+    """Calls on one workspace: the hand-off words of an earlier call (same
+    rounds, an older epoch) must never pass, and a call with another layout of
+    the same workspace clears them first."""
+    cfg = small_config(d=96, V=1201, Hs=32, r=64, P=6, B=5, dtype="bf16", biases=True)
+    say("case tree workspace reuse")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg)
+    m = oracle.Model.from_config(cfg, w)
+    Lb = m.base_logits(inp["H"])
+    head = dh.DraftHead.from_config(cfg, w)
+    H, L, t0 = head.upload(inp["H"]), head.upload(Lb), head.upload(inp["t0"])
+    ws = head.workspace(cfg.batch, dh.OP_TREE, 16, 12)
+    outs = []
+    for N, M, B in ((16, 12, 5), (16, 12, 5), (9, 12, 3), (16, 12, 5)):
+        out, _ = head.tree_draft(H[:B], L[:B], t0[:B], N, M, workspace=ws, check=False)
+        torch.cuda.synchronize()
+        assert dh.DraftHead.device_status(ws) == 0
+        g = {k: v.cpu().numpy() for k, v in out.items()}
+        o = m.tree(np.ascontiguousarray(inp["H"][:B]), np.ascontiguousarray(Lb[:B]), inp["t0"][:B], N, M)
+        _compare(g, o, f"reuse N={N} B={B}")
+        outs.append(g)
+    for k in ("parents", "tokens", "depth", "scores"):
+        assert np.array_equal(outs[0][k], outs[1][k]) and np.array_equal(outs[0][k], outs[3][k])
 
 
 def test_tree_single_candidate_and_zero_correction():
