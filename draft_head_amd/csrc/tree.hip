@@ -14,12 +14,15 @@
 //                   (value desc, index asc): a bound from the waves' maxima,
 //                   then a bitonic sort of the keys at or above it (a single
 //                   pass with a running threshold when too many pass)
-//  topm_merge       the row's top-M from its segment lists
-//  tree_zh          W1[:, :d] H for every position, fp64 matrix cores
-//  tree_init        empty heaps; the anchor as each sequence's first node
-//  per round (N rounds):
-//   tree_gru_mfma   fp64 GRU step of each sequence's current node (bf16
-//                   weights, matrix cores; tree_gru for fp32 weights)
+//  tree_prep        in one launch: the row's top-M from its segment lists
+//                   (topm_merge when T1 runs alone), W1[:, :d] H for every
+//                   position on the fp64 matrix cores, and the per-call set-up
+//                   (empty heaps; the anchor as each sequence's first node)
+//  bf16 weights: tree_gru_mfma (round 0's GRU step), then per round k one
+//   tree_round      round k's bottleneck, its score and pop, and round k+1's
+//                   GRU step, handing over through tagged words
+//  fp32 weights, per round:
+//   tree_gru        fp64 GRU step of each sequence's current node
 //   tree_bottleneck fp64 a = SiLU(W1 [H ; S] + b1) of those nodes
 //   tree_score_pop  score and push the node's M children, then pop the best entry
 #include <math.h>
@@ -198,9 +201,9 @@ __global__ __launch_bounds__(256) void topm_segment(const float* __restrict__ Lb
 }
 
 // merge the segment lists of one row into its top M
-__global__ __launch_bounds__(256) void topm_merge(const uint64_t* seg_keys, int M, int32_t* cand_idx, float* cand_val) {
+__device__ __forceinline__ void merge_row(const uint64_t* seg_keys, int M, int32_t* cand_idx, float* cand_val,
+                                          int row) {
   __shared__ uint64_t buf[kTopCap];
-  const int row = blockIdx.x;
   const uint64_t* src = seg_keys + (size_t)row * kTopSegs * M;
   int n = 64;  // the segment lists, padded to a power of two
   while (n < kTopSegs * M) n <<= 1;
@@ -212,6 +215,9 @@ __global__ __launch_bounds__(256) void topm_merge(const uint64_t* seg_keys, int 
     cand_idx[(size_t)row * M + j] = amax_index(k);
     cand_val[(size_t)row * M + j] = key_value(k);
   }
+}
+__global__ __launch_bounds__(256) void topm_merge(const uint64_t* seg_keys, int M, int32_t* cand_idx, float* cand_val) {
+  merge_row(seg_keys, M, cand_idx, cand_val, blockIdx.x);
 }
 
 // ---- per-sequence control state ---------------------------------------------------------
@@ -340,11 +346,11 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kZhWaves = 8, kZhPre = 10;
 
 template <class W>
-__global__ __launch_bounds__(64 * kZhWaves) void tree_zh(TreeArgs t) {
+__device__ __forceinline__ void zh_tile(const TreeArgs& t, int kx, int my) {
   __shared__ double red[kZhWaves][4][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int rr = lane & 15, kq = lane >> 4;
-  const int k0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+  const int k0 = kx * 16, m0 = my * 16;
   const int d = t.d, r = t.r, rows = t.B * t.P;
   const W* wrow = reinterpret_cast<const W*>(t.w1) + (size_t)min(k0 + rr, r - 1) * ((size_t)d + t.Hs);
   const W* hrow = reinterpret_cast<const W*>(t.H) + (size_t)min(m0 + rr, rows - 1) * d;
@@ -401,12 +407,13 @@ __global__ __launch_bounds__(64 * kZhWaves) void tree_zh(TreeArgs t) {
   }
 }
 
-// empty heaps; the anchor as each sequence's first node to expand.  Block 0
-// also advances the call counter that tags the hand-off words of the
-// one-launch-per-round schedule, after clearing those words on the first use
-// of this workspace layout (or before the counter would overflow the tags).
-__global__ void tree_init(TreeArgs t) {
-  if (blockIdx.x == 0) {
+// empty heaps; the anchor as each sequence's first node to expand (one
+// workgroup).  It also advances the call counter that tags the hand-off words
+// of the one-launch-per-round schedule, after clearing those words on the
+// first use of this workspace layout (or before the counter would overflow
+// the tags).
+__device__ __forceinline__ void tree_init(const TreeArgs& t) {
+  {
     __shared__ int fresh;
     __shared__ uint32_t epoch_in;
     if (threadIdx.x == 0) {
@@ -426,25 +433,48 @@ __global__ void tree_init(TreeArgs t) {
     }
     if (threadIdx.x == 0) *t.epoch = (fresh ? 0u : epoch_in) + 1u;
   }
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < t.B * t.r) t.zh_cur[i] = t.zh[((size_t)(i / t.r) * t.P) * t.r + i % t.r];  // depth 0: the anchor
-  const int b = i;
-  if (b >= t.B) return;
-  t.heap_count[b] = 0;
-  int32_t t0 = t.t0[b];
-  if (t0 < 0 || t0 >= t.V) {
-    atomicMax(t.status, 1);
-    t0 = 0;
+  for (int b = threadIdx.x; b < t.B; b += blockDim.x) {
+    t.heap_count[b] = 0;
+    int32_t t0 = t.t0[b];
+    if (t0 < 0 || t0 >= t.V) {
+      atomicMax(t.status, 1);
+      t0 = 0;
+    }
+    TreeCur c;
+    c.slot = 0;
+    c.parent_slot = -1;
+    c.token = t0;
+    c.depth = 0;
+    c.expand = t.P > 0 ? 1 : 0;
+    c.node = -1;
+    c.score = 0.0;
+    tree_cur(t, 0)[b] = c;
   }
-  TreeCur c;
-  c.slot = 0;
-  c.parent_slot = -1;
-  c.token = t0;
-  c.depth = 0;
-  c.expand = t.P > 0 ? 1 : 0;
-  c.node = -1;
-  c.score = 0.0;
-  tree_cur(t, 0)[b] = c;
+}
+
+// the H half at the anchor's depth (0) for round 0's bottleneck, by the first
+// workgroup of a round-0 GRU launch for its group of sequences
+__device__ __forceinline__ void zh_cur_anchor(const TreeArgs& t, int b0, int nb) {
+  for (int i = threadIdx.x; i < nb * t.r; i += blockDim.x) {
+    const int b = b0 + i / t.r, k = i % t.r;
+    t.zh_cur[(size_t)b * t.r + k] = t.zh[(size_t)b * t.P * t.r + k];
+  }
+}
+
+// After the top-M segments, in one launch: each row's merge of its segment
+// lists, the H half of the bottleneck in fp64 (tree_zh tiles) and the
+// per-call set-up, on workgroups of 8 waves (none depends on another).
+template <class W>
+__global__ __launch_bounds__(64 * kZhWaves) void tree_prep(TreeArgs t) {
+  const int rows = t.B * t.P, nzk = (t.r + 15) / 16, nzm = (rows + 15) / 16, wg = blockIdx.x;
+  if (wg < rows) {
+    merge_row(t.seg_keys, t.M, t.cand_idx, t.cand_val, wg);
+  } else if (wg < rows + nzk * nzm) {
+    const int z = wg - rows;
+    zh_tile<W>(t, z % nzk, z / nzk);
+  } else {
+    tree_init(t);
+  }
 }
 
 // ---- fp64 GRU step of each sequence's current node -----------------------------------------
@@ -468,6 +498,7 @@ __global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0, int k) {
   double* hl = reinterpret_cast<double*>(lds);                      // [kTreeSeqs][Hs]
   unsigned char* xl = lds + (size_t)kTreeSeqs * Hs * sizeof(double);  // [kTreeSeqs][d] stored type
   if (threadIdx.x < nb) sc[threadIdx.x] = tree_cur(t, k)[b0 + threadIdx.x];
+  if (k == 0 && blockIdx.x == 0) zh_cur_anchor(t, b0, nb);
   __syncthreads();
   // stage every sequence's parent state and embedding row: batches of kStage
   // 16-byte pieces per thread are loaded before any is stored, so their
@@ -755,6 +786,7 @@ __device__ __forceinline__ void gru_mfma_step(const TreeArgs& t, int b0, int ite
     c.score = 0.0;
   } else {
     c = tree_cur(t, kr)[b0 + sq];
+    if (kr == 0 && item == 0) zh_cur_anchor(t, b0, nb);
   }
   const bool has_h = c.expand && c.parent_slot >= 0;
   const uint16_t* xr = (const uint16_t*)t.embed + (size_t)min(max(c.token, 0), t.V - 1) * d;
@@ -1031,7 +1063,7 @@ __device__ __forceinline__ void bottleneck_rows(const TreeArgs& t, int b, int k0
   const size_t ld = (size_t)t.d + Hs;
   const W* w1s = reinterpret_cast<const W*>(t.w1) + t.d;  // state half of W1
   // Nothing here reads the cursor: the node expanded in round kr has state
-  // slot kr, and the previous pop (or tree_init) left the H half of its depth
+  // slot kr, and the previous pop (or round 0's GRU launch) left the H half of its depth
   // in zh_cur.  A sequence whose node is not expanded gets values that no
   // one reads.
   Run8<W> wr[U][4];
@@ -1523,14 +1555,13 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
   if (t.B <= 0) return hipSuccess;
   hipError_t e = hipSuccess;
   if (ev_start && ev_stop && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;
-  e = launch_topm_impl(t.Lb, t.B * t.P, t.V, t.M, t.seg_keys, t.cand_idx, t.cand_val, t.status, reset_status, s);
-  if (e != hipSuccess) return e;
-  const dim3 zh_grid((t.r + 15) / 16, (t.B * t.P + 15) / 16);
+  hipLaunchKernelGGL(topm_segment, dim3(kTopSegs, t.B * t.P), dim3(256), 0, s, t.Lb, t.V, t.M, t.seg_keys, t.status,
+                     reset_status ? 1 : 0);
+  const int prep = t.B * t.P + (t.r + 15) / 16 * ((t.B * t.P + 15) / 16) + 1;
   if (t.dtype == kBF16)
-    hipLaunchKernelGGL(tree_zh<uint16_t>, zh_grid, dim3(64 * kZhWaves), 0, s, t);
+    hipLaunchKernelGGL(tree_prep<uint16_t>, dim3(prep), dim3(64 * kZhWaves), 0, s, t);
   else
-    hipLaunchKernelGGL(tree_zh<float>, zh_grid, dim3(64 * kZhWaves), 0, s, t);
-  hipLaunchKernelGGL(tree_init, dim3((t.B * t.r + 255) / 256), dim3(256), 0, s, t);
+    hipLaunchKernelGGL(tree_prep<float>, dim3(prep), dim3(64 * kZhWaves), 0, s, t);
   // bf16 weights: the GRU step on the fp64 matrix cores (static LDS only)
   const bool mfma = t.dtype == kBF16;
   const size_t lds = mfma ? 0 : tree_gru_lds(t.d, t.Hs, t.dtype);
