@@ -16,9 +16,10 @@
 //                   pass with a running threshold when too many pass)
 //  tree_prep        in one launch: the row's top-M from its segment lists
 //                   (topm_merge when T1 runs alone), W1[:, :d] H for every
-//                   position on the fp64 matrix cores, and the per-call set-up
+//                   position on the fp64 matrix cores, the per-call set-up
 //                   (empty heaps; the anchor as each sequence's first node)
-//  bf16 weights: tree_gru_mfma (round 0's GRU step), then per round k one
+//                   and, with bf16 weights, round 0's GRU step
+//  bf16 weights, per round k one
 //   tree_round      round k's bottleneck, its score and pop, and round k+1's
 //                   GRU step, handing over through tagged words
 //  fp32 weights, per round:
@@ -452,29 +453,19 @@ __device__ __forceinline__ void tree_init(const TreeArgs& t) {
   }
 }
 
-// the H half at the anchor's depth (0) for round 0's bottleneck, by the first
-// workgroup of a round-0 GRU launch for its group of sequences
-__device__ __forceinline__ void zh_cur_anchor(const TreeArgs& t, int b0, int nb) {
-  for (int i = threadIdx.x; i < nb * t.r; i += blockDim.x) {
-    const int b = b0 + i / t.r, k = i % t.r;
-    t.zh_cur[(size_t)b * t.r + k] = t.zh[(size_t)b * t.P * t.r + k];
-  }
-}
-
-// After the top-M segments, in one launch: each row's merge of its segment
-// lists, the H half of the bottleneck in fp64 (tree_zh tiles) and the
-// per-call set-up, on workgroups of 8 waves (none depends on another).
-template <class W>
-__global__ __launch_bounds__(64 * kZhWaves) void tree_prep(TreeArgs t) {
-  const int rows = t.B * t.P, nzk = (t.r + 15) / 16, nzm = (rows + 15) / 16, wg = blockIdx.x;
-  if (wg < rows) {
-    merge_row(t.seg_keys, t.M, t.cand_idx, t.cand_val, wg);
-  } else if (wg < rows + nzk * nzm) {
-    const int z = wg - rows;
-    zh_tile<W>(t, z % nzk, z / nzk);
-  } else {
-    tree_init(t);
-  }
+// the node round 0 expands: the anchor, read from the first tokens (so that
+// round 0's GRU step need not wait for tree_init)
+__device__ __forceinline__ TreeCur anchor_cur(const TreeArgs& t, int b) {
+  TreeCur c;
+  c.slot = 0;
+  c.parent_slot = -1;
+  const int32_t t0 = t.t0[b];
+  c.token = t0 < 0 || t0 >= t.V ? 0 : t0;  // as tree_init reads it (which also flags it)
+  c.depth = 0;
+  c.expand = t.P > 0 ? 1 : 0;
+  c.node = -1;
+  c.score = 0.0;
+  return c;
 }
 
 // ---- fp64 GRU step of each sequence's current node -----------------------------------------
@@ -498,7 +489,6 @@ __global__ __launch_bounds__(1024) void tree_gru(TreeArgs t, int b0, int k) {
   double* hl = reinterpret_cast<double*>(lds);                      // [kTreeSeqs][Hs]
   unsigned char* xl = lds + (size_t)kTreeSeqs * Hs * sizeof(double);  // [kTreeSeqs][d] stored type
   if (threadIdx.x < nb) sc[threadIdx.x] = tree_cur(t, k)[b0 + threadIdx.x];
-  if (k == 0 && blockIdx.x == 0) zh_cur_anchor(t, b0, nb);
   __syncthreads();
   // stage every sequence's parent state and embedding row: batches of kStage
   // 16-byte pieces per thread are loaded before any is stored, so their
@@ -726,7 +716,7 @@ hipError_t launch_input_table_f64(int dtype, const void* E, const void* Wih, int
 
 
 
-constexpr int kGruWaves = 8;  // waves of tree_gru_mfma, splitting the k blocks
+constexpr int kGruWaves = 8;  // waves of a GRU-step workgroup (bf16 weights), splitting the k blocks
 constexpr int kGruPreI = 10;  // input-half blocks per wave whose loads are all issued up front
 constexpr int kGruPreH = 4;   // hidden-half blocks per wave whose loads are all issued up front
 
@@ -785,8 +775,7 @@ __device__ __forceinline__ void gru_mfma_step(const TreeArgs& t, int b0, int ite
     c.node = kr - 1;
     c.score = 0.0;
   } else {
-    c = tree_cur(t, kr)[b0 + sq];
-    if (kr == 0 && item == 0) zh_cur_anchor(t, b0, nb);
+    c = kr == 0 ? anchor_cur(t, b0 + sq) : tree_cur(t, kr)[b0 + sq];
   }
   const bool has_h = c.expand && c.parent_slot >= 0;
   const uint16_t* xr = (const uint16_t*)t.embed + (size_t)min(max(c.token, 0), t.V - 1) * d;
@@ -1045,10 +1034,6 @@ __device__ __forceinline__ void gru_tab_ll_step(const TreeArgs& t, int b0, int i
   }
 }
 
-template <bool kTab>
-__global__ __launch_bounds__(64 * kGruWaves) void tree_gru_mfma(TreeArgs t, int b0, int k) {
-  gru_mfma_step<kTab, false>(t, b0, blockIdx.x, k, 0u);
-}
 
 
 // ---- fp64 bottleneck of each sequence's current node: a = SiLU(W1 [H_delta ; S] + b1) -------
@@ -1063,8 +1048,8 @@ __device__ __forceinline__ void bottleneck_rows(const TreeArgs& t, int b, int k0
   const size_t ld = (size_t)t.d + Hs;
   const W* w1s = reinterpret_cast<const W*>(t.w1) + t.d;  // state half of W1
   // Nothing here reads the cursor: the node expanded in round kr has state
-  // slot kr, and the previous pop (or round 0's GRU launch) left the H half of its depth
-  // in zh_cur.  A sequence whose node is not expanded gets values that no
+  // slot kr, and the previous pop left the H half of its depth in zh_cur
+  // (round 0: the anchor, depth 0).  A sequence whose node is not expanded gets values that no
   // one reads.
   Run8<W> wr[U][4];
 #pragma unroll
@@ -1077,7 +1062,7 @@ __device__ __forceinline__ void bottleneck_rows(const TreeArgs& t, int b, int k0
   for (int u = 0; u < U; ++u) sv[u] = load_f64x8(st + min(lane * 8 + 512 * u, Hs - 8));
   // lane q < 4 finishes row k0 + q: its W1_H half and bias
   const int kq = min(k0 + (lane & 3), r - 1);
-  const double zq = t.zh_cur[(size_t)b * r + kq];
+  const double zq = kr == 0 ? t.zh[(size_t)b * t.P * r + kq] : t.zh_cur[(size_t)b * r + kq];
   const double bq = t.b1 ? (double)t.b1[kq] : 0.0;
   __builtin_amdgcn_sched_barrier(0);
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
@@ -1457,6 +1442,29 @@ __global__ __launch_bounds__(256) void tree_score_pop(TreeArgs t, int k) {
   score_pop<W, 4, false>(t, blockIdx.x, k, 0u);
 }
 
+// After the top-M segments, in one launch: each row's merge of its segment
+// lists, the H half of the bottleneck in fp64 (tree_zh tiles), the per-call
+// set-up and, with bf16 weights, round 0's GRU step (the anchor, whose token
+// is a first token and whose parent state is zero), on workgroups of 8 waves;
+// none reads what another writes.
+template <class W, bool kTab>
+__global__ __launch_bounds__(64 * kZhWaves) void tree_prep(TreeArgs t) {
+  static_assert(kZhWaves == kGruWaves, "one workgroup size for every part");
+  const int rows = t.B * t.P, nzk = (t.r + 15) / 16, nzm = (rows + 15) / 16, wg = blockIdx.x;
+  const int nz = rows + nzk * nzm;
+  if (wg < rows) {
+    merge_row(t.seg_keys, t.M, t.cand_idx, t.cand_val, wg);
+  } else if (wg < nz) {
+    const int z = wg - rows;
+    zh_tile<W>(t, z % nzk, z / nzk);
+  } else if (wg == nz) {
+    tree_init(t);
+  } else if constexpr (sizeof(W) == 2) {
+    const int g = wg - nz - 1, nu = (t.Hs + 3) / 4;
+    gru_mfma_step<kTab, false>(t, (g / nu) * kTreeSeqs, g - (g / nu) * nu, 0, 0u);
+  }
+}
+
 // ---- one launch per round (bf16 weights) ------------------------------------------------------
 // Launch k runs round k's bottleneck, its score and pop, and the GRU step of
 // round k + 1, in workgroups of 8 waves numbered in that order: ceil(r / 32)
@@ -1558,10 +1566,13 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
   hipLaunchKernelGGL(topm_segment, dim3(kTopSegs, t.B * t.P), dim3(256), 0, s, t.Lb, t.V, t.M, t.seg_keys, t.status,
                      reset_status ? 1 : 0);
   const int prep = t.B * t.P + (t.r + 15) / 16 * ((t.B * t.P + 15) / 16) + 1;
-  if (t.dtype == kBF16)
-    hipLaunchKernelGGL(tree_prep<uint16_t>, dim3(prep), dim3(64 * kZhWaves), 0, s, t);
+  const int ngr0 = (t.Hs + 3) / 4 * ((t.B + kTreeSeqs - 1) / kTreeSeqs);  // round 0's GRU workgroups (bf16)
+  if (t.dtype == kBF16 && t.xt)
+    hipLaunchKernelGGL((tree_prep<uint16_t, true>), dim3(prep + ngr0), dim3(64 * kZhWaves), 0, s, t);
+  else if (t.dtype == kBF16)
+    hipLaunchKernelGGL((tree_prep<uint16_t, false>), dim3(prep + ngr0), dim3(64 * kZhWaves), 0, s, t);
   else
-    hipLaunchKernelGGL(tree_prep<float>, dim3(prep), dim3(64 * kZhWaves), 0, s, t);
+    hipLaunchKernelGGL((tree_prep<float, false>), dim3(prep), dim3(64 * kZhWaves), 0, s, t);
   // bf16 weights: the GRU step on the fp64 matrix cores (static LDS only)
   const bool mfma = t.dtype == kBF16;
   const size_t lds = mfma ? 0 : tree_gru_lds(t.d, t.Hs, t.dtype);
@@ -1572,14 +1583,8 @@ hipError_t launch_tree(const TreeArgs& t, bool reset_status, hipStream_t s, hipE
     attr_lds = lds;
   }
   if (mfma) {
-    // bf16 weights: round 0's GRU step, then one launch per round (round k's
-    // bottleneck, score and pop, and round k + 1's GRU step)
-    for (int b0 = 0; b0 < t.B; b0 += kTreeSeqs) {
-      if (t.xt)
-        hipLaunchKernelGGL(tree_gru_mfma<true>, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), 0, s, t, b0, 0);
-      else
-        hipLaunchKernelGGL(tree_gru_mfma<false>, dim3((t.Hs + 3) / 4), dim3(64 * kGruWaves), 0, s, t, b0, 0);
-    }
+    // bf16 weights (round 0's GRU step ran in tree_prep): one launch per round
+    // (round k's bottleneck, score and pop, and round k + 1's GRU step)
     const int nbt = (t.r + 31) / 32 * t.B, ngr = (t.Hs + 3) / 4 * ((t.B + kTreeSeqs - 1) / kTreeSeqs);
     for (int k = 0; k < t.N; ++k) {
       const int grid = nbt + t.B + (k + 1 < t.N ? ngr : 0);
