@@ -184,9 +184,8 @@ __device__ __forceinline__ typename act<W>::type state_frag(const ChainArgs& a, 
   }
 }
 
-#ifndef DH_HIDDEN_SLEEP
-#define DH_HIDDEN_SLEEP 16
-#endif
+// s_sleep units between polls of the waits for the state off the critical path
+constexpr int kHiddenSleep = 16;
 
 // The same right operand from a hand-off slot with n elements per row
 // (bf16 weights: words [0, n/2) hold hi pairs, [n/2, n) lo pairs; fp32: one
@@ -360,7 +359,7 @@ __device__ __forceinline__ void gru_hidden_part(const ChainArgs& a, int p, int i
     }
     if constexpr (kLL) {  // h(p) was written at step p - 1; off the critical path, so polled gently
       const uint64_t* slot = a.ll_h + (size_t)p * B * Hs;
-      ll_wait<DH_HIDDEN_SLEEP>(a.status, [&] {
+      ll_wait<kHiddenSleep>(a.status, [&] {
         bool good = true;
 #pragma unroll
         for (int q = 0; q < U; ++q) {
@@ -871,12 +870,8 @@ __device__ __forceinline__ void bottleneck_item(const ChainArgs& a, int p, int i
 }
 
 // ---- phase O: W2 tiles [t_begin, t_end), base add, argmax ---------------------------
-#ifndef DH_O_EARLY
-#define DH_O_EARLY 2     // tiles of phase O issued before the activations are ready
-#endif
-#ifndef DH_W_SHARE
-#define DH_W_SHARE 3     // W2 share of a bottleneck workgroup, in eighths of the others'
-#endif
+constexpr int kOEarly = 2;  // tiles of phase O issued before the activations are ready
+constexpr int kWShare = 3;  // W2 share of a bottleneck workgroup, in eighths of the others'
 
 // Running argmax of one lane over the logits it has seen, in increasing
 // vocabulary order: the value and index of its first maximum (i < 0: none
@@ -893,9 +888,9 @@ __device__ __forceinline__ void lane_max(LaneMax& m, float L, int32_t idx, bool 
 __device__ __forceinline__ uint64_t lane_key(const LaneMax& m) { return m.i < 0 ? 0 : amax_key(m.v, (uint32_t)m.i); }
 
 // W2 tiles of workgroup `wg`: the bottleneck workgroups start phase O late,
-// so they take a smaller share (DH_W_SHARE / 8 of the others').
+// so they take a smaller share (kWShare / 8 of the others').
 __host__ __device__ inline void o_tile_range(int wg, int G, int nW, int T, int& t_begin, int& t_end) {
-  const int64_t wsh = DH_W_SHARE, units = (int64_t)nW * wsh + (int64_t)(G - nW) * 8;
+  const int64_t wsh = kWShare, units = (int64_t)nW * wsh + (int64_t)(G - nW) * 8;
   auto start_of = [&](int w) -> int64_t {
     const int64_t u = w <= nW ? (int64_t)w * wsh : (int64_t)nW * wsh + (int64_t)(w - nW) * 8;
     return (int64_t)T * u / units;
@@ -1337,12 +1332,12 @@ struct TileBuf {
 // any given one is fixed and the compiler's wait counts cover exactly the
 // tile being consumed; a buffer array indexed in a loop would instead be
 // rotated through register copies, each of which waits for its load.  The
-// first DH_O_EARLY tiles are issued before the activations exist (before
+// first kOEarly tiles are issued before the activations exist (before
 // `ready` in the stepwise schedule).
 template <class W, int RG, int KC, bool kWrite, bool kLL, class Ready, bool kSample = false>
 __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_begin, int t_end, uint64_t* sbest,
                                               Ready ready, uint32_t ep, uint32_t* act_s) {
-  static_assert(DH_O_EARLY >= 0 && DH_O_EARLY <= 2, "two tiles ahead");
+  static_assert(kOEarly >= 0 && kOEarly <= 2, "two tiles ahead");
   const int lane = opaque_lane(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15, kg = lane >> 4;
   const int t0 = t_begin + wv, n = t_end > t0 ? (t_end - t0 + 3) / 4 : 0;  // tiles of this wave
@@ -1354,13 +1349,13 @@ __device__ __forceinline__ bool logits_range_(const ChainArgs& a, int p, int t_b
     load_base_rows<RG, false>(a, p, t * 16 + row, kg, tb.lb, tb.b2);
   };
   TileBuf<W, RG, KC> s0, s1, s2;
-  if (DH_O_EARLY >= 1) issue(0, s0);
-  if (DH_O_EARLY >= 2) issue(1, s1);
+  if (kOEarly >= 1) issue(0, s0);
+  if (kOEarly >= 2) issue(1, s1);
   if constexpr (!kLL) {
     if (!ready()) return false;
   }
-  if (DH_O_EARLY < 1) issue(0, s0);
-  if (DH_O_EARLY < 2) issue(1, s1);
+  if (kOEarly < 1) issue(0, s0);
+  if (kOEarly < 2) issue(1, s1);
   if constexpr (kLL)
     stage_act_ll<W, KC>(a, p, ep, act_s);
   else
@@ -1932,21 +1927,15 @@ __global__ __launch_bounds__(256) void chain_persistent(ChainArgs a) {
     // W_hh h(p+1) for the next step: in the wait for the bottleneck, or, in
     // the bottleneck workgroups, after phase O
     const bool hidden = wg < nG && p + 1 < a.P;
-#ifndef DH_HIDDEN_LATE
     if (hidden && wg >= nW) gru_hidden_part<W, NCB, kGruLds, true>(a, p + 1, wg, gl, acc_h, ep);
-#endif
     // O: this workgroup's vocabulary tiles, then its argmax pairs
     if constexpr (NTW > 0)
       logits_resident<W, RG, KC, NTW, kSample>(a, p, t_begin, t_end, w2r, w2l, act_s, sbest, ep);
     else
       logits_range<W, RG, KC, true>(a, p, t_begin, t_end, sbest, [] { return true; }, ep, act_s);
     DH_STAMP(p, 5);
-#ifndef DH_HIDDEN_LATE
     if (hidden && wg < nW) gru_hidden_part<W, NCB, kGruLds, true>(a, p + 1, wg, gl, acc_h, ep);
     DH_STAMP(p, 15);
-#else
-    if (hidden) gru_hidden_part<W, NCB, kGruLds, true>(a, p + 1, wg, gl, acc_h, ep);
-#endif
   }
   ll_tokens_reduce(a, a.P - 1, ep, sred_t);
   if (wg == 0) {
@@ -2123,9 +2112,6 @@ static hipError_t launch_persistent(const ChainArgs& a, size_t lds_bytes, hipStr
               : launch_persistent_<W, RG, KC, kLds, NTW, false, kSample>(a, lds_bytes, s);
 }
 
-#ifndef DH_GRU16
-#define DH_GRU16 1
-#endif
 constexpr size_t kLdsBudget = 144 * 1024;  // dynamic LDS the persistent kernel may use (160 KB per CU)
 
 template <class W, int RG, int KC>
@@ -2169,7 +2155,7 @@ static hipError_t run_chain(const ChainArgs& a, int mode, hipStream_t s, bool& p
   const int nG = a.Hs / 4, nW = (a.r + 15) / 16, T = (a.V + 15) / 16;
   const int nO = T < cus ? T : (cus > 0 ? cus : 256);
   // phase G, bf16 weights: sixteen waves per work item
-  const bool gru16 = DH_GRU16 && sizeof(W) == 2;
+  const bool gru16 = sizeof(W) == 2;
   const bool tab = a.xt != nullptr;
   // the sixteen-wave GRU with the state staged in LDS (per-token table, more than 16
   // sequences, state within the LDS): 620 -> 605 us per block at 32 sequences, while

@@ -21,19 +21,15 @@
 
 namespace dh {
 
-#ifndef DH_STREAM_NT
-#define DH_STREAM_NT 2  // 16-column tiles per wave
-#endif
-#ifndef DH_STREAM_U
-#define DH_STREAM_U 4   // k chunks per batch of loads
-#endif
+constexpr int kStreamNT = 2;  // 16-column tiles per wave of gemm_stream
+constexpr int kStreamU = 4;   // k chunks per batch of loads
 
 // Each wave owns NT adjacent 16-column tiles and MT 16-row tiles of A, so one
 // A fragment feeds NT MFMAs and one B fragment MT MFMAs.
 template <class W, int MT, int NT>
 __global__ __launch_bounds__(256) void gemm_stream(const W* __restrict__ A, int lda, const W* __restrict__ B, int ldb,
                                                    float* __restrict__ C, int ldc, int M, int N, int K) {
-  constexpr int U = sizeof(W) == 2 ? DH_STREAM_U : (DH_STREAM_U > 2 ? DH_STREAM_U / 2 : 1);
+  constexpr int U = sizeof(W) == 2 ? kStreamU : (kStreamU > 2 ? kStreamU / 2 : 1);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n0 = (blockIdx.x * 4 + wv) * 16 * NT;
   if (n0 >= N) return;
@@ -88,12 +84,8 @@ __global__ __launch_bounds__(256) void gemm_stream(const W* __restrict__ A, int 
   }
 }
 
-#ifndef DH_R16_WAVES
-#define DH_R16_WAVES 16  // waves per workgroup of gemm_rows16
-#endif
-#ifndef DH_R16_U
-#define DH_R16_U 2       // k chunks per batch of loads in gemm_rows16
-#endif
+constexpr int kR16Waves = 16;  // waves per workgroup of gemm_rows16
+constexpr int kR16U = 2;       // k chunks per batch of loads in gemm_rows16
 
 // At most 16 rows of A (one draft block of one sequence): the product is
 // bound by reading B once, and what limits the rate is how evenly that read
@@ -323,12 +315,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_rows16_slab(const uint16_t* _
   }
 }
 
-#ifndef DH_WIDE_BK
-#define DH_WIDE_BK 64   // k depth of a stage of gemm_wide
-#endif
-#ifndef DH_WIDE_NBUF
-#define DH_WIDE_NBUF 2  // LDS stage buffers of gemm_wide
-#endif
+constexpr int kWideBK = 64;   // k depth of a stage of gemm_wide
+constexpr int kWideNBuf = 2;  // LDS stage buffers of gemm_wide
 
 // Many rows of A, bf16, K a multiple of BK.
 // Workgroup tile BM x BN (BM = 32 MT, BN = 64 NT), eight waves in 2 x 4, each
@@ -594,7 +582,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(const uint16_t* __restrict__ A
 template <class W>
 static hipError_t launch_stream(const W* A, int lda, const W* B, int ldb, float* C, int ldc, int M, int N, int K,
                                 hipStream_t s) {
-  constexpr int NT = DH_STREAM_NT;
+  constexpr int NT = kStreamNT;
   const int n_waves = (N + 16 * NT - 1) / (16 * NT);
   const int m_tiles = (M + 15) / 16;
   const int mt = m_tiles >= 4 ? 4 : (m_tiles >= 2 ? 2 : 1);
@@ -631,7 +619,7 @@ static hipError_t allow_lds(const void* fn, size_t bytes) {
 template <int MT, int NT>
 static hipError_t launch_wide(const uint16_t* A, int lda, const uint16_t* B, int ldb, float* C, int ldc, int M, int N,
                               int K, int cus, hipStream_t s) {
-  constexpr int BK = DH_WIDE_BK, NBUF = DH_WIDE_NBUF, BM = 2 * MT * 16, BN = 4 * NT * 16;
+  constexpr int BK = kWideBK, NBUF = kWideNBuf, BM = 2 * MT * 16, BN = 4 * NT * 16;
   constexpr size_t lds = (size_t)NBUF * (BM + BN) * BK * 2;
   static_assert(lds <= 160 * 1024, "LDS of a CU");
   const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
@@ -689,7 +677,7 @@ hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int 
                            lda, (const uint16_t*)B, ldb, C, ldc, M, N, K);
       return hipGetLastError();
     }
-    constexpr int WV = DH_R16_WAVES;
+    constexpr int WV = kR16Waves;
     const size_t lds = (size_t)((K + 31) / 32) * 64 * 16;
     if (cus > 0 && (N + 15) / 16 >= WV * cus && lds <= 128 * 1024) {
       static thread_local int attr_device = -1;
@@ -697,12 +685,12 @@ hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int 
       hipError_t e = hipGetDevice(&dev);
       if (e != hipSuccess) return e;
       if (attr_device != dev) {
-        e = hipFuncSetAttribute((const void*)gemm_rows16<WV, DH_R16_U>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        e = hipFuncSetAttribute((const void*)gemm_rows16<WV, kR16U>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 128 * 1024);
         if (e != hipSuccess) return e;
         attr_device = dev;
       }
-      hipLaunchKernelGGL((gemm_rows16<WV, DH_R16_U>), dim3(cus), dim3(64 * WV), lds, s, (const uint16_t*)A, lda,
+      hipLaunchKernelGGL((gemm_rows16<WV, kR16U>), dim3(cus), dim3(64 * WV), lds, s, (const uint16_t*)A, lda,
                          (const uint16_t*)B, ldb, C, ldc, M, N, K);
       return hipGetLastError();
     }
@@ -711,7 +699,7 @@ hipError_t launch_gemm_nt(int dtype, const void* A, int lda, const void* B, int 
   // 256 rows takes 320 columns, so that the 475 column tiles need at most two
   // rounds of the CUs (256 columns leave a third, partial round); above 256
   // rows the 256 x 256 tile is faster.
-  if (prefer_tiles && M > 16 && K % DH_WIDE_BK == 0 && lda % 8 == 0 && ldb % 8 == 0) {
+  if (prefer_tiles && M > 16 && K % kWideBK == 0 && lda % 8 == 0 && ldb % 8 == 0) {
     const int cus = device_cus();
     const uint16_t *a16 = (const uint16_t*)A, *b16 = (const uint16_t*)B;
     if (cus > 0 && M > 256) return launch_wide<8, 4>(a16, lda, b16, ldb, C, ldc, M, N, K, cus, s);
