@@ -305,7 +305,10 @@ domino_status domino_tree_candidates(const domino_dims *dims, const float *base_
  * limit.
  * workspace (device): domino_workspace_size(dims, batch, DOMINO_OP_TREE,
  * nodes, topm) bytes; device status 1 = a first token was outside [0, V)
- * and token 0 was used.
+ * and token 0 was used; 2 = with bf16 weights, where each round runs as one
+ * launch whose workgroups hand results to higher-numbered ones through the
+ * workspace, such a wait gave up after 2 s (the outputs are then undefined).
+ * Calls on one workspace must not overlap.
  */
 domino_status domino_tree_draft(const domino_dims *dims, const domino_weights *weights, const void *H,
                                 const float *base_logits, const int32_t *first_tokens, int32_t batch, int32_t nodes,
