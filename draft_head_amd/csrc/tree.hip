@@ -121,14 +121,28 @@ __device__ void topm_scan_iterative(const float* __restrict__ x, int v_begin, in
   for (int j = threadIdx.x; j < M; j += blockDim.x) out[j] = buf[j];
 }
 
+// Order-preserving 32-bit image of a value, the high word of amax_key before
+// -0.0 is folded: -0.0 maps to 0x7FFFFFFF, +0.0 to 0x80000000 (topm_fold).
+__device__ __forceinline__ uint32_t topm_image(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t topm_fold(uint32_t img) { return img == 0x7FFFFFFFu ? 0x80000000u : img; }
+// element e of a row through a 32-bit byte offset from the row's start
+__device__ __forceinline__ float topm_at(const float* x, int e) {
+  return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(x) + (uint32_t)e * 4u);
+}
+
 // Top M keys of one row segment, sorted, key 0 = none.  Two passes over the
-// segment.  Pass 1: every thread's largest key; within each wave the
-// ceil(M/4)-th largest of these maxima is reached by at least ceil(M/4)
-// distinct elements, so the smallest of the four waves' values, tau, is
-// reached by at least M elements and cannot exceed the segment's M-th key.
-// Pass 2 collects every key >= tau (for typical data a few times M), which
-// are then sorted.  More candidates than the LDS buffer holds send the
-// segment to topm_scan_iterative.
+// segment.  Pass 1: every thread takes one of its elements (its largest
+// value image); within each wave the ceil(M/4)-th largest of these keys is
+// reached by at least ceil(M/4) distinct elements, so the smallest of the
+// four waves' values, tau, is reached by at least M elements and cannot
+// exceed the segment's M-th key (for any choice of elements; the largest
+// makes it tight).  Pass 2 collects every key >= tau (for typical data a few
+// times M), which are then sorted; it compares value images first and forms
+// the whole key only where the image can reach tau.  More candidates than
+// the LDS buffer holds send the segment to topm_scan_iterative.
 __global__ __launch_bounds__(256) void topm_segment(const float* __restrict__ Lb, int V, int M, uint64_t* seg_keys,
                                                     int32_t* status, int reset_status) {
   __shared__ uint64_t buf[kTopCap];
@@ -146,18 +160,35 @@ __global__ __launch_bounds__(256) void topm_segment(const float* __restrict__ Lb
     for (int j = threadIdx.x; j < M; j += blockDim.x) out[j] = 0;
     return;
   }
-  // pass 1 (loads from clamped addresses, kTopInFlight in flight per thread)
-  uint64_t mk = 0;
-  for (int v0 = v_begin; v0 < v_end; v0 += kTopInFlight * 256) {
-    float f[kTopInFlight];
+  // kTopInFlight reads in flight per thread; the last, partial, block of a
+  // segment reads from clamped addresses
+  auto load_block = [&](int v0, bool full, float (&f)[kTopInFlight]) {
+    if (full) {
 #pragma unroll
-    for (int q = 0; q < kTopInFlight; ++q) f[q] = x[min(v0 + q * 256 + (int)threadIdx.x, v_end - 1)];
+      for (int q = 0; q < kTopInFlight; ++q) f[q] = topm_at(x, v0 + q * 256 + (int)threadIdx.x);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kTopInFlight; ++q) f[q] = topm_at(x, min(v0 + q * 256 + (int)threadIdx.x, v_end - 1));
+    }
+  };
+  // pass 1
+  uint32_t bu = 0;
+  int bi = -1;
+  for (int v0 = v_begin; v0 < v_end; v0 += kTopInFlight * 256) {
+    const bool full = v0 + kTopInFlight * 256 <= v_end;
+    float f[kTopInFlight];
+    load_block(v0, full, f);
 #pragma unroll
     for (int q = 0; q < kTopInFlight; ++q) {
       const int v = v0 + q * 256 + threadIdx.x;
-      if (v < v_end) mk = umax64(mk, amax_key(f[q], (uint32_t)v));
+      const uint32_t u = topm_image(f[q]);
+      if ((full || v < v_end) && u > bu) {
+        bu = u;
+        bi = v;
+      }
     }
   }
+  uint64_t mk = bi < 0 ? 0 : ((uint64_t)topm_fold(bu) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)bi);
   // descending bitonic sort of the 64 maxima across the wave
   for (int size = 2; size <= 64; size <<= 1)
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -172,18 +203,23 @@ __global__ __launch_bounds__(256) void topm_segment(const float* __restrict__ Lb
   __syncthreads();
   uint64_t tau = wq[0];
   for (int w = 1; w < (int)(blockDim.x >> 6); ++w) tau = wq[w] < tau ? wq[w] : tau;
-  // pass 2: every key >= tau
+  // pass 2: every key >= tau.  A key reaches tau only if its folded image
+  // reaches tau's high word tu, that is, only if the unfolded image reaches tu2.
+  const uint32_t tu = (uint32_t)(tau >> 32), tu2 = tu == 0x80000000u ? 0x7FFFFFFFu : tu;
   for (int v0 = v_begin; v0 < v_end; v0 += kTopInFlight * 256) {
+    const bool full = v0 + kTopInFlight * 256 <= v_end;
     float f[kTopInFlight];
-#pragma unroll
-    for (int q = 0; q < kTopInFlight; ++q) f[q] = x[min(v0 + q * 256 + (int)threadIdx.x, v_end - 1)];
+    load_block(v0, full, f);
 #pragma unroll
     for (int q = 0; q < kTopInFlight; ++q) {
       const int v = v0 + q * 256 + threadIdx.x;
-      const uint64_t k = amax_key(f[q], (uint32_t)v);
-      if (v < v_end && k >= tau && k != 0) {
-        const int pos = atomicAdd(&count, 1);
-        if (pos < kTopCap) buf[pos] = k;
+      const uint32_t u = topm_image(f[q]);
+      if ((full || v < v_end) && u >= tu2) {
+        const uint64_t k = ((uint64_t)topm_fold(u) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
+        if (k >= tau && k != 0) {
+          const int pos = atomicAdd(&count, 1);
+          if (pos < kTopCap) buf[pos] = k;
+        }
       }
     }
   }

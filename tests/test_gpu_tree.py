@@ -166,7 +166,7 @@ def test_tree_full_size_after_gpu_base_logits():
 
 
 @pytest.mark.parametrize("kind", ["random", "ties", "constant", "ascending", "small_v", "wide", "wide_m256",
-                                  "wide_m1", "one_wave_heavy"])
+                                  "wide_m1", "one_wave_heavy", "signed_zero_max"])
 def test_candidates_match_oracle_topm(kind):
     say(f"case top-M {kind}")
     B, P, V, M = 2, 3, 5003, 64
@@ -188,6 +188,13 @@ def test_candidates_match_oracle_topm(kind):
         Lb = (np.round(rng.standard_normal((B, P, V)) * 2) / 2).astype(np.float32)
         Lb[0, 0, :10] = -0.0
         Lb[0, 0, 10:20] = 0.0
+    elif kind == "signed_zero_max":
+        # the largest value is zero, stored as -0.0 and +0.0 in turn, so the
+        # threshold sits exactly at zero and -0.0 must count as +0.0
+        Lb = -np.abs(rng.standard_normal((B, P, V))).astype(np.float32) - np.float32(1e-3)
+        v = np.arange(V)
+        Lb[:, :, v % 7 == 0] = -0.0
+        Lb[:, :, v % 7 == 3] = 0.0
     elif kind == "constant":
         Lb = np.full((B, P, V), 0.25, np.float32)
     elif kind == "ascending":
